@@ -1,0 +1,422 @@
+"""Plain CPU oracle for speculative-sampling verification (TEST INFRASTRUCTURE ONLY).
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark may import this
+module.  The product path (the HIP library and its Python binding) never calls it and shares
+no code with it.
+
+Everything is computed in float64 with numpy, one row / one sequence at a time, in vocabulary
+index order, so that each step can be checked against the pages by eye.  Notation follows the
+page "Accelerating Large Language Model Decoding with Speculative Sampling" (Chen et al.
+notes): q is the TARGET model's distribution, p the DRAFT model's, x~ a draft token, K the
+number of draft tokens per call.  The page on "Fast Inference from Transformers via
+Speculative Decoding" (Leviathan et al. blog) uses the opposite letters; its formulas are
+restated here in the q=target / p=draft convention.
+
+Where the pages leave a step open, the reading used is stated next to the step.
+
+Pinning status: every public function here is pinned by tests under ``tests/`` that compare it
+with closed forms, brute force, library routines or values printed on the pages.
+``expected_tokens_per_call`` and ``walltime_speedup`` / ``ops_factor`` are pinned to the values
+printed on the Leviathan page (App. E figures); no function is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "row_distribution",
+    "accept_probability",
+    "residual_weights",
+    "inverse_cdf",
+    "inverse_cdf_margin",
+    "verify_sequence",
+    "verify_sequence_trials",
+    "spec_verify",
+    "sample_rows",
+    "tree_verify",
+    "expected_tokens_per_call",
+    "walltime_speedup",
+    "ops_factor",
+]
+
+
+# ---------------------------------------------------------------------------------------------
+# Per-row distribution: temperature, then top-k, then top-p.
+#
+# Page "Accelerating Large Language Model Decoding with Speculative Sampling", section A2
+# (方法细节), paragraph on compatibility with standard sampling methods: nucleus, top-k and
+# temperature are applied to the probabilities before the rejection scheme.  The Leviathan blog,
+# section 方法细节 ("标准化采样框架"), says the same: argmax, top-k, nucleus and temperature are
+# all a standard draw from an adjusted distribution.
+#
+# Readings (the pages are silent on these details):
+#   * order: temperature -> top-k -> top-p, the same parameters for q and p;
+#   * temperature 0 means argmax (one-hot, lowest index wins ties);
+#   * top-k keeps every logit >= the k-th largest logit (ties at the boundary all kept);
+#   * top-p keeps the smallest prefix of the probabilities sorted in decreasing order whose
+#     running sum reaches P, plus every token tied with the last one taken, and renormalises;
+#     when top-k is also on, top-p acts on the renormalised top-k distribution.
+# ---------------------------------------------------------------------------------------------
+def row_distribution(z, temperature, top_k=0, top_p=1.0, diagnostics=None):
+    """Return the float64 probability vector of one row of logits ``z``.
+
+    ``temperature``, ``top_p`` are used as float64 values of whatever the caller passes (the
+    tests pass float32 values, the same numbers the GPU library receives).  ``diagnostics``,
+    if a dict, receives ``topp_margin``: the distance of the running sum from P at the top-p
+    boundary (min over the last excluded and the first included prefix), which says how close
+    a floating-point decision was.
+    """
+    z = np.asarray(z, dtype=np.float64).ravel()
+    V = z.size
+    T = float(temperature)
+    if diagnostics is not None:
+        diagnostics["topp_margin"] = np.inf
+
+    if T == 0.0:
+        prob = np.zeros(V)
+        prob[int(np.argmax(z))] = 1.0  # np.argmax returns the first occurrence of the maximum
+        return prob
+
+    keep = np.ones(V, dtype=bool)
+    k = int(top_k)
+    if 0 < k < V:
+        t_k = np.partition(z, V - k)[V - k]  # k-th largest logit, counted with multiplicity
+        keep = z >= t_k
+
+    y = np.full(V, -np.inf)
+    y[keep] = z[keep] / T
+    m = y[keep].max()
+    e = np.zeros(V)
+    e[keep] = np.exp(y[keep] - m)
+    prob = e / e.sum()
+
+    P = float(top_p)
+    if P < 1.0:
+        idx = np.arange(V)
+        order = np.lexsort((idx, -prob))  # probability descending, index ascending on ties
+        c = np.cumsum(prob[order])
+        reached = np.nonzero(c >= P)[0]
+        if reached.size:
+            j_star = int(reached[0])
+        else:  # rounding left the total just below P: take every kept token
+            j_star = int(np.count_nonzero(prob > 0)) - 1
+        t_p = prob[order[j_star]]
+        if diagnostics is not None:
+            before = c[j_star - 1] if j_star > 0 else 0.0
+            diagnostics["topp_margin"] = float(min(abs(before - P), abs(c[j_star] - P)))
+        keep_p = (prob >= t_p) & (prob > 0)
+        prob = np.where(keep_p, prob, 0.0)
+        prob = prob / prob.sum()
+    return prob
+
+
+# ---------------------------------------------------------------------------------------------
+# Accept test.  Chen et al. notes, A2 "改进的拒绝采样": a draft token x~ drawn from p is kept
+# with probability min(1, q(x~)/p(x~)).  Leviathan blog, 扩展方向 / App. F (lenience): the
+# comparison is made after scaling, i.e. keep with probability min(1, q/(l p)), 0 < l <= 1.
+# Edge cases (reading): p(x~)=0<q(x~) -> 1; p(x~)=q(x~)=0 -> 0 (an impossible token is rejected).
+# ---------------------------------------------------------------------------------------------
+def accept_probability(q_x, p_x, lenience=1.0):
+    """min(1, q/(l*p)) with the edge cases above; works on scalars or arrays."""
+    q_x = np.asarray(q_x, dtype=np.float64)
+    p_x = np.asarray(p_x, dtype=np.float64)
+    l = float(lenience)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(p_x > 0, q_x / (l * np.where(p_x > 0, p_x, 1.0)), 0.0)
+    a = np.where(p_x > 0, np.minimum(1.0, ratio), np.where(q_x > 0, 1.0, 0.0))
+    return a if a.ndim else float(a)
+
+
+# ---------------------------------------------------------------------------------------------
+# Residual distribution.  Chen et al. notes, A2 and Theorem 1: after a rejection the token is
+# redrawn from (q - p)_+ where (f)_+ = max(0, f) / sum_x max(0, f).
+# Reading: if the sum is 0 (q == p up to rounding, so a rejection had probability 0 in exact
+# arithmetic) the draw falls back to q itself; the fallback is reported.
+# With lenience the residual is left unchanged (App. F only changes the comparison).
+# ---------------------------------------------------------------------------------------------
+def residual_weights(q, p):
+    """Return (w, fell_back): unnormalised weights max(0, q - p), or q if they sum to 0."""
+    q = np.asarray(q, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    w = np.maximum(0.0, q - p)
+    if not w.sum() > 0.0:
+        return q.copy(), True
+    return w, False
+
+
+# ---------------------------------------------------------------------------------------------
+# Inverse-CDF draw of one index from unnormalised weights w with a uniform u in [0, 1).
+# Reading (the pages only say "sample from"): cumulative sums C_i in vocabulary index order,
+# W = C_{V-1}; the token is the smallest i with C_i > u*W; if rounding runs past the end, the
+# last index with positive weight.
+# ---------------------------------------------------------------------------------------------
+def inverse_cdf(w, u):
+    """Draw index/indices from weights ``w`` (1-D) using uniform(s) ``u`` (scalar or array).
+
+    Because C is non-decreasing, the smallest i with C_i > u*W equals the number of i with
+    C_i <= u*W; that count is what is computed here.
+    """
+    w = np.asarray(w, dtype=np.float64)
+    C = np.cumsum(w)
+    W = C[-1]
+    u_arr = np.atleast_1d(np.asarray(u, dtype=np.float64)).ravel()
+    target = u_arr * W
+    out = np.empty(u_arr.size, dtype=np.int64)
+    block = max(1, 4_000_000 // max(1, w.size))
+    for s0 in range(0, u_arr.size, block):
+        s1 = min(u_arr.size, s0 + block)
+        out[s0:s1] = np.count_nonzero(C[None, :] <= target[s0:s1, None], axis=1)
+    positive = np.nonzero(w > 0)[0]
+    last_positive = int(positive[-1]) if positive.size else w.size - 1
+    out[out >= w.size] = last_positive
+    return out.reshape(np.shape(u)) if np.ndim(u) else int(out[0])
+
+
+def inverse_cdf_margin(w, u, tok):
+    """How far u*W lies outside the CDF interval [C_{tok-1}, C_tok) of ``tok``, relative to W.
+
+    0 means ``tok`` is exactly the inverse-CDF draw; a small positive value means ``tok`` would
+    be the draw if u moved by that much (used to classify boundary flips).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    C = np.cumsum(w)
+    W = C[-1]
+    if not (0 <= tok < w.size) or W <= 0:
+        return np.inf
+    lo = C[tok - 1] if tok > 0 else 0.0
+    hi = C[tok]
+    target = float(u) * W
+    if lo <= target < hi:
+        return 0.0
+    return float(min(abs(target - lo), abs(target - hi)) / W)
+
+
+# ---------------------------------------------------------------------------------------------
+# One verification step for one sequence (Chen et al. notes, A2 "改进的拒绝采样" and the bonus
+# token paragraph; Leviathan blog, 基准设计 "草稿-验收-修正"):
+#   for k = 0..K-1: a_k = accept probability of x~_k at position k; accept iff u_k < a_k;
+#   n = first k that is not accepted (K if all are);
+#   n < K: draw from the residual of position n with u_K;  n = K: draw the bonus token from the
+#   target distribution of position K with u_K.
+# Readings: one fresh uniform per accept test plus one for the final draw (u has K+1 entries);
+#   strict comparison u < a, u in [0,1), so p == q always accepts; a draft token outside
+#   [0, V) has p = q = 0 and is rejected.
+# ---------------------------------------------------------------------------------------------
+def _verify_core(q_rows, p_rows, drafts, u, lenience):
+    K = len(drafts)
+    V = q_rows[0].size
+    q_x = np.zeros(K)
+    p_x = np.zeros(K)
+    for k in range(K):
+        x = int(drafts[k])
+        if 0 <= x < V:
+            q_x[k] = q_rows[k][x]
+            p_x[k] = p_rows[k][x]
+    a = accept_probability(q_x, p_x, lenience) if K else np.zeros(0)
+    a = np.atleast_1d(a)
+    n = K
+    for k in range(K):
+        if not (float(u[k]) < a[k]):
+            n = k
+            break
+    if n < K:
+        w, fell_back = residual_weights(q_rows[n], p_rows[n])
+    else:
+        w, fell_back = np.asarray(q_rows[K], dtype=np.float64), False
+    tok = inverse_cdf(w, float(u[K]))
+    margin = inverse_cdf_margin(w, float(u[K]), tok)
+    tokens = np.full(K + 1, -1, dtype=np.int64)
+    tokens[:n] = np.asarray(drafts[:n], dtype=np.int64)
+    tokens[n] = tok
+    return {
+        "tokens": tokens,
+        "n": n,
+        "a": a,
+        "q_x": q_x,
+        "p_x": p_x,
+        "fallback": fell_back,
+        "weights": w,
+        "draw_margin": margin,
+    }
+
+
+def verify_sequence(q_rows, p_rows, drafts, u, lenience=1.0):
+    """Verify one sequence given its processed distributions.
+
+    q_rows: K+1 target probability vectors; p_rows: at least K draft probability vectors;
+    drafts: K draft tokens; u: K+1 uniforms.  Returns a dict with tokens (K+1, -1 padded),
+    n (accepted count), a, q_x, p_x (per position), fallback, weights of the final draw and
+    draw_margin (0 unless the draw sits on a CDF boundary).
+    """
+    q_rows = [np.asarray(r, dtype=np.float64) for r in q_rows]
+    p_rows = [np.asarray(r, dtype=np.float64) for r in p_rows]
+    return _verify_core(q_rows, p_rows, list(drafts), list(u), lenience)
+
+
+def verify_sequence_trials(q_rows, p_rows, drafts, u, lenience=1.0):
+    """Many independent trials of one sequence with fixed rows (for statistical pins).
+
+    drafts: [T, K] int, u: [T, K+1].  Same steps as ``verify_sequence``; each numpy call acts
+    on all trials at once.  Returns (n [T], first emitted token [T], emitted tokens [T, K+1]).
+    """
+    q_rows = [np.asarray(r, dtype=np.float64) for r in q_rows]
+    p_rows = [np.asarray(r, dtype=np.float64) for r in p_rows]
+    drafts = np.asarray(drafts, dtype=np.int64)
+    u = np.asarray(u, dtype=np.float64)
+    trials, K = drafts.shape
+    a = np.zeros((trials, K))
+    for k in range(K):
+        x = drafts[:, k]
+        a[:, k] = accept_probability(q_rows[k][x], p_rows[k][x], lenience)
+    accepted = u[:, :K] < a
+    rejected_any = ~accepted
+    n = np.where(rejected_any.any(axis=1), rejected_any.argmax(axis=1), K)
+    final = np.empty(trials, dtype=np.int64)
+    for pos in range(K + 1):
+        sel = n == pos
+        if not sel.any():
+            continue
+        if pos < K:
+            w, _ = residual_weights(q_rows[pos], p_rows[pos])
+        else:
+            w = q_rows[K]
+        final[sel] = inverse_cdf(w, u[sel, K])
+    tokens = np.full((trials, K + 1), -1, dtype=np.int64)
+    for pos in range(K + 1):
+        sel = n == pos
+        tokens[sel, :pos] = drafts[sel, :pos]
+        tokens[sel, pos] = final[sel]
+    return n, tokens[:, 0], tokens
+
+
+def spec_verify(target_logits, draft_logits, drafts, uniforms, temperature=1.0, top_k=0,
+                top_p=1.0, lenience=1.0):
+    """Batch verification: target [B, K+1, V], draft [B, >=K, V], drafts [B, K], uniforms [B, K+1].
+
+    Returns a dict of arrays: tokens [B, K+1], n [B], a / q_x / p_x [B, K], fallback [B],
+    draw_margin [B], topp_margin_t [B, K+1], topp_margin_d [B, K].
+    """
+    target_logits = np.asarray(target_logits)
+    draft_logits = np.asarray(draft_logits)
+    drafts = np.asarray(drafts)
+    uniforms = np.asarray(uniforms)
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    out = {
+        "tokens": np.full((B, K + 1), -1, dtype=np.int64),
+        "n": np.zeros(B, dtype=np.int64),
+        "a": np.zeros((B, K)),
+        "q_x": np.zeros((B, K)),
+        "p_x": np.zeros((B, K)),
+        "fallback": np.zeros(B, dtype=bool),
+        "draw_margin": np.zeros(B),
+        "topp_margin_t": np.full((B, K + 1), np.inf),
+        "topp_margin_d": np.full((B, K), np.inf),
+    }
+    for b in range(B):
+        q_rows, p_rows = [], []
+        for k in range(K + 1):
+            d = {}
+            q_rows.append(row_distribution(target_logits[b, k], temperature, top_k, top_p, d))
+            out["topp_margin_t"][b, k] = d["topp_margin"]
+        for k in range(K):
+            d = {}
+            p_rows.append(row_distribution(draft_logits[b, k], temperature, top_k, top_p, d))
+            out["topp_margin_d"][b, k] = d["topp_margin"]
+        r = _verify_core(q_rows, p_rows, list(drafts[b]), list(uniforms[b]), lenience)
+        out["tokens"][b] = r["tokens"]
+        out["n"][b] = r["n"]
+        out["a"][b] = r["a"]
+        out["q_x"][b] = r["q_x"]
+        out["p_x"][b] = r["p_x"]
+        out["fallback"][b] = r["fallback"]
+        out["draw_margin"][b] = r["draw_margin"]
+    return out
+
+
+def sample_rows(logits, u, temperature=1.0, top_k=0, top_p=1.0):
+    """Draw one token per row of ``logits`` [R, V] from its processed distribution (draft draw).
+
+    This is the draft model's own sampling step (Chen et al. notes, A1: the draft model samples
+    K tokens autoregressively), done with the same inverse-CDF rule as the final draw.
+    """
+    logits = np.asarray(logits)
+    R = logits.shape[0]
+    out = np.empty(R, dtype=np.int64)
+    for r in range(R):
+        prob = row_distribution(logits[r], temperature, top_k, top_p)
+        out[r] = inverse_cdf(prob, float(u[r]))
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# Greedy token-tree verification (REST article, section "REST: 基于检索的投机解码"): the drafts
+# form a tree laid out as a BFS pseudo-sequence; one target forward scores every node; a draft
+# token is accepted exactly when it equals the token the target model would emit greedily.
+# Readings: node 0 is the root (the last committed token); parents precede children
+# (0 <= parent[n] < n for n >= 1), anything else marks the node as not accepted; a node deeper
+# than max_depth is not accepted; argmax ties go to the lowest vocabulary index; among the
+# deepest accepted nodes the lowest node index wins.  Output: the tokens on the root->d path
+# (root excluded), then the bonus argmax of node d's row.
+# ---------------------------------------------------------------------------------------------
+def tree_verify(target_logits, parent, node_tokens, max_depth):
+    """target_logits [B, N, V]; parent, node_tokens [B, N]; returns tokens [B, max_depth+1],
+    n [B] (depth of the deepest accepted node) and last_node [B]."""
+    target_logits = np.asarray(target_logits)
+    parent = np.asarray(parent, dtype=np.int64)
+    node_tokens = np.asarray(node_tokens, dtype=np.int64)
+    B, N, V = target_logits.shape
+    tokens = np.full((B, max_depth + 1), -1, dtype=np.int64)
+    n_acc = np.zeros(B, dtype=np.int64)
+    last = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        g = [int(np.argmax(np.asarray(target_logits[b, i], dtype=np.float64))) for i in range(N)]
+        accepted = [False] * N
+        depth = [0] * N
+        accepted[0] = True
+        for i in range(1, N):
+            par = int(parent[b, i])
+            if not (0 <= par < i):
+                continue
+            depth[i] = depth[par] + 1
+            accepted[i] = (accepted[par] and depth[i] <= max_depth
+                           and int(node_tokens[b, i]) == g[par])
+        best = 0
+        for i in range(N):
+            if accepted[i] and depth[i] > depth[best]:
+                best = i
+        path = []
+        i = best
+        while i != 0:
+            path.append(int(node_tokens[b, i]))
+            i = int(parent[b, i])
+        path.reverse()
+        tokens[b, : len(path)] = path
+        tokens[b, len(path)] = g[best]
+        n_acc[b] = len(path)
+        last[b] = best
+    return {"tokens": tokens, "n": n_acc, "last_node": last}
+
+
+# ---------------------------------------------------------------------------------------------
+# Analytics (Leviathan blog, section 方法细节: expected tokens per call, wall-clock factor and
+# operation count; App. E figures).  With i.i.d. acceptance rate alpha and gamma = K drafts:
+#   E[#tokens] = (1 - alpha^(K+1)) / (1 - alpha)
+#   wall-clock factor = (1 - alpha^(K+1)) / ((1 - alpha) (K c + 1)), c = draft/target cost
+#   operations factor = (1 - alpha) (K c_hat + K + 1) / (1 - alpha^(K+1))
+# ---------------------------------------------------------------------------------------------
+def expected_tokens_per_call(alpha, K):
+    """Expected tokens emitted per target call (accepted drafts + the one drawn token)."""
+    alpha = float(alpha)
+    if alpha == 1.0:
+        return float(K + 1)
+    return (1.0 - alpha ** (K + 1)) / (1.0 - alpha)
+
+
+def walltime_speedup(alpha, K, c):
+    return expected_tokens_per_call(alpha, K) / (K * float(c) + 1.0)
+
+
+def ops_factor(alpha, K, c_hat):
+    return (K * float(c_hat) + K + 1.0) / expected_tokens_per_call(alpha, K)
