@@ -1,0 +1,154 @@
+/*
+ * spec_verify.h -- C ABI of libspecverify.so, the verify-and-resample step of speculative
+ * sampling on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (notation of the page "Accelerating Large Language Model Decoding with
+ * Speculative Sampling", Chen et al. notes: q = TARGET distribution, p = DRAFT distribution,
+ * x~ = draft token, K = draft tokens per call):
+ *
+ *   1. Every logit row is turned into a distribution by temperature, then top-k, then top-p
+ *      (section A2, compatibility with standard sampling methods; the Leviathan blog's
+ *      section on the standardised sampling framework says the same).  Temperature 0 means
+ *      argmax.  Top-k keeps every logit >= the k-th largest (ties kept); top-p keeps the
+ *      smallest decreasing-probability prefix whose mass reaches P plus every token tied with
+ *      its last member, and renormalises; top-p acts after top-k.
+ *   2. Draft token k is accepted with probability a_k = min(1, q_k(x~_k) / (l * p_k(x~_k)))
+ *      (section A2, modified rejection sampling; lenience l from the Leviathan blog, App. F),
+ *      decided as u[b,k] < a_k.  p = 0 < q gives a = 1; p = q = 0 gives a = 0.
+ *   3. n = the first rejected position (K if none).
+ *   4. n < K: the token at position n is drawn from (q_n - p_n)_+ (Theorem 1); if that has
+ *      zero mass, from q_n.  n = K: a bonus token is drawn from q_K (section A2, the remark
+ *      that a call yields up to K+1 tokens).  The draw is the inverse CDF in vocabulary index
+ *      order with u[b,K]: the smallest i whose cumulative weight exceeds u * (total weight).
+ *
+ * spec_verify_tree is the greedy exact-match rule for a token tree laid out in BFS order (the
+ * REST article, section on retrieval-based speculative decoding): a node is accepted iff its
+ * parent is accepted and its token equals the argmax of the parent's target row.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are caller-owned DEVICE memory, row-major and contiguous along V.
+ *     Scalars and sv_sampling are host values.
+ *   - The library allocates nothing and never synchronises.  All work is enqueued on
+ *     `stream`; outputs are valid once the caller synchronises with that stream.
+ *   - Arguments are checked on the host before anything is enqueued; on an error status
+ *     nothing is enqueued and the outputs are untouched.  A failed kernel launch returns
+ *     SV_ERR_LAUNCH.  Device data (tokens, parents) is not checked on the host; the rules for
+ *     out-of-range device values are stated per argument.
+ *   - Logits must be finite or -inf, and every row needs at least one finite logit.
+ *   - `workspace` is caller-owned device memory of at least *_workspace_size() bytes.  It
+ *     needs no initialisation; calls that share a workspace must be ordered on one stream.
+ *   - The library keeps no global state and is deterministic: equal inputs give bitwise equal
+ *     outputs (fixed-order reductions, no floating-point atomics).
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SV_OK = 0,
+  SV_ERR_INVALID_ARG = 1,          /* a size, pointer or sampling parameter is out of range */
+  SV_ERR_UNSUPPORTED_DTYPE = 2,    /* dtype is not SV_DTYPE_F32 / SV_DTYPE_BF16 */
+  SV_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < the matching *_workspace_size() */
+  SV_ERR_LAUNCH = 4                /* a kernel launch failed (hipGetLastError) */
+} sv_status;
+
+typedef enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 } sv_dtype;
+
+/* Sampling parameters, applied identically to q and p (Chen et al. notes, A2). */
+typedef struct {
+  float temperature; /* >= 0.  0 = argmax (lowest index on ties) */
+  int32_t top_k;     /* >= 0.  0, or >= V, = off */
+  float top_p;       /* in (0, 1].  1 = off */
+  float lenience;    /* in (0, 1].  1 = the lossless rule; < 1 = App. F of the Leviathan blog */
+} sv_sampling;
+
+/* Bytes of workspace spec_verify needs for these sizes and parameters (0 on invalid input). */
+size_t spec_verify_workspace_size(int B, int K, int V, sv_dtype dtype, const sv_sampling* params);
+
+/*
+ * One verify-and-resample step for B sequences.
+ *
+ *   target_logits  [B, K+1, V]          target rows; row K feeds the bonus draw
+ *   draft_logits   [B, draft_rows, V]   draft rows; rows 0..K-1 are read; draft_rows in {K, K+1}
+ *                                       (may be NULL when K == 0)
+ *   dtype          element type of both logit tensors
+ *   B >= 1, K >= 0, V >= 1; B*(2K+1) rows must fit in int32 and V*(K+1) elements per sequence
+ *   draft_tokens   [B, K] int32; a token outside [0, V) has p = q = 0 and is rejected
+ *   uniforms       [B, K+1] float in [0, 1): u[b,k] for accept test k, u[b,K] for the final draw
+ *   params         host pointer, see sv_sampling
+ *   out_tokens     [B, K+1] int32: x~_0..x~_{n-1}, the drawn token at n, then -1
+ *   out_num_accepted [B] int32: n in 0..K (n+1 tokens are emitted)
+ *   out_accept_prob  [B, K] float or NULL: a_k for EVERY k, also past the first rejection
+ *   out_q_draft      [B, K] float or NULL: q_k(x~_k)
+ *   out_p_draft      [B, K] float or NULL: p_k(x~_k)
+ */
+int spec_verify(const void* target_logits, const void* draft_logits, sv_dtype dtype, int B, int K,
+                int V, int draft_rows, const int32_t* draft_tokens, const float* uniforms,
+                const sv_sampling* params, int32_t* out_tokens, int32_t* out_num_accepted,
+                float* out_accept_prob, float* out_q_draft, float* out_p_draft, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * spec_verify with per-phase timing, for profiling.  `events` holds n_events >= 2 events
+ * created by the caller with hipEventCreate; the library records events[0] before its first
+ * kernel, events[1] after the row-streaming kernel (the one that reads every logit), and, if
+ * n_events >= 3, events[2] after its last kernel.  Results are identical to spec_verify.
+ */
+int spec_verify_profiled(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                         int B, int K, int V, int draft_rows, const int32_t* draft_tokens,
+                         const float* uniforms, const sv_sampling* params, int32_t* out_tokens,
+                         int32_t* out_num_accepted, float* out_accept_prob, float* out_q_draft,
+                         float* out_p_draft, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream, hipEvent_t* events, int n_events);
+
+/*
+ * Draw one token per row from its processed distribution: the draft model's own sampling
+ * step (Chen et al. notes, A1: the draft samples its K tokens one at a time).  Identical to
+ * spec_verify with K = 0 on each row (the "bonus" draw).
+ *   logits [R, V], uniforms [R] in [0, 1), out_tokens [R] int32.
+ */
+size_t spec_sample_workspace_size(int R, int V, sv_dtype dtype, const sv_sampling* params);
+int spec_sample(const void* logits, sv_dtype dtype, int R, int V, const float* uniforms,
+                const sv_sampling* params, int32_t* out_tokens, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace spec_verify_tree needs (0 on invalid input). */
+size_t spec_verify_tree_workspace_size(int B, int N, int V, sv_dtype dtype);
+
+/*
+ * Greedy verification of a draft token tree (REST article, retrieval-based speculative
+ * decoding: BFS pseudo-sequence, tree attention, exact-match acceptance).
+ *
+ *   target_logits [B, N, V]: row n = the target's next-token logits after the path root..n
+ *   B >= 1, N >= 1, V >= 1, 0 <= max_depth
+ *   parent      [B, N] int32: parent[., 0] is ignored (node 0 is the root, the last committed
+ *               token); for n >= 1 a valid parent satisfies 0 <= parent < n.  A node with an
+ *               invalid parent, or deeper than max_depth, is not accepted.
+ *   node_tokens [B, N] int32: token of each node (node 0's is ignored)
+ *   out_tokens  [B, max_depth+1] int32: tokens of the accepted path root->d (root excluded),
+ *               then the argmax of node d's row (the bonus token), then -1
+ *   out_num_accepted [B] int32: depth of d.  d is the deepest accepted node, lowest index on ties.
+ *   out_last_node    [B] int32 or NULL: d
+ *   Argmax ties go to the lowest vocabulary index.
+ */
+int spec_verify_tree(const void* target_logits, sv_dtype dtype, int B, int N, int V,
+                     const int32_t* parent, const int32_t* node_tokens, int max_depth,
+                     int32_t* out_tokens, int32_t* out_num_accepted, int32_t* out_last_node,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static string for a status code. */
+const char* spec_verify_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

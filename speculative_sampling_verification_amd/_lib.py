@@ -1,0 +1,232 @@
+"""ctypes binding to libspecverify.so.
+
+Argument marshalling only: tensors are checked for device, dtype and layout, and their
+``data_ptr()`` values and torch's current HIP stream are passed to the C ABI.  Every step of
+the computation runs in the library's kernels.  There is no fallback: if the library is
+missing the import fails.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so that the library binds to torch's HIP runtime
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libspecverify.so")
+
+SV_OK = 0
+SV_DTYPE_F32 = 0
+SV_DTYPE_BF16 = 1
+
+
+class SVSampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
+                ("top_p", ctypes.c_float), ("lenience", ctypes.c_float)]
+
+
+EXPORTS = [
+    "spec_verify_workspace_size", "spec_verify", "spec_verify_profiled",
+    "spec_sample_workspace_size", "spec_sample",
+    "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_status_string",
+]
+
+
+def load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with speculative_sampling_verification_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    psamp = ctypes.POINTER(SVSampling)
+    lib.spec_verify_workspace_size.argtypes = [i32, i32, i32, i32, psamp]
+    lib.spec_verify_workspace_size.restype = sz
+    lib.spec_verify.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, psamp, vp, vp, vp, vp, vp,
+                                vp, sz, vp]
+    lib.spec_verify.restype = i32
+    lib.spec_verify_profiled.argtypes = lib.spec_verify.argtypes + [vp, i32]
+    lib.spec_verify_profiled.restype = i32
+    lib.spec_sample_workspace_size.argtypes = [i32, i32, i32, psamp]
+    lib.spec_sample_workspace_size.restype = sz
+    lib.spec_sample.argtypes = [vp, i32, i32, i32, vp, psamp, vp, vp, sz, vp]
+    lib.spec_sample.restype = i32
+    lib.spec_verify_tree_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.spec_verify_tree_workspace_size.restype = sz
+    lib.spec_verify_tree.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_tree.restype = i32
+    lib.spec_verify_status_string.argtypes = [i32]
+    lib.spec_verify_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = load()
+
+
+def lib():
+    return _lib
+
+
+def status_string(code):
+    return _lib.spec_verify_status_string(int(code)).decode()
+
+
+class SpecVerifyError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {status_string(code)} (status {code})")
+        self.code = code
+
+
+def _check(fn, code):
+    if code != SV_OK:
+        raise SpecVerifyError(fn, code)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return SV_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SV_DTYPE_F32
+    raise TypeError(f"logits must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def sampling(temperature=1.0, top_k=0, top_p=1.0, lenience=1.0):
+    return SVSampling(float(temperature), int(top_k), float(top_p), float(lenience))
+
+
+_workspaces = {}
+
+
+def workspace(device, nbytes):
+    """A cached uint8 device buffer of at least nbytes (grown on demand, never shrunk)."""
+    key = (device.type, device.index)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperature=1.0, top_k=0,
+                top_p=1.0, lenience=1.0, out=None, want_probs=True, stream=None, events=None):
+    """Verify-and-resample for a batch (see include/spec_verify.h).
+
+    target_logits [B, K+1, V], draft_logits [B, K or K+1, V] (bf16 or fp32, same dtype),
+    draft_tokens [B, K] int32, uniforms [B, K+1] float32, all on one GPU.
+    Returns a dict: tokens [B, K+1], num_accepted [B], and if want_probs accept_prob / q_draft /
+    p_draft [B, K].  ``out`` may hold preallocated tensors under the same keys.
+    ``events``: optional list of >= 2 hipEvent_t handles (ints) for per-phase timing.
+    """
+    dev = target_logits.device
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    _need(target_logits, "target_logits", dev)
+    dt = _dtype_code(target_logits)
+    if K > 0:
+        _need(draft_logits, "draft_logits", dev, target_logits.dtype)
+        if draft_logits.dim() != 3 or draft_logits.shape[0] != B or draft_logits.shape[2] != V:
+            raise ValueError("draft_logits must be [B, K or K+1, V]")
+        draft_rows = draft_logits.shape[1]
+        _need(draft_tokens, "draft_tokens", dev, torch.int32, (B, K))
+    else:
+        draft_rows = 0
+    _need(uniforms, "uniforms", dev, torch.float32, (B, K + 1))
+    out = dict(out or {})
+    if "tokens" not in out:
+        out["tokens"] = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    if "num_accepted" not in out:
+        out["num_accepted"] = torch.empty((B,), dtype=torch.int32, device=dev)
+    if want_probs:
+        for k in ("accept_prob", "q_draft", "p_draft"):
+            if k not in out:
+                out[k] = torch.empty((B, K), dtype=torch.float32, device=dev)
+    _need(out["tokens"], "out tokens", dev, torch.int32, (B, K + 1))
+    _need(out["num_accepted"], "out num_accepted", dev, torch.int32, (B,))
+    for k in ("accept_prob", "q_draft", "p_draft"):
+        if k in out:
+            _need(out[k], f"out {k}", dev, torch.float32, (B, K))
+    samp = sampling(temperature, top_k, top_p, lenience)
+    need = _lib.spec_verify_workspace_size(B, K, V, dt, ctypes.byref(samp))
+    if need == 0:
+        raise SpecVerifyError("spec_verify_workspace_size", 1)
+    ws = workspace(dev, need)
+    args = [_ptr(target_logits), _ptr(draft_logits) if K > 0 else None, dt, B, K, V, draft_rows,
+            _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms), ctypes.byref(samp),
+            _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out.get("accept_prob")),
+            _ptr(out.get("q_draft")), _ptr(out.get("p_draft")), _ptr(ws), ws.numel(),
+            _stream(dev, stream)]
+    if events is None:
+        _check("spec_verify", _lib.spec_verify(*args))
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check("spec_verify_profiled", _lib.spec_verify_profiled(*args, arr, len(events)))
+    return out
+
+
+def spec_sample(logits, uniforms, *, temperature=1.0, top_k=0, top_p=1.0, out=None, stream=None):
+    """One token per row of logits [R, V] from its processed distribution; uniforms [R]."""
+    dev = logits.device
+    R, V = logits.shape
+    _need(logits, "logits", dev)
+    dt = _dtype_code(logits)
+    _need(uniforms, "uniforms", dev, torch.float32, (R,))
+    if out is None:
+        out = torch.empty((R,), dtype=torch.int32, device=dev)
+    _need(out, "out", dev, torch.int32, (R,))
+    samp = sampling(temperature, top_k, top_p, 1.0)
+    need = _lib.spec_sample_workspace_size(R, V, dt, ctypes.byref(samp))
+    if need == 0:
+        raise SpecVerifyError("spec_sample_workspace_size", 1)
+    ws = workspace(dev, need)
+    _check("spec_sample", _lib.spec_sample(_ptr(logits), dt, R, V, _ptr(uniforms),
+                                           ctypes.byref(samp), _ptr(out), _ptr(ws), ws.numel(),
+                                           _stream(dev, stream)))
+    return out
+
+
+def spec_verify_tree(target_logits, parent, node_tokens, max_depth, *, out=None, stream=None):
+    """Greedy tree verification: target_logits [B, N, V], parent / node_tokens [B, N] int32."""
+    dev = target_logits.device
+    B, N, V = target_logits.shape
+    _need(target_logits, "target_logits", dev)
+    dt = _dtype_code(target_logits)
+    _need(parent, "parent", dev, torch.int32, (B, N))
+    _need(node_tokens, "node_tokens", dev, torch.int32, (B, N))
+    out = dict(out or {})
+    out.setdefault("tokens", torch.empty((B, max_depth + 1), dtype=torch.int32, device=dev))
+    out.setdefault("num_accepted", torch.empty((B,), dtype=torch.int32, device=dev))
+    out.setdefault("last_node", torch.empty((B,), dtype=torch.int32, device=dev))
+    _need(out["tokens"], "out tokens", dev, torch.int32, (B, max_depth + 1))
+    _need(out["num_accepted"], "out num_accepted", dev, torch.int32, (B,))
+    _need(out["last_node"], "out last_node", dev, torch.int32, (B,))
+    need = _lib.spec_verify_tree_workspace_size(B, N, V, dt)
+    if need == 0:
+        raise SpecVerifyError("spec_verify_tree_workspace_size", 1)
+    ws = workspace(dev, need)
+    _check("spec_verify_tree", _lib.spec_verify_tree(
+        _ptr(target_logits), dt, B, N, V, _ptr(parent), _ptr(node_tokens), int(max_depth),
+        _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["last_node"]), _ptr(ws),
+        ws.numel(), _stream(dev, stream)))
+    return out

@@ -1,0 +1,238 @@
+// extern "C" entry points of libspecverify.so: host-side argument checks, workspace layout and
+// kernel dispatch.  No allocation, no synchronisation; everything is enqueued on the caller's
+// stream.  See include/spec_verify.h for the contract of each function.
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "sv_internal.hpp"
+
+namespace sv {
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Appends a segment of `bytes` to the layout; returns its offset.
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  }
+};
+
+template <class T>
+T* at(void* base, size_t off) {
+  return base ? reinterpret_cast<T*>(static_cast<char*>(base) + off) : nullptr;
+}
+
+bool valid_dtype(sv_dtype dt) { return dt == SV_DTYPE_F32 || dt == SV_DTYPE_BF16; }
+size_t esize(sv_dtype dt) { return dt == SV_DTYPE_BF16 ? 2 : 4; }
+
+bool valid_params(const sv_sampling* p) {
+  if (!p) return false;
+  if (!(p->temperature >= 0.0f) || !std::isfinite(p->temperature)) return false;
+  if (p->top_k < 0) return false;
+  if (!(p->top_p > 0.0f && p->top_p <= 1.0f)) return false;
+  if (!(p->lenience > 0.0f && p->lenience <= 1.0f)) return false;
+  return true;
+}
+
+Samp make_samp(const sv_sampling* p, int V) {
+  Samp s{};
+  s.temperature = p->temperature;
+  s.greedy = p->temperature == 0.0f;
+  s.inv_t = s.greedy ? 0.0f : 1.0f / p->temperature;
+  s.top_k = (p->top_k > 0 && p->top_k < V) ? p->top_k : 0;
+  s.top_p = p->top_p;
+  s.lenience = p->lenience;
+  s.compact = !s.greedy && s.top_k > 0 && s.top_k <= kCompactMaxK;
+  s.generic_trunc = !s.greedy && ((s.top_k > kCompactMaxK) || (s.top_p < 1.0f && !s.compact));
+  return s;
+}
+
+// Fills Dims for a verify-shaped problem; false if the sizes do not fit the indexing.
+bool make_dims(int B, int K, int V, int draft_rows, sv_dtype dt, Dims* d) {
+  if (B < 1 || K < 0 || V < 1) return false;
+  const long long rps = 2LL * K + 1;
+  const long long rows = (long long)B * rps;
+  if (rows > INT_MAX) return false;
+  const int ce = chunk_elems_for(dt);
+  const long long nch = ((long long)V + ce - 1) / ce;
+  if (rows * nch > (long long)INT_MAX) return false;
+  if ((long long)B * nch > (long long)INT_MAX) return false;
+  d->B = B;
+  d->K = K;
+  d->V = V;
+  d->draft_rows = draft_rows;
+  d->rows_per_seq = (int)rps;
+  d->rows = (int)rows;
+  d->chunk_elems = ce;
+  d->nchunks = (int)nch;
+  d->vec = 0;
+  return true;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
+  Carver c;
+  const size_t rows = (size_t)d.rows, nch = (size_t)d.nchunks;
+  const size_t o_parts = c.take(rows * nch * sizeof(ChunkPart));
+  const size_t o_cand = c.take(s.compact ? rows * nch * kChunkCap * sizeof(uint2) : 0);
+  const size_t o_rstat = c.take(rows * sizeof(RowStat));
+  const size_t o_kept = c.take(s.compact ? rows * kKeptCap * sizeof(uint2) : 0);
+  const size_t o_seq = c.take((size_t)d.B * sizeof(SeqState));
+  const size_t o_fpart = c.take(s.greedy ? 0 : (size_t)d.B * nch * sizeof(double2));
+  const size_t o_n = c.take((size_t)d.B * sizeof(int32_t));
+  if (ws) {
+    ws->parts = at<ChunkPart>(base, o_parts);
+    ws->cand = s.compact ? at<uint2>(base, o_cand) : nullptr;
+    ws->rstat = at<RowStat>(base, o_rstat);
+    ws->kept = s.compact ? at<uint2>(base, o_kept) : nullptr;
+    ws->seq = at<SeqState>(base, o_seq);
+    ws->fpart = s.greedy ? nullptr : at<double2>(base, o_fpart);
+    ws->nbuf = at<int32_t>(base, o_n);
+  }
+  return c.off;
+}
+
+size_t layout_tree(const Dims& d, void* base, Workspace* ws) {
+  Carver c;
+  const size_t o_parts = c.take((size_t)d.rows * d.nchunks * sizeof(ChunkPart));
+  if (ws) {
+    *ws = Workspace{};
+    ws->parts = at<ChunkPart>(base, o_parts);
+  }
+  return c.off;
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+namespace {
+
+int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, int K, int V,
+                int draft_rows, const int32_t* drafts, const float* uniforms,
+                const sv_sampling* params, int32_t* out_tokens, int32_t* out_n, float* out_a,
+                float* out_q, float* out_p, void* workspace, size_t workspace_bytes,
+                hipStream_t stream, hipEvent_t* events, int n_events) {
+  if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
+  if (!valid_params(params)) return SV_ERR_INVALID_ARG;
+  if (K > 0 && draft_rows != K && draft_rows != K + 1) return SV_ERR_INVALID_ARG;
+  Dims d{};
+  if (!make_dims(B, K, V, K > 0 ? draft_rows : 0, dtype, &d)) return SV_ERR_INVALID_ARG;
+  if (!target || !uniforms || !out_tokens) return SV_ERR_INVALID_ARG;
+  if (K > 0 && (!draft || !drafts)) return SV_ERR_INVALID_ARG;
+  if (events && n_events < 2) return SV_ERR_INVALID_ARG;
+  const Samp s = make_samp(params, V);
+  const size_t need = layout_verify(d, s, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+  d.vec = ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target) &&
+          (K == 0 || aligned16(draft));
+  Workspace ws{};
+  layout_verify(d, s, workspace, &ws);
+  if (!out_n) out_n = ws.nbuf;
+  const hipError_t e = launch_verify(target, draft, dtype, d, s, drafts, uniforms, out_tokens,
+                                     out_n, out_a, out_q, out_p, ws, stream, events, n_events);
+  return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t spec_verify_workspace_size(int B, int K, int V, sv_dtype dtype, const sv_sampling* params) {
+  if (!valid_dtype(dtype) || !valid_params(params)) return 0;
+  Dims d{};
+  if (!make_dims(B, K, V, K, dtype, &d)) return 0;
+  return layout_verify(d, make_samp(params, V), nullptr, nullptr);
+}
+
+int spec_verify(const void* target_logits, const void* draft_logits, sv_dtype dtype, int B, int K,
+                int V, int draft_rows, const int32_t* draft_tokens, const float* uniforms,
+                const sv_sampling* params, int32_t* out_tokens, int32_t* out_num_accepted,
+                float* out_accept_prob, float* out_q_draft, float* out_p_draft, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  if (!out_num_accepted) return SV_ERR_INVALID_ARG;
+  return verify_impl(target_logits, draft_logits, dtype, B, K, V, draft_rows, draft_tokens,
+                     uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
+                     out_q_draft, out_p_draft, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int spec_verify_profiled(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                         int B, int K, int V, int draft_rows, const int32_t* draft_tokens,
+                         const float* uniforms, const sv_sampling* params, int32_t* out_tokens,
+                         int32_t* out_num_accepted, float* out_accept_prob, float* out_q_draft,
+                         float* out_p_draft, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream, hipEvent_t* events, int n_events) {
+  if (!out_num_accepted || !events) return SV_ERR_INVALID_ARG;
+  return verify_impl(target_logits, draft_logits, dtype, B, K, V, draft_rows, draft_tokens,
+                     uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
+                     out_q_draft, out_p_draft, workspace, workspace_bytes, stream, events,
+                     n_events);
+}
+
+size_t spec_sample_workspace_size(int R, int V, sv_dtype dtype, const sv_sampling* params) {
+  return spec_verify_workspace_size(R, 0, V, dtype, params);
+}
+
+int spec_sample(const void* logits, sv_dtype dtype, int R, int V, const float* uniforms,
+                const sv_sampling* params, int32_t* out_tokens, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  return verify_impl(logits, nullptr, dtype, R, 0, V, 0, nullptr, uniforms, params, out_tokens,
+                     nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+                     nullptr, 0);
+}
+
+size_t spec_verify_tree_workspace_size(int B, int N, int V, sv_dtype dtype) {
+  if (!valid_dtype(dtype) || B < 1 || N < 1 || N > 2048) return 0;
+  if ((long long)B * N > INT_MAX) return 0;
+  Dims d{};
+  if (!make_dims(B * N, 0, V, 0, dtype, &d)) return 0;
+  return layout_tree(d, nullptr, nullptr);
+}
+
+int spec_verify_tree(const void* target_logits, sv_dtype dtype, int B, int N, int V,
+                     const int32_t* parent, const int32_t* node_tokens, int max_depth,
+                     int32_t* out_tokens, int32_t* out_num_accepted, int32_t* out_last_node,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
+  if (B < 1 || N < 1 || N > 2048 || V < 1 || max_depth < 0) return SV_ERR_INVALID_ARG;
+  if ((long long)B * N > INT_MAX) return SV_ERR_INVALID_ARG;
+  if (!target_logits || !parent || !node_tokens || !out_tokens || !out_num_accepted)
+    return SV_ERR_INVALID_ARG;
+  Dims d{};
+  if (!make_dims(B * N, 0, V, 0, dtype, &d)) return SV_ERR_INVALID_ARG;
+  const size_t need = layout_tree(d, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+  d.vec = ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target_logits);
+  Workspace ws{};
+  layout_tree(d, workspace, &ws);
+  // the walk kernel reads B and the node count from Dims
+  d.B = B;
+  d.K = N;
+  const hipError_t e = launch_tree(target_logits, dtype, d, parent, node_tokens, max_depth,
+                                   out_tokens, out_num_accepted, out_last_node, ws, stream);
+  return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+const char* spec_verify_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_ERR_INVALID_ARG: return "invalid argument";
+    case SV_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case SV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SV_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,114 @@
+// Internal declarations shared by the kernels (sv_kernels.hip) and the C ABI (sv_abi.hip).
+//
+// Data flow of one spec_verify call (all on the caller's stream):
+//   k_chunk   grid = rows x chunks : streams every logit once; per chunk a max (and a sum of
+//                                     exponentials, an argmax, or top-k candidates)
+//   k_row     grid = rows          : merges the chunks of a row into its distribution
+//                                     parameters (max m, threshold thr, normaliser S), and for
+//                                     compact top-k rows the kept tokens sorted by index
+//   k_seq     grid = B             : accept tests, first-rejection scan, and the final draw when
+//                                     the final row is compact or greedy
+//   k_final_partial / k_final_pick : the final draw over a full row pair when it is not compact
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "spec_verify.h"
+
+namespace sv {
+
+constexpr int kThreads = 256;        // threads per workgroup of the streaming kernels (4 waves)
+constexpr int kVecPerThread = 16;    // 16-byte vectors each thread holds per chunk
+constexpr int kCompactMaxK = 256;    // top-k <= this uses the compact candidate path
+constexpr int kChunkCap = 512;       // candidates one chunk may emit
+constexpr int kRowGatherCap = 4096;  // candidates one row merge may gather in LDS
+constexpr int kKeptCap = 1024;       // kept tokens a compact row may hold
+constexpr int kSeqThreads = 64;      // one wave per sequence
+
+// Row kinds written by k_row.
+enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
+
+// Mode of k_chunk.
+enum ChunkMode : int { kChunkDense = 0, kChunkArgmax = 1, kChunkTopK = 2 };
+
+struct alignas(16) ChunkPart {
+  float vmax;      // largest logit of the chunk
+  int argmax;      // lowest index holding vmax (argmax mode), else -1
+  double sum;      // sum of exp((z - vmax) / T) over the chunk (dense mode), else 0
+  int count;       // candidates written (top-k mode)
+  int overflow;    // 1 if the chunk had more than kChunkCap candidates
+  int pad[2];
+};
+
+struct alignas(16) RowStat {
+  float m;         // largest logit of the row
+  float thr;       // kept tokens are those with z >= thr (-inf: all)
+  double S;        // sum over kept tokens of exp((z - m) / T)
+  int argmax;      // lowest index of the maximum (greedy rows)
+  int nkept;       // number of kept tokens (compact rows), else -1
+  int kind;        // RowKind
+  int pad;
+};
+
+struct alignas(16) SeqState {
+  int n;           // accepted drafts
+  int need_dense;  // 1 if the final draw runs in k_final_partial / k_final_pick
+  int fallback;    // 1 if the residual had zero mass and q was used
+  int pad;
+};
+
+struct Dims {
+  int B, K, V;
+  int draft_rows;   // rows per sequence in the draft tensor
+  int rows_per_seq; // 2K+1 for verify, 1 for plain row sets
+  int rows;         // total rows
+  int chunk_elems;  // elements per chunk
+  int nchunks;      // chunks per row
+  int vec;          // 1: 16-byte loads are legal for every row
+};
+
+struct Samp {
+  float temperature;
+  float inv_t;      // 1 / temperature (0 when greedy)
+  int top_k;        // effective top-k (0 = off)
+  float top_p;      // effective top-p (1 = off)
+  float lenience;
+  int greedy;       // temperature == 0
+  int compact;      // compact top-k path
+  int generic_trunc;// truncation that needs the row-pass selection (top-k > kCompactMaxK or top-p
+                    // without a compact list)
+};
+
+struct Workspace {
+  ChunkPart* parts;  // [rows][nchunks]
+  uint2* cand;       // [rows][nchunks][kChunkCap]  (index, key)   compact only
+  RowStat* rstat;    // [rows]
+  uint2* kept;       // [rows][kKeptCap]  (index, float bits)      compact only
+  SeqState* seq;     // [B]
+  double2* fpart;    // [B][nchunks]  (residual mass, target mass)
+  int32_t* nbuf;     // [B] accepted counts when the caller does not want them
+};
+
+inline int chunk_elems_for(sv_dtype dt) {
+  return kThreads * kVecPerThread * (dt == SV_DTYPE_BF16 ? 8 : 4);
+}
+
+// Workspace layout; returns the byte size and, when base != nullptr, fills ws.
+size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws);
+size_t layout_tree(const Dims& d, void* base, Workspace* ws);
+
+// Kernel launchers (sv_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, const Dims& d,
+                         const Samp& s, const int32_t* drafts, const float* uniforms,
+                         int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
+                         float* out_p, const Workspace& ws, hipStream_t stream,
+                         hipEvent_t* events, int n_events);
+hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,
+                       const int32_t* tokens, int max_depth, int32_t* out_tokens,
+                       int32_t* out_n, int32_t* out_last, const Workspace& ws,
+                       hipStream_t stream);
+
+}  // namespace sv

@@ -1,0 +1,1229 @@
+// HIP kernels for gfx950 (CDNA4): verify-and-resample of speculative sampling and greedy tree
+// verification.  Every row of logits is streamed from HBM once by k_chunk with coalesced
+// 16-byte loads and kept in registers while it is reduced; all later kernels touch only small
+// per-row summaries, except where a row has no compact summary (no truncation, top-p, or a
+// top-k tie set too large for the candidate lists), where the final draw re-reads one row pair.
+//
+// Method (page "Accelerating Large Language Model Decoding with Speculative Sampling", Chen et
+// al. notes; q = target, p = draft): section A2 "modified rejection sampling" for the accept
+// test and the (q - p)_+ residual, the bonus-token remark of the same section, Theorem 1 in the
+// appendix; temperature / top-k / top-p applied before the scheme (section A2, compatibility
+// with standard sampling methods); lenience from App. F of the "Fast Inference from
+// Transformers via Speculative Decoding" blog; greedy tree acceptance from the REST article.
+//
+// Reductions use fixed orders only (wave butterflies, then the 4 waves in order; chunks in
+// order; kept tokens in index order), and integer atomics only, so results are bitwise
+// reproducible.
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+
+#include "sv_internal.hpp"
+
+namespace sv {
+namespace {
+
+// ------------------------------------------------------------------------------------------
+// Element traits.  bf16 is handled as raw 16-bit patterns, two per 32-bit register.
+//
+// Keys: an order-preserving map from the element's bits to an unsigned integer (flip all bits
+// of negatives, set the sign bit of non-negatives).  -0 and +0 get adjacent keys; canon()
+// merges them, so that equal floating-point values have equal keys.
+// ------------------------------------------------------------------------------------------
+template <class E>
+struct Tr;
+
+template <>
+struct Tr<uint16_t> {
+  static constexpr int kEpv = 8;        // elements per 16-byte vector
+  static constexpr int kPerDword = 2;   // elements per 32-bit register
+  static constexpr int kKeyBits = 16;
+  static constexpr uint32_t kKeyPos0 = 0x8000u;
+  static constexpr uint32_t kKeyNeg0 = 0x7FFFu;
+  static constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two -inf
+  static constexpr uint32_t kKey0Pair = 0xFFFFFFFFu;    // bits whose keys are 0 (never kept)
+
+  __device__ static float elem(uint32_t w, int h) {
+    return __uint_as_float(h ? (w & 0xFFFF0000u) : (w << 16));
+  }
+  __device__ static uint32_t bits_of(uint16_t v) { return v; }
+  __device__ static float to_float(uint32_t bits) { return __uint_as_float(bits << 16); }
+  __device__ static uint32_t key_of_bits(uint32_t b) {
+    return (b & 0x8000u) ? (~b & 0xFFFFu) : (b | 0x8000u);
+  }
+  // two keys at once: per 16-bit half, bits ^ (negative ? 0xFFFF : 0x8000)
+  __device__ static uint32_t keys_of_dword(uint32_t w) {
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    s2 v = __builtin_bit_cast(s2, w);
+    s2 sh = v >> (s2){15, 15};
+    return w ^ (__builtin_bit_cast(uint32_t, sh) | 0x80008000u);
+  }
+  __device__ static uint32_t dword_max(uint32_t a, uint32_t b) {
+    typedef unsigned short u2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(
+        uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u2, a), __builtin_bit_cast(u2, b)));
+  }
+  __device__ static uint32_t dword_hmax(uint32_t w) {
+    uint32_t lo = w & 0xFFFFu, hi = w >> 16;
+    return lo > hi ? lo : hi;
+  }
+  __device__ static float key_to_float(uint32_t key) {
+    uint32_t b = (key & 0x8000u) ? (key ^ 0x8000u) : (~key & 0xFFFFu);
+    return __uint_as_float(b << 16);
+  }
+  __device__ static uint32_t canon(uint32_t key) { return key == kKeyNeg0 ? kKeyPos0 : key; }
+};
+
+template <>
+struct Tr<float> {
+  static constexpr int kEpv = 4;
+  static constexpr int kPerDword = 1;
+  static constexpr int kKeyBits = 32;
+  static constexpr uint32_t kKeyPos0 = 0x80000000u;
+  static constexpr uint32_t kKeyNeg0 = 0x7FFFFFFFu;
+  static constexpr uint32_t kNegInfPair = 0xFF800000u;
+  static constexpr uint32_t kKey0Pair = 0xFFFFFFFFu;
+
+  __device__ static float elem(uint32_t w, int) { return __uint_as_float(w); }
+  __device__ static uint32_t bits_of(float v) { return __float_as_uint(v); }
+  __device__ static float to_float(uint32_t bits) { return __uint_as_float(bits); }
+  __device__ static uint32_t key_of_bits(uint32_t b) {
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  }
+  __device__ static uint32_t keys_of_dword(uint32_t w) {
+    return w ^ ((uint32_t)((int32_t)w >> 31) | 0x80000000u);
+  }
+  __device__ static uint32_t dword_max(uint32_t a, uint32_t b) { return a > b ? a : b; }
+  __device__ static uint32_t dword_hmax(uint32_t w) { return w; }
+  __device__ static float key_to_float(uint32_t key) {
+    uint32_t b = (key & 0x80000000u) ? (key ^ 0x80000000u) : ~key;
+    return __uint_as_float(b);
+  }
+  __device__ static uint32_t canon(uint32_t key) { return key == kKeyNeg0 ? kKeyPos0 : key; }
+};
+
+constexpr int kRegs = kVecPerThread * 4;  // 32-bit registers per thread holding one chunk
+
+// ------------------------------------------------------------------------------------------
+// Block reductions (256 threads = 4 waves of 64).  Fixed butterfly inside a wave, then the
+// four wave results in order: deterministic.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
+  return v;
+}
+
+struct RedScratch {
+  double d[4];
+  float f[4];
+  int i[4];
+  unsigned long long u[4];
+};
+
+__device__ double block_sum_d(double v, RedScratch& s) {
+  v = wave_reduce(v, [](double a, double b) { return a + b; });
+  __syncthreads();
+  if (lane_id() == 0) s.d[wave_id()] = v;
+  __syncthreads();
+  return ((s.d[0] + s.d[1]) + s.d[2]) + s.d[3];
+}
+
+__device__ float block_max_f(float v, RedScratch& s) {
+  v = wave_reduce(v, [](float a, float b) { return fmaxf(a, b); });
+  __syncthreads();
+  if (lane_id() == 0) s.f[wave_id()] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(s.f[0], s.f[1]), fmaxf(s.f[2], s.f[3]));
+}
+
+__device__ int block_min_i(int v, RedScratch& s) {
+  v = wave_reduce(v, [](int a, int b) { return a < b ? a : b; });
+  __syncthreads();
+  if (lane_id() == 0) s.i[wave_id()] = v;
+  __syncthreads();
+  int a = s.i[0] < s.i[1] ? s.i[0] : s.i[1];
+  int b = s.i[2] < s.i[3] ? s.i[2] : s.i[3];
+  return a < b ? a : b;
+}
+
+__device__ int block_max_i(int v, RedScratch& s) {
+  v = wave_reduce(v, [](int a, int b) { return a > b ? a : b; });
+  __syncthreads();
+  if (lane_id() == 0) s.i[wave_id()] = v;
+  __syncthreads();
+  int a = s.i[0] > s.i[1] ? s.i[0] : s.i[1];
+  int b = s.i[2] > s.i[3] ? s.i[2] : s.i[3];
+  return a > b ? a : b;
+}
+
+__device__ int block_sum_i(int v, RedScratch& s) {
+  v = wave_reduce(v, [](int a, int b) { return a + b; });
+  __syncthreads();
+  if (lane_id() == 0) s.i[wave_id()] = v;
+  __syncthreads();
+  return s.i[0] + s.i[1] + s.i[2] + s.i[3];
+}
+
+// ------------------------------------------------------------------------------------------
+// Row addressing.  With rows_per_seq == 2K+1 a sequence's rows are ordered
+// target 0..K, then draft 0..K-1; with rows_per_seq == 1 rows are consecutive in `t`.
+// ------------------------------------------------------------------------------------------
+template <class E>
+__device__ __forceinline__ const E* row_ptr(const Dims& dm, const E* t, const E* d, int r) {
+  if (dm.rows_per_seq == 1) return t + (size_t)r * dm.V;
+  const int b = r / dm.rows_per_seq;
+  const int j = r - b * dm.rows_per_seq;
+  if (j <= dm.K) return t + ((size_t)b * (dm.K + 1) + j) * dm.V;
+  return d + ((size_t)b * dm.draft_rows + (j - dm.K - 1)) * dm.V;
+}
+
+__device__ __forceinline__ int target_row(const Dims& dm, int b, int k) {
+  return b * dm.rows_per_seq + k;
+}
+__device__ __forceinline__ int draft_row(const Dims& dm, int b, int k) {
+  return b * dm.rows_per_seq + dm.K + 1 + k;
+}
+
+// Load this thread's share of one chunk: vector i of thread t covers elements
+// c0 + (t + 256 i) * EPV ... + EPV - 1.  Slots past the row end hold `fill`.
+template <class E, bool VEC>
+__device__ __forceinline__ void load_chunk(const E* __restrict__ row, int V, int c0, int clen,
+                                           uint32_t (&regs)[kRegs], uint32_t fill) {
+  constexpr int EPV = Tr<E>::kEpv;
+  const int tid = threadIdx.x;
+  if constexpr (VEC) {
+    const uint4* vp = reinterpret_cast<const uint4*>(row + c0);
+    const int nvec = clen / EPV;  // clen is a multiple of EPV when VEC
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int v = tid + kThreads * i;
+      uint4 x = make_uint4(fill, fill, fill, fill);
+      if (v < nvec) x = vp[v];
+      regs[4 * i + 0] = x.x;
+      regs[4 * i + 1] = x.y;
+      regs[4 * i + 2] = x.z;
+      regs[4 * i + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const int e0 = c0 + (tid + kThreads * i) * EPV;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+          const int idx = e0 + d * Tr<E>::kPerDword + h;
+          uint32_t bits;
+          if (idx < V)
+            bits = Tr<E>::bits_of(row[idx]);
+          else
+            bits = (Tr<E>::kPerDword == 2) ? (fill & 0xFFFFu) : fill;
+          w |= bits << (16 * h * (Tr<E>::kPerDword == 2));
+        }
+        regs[4 * i + d] = w;
+      }
+    }
+  }
+}
+
+// Element index of slot (vector i, register d, half h) of this thread in chunk starting at c0.
+template <class E>
+__device__ __forceinline__ int slot_index(int c0, int i, int d, int h) {
+  return c0 + (threadIdx.x + kThreads * i) * Tr<E>::kEpv + d * Tr<E>::kPerDword + h;
+}
+
+// ------------------------------------------------------------------------------------------
+// k_chunk: one workgroup per (row, chunk).  Reads each logit of the chunk once.
+//   dense : vmax and sum exp((z - vmax) / T) over the chunk
+//   argmax: vmax and the lowest index holding it
+//   top-k : vmax and every element with key >= tau, where tau = the k-th largest of the 256
+//           per-thread maxima.  tau never exceeds the chunk's k-th largest element (the k
+//           largest thread maxima are k distinct elements), and the row's k-th largest is at
+//           least the chunk's, so the union of the chunks' candidates holds every element of
+//           the row's top-k set, ties included.
+// ------------------------------------------------------------------------------------------
+template <class E, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
+                                                    const E* __restrict__ drf, Dims dm, Samp sp,
+                                                    Workspace ws) {
+  const int bid = blockIdx.x;
+  const int r = bid / dm.nchunks;
+  const int c = bid - r * dm.nchunks;
+  const E* row = row_ptr(dm, tgt, drf, r);
+  const int c0 = c * dm.chunk_elems;
+  const int clen = min(dm.chunk_elems, dm.V - c0);
+  const int tid = threadIdx.x;
+  __shared__ RedScratch red;
+
+  uint32_t regs[kRegs];
+  ChunkPart* part = ws.parts + (size_t)r * dm.nchunks + c;
+
+  if constexpr (MODE == kChunkTopK) {
+    __shared__ uint32_t s_tmax[kThreads];
+    __shared__ uint2 s_list[kChunkCap];
+    __shared__ uint32_t s_tau, s_bmax;
+    __shared__ int s_cnt;
+
+    load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kKey0Pair);
+    uint32_t tm = 0;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+      regs[j] = Tr<E>::keys_of_dword(regs[j]);
+      tm = Tr<E>::dword_max(tm, regs[j]);
+    }
+    s_tmax[tid] = Tr<E>::dword_hmax(tm);
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    if (wave_id() == 0) {
+      const int lane = lane_id();
+      const uint32_t a0 = s_tmax[lane], a1 = s_tmax[lane + 64];
+      const uint32_t a2 = s_tmax[lane + 128], a3 = s_tmax[lane + 192];
+      uint32_t bm = max(max(a0, a1), max(a2, a3));
+      bm = wave_reduce(bm, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+      const int k = sp.top_k;
+      uint32_t x = 0;
+      for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+        const uint32_t cand = x | (1u << bit);
+        const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand)) +
+                        __popcll(__ballot(a2 >= cand)) + __popcll(__ballot(a3 >= cand));
+        if (cnt >= k) x = cand;
+      }
+      if (x < 1u) x = 1u;                              // key 0 marks slots past the row end
+      if (x == Tr<E>::kKeyPos0) x = Tr<E>::kKeyNeg0;  // -0 equals +0
+      if (lane == 0) {
+        s_tau = x;
+        s_bmax = bm;
+      }
+    }
+    __syncthreads();
+    const uint32_t tau = s_tau;
+    if constexpr (Tr<E>::kPerDword == 2) {
+      const uint32_t tm1 = tau - 1u;
+      const uint32_t tpair = tm1 | (tm1 << 16);
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t w = regs[4 * i + d];
+          if (Tr<E>::dword_max(w, tpair) != tpair) {  // some half >= tau
+            const uint32_t k0 = w & 0xFFFFu, k1 = w >> 16;
+            if (k0 >= tau) {
+              const int pos = atomicAdd(&s_cnt, 1);
+              if (pos < kChunkCap) s_list[pos] = make_uint2(slot_index<E>(c0, i, d, 0), k0);
+            }
+            if (k1 >= tau) {
+              const int pos = atomicAdd(&s_cnt, 1);
+              if (pos < kChunkCap) s_list[pos] = make_uint2(slot_index<E>(c0, i, d, 1), k1);
+            }
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          const uint32_t w = regs[4 * i + d];
+          if (w >= tau) {
+            const int pos = atomicAdd(&s_cnt, 1);
+            if (pos < kChunkCap) s_list[pos] = make_uint2(slot_index<E>(c0, i, d, 0), w);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    const int nw = cnt < kChunkCap ? cnt : kChunkCap;
+    uint2* out = ws.cand + ((size_t)r * dm.nchunks + c) * kChunkCap;
+    for (int j = tid; j < nw; j += kThreads) out[j] = s_list[j];
+    if (tid == 0) {
+      ChunkPart p;
+      p.vmax = Tr<E>::key_to_float(s_bmax);
+      p.argmax = -1;
+      p.sum = 0.0;
+      p.count = nw;
+      p.overflow = cnt > kChunkCap;
+      p.pad[0] = p.pad[1] = 0;
+      *part = p;
+    }
+  } else {
+    load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kNegInfPair);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+#pragma unroll
+      for (int h = 0; h < Tr<E>::kPerDword; ++h) mx = fmaxf(mx, Tr<E>::elem(regs[j], h));
+    }
+    mx = block_max_f(mx, red);
+    ChunkPart p;
+    p.vmax = mx;
+    p.argmax = -1;
+    p.sum = 0.0;
+    p.count = 0;
+    p.overflow = 0;
+    p.pad[0] = p.pad[1] = 0;
+    if constexpr (MODE == kChunkDense) {
+      double s = 0.0;
+      if (mx > -INFINITY) {
+        const float it = sp.inv_t;
+#pragma unroll
+        for (int i = 0; i < kVecPerThread; ++i) {
+          float sv = 0.f;  // one vector's EPV terms in fp32, then into the fp64 total
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+#pragma unroll
+            for (int h = 0; h < Tr<E>::kPerDword; ++h)
+              sv += expf((Tr<E>::elem(regs[4 * i + d], h) - mx) * it);
+          }
+          s += (double)sv;
+        }
+      }
+      p.sum = block_sum_d(s, red);
+    } else {
+      int best = INT_MAX;
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+            const int idx = slot_index<E>(c0, i, d, h);
+            if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx < best) best = idx;
+          }
+        }
+      }
+      p.argmax = block_min_i(best, red);
+    }
+    if (tid == 0) *part = p;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Whole-row helpers for k_row's selection paths (re-read the row from memory).
+// ------------------------------------------------------------------------------------------
+template <class E, bool VEC, class F>
+__device__ __forceinline__ void row_foreach(const E* __restrict__ row, int V, F&& f) {
+  constexpr int EPV = Tr<E>::kEpv;
+  if constexpr (VEC) {
+    const uint4* vp = reinterpret_cast<const uint4*>(row);
+    const int nvec = V / EPV;
+    for (int v = threadIdx.x; v < nvec; v += kThreads) {
+      const uint4 x = vp[v];
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+          const uint32_t bits =
+              (Tr<E>::kPerDword == 2) ? (h ? (w[d] >> 16) : (w[d] & 0xFFFFu)) : w[d];
+          f(v * EPV + d * Tr<E>::kPerDword + h, Tr<E>::elem(w[d], h), bits);
+        }
+      }
+    }
+  } else {
+    for (int i = threadIdx.x; i < V; i += kThreads) {
+      const uint32_t bits = Tr<E>::bits_of(row[i]);
+      f(i, Tr<E>::to_float(bits), bits);
+    }
+  }
+}
+
+template <class E, bool VEC>
+__device__ double dense_sum(const E* row, int V, float m, float it, float thr, RedScratch& red) {
+  double s = 0.0;
+  row_foreach<E, VEC>(row, V, [&](int, float z, uint32_t) {
+    if (z >= thr) s += (double)expf((z - m) * it);
+  });
+  return block_sum_d(s, red);
+}
+
+// Largest key v with weight(key >= v) >= target, by most-significant-digit radix selection over
+// canonical keys, restricted to keys >= lower.  MASS: weight = exp((z - m) / T) in 2^-40 fixed
+// point (integer atomics, deterministic), target = ceil(P * total); else weight 1, target = k.
+template <class E, bool VEC, bool MASS>
+__device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_t lower,
+                                 double P_or_k, unsigned long long* s_bins, RedScratch& red) {
+  constexpr int KB = Tr<E>::kKeyBits;
+  constexpr int NLEV = KB == 16 ? 2 : 3;
+  // digits, most significant first: 16-bit keys 8+8 bits, 32-bit keys 11+11+10 bits
+  constexpr int kShift[3] = {KB == 16 ? 8 : 21, KB == 16 ? 0 : 10, 0};
+  constexpr int kWidth[3] = {KB == 16 ? 8 : 11, KB == 16 ? 8 : 11, 10};
+  const int tid = threadIdx.x;
+  __shared__ unsigned long long s_tot[kThreads];
+  __shared__ unsigned long long s_target, s_above;
+  __shared__ uint32_t s_prefix;
+  if (tid == 0) {
+    s_above = 0;
+    s_prefix = 0;
+  }
+  for (int L = 0; L < NLEV; ++L) {
+    const int shift = kShift[L];
+    const int bits = kWidth[L];
+    const int nb = 1 << bits;
+    for (int j = tid; j < nb; j += kThreads) s_bins[j] = 0ull;
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+    const int hshift = shift + bits;
+    row_foreach<E, VEC>(row, V, [&](int, float z, uint32_t b) {
+      const uint32_t key = Tr<E>::canon(Tr<E>::key_of_bits(b));
+      if (key < lower) return;
+      if (L > 0 && (hshift >= 32 ? 0u : (key >> hshift)) != prefix) return;
+      unsigned long long w = 1ull;
+      if constexpr (MASS) w = (unsigned long long)rintf(expf((z - m) * it) * 0x1p40f);
+      if (w) atomicAdd(&s_bins[(key >> shift) & (uint32_t)(nb - 1)], w);
+    });
+    __syncthreads();
+    // per-thread totals of consecutive bins, then suffix sums over threads
+    const int per = nb / kThreads > 0 ? nb / kThreads : 1;
+    const int b0 = tid * per;
+    unsigned long long mine = 0;
+    if (b0 < nb)
+      for (int j = 0; j < per; ++j) mine += s_bins[b0 + j];
+    s_tot[tid] = mine;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {  // inclusive suffix scan
+      const unsigned long long add = (tid + off < kThreads) ? s_tot[tid + off] : 0ull;
+      __syncthreads();
+      s_tot[tid] += add;
+      __syncthreads();
+    }
+    if (L == 0 && tid == 0) {
+      const unsigned long long total = s_tot[0];
+      unsigned long long t;
+      if constexpr (MASS) {
+        double tt = ceil(P_or_k * (double)total);
+        t = tt < 1.0 ? 1ull : (unsigned long long)tt;
+        if (t > total) t = total;
+      } else {
+        t = (unsigned long long)P_or_k;
+      }
+      s_target = t;
+    }
+    __syncthreads();
+    const unsigned long long target = s_target;
+    const unsigned long long above = s_above;
+    const unsigned long long after = (tid + 1 < kThreads) ? s_tot[tid + 1] : 0ull;
+    __syncthreads();
+    if (b0 < nb) {
+      unsigned long long cum = above + after;
+      for (int j = per - 1; j >= 0; --j) {
+        const unsigned long long before = cum;
+        cum += s_bins[b0 + j];
+        if (cum >= target && before < target) {
+          s_above = before;
+          s_prefix = (prefix << bits) | (uint32_t)(b0 + j);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  return s_prefix;
+}
+
+// ------------------------------------------------------------------------------------------
+// k_row: one workgroup per row.  Produces RowStat (m, thr, S) and, for compact top-k rows,
+// the kept tokens sorted by vocabulary index.
+// ------------------------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
+                                                  const E* __restrict__ drf, Dims dm, Samp sp,
+                                                  Workspace ws) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const E* row = row_ptr(dm, tgt, drf, r);
+  const ChunkPart* parts = ws.parts + (size_t)r * dm.nchunks;
+  __shared__ RedScratch red;
+  __shared__ unsigned long long s_bins[2048];  // radix bins; reused as kept-list storage
+  __shared__ uint2 s_c[kRowGatherCap];
+  __shared__ float s_m;
+  __shared__ int s_argmax, s_total, s_overflow, s_nk;
+  __shared__ double s_S;
+  __shared__ int s_off[1];
+
+  if (tid == 0) {
+    float m = -INFINITY;
+    int am = INT_MAX, total = 0, ovf = 0;
+    for (int c = 0; c < dm.nchunks; ++c) {
+      const ChunkPart p = parts[c];
+      if (p.vmax > m) {
+        m = p.vmax;
+        am = p.argmax;
+      }
+      total += p.count;
+      ovf |= p.overflow;
+    }
+    double S = 0.0;
+    if (!sp.greedy && !sp.compact) {
+      for (int c = 0; c < dm.nchunks; ++c) {
+        const ChunkPart p = parts[c];
+        if (p.sum > 0.0) S += p.sum * exp((double)(p.vmax - m) / (double)sp.temperature);
+      }
+    }
+    s_m = m;
+    s_argmax = am;
+    s_total = total;
+    s_overflow = ovf;
+    s_S = S;
+    s_off[0] = 0;
+  }
+  __syncthreads();
+  const float m = s_m;
+  RowStat out;
+  out.m = m;
+  out.argmax = -1;
+  out.nkept = -1;
+  out.pad = 0;
+
+  if (sp.greedy) {
+    if (tid == 0) {
+      out.thr = -INFINITY;
+      out.S = 1.0;
+      out.argmax = s_argmax;
+      out.nkept = 1;
+      out.kind = kRowGreedy;
+      ws.rstat[r] = out;
+    }
+    return;
+  }
+
+  const float it = sp.inv_t;
+  uint32_t lower_key = 0;       // exact top-k threshold key once known
+  bool have_topk_key = false;
+
+  if (sp.compact && !s_overflow && s_total <= kRowGatherCap) {
+    // gather the chunks' candidates (canonical keys) into LDS, chunk order
+    int off = 0;
+    for (int c = 0; c < dm.nchunks; ++c) {
+      const int cnt = parts[c].count;
+      const uint2* src = ws.cand + ((size_t)r * dm.nchunks + c) * kChunkCap;
+      for (int j = tid; j < cnt; j += kThreads) {
+        uint2 e = src[j];
+        e.y = Tr<E>::canon(e.y);
+        s_c[off + j] = e;
+      }
+      off += cnt;
+    }
+    const int tot = off;
+    __syncthreads();
+    // k-th largest key among the candidates = the row's k-th largest
+    uint32_t x = 0;
+    for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+      const uint32_t cand = x | (1u << bit);
+      int local = 0;
+      for (int j = tid; j < tot; j += kThreads) local += (s_c[j].y >= cand);
+      if (block_sum_i(local, red) >= sp.top_k) x = cand;
+    }
+    lower_key = x;
+    have_topk_key = true;
+    // kept = candidates with key >= x, placed by their rank in index order
+    uint2* s_k = reinterpret_cast<uint2*>(s_bins);  // up to kKeptCap entries (8 KB)
+    int nk_local = 0;
+    for (int j = tid; j < tot; j += kThreads) nk_local += (s_c[j].y >= x);
+    const int nk = block_sum_i(nk_local, red);
+    if (nk <= kKeptCap) {
+      for (int j = tid; j < tot; j += kThreads) {
+        const uint2 e = s_c[j];
+        if (e.y < x) continue;
+        int rank = 0;
+        for (int i = 0; i < tot; ++i) rank += (s_c[i].y >= x) && (s_c[i].x < e.x);
+        s_k[rank] = e;
+      }
+      __syncthreads();
+      // exponentials in index order
+      double* s_e = reinterpret_cast<double*>(s_bins) + kKeptCap;  // second 8 KB
+      for (int j = tid; j < nk; j += kThreads)
+        s_e[j] = (double)expf((Tr<E>::key_to_float(s_k[j].y) - m) * it);
+      __syncthreads();
+      double part = 0.0;
+      for (int j = tid; j < nk; j += kThreads) part += s_e[j];
+      double S = block_sum_d(part, red);
+      float thr = Tr<E>::key_to_float(x);
+      int nkeep = nk;
+      if (sp.top_p < 1.0f) {
+        // order by (z descending, index ascending); s_c is free now
+        __syncthreads();
+        int* s_ord = reinterpret_cast<int*>(s_c);
+        for (int j = tid; j < nk; j += kThreads) {
+          const uint32_t kj = s_k[j].y;
+          int rank = 0;
+          for (int i = 0; i < nk; ++i) {
+            const uint32_t ki = s_k[i].y;
+            rank += (ki > kj) || (ki == kj && i < j);
+          }
+          s_ord[rank] = j;
+        }
+        __syncthreads();
+        if (tid == 0) {
+          const double P = (double)sp.top_p;
+          double cum = 0.0;
+          uint32_t tkey = s_k[s_ord[nk - 1]].y;
+          for (int q = 0; q < nk; ++q) {
+            const int j = s_ord[q];
+            cum += s_e[j] / S;
+            if (cum >= P) {
+              tkey = s_k[j].y;
+              break;
+            }
+          }
+          // keep z >= the boundary value, preserving index order
+          int w = 0;
+          double S2 = 0.0;
+          for (int j = 0; j < nk; ++j) {
+            if (s_k[j].y >= tkey) {
+              s_k[w] = s_k[j];
+              s_e[w] = s_e[j];
+              S2 += s_e[j];
+              ++w;
+            }
+          }
+          s_nk = w;
+          s_S = S2;
+          s_off[0] = (int)tkey;
+        }
+        __syncthreads();
+        nkeep = s_nk;
+        S = s_S;
+        thr = Tr<E>::key_to_float((uint32_t)s_off[0]);
+      }
+      uint2* dst = ws.kept + (size_t)r * kKeptCap;
+      for (int j = tid; j < nkeep; j += kThreads)
+        dst[j] = make_uint2(s_k[j].x, __float_as_uint(Tr<E>::key_to_float(s_k[j].y)));
+      if (tid == 0) {
+        out.thr = thr;
+        out.S = S;
+        out.nkept = nkeep;
+        out.kind = kRowCompact;
+        ws.rstat[r] = out;
+      }
+      return;
+    }
+    __syncthreads();
+  }
+
+  // Whole-row path: exact selections by re-reading the row.
+  const bool topk_on = sp.top_k > 0 && sp.top_k < dm.V;
+  if (topk_on && !have_topk_key)
+    lower_key = radix_select<E, VEC, false>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins, red);
+  if (sp.top_p < 1.0f)
+    lower_key =
+        radix_select<E, VEC, true>(row, dm.V, m, it, lower_key, (double)sp.top_p, s_bins, red);
+  const bool trunc = topk_on || sp.top_p < 1.0f;
+  const float thr = (trunc && lower_key) ? Tr<E>::key_to_float(lower_key) : -INFINITY;
+  double S = trunc ? dense_sum<E, VEC>(row, dm.V, m, it, thr, red) : s_S;
+  if (tid == 0) {
+    out.thr = thr;
+    out.S = S;
+    out.kind = kRowDense;
+    ws.rstat[r] = out;
+  }
+}
+
+// Unnormalised weight of a logit in a row's kept set: exp((z - m) / T) in fp32.
+__device__ __forceinline__ float kept_exp(float z, const RowStat& rs, float it) {
+  return z >= rs.thr ? expf((z - rs.m) * it) : 0.0f;
+}
+
+template <class E>
+__device__ __forceinline__ float load_logit(const E* row, int idx) {
+  return Tr<E>::to_float(Tr<E>::bits_of(row[idx]));
+}
+
+// ------------------------------------------------------------------------------------------
+// k_seq: one wave per sequence.  Accept tests (lane k = position k), first rejection, and the
+// final draw when the final row is greedy or compact.
+// ------------------------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
+                                                     const E* __restrict__ drf, Dims dm,
+                                                     Samp sp, Workspace ws,
+                                                     const int32_t* __restrict__ drafts,
+                                                     const float* __restrict__ uni,
+                                                     int32_t* __restrict__ out_tokens,
+                                                     int32_t* __restrict__ out_n,
+                                                     float* __restrict__ out_a,
+                                                     float* __restrict__ out_q,
+                                                     float* __restrict__ out_p) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int K = dm.K, V = dm.V;
+  const double T = (double)sp.temperature;
+  __shared__ double s_w[kKeptCap];
+  __shared__ double s_q[kKeptCap];
+
+  int n = K;
+  bool found = false;
+  for (int k0 = 0; k0 < K; k0 += kSeqThreads) {
+    const int k = k0 + lane;
+    bool rej = false;
+    if (k < K) {
+      const int x = drafts[(size_t)b * K + k];
+      const RowStat rt = ws.rstat[target_row(dm, b, k)];
+      const RowStat rd = ws.rstat[draft_row(dm, b, k)];
+      double q = 0.0, p = 0.0;
+      if (x >= 0 && x < V) {
+        if (sp.greedy) {
+          q = (x == rt.argmax) ? 1.0 : 0.0;
+          p = (x == rd.argmax) ? 1.0 : 0.0;
+        } else {
+          const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
+          const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
+          const float zt = load_logit(trow, x);
+          const float zd = load_logit(drow, x);
+          if (zt >= rt.thr) q = exp(((double)zt - (double)rt.m) / T) / rt.S;
+          if (zd >= rd.thr) p = exp(((double)zd - (double)rd.m) / T) / rd.S;
+        }
+      }
+      double a;
+      if (p > 0.0) {
+        a = q / ((double)sp.lenience * p);
+        a = a < 1.0 ? a : 1.0;
+      } else {
+        a = q > 0.0 ? 1.0 : 0.0;
+      }
+      rej = !((double)uni[(size_t)b * (K + 1) + k] < a);
+      if (out_a) out_a[(size_t)b * K + k] = (float)a;
+      if (out_q) out_q[(size_t)b * K + k] = (float)q;
+      if (out_p) out_p[(size_t)b * K + k] = (float)p;
+    }
+    const unsigned long long mask = __ballot(rej);
+    if (!found && mask) {
+      n = k0 + __ffsll((long long)mask) - 1;
+      found = true;
+    }
+  }
+
+  // accepted drafts and padding
+  for (int j = lane; j <= K; j += kSeqThreads) {
+    if (j < n) out_tokens[(size_t)b * (K + 1) + j] = drafts[(size_t)b * K + j];
+    if (j > n) out_tokens[(size_t)b * (K + 1) + j] = -1;
+  }
+  if (lane == 0) out_n[b] = n;
+
+  const RowStat rt = ws.rstat[target_row(dm, b, n)];
+  SeqState st;
+  st.n = n;
+  st.need_dense = 0;
+  st.fallback = 0;
+  st.pad = 0;
+  int tok = -1;
+  if (rt.kind == kRowGreedy) {
+    // one-hot q and p: the residual is one-hot at the target argmax or empty (then q is used)
+    tok = rt.argmax;
+  } else if (rt.kind == kRowCompact) {
+    const float it = sp.inv_t;
+    const int nk = rt.nkept;
+    const uint2* kept = ws.kept + (size_t)target_row(dm, b, n) * kKeptCap;
+    const bool resid = n < K;
+    RowStat rd;
+    const E* drow = nullptr;
+    if (resid) {
+      rd = ws.rstat[draft_row(dm, b, n)];
+      drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
+    }
+    for (int j = lane; j < nk; j += kSeqThreads) {
+      const uint2 e = kept[j];
+      const double q = (double)expf((__uint_as_float(e.y) - rt.m) * it) / rt.S;
+      double w = q;
+      if (resid) {
+        const double p = (double)kept_exp(load_logit(drow, (int)e.x), rd, it) / rd.S;
+        w = q - p > 0.0 ? q - p : 0.0;
+      }
+      s_q[j] = q;
+      s_w[j] = w;
+    }
+    __syncthreads();
+    if (lane == 0) {
+      double W = 0.0;
+      for (int j = 0; j < nk; ++j) W += s_w[j];
+      const double* wv = s_w;
+      if (!(W > 0.0)) {
+        st.fallback = 1;
+        W = 0.0;
+        for (int j = 0; j < nk; ++j) W += s_q[j];
+        wv = s_q;
+      }
+      const double target = (double)uni[(size_t)b * (K + 1) + K] * W;
+      double cum = 0.0;
+      int pick = -1, last_pos = -1;
+      for (int j = 0; j < nk; ++j) {
+        if (wv[j] > 0.0) last_pos = j;
+        cum += wv[j];
+        if (pick < 0 && cum > target) pick = j;
+      }
+      if (pick < 0) pick = last_pos;
+      if (pick < 0) pick = 0;
+      tok = (int)kept[pick].x;
+    }
+  } else {
+    st.need_dense = 1;
+  }
+  if (lane == 0) {
+    if (!st.need_dense) out_tokens[(size_t)b * (K + 1) + n] = tok;
+    ws.seq[b] = st;
+  }
+}
+
+// Weight of element z of the final row pair: (q - p)_+ (residual) or q (bonus / fallback).
+__device__ __forceinline__ double final_weight(float zt, float zd, const RowStat& rt,
+                                               const RowStat& rd, bool resid, bool use_q,
+                                               float it) {
+  const double q = (double)kept_exp(zt, rt, it) / rt.S;
+  if (!resid || use_q) return q;
+  const double p = (double)kept_exp(zd, rd, it) / rd.S;
+  return q - p > 0.0 ? q - p : 0.0;
+}
+
+// Load elements [e0, e0 + EPV) of a row as floats; past the row end: -inf (weight 0).
+template <class E, bool VEC>
+__device__ __forceinline__ void load_vec_f(const E* row, int V, int e0, float (&z)[Tr<E>::kEpv]) {
+  constexpr int EPV = Tr<E>::kEpv;
+  if constexpr (VEC) {
+    if (e0 < V) {
+      const uint4 x = *reinterpret_cast<const uint4*>(row + e0);
+      const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h)
+          z[d * Tr<E>::kPerDword + h] = Tr<E>::elem(w[d], h);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) z[e] = -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) z[e] = (e0 + e < V) ? load_logit(row, e0 + e) : -INFINITY;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// k_final_partial: grid = B x chunks; mass of the final weights per chunk (residual, target).
+// ------------------------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict__ tgt,
+                                                            const E* __restrict__ drf, Dims dm,
+                                                            Samp sp, Workspace ws) {
+  const int b = blockIdx.x / dm.nchunks;
+  const int c = blockIdx.x - b * dm.nchunks;
+  const SeqState st = ws.seq[b];
+  if (!st.need_dense) return;
+  __shared__ RedScratch red;
+  const int n = st.n;
+  const bool resid = n < dm.K;
+  const RowStat rt = ws.rstat[target_row(dm, b, n)];
+  RowStat rd = rt;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
+  const E* drow = trow;
+  if (resid) {
+    rd = ws.rstat[draft_row(dm, b, n)];
+    drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
+  }
+  constexpr int EPV = Tr<E>::kEpv;
+  const int c0 = c * dm.chunk_elems;
+  const int clen = min(dm.chunk_elems, dm.V - c0);
+  const int nvec = (clen + EPV - 1) / EPV;
+  const float it = sp.inv_t;
+  double W = 0.0, Q = 0.0;
+  for (int v = threadIdx.x; v < nvec; v += kThreads) {
+    float zt[EPV], zd[EPV];
+    load_vec_f<E, VEC>(trow, dm.V, c0 + v * EPV, zt);
+    if (resid) load_vec_f<E, VEC>(drow, dm.V, c0 + v * EPV, zd);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      W += final_weight(zt[e], resid ? zd[e] : 0.f, rt, rd, resid, false, it);
+      Q += final_weight(zt[e], 0.f, rt, rd, false, true, it);
+    }
+  }
+  W = block_sum_d(W, red);
+  Q = block_sum_d(Q, red);
+  if (threadIdx.x == 0) ws.fpart[(size_t)b * dm.nchunks + c] = make_double2(W, Q);
+}
+
+// ------------------------------------------------------------------------------------------
+// k_final_pick: grid = B.  Chooses the chunk holding u*W, then scans it in index order.
+// ------------------------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ tgt,
+                                                         const E* __restrict__ drf, Dims dm,
+                                                         Samp sp, Workspace ws,
+                                                         const float* __restrict__ uni,
+                                                         int32_t* __restrict__ out_tokens) {
+  const int b = blockIdx.x;
+  const SeqState st = ws.seq[b];
+  if (!st.need_dense) return;
+  const int tid = threadIdx.x;
+  __shared__ RedScratch red;
+  __shared__ double s_scan[kThreads];
+  __shared__ double s_before, s_target;
+  __shared__ int s_chunk, s_useq;
+  const int n = st.n;
+  const int K = dm.K;
+  const bool resid = n < K;
+  const double2* fp = ws.fpart + (size_t)b * dm.nchunks;
+  if (tid == 0) {
+    double W = 0.0;
+    for (int c = 0; c < dm.nchunks; ++c) W += fp[c].x;
+    int useq = !(W > 0.0) || !resid;
+    if (useq) {
+      W = 0.0;
+      for (int c = 0; c < dm.nchunks; ++c) W += fp[c].y;
+    }
+    const double target = (double)uni[(size_t)b * (K + 1) + K] * W;
+    double cum = 0.0;
+    int ch = -1, lastpos = 0;
+    double before_last = 0.0;
+    for (int c = 0; c < dm.nchunks; ++c) {
+      const double v = useq ? fp[c].y : fp[c].x;
+      if (v > 0.0) {
+        lastpos = c;
+        before_last = cum;
+      }
+      if (cum + v > target) {
+        ch = c;
+        break;
+      }
+      cum += v;
+    }
+    if (ch < 0) {
+      ch = lastpos;
+      cum = before_last;
+    }
+    s_chunk = ch;
+    s_before = cum;
+    s_target = target;
+    s_useq = useq;
+    if (resid && !(useq == 0)) {
+      // residual had zero mass: q is used (reported)
+      SeqState s2 = st;
+      s2.fallback = 1;
+      ws.seq[b] = s2;
+    }
+  }
+  __syncthreads();
+  const int c = s_chunk;
+  const bool use_q = s_useq != 0;
+  const double target = s_target;
+  const RowStat rt = ws.rstat[target_row(dm, b, n)];
+  RowStat rd = rt;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
+  const E* drow = trow;
+  if (resid) {
+    rd = ws.rstat[draft_row(dm, b, n)];
+    drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
+  }
+  constexpr int EPV = Tr<E>::kEpv;
+  const int c0 = c * dm.chunk_elems;
+  const int clen = min(dm.chunk_elems, dm.V - c0);
+  const int nvec = (clen + EPV - 1) / EPV;
+  const float it = sp.inv_t;
+  double carry = s_before;
+  int pick = INT_MAX, lastpos = -1;
+  for (int v0 = 0; v0 < nvec; v0 += kThreads) {
+    const int v = v0 + tid;
+    double w[EPV];
+    double local = 0.0;
+    {
+      float zt[EPV], zd[EPV];
+      if (v < nvec) {
+        load_vec_f<E, VEC>(trow, dm.V, c0 + v * EPV, zt);
+        if (resid) load_vec_f<E, VEC>(drow, dm.V, c0 + v * EPV, zd);
+      }
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        w[e] = (v < nvec) ? final_weight(zt[e], resid ? zd[e] : 0.f, rt, rd, resid, use_q, it)
+                          : 0.0;
+        local += w[e];
+      }
+    }
+    // inclusive scan of `local` over the 256 threads (index order), fp64
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const double add = tid >= off ? s_scan[tid - off] : 0.0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    double cum = carry + (s_scan[tid] - local);
+    int mine = INT_MAX, mylast = -1;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      if (w[e] > 0.0) mylast = c0 + v * EPV + e;
+      cum += w[e];
+      if (mine == INT_MAX && cum > target && w[e] > 0.0) mine = c0 + v * EPV + e;
+    }
+    const double round_total = s_scan[kThreads - 1];
+    const int got = block_min_i(mine, red);
+    const int lp = block_max_i(mylast, red);
+    if (lp > lastpos) lastpos = lp;
+    if (got != INT_MAX) {
+      pick = got;
+      break;
+    }
+    carry += round_total;
+  }
+  if (tid == 0) out_tokens[(size_t)b * (K + 1) + n] = pick != INT_MAX ? pick : lastpos;
+}
+
+// ------------------------------------------------------------------------------------------
+// Tree walk: one wave per sequence.  Node argmaxes from the chunk parts (first chunk wins
+// ties, so the lowest index), then acceptance in index order (parents precede children).
+// ------------------------------------------------------------------------------------------
+constexpr int kTreeMaxNodes = 2048;
+
+__global__ __launch_bounds__(kSeqThreads) void k_tree_walk(Dims dm, Workspace ws,
+                                                           const int32_t* __restrict__ parent,
+                                                           const int32_t* __restrict__ tokens,
+                                                           int max_depth,
+                                                           int32_t* __restrict__ out_tokens,
+                                                           int32_t* __restrict__ out_n,
+                                                           int32_t* __restrict__ out_last) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int N = dm.K;  // nodes per tree (stored in K for the tree launch)
+  __shared__ int s_g[kTreeMaxNodes];
+  __shared__ int s_par[kTreeMaxNodes];
+  __shared__ int s_tok[kTreeMaxNodes];
+  __shared__ int s_depth[kTreeMaxNodes];
+  __shared__ unsigned char s_acc[kTreeMaxNodes];
+  for (int i = lane; i < N; i += kSeqThreads) {
+    const ChunkPart* p = ws.parts + ((size_t)b * N + i) * dm.nchunks;
+    float best = p[0].vmax;
+    int am = p[0].argmax;
+    for (int c = 1; c < dm.nchunks; ++c) {
+      if (p[c].vmax > best) {
+        best = p[c].vmax;
+        am = p[c].argmax;
+      }
+    }
+    s_g[i] = am;
+    s_par[i] = parent[(size_t)b * N + i];
+    s_tok[i] = tokens[(size_t)b * N + i];
+  }
+  __syncthreads();
+  if (lane == 0) {
+    s_acc[0] = 1;
+    s_depth[0] = 0;
+    int best = 0;
+    for (int i = 1; i < N; ++i) {
+      const int par = s_par[i];
+      s_acc[i] = 0;
+      s_depth[i] = 0;
+      if (par < 0 || par >= i) continue;
+      const int dep = s_depth[par] + 1;
+      s_depth[i] = dep;
+      s_acc[i] = s_acc[par] && dep <= max_depth && s_tok[i] == s_g[par];
+      if (s_acc[i] && dep > s_depth[best]) best = i;
+    }
+    const int depth = s_depth[best];
+    int32_t* o = out_tokens + (size_t)b * (max_depth + 1);
+    int i = best;
+    for (int j = depth - 1; j >= 0; --j) {
+      o[j] = s_tok[i];
+      i = s_par[i];
+    }
+    o[depth] = s_g[best];
+    for (int j = depth + 1; j <= max_depth; ++j) o[j] = -1;
+    out_n[b] = depth;
+    if (out_last) out_last[b] = best;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Launch helpers
+// ------------------------------------------------------------------------------------------
+template <class E, bool VEC>
+hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& sp,
+                           const int32_t* drafts, const float* uni, int32_t* out_tokens,
+                           int32_t* out_n, float* out_a, float* out_q, float* out_p,
+                           const Workspace& ws, hipStream_t st, hipEvent_t* ev, int nev) {
+  if (ev && nev >= 1) (void)hipEventRecord(ev[0], st);
+  const unsigned grid_chunks = (unsigned)((size_t)dm.rows * dm.nchunks);
+  if (sp.greedy)
+    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkArgmax>), dim3(grid_chunks), dim3(kThreads), 0, st,
+                       t, d, dm, sp, ws);
+  else if (sp.compact)
+    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkTopK>), dim3(grid_chunks), dim3(kThreads), 0, st,
+                       t, d, dm, sp, ws);
+  else
+    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkDense>), dim3(grid_chunks), dim3(kThreads), 0, st,
+                       t, d, dm, sp, ws);
+  if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
+  hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
+  hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, drafts,
+                     uni, out_tokens, out_n, out_a, out_q, out_p);
+  if (!sp.greedy) {
+    hipLaunchKernelGGL((k_final_partial<E, VEC>), dim3((unsigned)((size_t)dm.B * dm.nchunks)),
+                       dim3(kThreads), 0, st, t, d, dm, sp, ws);
+    hipLaunchKernelGGL((k_final_pick<E, VEC>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm, sp,
+                       ws, uni, out_tokens);
+  }
+  if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, const Dims& d,
+                         const Samp& s, const int32_t* drafts, const float* uniforms,
+                         int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
+                         float* out_p, const Workspace& ws, hipStream_t stream,
+                         hipEvent_t* events, int n_events) {
+  (void)hipGetLastError();  // clear a stale error so the status reflects these launches
+  if (dt == SV_DTYPE_BF16) {
+    auto t = static_cast<const uint16_t*>(target);
+    auto dr = static_cast<const uint16_t*>(draft);
+    if (d.vec)
+      return launch_verify_t<uint16_t, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
+                                             out_a, out_q, out_p, ws, stream, events, n_events);
+    return launch_verify_t<uint16_t, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
+                                            out_a, out_q, out_p, ws, stream, events, n_events);
+  }
+  auto t = static_cast<const float*>(target);
+  auto dr = static_cast<const float*>(draft);
+  if (d.vec)
+    return launch_verify_t<float, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
+                                        out_q, out_p, ws, stream, events, n_events);
+  return launch_verify_t<float, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
+                                       out_q, out_p, ws, stream, events, n_events);
+}
+
+hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,
+                       const int32_t* tokens, int max_depth, int32_t* out_tokens,
+                       int32_t* out_n, int32_t* out_last, const Workspace& ws,
+                       hipStream_t stream) {
+  (void)hipGetLastError();
+  Samp sp{};
+  sp.greedy = 1;
+  const unsigned grid = (unsigned)((size_t)d.rows * d.nchunks);
+  if (dt == SV_DTYPE_BF16) {
+    auto t = static_cast<const uint16_t*>(target);
+    if (d.vec)
+      hipLaunchKernelGGL((k_chunk<uint16_t, true, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
+                         stream, t, t, d, sp, ws);
+    else
+      hipLaunchKernelGGL((k_chunk<uint16_t, false, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
+                         stream, t, t, d, sp, ws);
+  } else {
+    auto t = static_cast<const float*>(target);
+    if (d.vec)
+      hipLaunchKernelGGL((k_chunk<float, true, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
+                         stream, t, t, d, sp, ws);
+    else
+      hipLaunchKernelGGL((k_chunk<float, false, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
+                         stream, t, t, d, sp, ws);
+  }
+  hipLaunchKernelGGL(k_tree_walk, dim3(d.B), dim3(kSeqThreads), 0, stream, d, ws, parent, tokens,
+                     max_depth, out_tokens, out_n, out_last);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,87 @@
+"""GPU parity of spec_verify_tree (greedy token-tree verification) against the CPU oracle."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.spec_verify_oracle as O
+from workloads import synthetic as S
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def _run(logits, parent, tokens, max_depth):
+    import speculative_sampling_verification_amd as svm
+    out = svm.spec_verify_tree(logits.cuda(), torch.from_numpy(parent).cuda(),
+                               torch.from_numpy(tokens).cuda(), max_depth)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _check(logits, parent, tokens, max_depth):
+    g = _run(logits, parent, tokens, max_depth)
+    o = O.tree_verify(logits.float().cpu().numpy(), parent, tokens, max_depth)
+    np.testing.assert_array_equal(g["num_accepted"], o["n"])
+    np.testing.assert_array_equal(g["last_node"], o["last_node"])
+    np.testing.assert_array_equal(g["tokens"], o["tokens"])
+    return g
+
+
+@pytest.mark.parametrize("planted", [True, False])
+def test_tree_full_size(planted):
+    _announce(f"tree B=32 N=64 V=32000 bf16 planted={planted}")
+    logits, parent, tokens = S.tree_inputs(32, 64, 32000, planted=planted, seed=41)
+    g = _check(logits, parent, tokens, 6)
+    if planted:
+        assert g["num_accepted"].max() >= 2
+
+
+def test_tree_ties_small_vocab_fp32_multichunk():
+    _announce("tree fp32 V=40000 (3 chunks) with argmax ties and duplicate sibling tokens")
+    logits, parent, tokens = S.tree_inputs(8, 64, 40000, planted=True, dtype="f32", seed=42)
+    logits = torch.round(logits * 2) / 2  # many ties
+    _check(logits, parent, tokens, 6)
+    tokens2 = tokens.copy()
+    tokens2[:, 1:] = tokens2[:, 1:] % 7  # heavy duplication of sibling tokens
+    _check(logits, parent, tokens2, 6)
+
+
+def test_tree_max_depth_and_invalid_parents():
+    _announce("tree with max_depth 2 and invalid parent entries")
+    logits, parent, tokens = S.tree_inputs(8, 64, 32000, planted=True, seed=43)
+    _check(logits, parent, tokens, 2)
+    _check(logits, parent, tokens, 0)
+    bad = parent.copy()
+    bad[:, 10] = 63
+    bad[:, 20] = -5
+    _check(logits, bad, tokens, 6)
+
+
+def test_tree_unaligned_vocab():
+    _announce("tree bf16 V=32001 (scalar loads)")
+    logits, parent, tokens = S.tree_inputs(4, 64, 32001, planted=True, seed=44)
+    _check(logits, parent, tokens, 6)
+
+
+def test_chain_tree_equals_greedy_spec_verify():
+    _announce("chain tree == spec_verify at temperature 0")
+    import speculative_sampling_verification_amd as svm
+    N, V, B = 8, 32000, 6
+    g = torch.Generator().manual_seed(45)
+    logits = torch.randn((B, N, V), generator=g).to(torch.bfloat16)
+    parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+    am = logits.float().argmax(dim=2).numpy()
+    rng = np.random.default_rng(45)
+    tokens = np.where(rng.random((B, N)) < 0.85, np.roll(am, 1, axis=1),
+                      rng.integers(0, V, (B, N))).astype(np.int32)
+    tr = _run(logits, parent, tokens, N - 1)
+    sv = svm.spec_verify(logits.cuda(), torch.randn((B, N - 1, V)).to(torch.bfloat16).cuda(),
+                         torch.from_numpy(tokens[:, 1:].copy()).cuda(),
+                         torch.rand((B, N)).cuda(), temperature=0.0)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(tr["num_accepted"], sv["num_accepted"].cpu().numpy())
+    np.testing.assert_array_equal(tr["tokens"], sv["tokens"].cpu().numpy())
