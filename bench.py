@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Verify-step throughput on one MI355X.
+
+Default workload: B=256 sequences, K=7 draft tokens, V=128256, bf16 logits, temperature 0.7,
+top-k 50 on both distributions (Zipf-shaped synthetic logits, see workloads/synthetic.py).
+A step is one spec_verify call over the whole batch: every target row (B*(K+1)) and draft row
+(B*K) is read, distributions formed, drafts accepted or rejected, and the final token drawn.
+Inputs are resident in HBM before the timed region; draft tokens are drawn on the GPU from the
+draft rows (spec_sample) beforehand.
+
+Prints one JSON line.  value = logit elements per second over the timed steps.  "roofline"
+covers the dominant kernel (the row-streaming kernel), timed with HIP events recorded on the
+library's stream around that kernel in every timed step.  "cpu_baseline" times the CPU oracle
+(numpy, float64, single process) on a bounded sample of the same workload.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verify throughput: logit elems/s + % HBM peak, B=256 K=7 V=128256 bf16"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+KERNEL_SOURCE = os.path.join(ROOT, "speculative_sampling_verification_amd", "csrc",
+                             "sv_kernels.hip")
+
+
+def _hip_runtime():
+    """The HIP runtime torch already loaded (the library binds to the same one)."""
+    paths = [l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l]
+    hip = ctypes.CDLL(paths[0])
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def _source_tag():
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:12]
+
+
+def _traffic_from_profiles(kernel, workload):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    tag = re.search(r"source_sha256_12:\s*([0-9a-f]+)", text)
+    fetch = re.search(r"fetch_bytes_per_launch:\s*([0-9.e+]+)", text)
+    write = re.search(r"write_bytes_per_launch:\s*([0-9.e+]+)", text)
+    if not (tag and fetch and write) or tag.group(1) != _source_tag():
+        return None
+    return float(fetch.group(1)) + float(write.group(1))
+
+
+def cpu_baseline(name, target, draft, budget_seqs):
+    """Time the CPU oracle on the first `budget_seqs` sequences of the same inputs."""
+    import numpy as np
+    import oracle.spec_verify_oracle as O
+    from workloads import synthetic as S
+    cfg = S.WORKLOADS[name]
+    B, K, V = cfg["B"], cfg["K"], cfg["V"]
+    nseq = min(B, budget_seqs)
+    tf = target[:nseq].float().cpu().numpy()
+    df = draft[:nseq].float().cpu().numpy()
+    T, k, P = np.float32(cfg["temperature"]), cfg["top_k"], np.float32(cfg["top_p"])
+    u_draw = S.philox_uniforms(101, (nseq, K))
+    drafts = np.stack([O.sample_rows(df[:, j], u_draw[:, j], T, k, P) for j in range(K)], axis=1)
+    u = S.philox_uniforms(102, (nseq, K + 1))
+    t0 = time.perf_counter()
+    O.spec_verify(tf, df, drafts, u, T, k, P, np.float32(cfg["lenience"]))
+    dt = time.perf_counter() - t0
+    elems = nseq * (2 * K + 1) * V
+    return {"value": elems / dt, "unit": "logit elems/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nseq} of {B} sequences of one step ({elems} logits), "
+                      f"{dt:.2f} s, numpy float64, one process"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the metric one)")
+    ap.add_argument("--cpu-seqs", type=int, default=128,
+                    help="sequences of the step the CPU oracle is timed on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference-mib", type=int, default=512,
+                    help="after the timed steps, copy a tensor of this size 3 times (a plain "
+                         "copy kernel of known size for calibrating rocprofv3 byte counters); "
+                         "0 disables")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the verify step is data-parallel over sequences and needs no exchange, so "
+              "N GPUs would each run this benchmark on their own share)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import speculative_sampling_verification_amd as svm
+    from workloads import synthetic as S
+
+    name = args.workload or S.METRIC_WORKLOAD
+    cfg = S.WORKLOADS[name]
+    if cfg["gen"] == "tree":
+        raise SystemExit("bench.py times spec_verify workloads; the tree workload is covered "
+                         "by the tests")
+    B, K, V = cfg["B"], cfg["K"], cfg["V"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    target, draft = S.workload_inputs(name, device=dev, seed=1)
+    kw = dict(temperature=cfg["temperature"], top_k=cfg["top_k"], top_p=cfg["top_p"],
+              lenience=cfg["lenience"])
+    u_draw = torch.from_numpy(S.philox_uniforms(2, (B * K,))).to(dev)
+    drafts = svm.spec_sample(draft.view(B * K, V), u_draw, temperature=cfg["temperature"],
+                             top_k=cfg["top_k"], top_p=cfg["top_p"]).view(B, K)
+    u = torch.from_numpy(S.philox_uniforms(3, (B, K + 1))).to(dev)
+    out = svm.spec_verify(target, draft, drafts, u, **kw)
+    torch.cuda.synchronize()
+
+    hip = _hip_runtime()
+
+    def new_event():
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    evs = [[new_event() for _ in range(3)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        svm.spec_verify(target, draft, drafts, u, out=out, **kw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        svm.spec_verify(target, draft, drafts, u, out=out, events=evs[i], **kw)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    def elapsed(a, b):
+        f = ctypes.c_float()
+        hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        return f.value
+
+    if args.copy_reference_mib > 0:
+        src = torch.empty(args.copy_reference_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    kern_ms = [elapsed(e[0], e[1]) for e in evs]
+    step_ms = [elapsed(e[0], e[2]) for e in evs]
+    gpu_region_ms = elapsed(evs[0][0], evs[-1][2])
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+
+    esz = target.element_size()
+    elems = B * (2 * K + 1) * V
+    logit_bytes = elems * esz
+    ms_per_step = wall * 1e3 / args.steps
+    kern_avg = float(np.mean(kern_ms))
+    achieved = logit_bytes / (kern_avg * 1e-3) / 1e9
+    dominant = "k_topk_row" if 0 < cfg["top_k"] <= 256 and cfg["temperature"] > 0 else "k_chunk"
+    traffic = _traffic_from_profiles(dominant, name)
+    n = out["num_accepted"].cpu().numpy()
+    a = out["accept_prob"].cpu().numpy()
+    res = {
+        "metric": METRIC,
+        "value": elems / (ms_per_step * 1e-3),
+        "unit": "logit elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {2: "bf16", 4: "f32"}[esz],
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "K": K, "V": V, "temperature": cfg["temperature"],
+                   "top_k": cfg["top_k"], "top_p": cfg["top_p"], "lenience": cfg["lenience"]},
+        "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel_ms": kern_avg,
+                     "algorithmic_bytes_per_launch": logit_bytes},
+        "rows_per_s": B * (2 * K + 1) / (ms_per_step * 1e-3),
+        "step_gbs": logit_bytes / (ms_per_step * 1e-3) / 1e9,
+        "step_frac_hbm_peak": logit_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "gpu_event_ms_per_step": float(np.median(step_ms)),
+        "gpu_region_ms_per_step": gpu_region_ms / args.steps,
+        "mean_accept_prob": float(a.mean()) if a.size else None,
+        "mean_tokens_per_call": float(n.mean() + 1.0),
+        "accepted_hist": np.bincount(n, minlength=K + 1).tolist(),
+        "source_sha256_12": _source_tag(),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -91,6 +91,7 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const size_t o_seq = c.take((size_t)d.B * sizeof(SeqState));
   const size_t o_fpart = c.take(s.greedy ? 0 : (size_t)d.B * nch * sizeof(double2));
   const size_t o_n = c.take((size_t)d.B * sizeof(int32_t));
+  const size_t o_cnt = c.take(s.compact ? (rows + (size_t)d.B) * sizeof(int) : 0);
   if (ws) {
     ws->parts = at<ChunkPart>(base, o_parts);
     ws->cand = s.compact ? at<uint2>(base, o_cand) : nullptr;
@@ -99,6 +100,8 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
     ws->seq = at<SeqState>(base, o_seq);
     ws->fpart = s.greedy ? nullptr : at<double2>(base, o_fpart);
     ws->nbuf = at<int32_t>(base, o_n);
+    ws->row_cnt = s.compact ? at<int>(base, o_cnt) : nullptr;
+    ws->seq_cnt = s.compact ? ws->row_cnt + rows : nullptr;
   }
   return c.off;
 }

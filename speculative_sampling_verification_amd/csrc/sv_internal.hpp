@@ -9,6 +9,8 @@
 //   k_seq     grid = B             : accept tests, first-rejection scan, and the final draw when
 //                                     the final row is compact or greedy
 //   k_final_partial / k_final_pick : the final draw over a full row pair when it is not compact
+// With compact top-k rows all of this runs in one launch, k_topk_fused (after k_zero clears its
+// counters): the last chunk of a row merges the row, the last row of a sequence finishes it.
 #pragma once
 
 #include <stddef.h>
@@ -90,6 +92,8 @@ struct Workspace {
   SeqState* seq;     // [B]
   double2* fpart;    // [B][nchunks]  (residual mass, target mass)
   int32_t* nbuf;     // [B] accepted counts when the caller does not want them
+  int* row_cnt;      // [rows] finished chunks per row        (compact only; zeroed per call)
+  int* seq_cnt;      // [B] merged rows per sequence            (compact only; zeroed per call)
 };
 
 inline int chunk_elems_for(sv_dtype dt) {

@@ -199,17 +199,32 @@ __device__ __forceinline__ void load_chunk(const E* __restrict__ row, int V, int
   constexpr int EPV = Tr<E>::kEpv;
   const int tid = threadIdx.x;
   if constexpr (VEC) {
-    const uint4* vp = reinterpret_cast<const uint4*>(row + c0);
+    // Raw buffer loads over [c0, c0 + clen): one per-lane offset register, the per-vector
+    // offsets in scalar registers, and the hardware range check returns 0 past the end
+    // instead of touching memory.  Logits are read exactly once, so the loads are
+    // non-temporal (cache policy bit 1) and do not displace the small per-row summaries.
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(row + c0), (short)0, clen * (int)sizeof(E), 0x00020000);
     const int nvec = clen / EPV;  // clen is a multiple of EPV when VEC
 #pragma unroll
     for (int i = 0; i < kVecPerThread; ++i) {
-      const int v = tid + kThreads * i;
-      uint4 x = make_uint4(fill, fill, fill, fill);
-      if (v < nvec) x = vp[v];
+      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, i * kThreads * 16, 2);
       regs[4 * i + 0] = x.x;
       regs[4 * i + 1] = x.y;
       regs[4 * i + 2] = x.z;
       regs[4 * i + 3] = x.w;
+    }
+    if (nvec < kThreads * kVecPerThread) {  // ragged last tile: slots past the end get `fill`
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) {
+        if (tid + kThreads * i >= nvec) {
+          regs[4 * i + 0] = fill;
+          regs[4 * i + 1] = fill;
+          regs[4 * i + 2] = fill;
+          regs[4 * i + 3] = fill;
+        }
+      }
     }
   } else {
 #pragma unroll
@@ -448,14 +463,12 @@ __device__ double dense_sum(const E* row, int V, float m, float it, float thr, R
 // Largest key v with weight(key >= v) >= target, by most-significant-digit radix selection over
 // canonical keys, restricted to keys >= lower.  MASS: weight = exp((z - m) / T) in 2^-40 fixed
 // point (integer atomics, deterministic), target = ceil(P * total); else weight 1, target = k.
-template <class E, bool VEC, bool MASS>
+// Digits of D bits, most significant first (the last one may be narrower); s_bins holds 2^D.
+template <class E, bool VEC, bool MASS, int D = (Tr<E>::kKeyBits == 16 ? 8 : 11)>
 __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_t lower,
                                  double P_or_k, unsigned long long* s_bins, RedScratch& red) {
   constexpr int KB = Tr<E>::kKeyBits;
-  constexpr int NLEV = KB == 16 ? 2 : 3;
-  // digits, most significant first: 16-bit keys 8+8 bits, 32-bit keys 11+11+10 bits
-  constexpr int kShift[3] = {KB == 16 ? 8 : 21, KB == 16 ? 0 : 10, 0};
-  constexpr int kWidth[3] = {KB == 16 ? 8 : 11, KB == 16 ? 8 : 11, 10};
+  constexpr int NLEV = (KB + D - 1) / D;
   const int tid = threadIdx.x;
   __shared__ unsigned long long s_tot[kThreads];
   __shared__ unsigned long long s_target, s_above;
@@ -465,8 +478,8 @@ __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_
     s_prefix = 0;
   }
   for (int L = 0; L < NLEV; ++L) {
-    const int shift = kShift[L];
-    const int bits = kWidth[L];
+    const int shift = KB - (L + 1) * D > 0 ? KB - (L + 1) * D : 0;
+    const int bits = KB - L * D - shift;
     const int nb = 1 << bits;
     for (int j = tid; j < nb; j += kThreads) s_bins[j] = 0ull;
     __syncthreads();
@@ -736,35 +749,34 @@ __device__ __forceinline__ float load_logit(const E* row, int idx) {
   return Tr<E>::to_float(Tr<E>::bits_of(row[idx]));
 }
 
-// ------------------------------------------------------------------------------------------
-// k_seq: one wave per sequence.  Accept tests (lane k = position k), first rejection, and the
-// final draw when the final row is greedy or compact.
-// ------------------------------------------------------------------------------------------
+struct Outs {
+  const int32_t* drafts;  // [B, K]
+  const float* uni;       // [B, K+1]
+  int32_t* tokens;        // [B, K+1]
+  int32_t* n;             // [B]
+  float* a;               // [B, K] or null
+  float* q;               // [B, K] or null
+  float* p;               // [B, K] or null
+};
+
+// Accept tests of sequence b by one wave: lane k handles position k (Chen et al. notes, A2:
+// accept x~_k with probability min(1, q/p); lenience scales the comparison, App. F of the
+// Leviathan blog).  Writes a/q/p, the accepted drafts, the -1 padding after position n and n;
+// position n itself is written by the final draw.  Returns n in every lane.
 template <class E>
-__global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
-                                                     const E* __restrict__ drf, Dims dm,
-                                                     Samp sp, Workspace ws,
-                                                     const int32_t* __restrict__ drafts,
-                                                     const float* __restrict__ uni,
-                                                     int32_t* __restrict__ out_tokens,
-                                                     int32_t* __restrict__ out_n,
-                                                     float* __restrict__ out_a,
-                                                     float* __restrict__ out_q,
-                                                     float* __restrict__ out_p) {
-  const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+__device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
+                               const Dims& dm, const Samp& sp, const Workspace& ws,
+                               const Outs& o, int b) {
+  const int lane = lane_id();
   const int K = dm.K, V = dm.V;
   const double T = (double)sp.temperature;
-  __shared__ double s_w[kKeptCap];
-  __shared__ double s_q[kKeptCap];
-
   int n = K;
   bool found = false;
-  for (int k0 = 0; k0 < K; k0 += kSeqThreads) {
+  for (int k0 = 0; k0 < K; k0 += 64) {
     const int k = k0 + lane;
     bool rej = false;
     if (k < K) {
-      const int x = drafts[(size_t)b * K + k];
+      const int x = o.drafts[(size_t)b * K + k];
       const RowStat rt = ws.rstat[target_row(dm, b, k)];
       const RowStat rd = ws.rstat[draft_row(dm, b, k)];
       double q = 0.0, p = 0.0;
@@ -775,8 +787,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
         } else {
           const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
           const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
-          const float zt = load_logit(trow, x);
-          const float zd = load_logit(drow, x);
+          const float zt = Tr<E>::to_float(Tr<E>::bits_of(trow[x]));
+          const float zd = Tr<E>::to_float(Tr<E>::bits_of(drow[x]));
           if (zt >= rt.thr) q = exp(((double)zt - (double)rt.m) / T) / rt.S;
           if (zd >= rd.thr) p = exp(((double)zd - (double)rd.m) / T) / rd.S;
         }
@@ -788,10 +800,10 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
       } else {
         a = q > 0.0 ? 1.0 : 0.0;
       }
-      rej = !((double)uni[(size_t)b * (K + 1) + k] < a);
-      if (out_a) out_a[(size_t)b * K + k] = (float)a;
-      if (out_q) out_q[(size_t)b * K + k] = (float)q;
-      if (out_p) out_p[(size_t)b * K + k] = (float)p;
+      rej = !((double)o.uni[(size_t)b * (K + 1) + k] < a);
+      if (o.a) o.a[(size_t)b * K + k] = (float)a;
+      if (o.q) o.q[(size_t)b * K + k] = (float)q;
+      if (o.p) o.p[(size_t)b * K + k] = (float)p;
     }
     const unsigned long long mask = __ballot(rej);
     if (!found && mask) {
@@ -799,13 +811,31 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
       found = true;
     }
   }
-
-  // accepted drafts and padding
-  for (int j = lane; j <= K; j += kSeqThreads) {
-    if (j < n) out_tokens[(size_t)b * (K + 1) + j] = drafts[(size_t)b * K + j];
-    if (j > n) out_tokens[(size_t)b * (K + 1) + j] = -1;
+  for (int j = lane; j <= K; j += 64) {
+    if (j < n) o.tokens[(size_t)b * (K + 1) + j] = o.drafts[(size_t)b * K + j];
+    if (j > n) o.tokens[(size_t)b * (K + 1) + j] = -1;
   }
-  if (lane == 0) out_n[b] = n;
+  if (lane == 0) o.n[b] = n;
+  return n;
+}
+
+// ------------------------------------------------------------------------------------------
+// k_seq: one wave per sequence.  Accept tests, first rejection, and the final draw when the
+// final row is greedy or compact.
+// ------------------------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
+                                                     const E* __restrict__ drf, Dims dm,
+                                                     Samp sp, Workspace ws, Outs o) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int K = dm.K;
+  const float* uni = o.uni;
+  int32_t* out_tokens = o.tokens;
+  __shared__ double s_w[kKeptCap];
+  __shared__ double s_q[kKeptCap];
+
+  const int n = seq_accept_wave(tgt, drf, dm, sp, ws, o, b);
 
   const RowStat rt = ws.rstat[target_row(dm, b, n)];
   SeqState st;
@@ -1074,6 +1104,439 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
 }
 
 // ------------------------------------------------------------------------------------------
+// Compact top-k path, two launches and no communication between workgroups inside a launch
+// (on this GPU an agent-scope release per workgroup, needed to publish partial results to
+// another workgroup, costs far more than the streaming itself).
+//   k_topk_row : one workgroup per row streams the row in chunk-sized register tiles; each
+//                tile's candidates (key >= tau, tau = the k-th largest of the 256 per-thread
+//                maxima, which never exceeds the tile's k-th largest) are appended to an LDS
+//                list; at the end one wave selects the row's k-th largest among them (the row's
+//                top-k set, ties included, is contained in the union of the tiles' candidate
+//                sets) and writes (m, thr, S) and the kept tokens.
+//   k_seq_compact : one workgroup per sequence: accept tests, first rejection, final draw.
+// ------------------------------------------------------------------------------------------
+constexpr int kWaveCap = 128;      // candidates one wave may emit per tile
+constexpr int kRowCandCap = 1024;  // candidates one row may hold in LDS
+
+// Order-preserving barrier between lanes of one wave communicating through LDS.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+__device__ __forceinline__ unsigned long long lanes_below() {
+  return (1ull << lane_id()) - 1ull;
+}
+
+struct TileLds {
+  uint32_t tmax[kThreads];
+  uint2 wl[4 * kWaveCap];  // per-wave candidate lists of the current tile
+  int wcnt[4];
+  uint32_t tau, bmax;
+};
+
+// One tile [c0, c0 + clen) of the row: candidates appended to (s_key, s_idx) in (wave,
+// register, lane) order, so the list is identical on every run.  nrow, ovf and bmax are
+// updated identically in every thread.
+template <class E, bool VEC>
+__device__ void topk_tile(const E* __restrict__ row, int V, int k, int c0, int clen,
+                          TileLds& t, uint32_t* s_key, uint32_t* s_idx, int& nrow, int& ovf,
+                          uint32_t& bmax) {
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  uint32_t regs[kRegs];
+  load_chunk<E, VEC>(row, V, c0, clen, regs, Tr<E>::kKey0Pair);
+  uint32_t tm = 0;
+#pragma unroll
+  for (int j = 0; j < kRegs; ++j) {
+    regs[j] = Tr<E>::keys_of_dword(regs[j]);
+    tm = Tr<E>::dword_max(tm, regs[j]);
+  }
+  t.tmax[tid] = Tr<E>::dword_hmax(tm);
+  __syncthreads();
+  if (wv == 0) {
+    const uint32_t a0 = t.tmax[lane], a1 = t.tmax[lane + 64];
+    const uint32_t a2 = t.tmax[lane + 128], a3 = t.tmax[lane + 192];
+    uint32_t bm = max(max(a0, a1), max(a2, a3));
+    bm = wave_reduce(bm, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    uint32_t x = 0;
+    for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+      const uint32_t cand = x | (1u << bit);
+      const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand)) +
+                      __popcll(__ballot(a2 >= cand)) + __popcll(__ballot(a3 >= cand));
+      if (cnt >= k) x = cand;
+    }
+    if (x < 1u) x = 1u;                              // key 0 marks slots past the row end
+    if (x == Tr<E>::kKeyPos0) x = Tr<E>::kKeyNeg0;  // -0 equals +0
+    if (lane == 0) {
+      t.tau = x;
+      t.bmax = bm;
+    }
+  }
+  __syncthreads();
+  const uint32_t tau = t.tau;
+  const unsigned long long below = lanes_below();
+  uint2* mine = t.wl + wv * kWaveCap;
+  int wcount = 0;  // same value in every lane of the wave
+  auto push = [&](bool hit, int idx, uint32_t key) {
+    const unsigned long long m = __ballot(hit);
+    if (hit) {
+      const int pos = wcount + __popcll(m & below);
+      if (pos < kWaveCap) mine[pos] = make_uint2((uint32_t)idx, key);
+    }
+    wcount += __popcll(m);
+  };
+  if constexpr (Tr<E>::kPerDword == 2) {
+    const uint32_t tm1 = tau - 1u;
+    const uint32_t tpair = tm1 | (tm1 << 16);
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = regs[4 * i + d];
+        const bool any = Tr<E>::dword_max(w, tpair) != tpair;  // some half >= tau
+        if (__ballot(any)) {
+          const uint32_t k0 = w & 0xFFFFu, k1 = w >> 16;
+          push(any && k0 >= tau, slot_index<E>(c0, i, d, 0), k0);
+          push(any && k1 >= tau, slot_index<E>(c0, i, d, 1), k1);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const uint32_t w = regs[4 * i + d];
+        if (__ballot(w >= tau)) push(w >= tau, slot_index<E>(c0, i, d, 0), w);
+      }
+    }
+  }
+  if (lane == 0) t.wcnt[wv] = wcount;
+  __syncthreads();
+  int off = nrow, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int cw = t.wcnt[w];
+    ovf |= cw > kWaveCap;
+    const int cc = cw < kWaveCap ? cw : kWaveCap;
+    if (w < wv) off += cc;
+    total += cc;
+  }
+  const int cmine = t.wcnt[wv] < kWaveCap ? t.wcnt[wv] : kWaveCap;
+  for (int j = lane; j < cmine; j += 64) {
+    if (off + j < kRowCandCap) {
+      const uint2 e = mine[j];
+      s_idx[off + j] = e.x;
+      s_key[off + j] = Tr<E>::canon(e.y);
+    }
+  }
+  nrow += total;
+  ovf |= nrow > kRowCandCap;
+  bmax = t.bmax > bmax ? t.bmax : bmax;
+  __syncthreads();
+}
+
+// One wave: the row's k-th largest key among the `total` LDS candidates, then top-p on the
+// kept list if requested; writes RowStat and the kept list (candidate order).
+template <class E>
+__device__ void row_merge_lds(const Samp& sp, int r, const Workspace& ws, float m,
+                              const uint32_t* s_key, const uint32_t* s_idx, float* s_e,
+                              int total) {
+  const int lane = lane_id();
+  uint32_t x = 0;
+  for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+    const uint32_t cand = x | (1u << bit);
+    int c = 0;
+    for (int e0 = 0; e0 < total; e0 += 64) {
+      const int e = e0 + lane;
+      c += __popcll(__ballot(e < total && s_key[e] >= cand));
+    }
+    if (c >= sp.top_k) x = cand;
+  }
+  const float it = sp.inv_t;
+  double part = 0.0;
+  for (int e = lane; e < total; e += 64) {
+    float ev = 0.0f;
+    if (s_key[e] >= x) ev = expf((Tr<E>::key_to_float(s_key[e]) - m) * it);
+    s_e[e] = ev;
+    part += (double)ev;
+  }
+  double S = wave_reduce(part, [](double a, double b) { return a + b; });
+  uint32_t tkey = x;
+  if (sp.top_p < 1.0f) {
+    // For each kept entry, the mass of the kept entries ordered before it by (logit
+    // descending, index ascending); the boundary is the entry whose running sum first
+    // reaches P.
+    wave_lds_sync();
+    const double P = (double)sp.top_p;
+    uint32_t hit = 0;
+    for (int e = lane; e < total; e += 64) {
+      const uint32_t ke = s_key[e], ie = s_idx[e];
+      if (ke < x) continue;
+      double ex = 0.0;
+      for (int q = 0; q < total; ++q) {
+        const uint32_t kq = s_key[q];
+        if (kq >= x && (kq > ke || (kq == ke && s_idx[q] < ie))) ex += (double)s_e[q];
+      }
+      const double lo = ex / S, hi = (ex + (double)s_e[e]) / S;
+      if (hi >= P && lo < P) hit = ke;
+    }
+    hit = wave_reduce(hit, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+    if (hit != 0) tkey = hit;  // otherwise rounding left the total below P: keep everything
+    part = 0.0;
+    for (int e = lane; e < total; e += 64)
+      if (s_key[e] >= tkey) part += (double)s_e[e];
+    S = wave_reduce(part, [](double a, double b) { return a + b; });
+  }
+  uint2* dst = ws.kept + (size_t)r * kKeptCap;
+  const unsigned long long below = lanes_below();
+  int base = 0;
+  for (int e0 = 0; e0 < total; e0 += 64) {
+    const int e = e0 + lane;
+    const bool keep = e < total && s_key[e] >= tkey;
+    const unsigned long long mk = __ballot(keep);
+    if (keep)
+      dst[base + __popcll(mk & below)] =
+          make_uint2(s_idx[e], __float_as_uint(Tr<E>::key_to_float(s_key[e])));
+    base += __popcll(mk);
+  }
+  if (lane == 0) {
+    RowStat rs;
+    rs.m = m;
+    rs.thr = Tr<E>::key_to_float(tkey);
+    rs.S = S;
+    rs.argmax = -1;
+    rs.nkept = base;
+    rs.kind = kRowCompact;
+    rs.pad = 0;
+    ws.rstat[r] = rs;
+  }
+}
+
+// Whole-row fallback (all threads) when the candidates do not fit in LDS: exact selections
+// by re-reading the row, 8-bit radix digits (2 KB of bins).  Writes a dense RowStat.
+template <class E, bool VEC>
+__device__ void row_merge_block(const E* __restrict__ row, const Dims& dm, const Samp& sp, int r,
+                                const Workspace& ws, float m, unsigned long long* s_bins,
+                                RedScratch& red) {
+  const float it = sp.inv_t;
+  uint32_t key = radix_select<E, VEC, false, 8>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins,
+                                                 red);
+  if (sp.top_p < 1.0f)
+    key = radix_select<E, VEC, true, 8>(row, dm.V, m, it, key, (double)sp.top_p, s_bins, red);
+  const float thr = Tr<E>::key_to_float(key);
+  const double S = dense_sum<E, VEC>(row, dm.V, m, it, thr, red);
+  if (threadIdx.x == 0) {
+    RowStat rs;
+    rs.m = m;
+    rs.thr = thr;
+    rs.S = S;
+    rs.argmax = -1;
+    rs.nkept = -1;
+    rs.kind = kRowDense;
+    rs.pad = 0;
+    ws.rstat[r] = rs;
+  }
+}
+
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt,
+                                                       const E* __restrict__ drf, Dims dm,
+                                                       Samp sp, Workspace ws) {
+  const int r = blockIdx.x;
+  __shared__ TileLds t;
+  __shared__ uint32_t s_key[kRowCandCap];
+  __shared__ uint32_t s_idx[kRowCandCap];
+  __shared__ float s_e[kRowCandCap];
+  __shared__ unsigned long long s_bins[256];
+  __shared__ RedScratch red;
+  const E* row = row_ptr(dm, tgt, drf, r);
+  int nrow = 0, ovf = 0;
+  uint32_t bmax = 0;
+  for (int c = 0; c < dm.nchunks; ++c) {
+    const int c0 = c * dm.chunk_elems;
+    topk_tile<E, VEC>(row, dm.V, sp.top_k, c0, min(dm.chunk_elems, dm.V - c0), t, s_key, s_idx,
+                      nrow, ovf, bmax);
+  }
+  const float m = Tr<E>::key_to_float(bmax);
+  if (!ovf) {
+    if (wave_id() == 0) row_merge_lds<E>(sp, r, ws, m, s_key, s_idx, s_e, nrow);
+  } else {
+    row_merge_block<E, VEC>(row, dm, sp, r, ws, m, s_bins, red);
+  }
+}
+
+// Final draw over a compact row, one wave.  Weights (q - p)_+ (or q for the bonus row, or q
+// when the residual is empty); the token is the smallest index whose cumulative weight in
+// index order exceeds u * W.  Entries are staged in LDS (s_idx / s_w).
+template <class E>
+__device__ int final_draw_compact_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
+                                       const Dims& dm, const Samp& sp, const Workspace& ws, int b,
+                                       int n, double u, uint32_t* s_idx, double* s_w) {
+  const int lane = lane_id();
+  const RowStat rt = ws.rstat[target_row(dm, b, n)];
+  const int nk = rt.nkept;
+  const uint2* kept = ws.kept + (size_t)target_row(dm, b, n) * kKeptCap;
+  const bool resid = n < dm.K;
+  RowStat rd = rt;
+  const E* drow = nullptr;
+  if (resid) {
+    rd = ws.rstat[draft_row(dm, b, n)];
+    drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
+  }
+  const float it = sp.inv_t;
+  double Wp = 0.0;
+  for (int e = lane; e < nk; e += 64) {
+    const uint2 v = kept[e];
+    const double q = (double)expf((__uint_as_float(v.y) - rt.m) * it) / rt.S;
+    double w = q;
+    if (resid) {
+      const float zd = Tr<E>::to_float(Tr<E>::bits_of(drow[v.x]));
+      const double p = (double)kept_exp(zd, rd, it) / rd.S;
+      w = q - p > 0.0 ? q - p : 0.0;
+    }
+    s_idx[e] = v.x;
+    s_w[e] = w;
+    Wp += w;
+  }
+  double W = wave_reduce(Wp, [](double a, double c) { return a + c; });
+  if (!(W > 0.0)) {  // empty residual: draw from q
+    double Qp = 0.0;
+    for (int e = lane; e < nk; e += 64) {
+      const double q = (double)expf((__uint_as_float(kept[e].y) - rt.m) * it) / rt.S;
+      s_w[e] = q;
+      Qp += q;
+    }
+    W = wave_reduce(Qp, [](double a, double c) { return a + c; });
+  }
+  wave_lds_sync();
+  const double target = u * W;
+  uint32_t pick = 0xFFFFFFFFu;
+  int lastpos = -1;
+  for (int e = lane; e < nk; e += 64) {
+    const uint32_t ie = s_idx[e];
+    const double we = s_w[e];
+    double pre = 0.0;
+    for (int j = 0; j < nk; ++j)
+      if (s_idx[j] <= ie) pre += s_w[j];
+    if (we > 0.0) {
+      if (pre > target && ie < pick) pick = ie;
+      if ((int)ie > lastpos) lastpos = (int)ie;
+    }
+  }
+  pick = wave_reduce(pick, [](uint32_t a, uint32_t c) { return a < c ? a : c; });
+  lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
+  wave_lds_sync();
+  return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
+}
+
+// Final draw over a full row pair (all threads): totals, then a scan in index order.
+template <class E, bool VEC>
+__device__ int final_draw_dense_block(const E* __restrict__ trow, const E* __restrict__ drow,
+                                      const RowStat& rt, const RowStat& rd, bool resid, float it,
+                                      int V, double u, RedScratch& red, double* s_scan) {
+  constexpr int EPV = Tr<E>::kEpv;
+  const int tid = threadIdx.x;
+  const int nvec = (V + EPV - 1) / EPV;
+  double W = 0.0, Q = 0.0;
+  for (int v = tid; v < nvec; v += kThreads) {
+    float zt[EPV], zd[EPV];
+    load_vec_f<E, VEC>(trow, V, v * EPV, zt);
+    if (resid) load_vec_f<E, VEC>(drow, V, v * EPV, zd);
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      W += final_weight(zt[e], resid ? zd[e] : 0.f, rt, rd, resid, false, it);
+      Q += final_weight(zt[e], 0.f, rt, rd, false, true, it);
+    }
+  }
+  W = block_sum_d(W, red);
+  Q = block_sum_d(Q, red);
+  const bool use_q = !(W > 0.0) || !resid;
+  const double target = u * (use_q ? Q : W);
+  double carry = 0.0;
+  int pick = INT_MAX, lastpos = -1;
+  for (int v0 = 0; v0 < nvec; v0 += kThreads) {
+    const int v = v0 + tid;
+    double w[EPV];
+    double local = 0.0;
+    float zt[EPV], zd[EPV];
+    if (v < nvec) {
+      load_vec_f<E, VEC>(trow, V, v * EPV, zt);
+      if (resid) load_vec_f<E, VEC>(drow, V, v * EPV, zd);
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      w[e] = (v < nvec) ? final_weight(zt[e], resid ? zd[e] : 0.f, rt, rd, resid, use_q, it) : 0.0;
+      local += w[e];
+    }
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < kThreads; off <<= 1) {
+      const double add = tid >= off ? s_scan[tid - off] : 0.0;
+      __syncthreads();
+      s_scan[tid] += add;
+      __syncthreads();
+    }
+    double cum = carry + (s_scan[tid] - local);
+    int mine = INT_MAX, mylast = -1;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      if (w[e] > 0.0) mylast = v * EPV + e;
+      cum += w[e];
+      if (mine == INT_MAX && cum > target && w[e] > 0.0) mine = v * EPV + e;
+    }
+    const double round_total = s_scan[kThreads - 1];
+    const int got = block_min_i(mine, red);
+    const int lp = block_max_i(mylast, red);
+    if (lp > lastpos) lastpos = lp;
+    if (got != INT_MAX) {
+      pick = got;
+      break;
+    }
+    carry += round_total;
+  }
+  return pick != INT_MAX ? pick : lastpos;
+}
+
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_seq_compact(const E* __restrict__ tgt,
+                                                          const E* __restrict__ drf, Dims dm,
+                                                          Samp sp, Workspace ws, Outs o) {
+  const int b = blockIdx.x;
+  const int K = dm.K;
+  __shared__ double s_w[kKeptCap];
+  __shared__ uint32_t s_idx[kKeptCap];
+  __shared__ int s_n, s_kind;
+  __shared__ RedScratch red;
+  const double u = (double)o.uni[(size_t)b * (K + 1) + K];
+  if (wave_id() == 0) {
+    const int n = seq_accept_wave<E>(tgt, drf, dm, sp, ws, o, b);
+    const RowStat rt = ws.rstat[target_row(dm, b, n)];
+    if (lane_id() == 0) {
+      s_n = n;
+      s_kind = rt.kind;
+    }
+    if (rt.kind == kRowCompact) {
+      const int tok = final_draw_compact_wave<E>(tgt, drf, dm, sp, ws, b, n, u, s_idx, s_w);
+      if (lane_id() == 0) o.tokens[(size_t)b * (K + 1) + n] = tok;
+    }
+  }
+  __syncthreads();
+  if (s_kind != kRowCompact) {  // a row whose candidates overflowed: draw over the full rows
+    const int n = s_n;
+    const RowStat rt = ws.rstat[target_row(dm, b, n)];
+    const bool resid = n < K;
+    const RowStat rd = resid ? ws.rstat[draft_row(dm, b, n)] : rt;
+    const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
+    const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : trow;
+    const int tok = final_draw_dense_block<E, VEC>(trow, drow, rt, rd, resid, sp.inv_t, dm.V, u,
+                                                   red, s_w);
+    if (threadIdx.x == 0) o.tokens[(size_t)b * (K + 1) + n] = tok;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // Tree walk: one wave per sequence.  Node argmaxes from the chunk parts (first chunk wins
 // ties, so the lowest index), then acceptance in index order (parents precede children).
 // ------------------------------------------------------------------------------------------
@@ -1147,19 +1610,25 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
                            const Workspace& ws, hipStream_t st, hipEvent_t* ev, int nev) {
   if (ev && nev >= 1) (void)hipEventRecord(ev[0], st);
   const unsigned grid_chunks = (unsigned)((size_t)dm.rows * dm.nchunks);
+  const Outs o{drafts, uni, out_tokens, out_n, out_a, out_q, out_p};
+  if (sp.compact) {
+    hipLaunchKernelGGL((k_topk_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
+                       ws);
+    if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
+    hipLaunchKernelGGL((k_seq_compact<E, VEC>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm, sp,
+                       ws, o);
+    if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);
+    return hipGetLastError();
+  }
   if (sp.greedy)
     hipLaunchKernelGGL((k_chunk<E, VEC, kChunkArgmax>), dim3(grid_chunks), dim3(kThreads), 0, st,
-                       t, d, dm, sp, ws);
-  else if (sp.compact)
-    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkTopK>), dim3(grid_chunks), dim3(kThreads), 0, st,
                        t, d, dm, sp, ws);
   else
     hipLaunchKernelGGL((k_chunk<E, VEC, kChunkDense>), dim3(grid_chunks), dim3(kThreads), 0, st,
                        t, d, dm, sp, ws);
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
-  hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, drafts,
-                     uni, out_tokens, out_n, out_a, out_q, out_p);
+  hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
   if (!sp.greedy) {
     hipLaunchKernelGGL((k_final_partial<E, VEC>), dim3((unsigned)((size_t)dm.B * dm.nchunks)),
                        dim3(kThreads), 0, st, t, d, dm, sp, ws);
