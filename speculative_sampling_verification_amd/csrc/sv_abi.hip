@@ -84,24 +84,19 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   Carver c;
   const size_t rows = (size_t)d.rows, nch = (size_t)d.nchunks;
-  const size_t o_parts = c.take(rows * nch * sizeof(ChunkPart));
-  const size_t o_cand = c.take(s.compact ? rows * nch * kChunkCap * sizeof(uint2) : 0);
+  const size_t o_parts = c.take(s.compact ? 0 : rows * nch * sizeof(ChunkPart));
   const size_t o_rstat = c.take(rows * sizeof(RowStat));
   const size_t o_kept = c.take(s.compact ? rows * kKeptCap * sizeof(uint2) : 0);
   const size_t o_seq = c.take((size_t)d.B * sizeof(SeqState));
   const size_t o_fpart = c.take(s.greedy ? 0 : (size_t)d.B * nch * sizeof(double2));
   const size_t o_n = c.take((size_t)d.B * sizeof(int32_t));
-  const size_t o_cnt = c.take(s.compact ? (rows + (size_t)d.B) * sizeof(int) : 0);
   if (ws) {
-    ws->parts = at<ChunkPart>(base, o_parts);
-    ws->cand = s.compact ? at<uint2>(base, o_cand) : nullptr;
+    ws->parts = s.compact ? nullptr : at<ChunkPart>(base, o_parts);
     ws->rstat = at<RowStat>(base, o_rstat);
     ws->kept = s.compact ? at<uint2>(base, o_kept) : nullptr;
     ws->seq = at<SeqState>(base, o_seq);
     ws->fpart = s.greedy ? nullptr : at<double2>(base, o_fpart);
     ws->nbuf = at<int32_t>(base, o_n);
-    ws->row_cnt = s.compact ? at<int>(base, o_cnt) : nullptr;
-    ws->seq_cnt = s.compact ? ws->row_cnt + rows : nullptr;
   }
   return c.off;
 }

@@ -1,16 +1,16 @@
 // Internal declarations shared by the kernels (sv_kernels.hip) and the C ABI (sv_abi.hip).
 //
 // Data flow of one spec_verify call (all on the caller's stream):
-//   k_chunk   grid = rows x chunks : streams every logit once; per chunk a max (and a sum of
-//                                     exponentials, an argmax, or top-k candidates)
+//   k_chunk   grid = rows x chunks : streams every logit once; per chunk a max and a sum of
+//                                     exponentials (or an argmax when greedy)
 //   k_row     grid = rows          : merges the chunks of a row into its distribution
-//                                     parameters (max m, threshold thr, normaliser S), and for
-//                                     compact top-k rows the kept tokens sorted by index
+//                                     parameters (max m, threshold thr, normaliser S)
 //   k_seq     grid = B             : accept tests, first-rejection scan, and the final draw when
-//                                     the final row is compact or greedy
-//   k_final_partial / k_final_pick : the final draw over a full row pair when it is not compact
-// With compact top-k rows all of this runs in one launch, k_topk_fused (after k_zero clears its
-// counters): the last chunk of a row merges the row, the last row of a sequence finishes it.
+//                                     the final row is greedy
+//   k_final_partial / k_final_pick : the final draw over a full row pair
+// With compact top-k rows (top-k <= kCompactMaxK) two launches do everything: k_topk_row (one
+// workgroup per row: streaming, candidate selection and the row merge) and k_seq_compact (one
+// workgroup per sequence: accept tests and the final draw).
 #pragma once
 
 #include <stddef.h>
@@ -25,8 +25,6 @@ namespace sv {
 constexpr int kThreads = 256;        // threads per workgroup of the streaming kernels (4 waves)
 constexpr int kVecPerThread = 16;    // 16-byte vectors each thread holds per chunk
 constexpr int kCompactMaxK = 256;    // top-k <= this uses the compact candidate path
-constexpr int kChunkCap = 512;       // candidates one chunk may emit
-constexpr int kRowGatherCap = 4096;  // candidates one row merge may gather in LDS
 constexpr int kKeptCap = 1024;       // kept tokens a compact row may hold
 constexpr int kSeqThreads = 64;      // one wave per sequence
 
@@ -34,15 +32,13 @@ constexpr int kSeqThreads = 64;      // one wave per sequence
 enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
 
 // Mode of k_chunk.
-enum ChunkMode : int { kChunkDense = 0, kChunkArgmax = 1, kChunkTopK = 2 };
+enum ChunkMode : int { kChunkDense = 0, kChunkArgmax = 1 };
 
 struct alignas(16) ChunkPart {
   float vmax;      // largest logit of the chunk
   int argmax;      // lowest index holding vmax (argmax mode), else -1
   double sum;      // sum of exp((z - vmax) / T) over the chunk (dense mode), else 0
-  int count;       // candidates written (top-k mode)
-  int overflow;    // 1 if the chunk had more than kChunkCap candidates
-  int pad[2];
+  int pad[4];
 };
 
 struct alignas(16) RowStat {
@@ -86,14 +82,11 @@ struct Samp {
 
 struct Workspace {
   ChunkPart* parts;  // [rows][nchunks]
-  uint2* cand;       // [rows][nchunks][kChunkCap]  (index, key)   compact only
   RowStat* rstat;    // [rows]
   uint2* kept;       // [rows][kKeptCap]  (index, float bits)      compact only
   SeqState* seq;     // [B]
   double2* fpart;    // [B][nchunks]  (residual mass, target mass)
   int32_t* nbuf;     // [B] accepted counts when the caller does not want them
-  int* row_cnt;      // [rows] finished chunks per row        (compact only; zeroed per call)
-  int* seq_cnt;      // [B] merged rows per sequence            (compact only; zeroed per call)
 };
 
 inline int chunk_elems_for(sv_dtype dt) {

@@ -259,11 +259,6 @@ __device__ __forceinline__ int slot_index(int c0, int i, int d, int h) {
 // k_chunk: one workgroup per (row, chunk).  Reads each logit of the chunk once.
 //   dense : vmax and sum exp((z - vmax) / T) over the chunk
 //   argmax: vmax and the lowest index holding it
-//   top-k : vmax and every element with key >= tau, where tau = the k-th largest of the 256
-//           per-thread maxima.  tau never exceeds the chunk's k-th largest element (the k
-//           largest thread maxima are k distinct elements), and the row's k-th largest is at
-//           least the chunk's, so the union of the chunks' candidates holds every element of
-//           the row's top-k set, ties included.
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
@@ -281,144 +276,52 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
   uint32_t regs[kRegs];
   ChunkPart* part = ws.parts + (size_t)r * dm.nchunks + c;
 
-  if constexpr (MODE == kChunkTopK) {
-    __shared__ uint32_t s_tmax[kThreads];
-    __shared__ uint2 s_list[kChunkCap];
-    __shared__ uint32_t s_tau, s_bmax;
-    __shared__ int s_cnt;
-
-    load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kKey0Pair);
-    uint32_t tm = 0;
+  load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kNegInfPair);
+  float mx = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < kRegs; ++j) {
-      regs[j] = Tr<E>::keys_of_dword(regs[j]);
-      tm = Tr<E>::dword_max(tm, regs[j]);
-    }
-    s_tmax[tid] = Tr<E>::dword_hmax(tm);
-    if (tid == 0) s_cnt = 0;
-    __syncthreads();
-    if (wave_id() == 0) {
-      const int lane = lane_id();
-      const uint32_t a0 = s_tmax[lane], a1 = s_tmax[lane + 64];
-      const uint32_t a2 = s_tmax[lane + 128], a3 = s_tmax[lane + 192];
-      uint32_t bm = max(max(a0, a1), max(a2, a3));
-      bm = wave_reduce(bm, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
-      const int k = sp.top_k;
-      uint32_t x = 0;
-      for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
-        const uint32_t cand = x | (1u << bit);
-        const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand)) +
-                        __popcll(__ballot(a2 >= cand)) + __popcll(__ballot(a3 >= cand));
-        if (cnt >= k) x = cand;
-      }
-      if (x < 1u) x = 1u;                              // key 0 marks slots past the row end
-      if (x == Tr<E>::kKeyPos0) x = Tr<E>::kKeyNeg0;  // -0 equals +0
-      if (lane == 0) {
-        s_tau = x;
-        s_bmax = bm;
-      }
-    }
-    __syncthreads();
-    const uint32_t tau = s_tau;
-    if constexpr (Tr<E>::kPerDword == 2) {
-      const uint32_t tm1 = tau - 1u;
-      const uint32_t tpair = tm1 | (tm1 << 16);
+  for (int j = 0; j < kRegs; ++j) {
 #pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t w = regs[4 * i + d];
-          if (Tr<E>::dword_max(w, tpair) != tpair) {  // some half >= tau
-            const uint32_t k0 = w & 0xFFFFu, k1 = w >> 16;
-            if (k0 >= tau) {
-              const int pos = atomicAdd(&s_cnt, 1);
-              if (pos < kChunkCap) s_list[pos] = make_uint2(slot_index<E>(c0, i, d, 0), k0);
-            }
-            if (k1 >= tau) {
-              const int pos = atomicAdd(&s_cnt, 1);
-              if (pos < kChunkCap) s_list[pos] = make_uint2(slot_index<E>(c0, i, d, 1), k1);
-            }
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t w = regs[4 * i + d];
-          if (w >= tau) {
-            const int pos = atomicAdd(&s_cnt, 1);
-            if (pos < kChunkCap) s_list[pos] = make_uint2(slot_index<E>(c0, i, d, 0), w);
-          }
-        }
-      }
-    }
-    __syncthreads();
-    const int cnt = s_cnt;
-    const int nw = cnt < kChunkCap ? cnt : kChunkCap;
-    uint2* out = ws.cand + ((size_t)r * dm.nchunks + c) * kChunkCap;
-    for (int j = tid; j < nw; j += kThreads) out[j] = s_list[j];
-    if (tid == 0) {
-      ChunkPart p;
-      p.vmax = Tr<E>::key_to_float(s_bmax);
-      p.argmax = -1;
-      p.sum = 0.0;
-      p.count = nw;
-      p.overflow = cnt > kChunkCap;
-      p.pad[0] = p.pad[1] = 0;
-      *part = p;
-    }
-  } else {
-    load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kNegInfPair);
-    float mx = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kRegs; ++j) {
-#pragma unroll
-      for (int h = 0; h < Tr<E>::kPerDword; ++h) mx = fmaxf(mx, Tr<E>::elem(regs[j], h));
-    }
-    mx = block_max_f(mx, red);
-    ChunkPart p;
-    p.vmax = mx;
-    p.argmax = -1;
-    p.sum = 0.0;
-    p.count = 0;
-    p.overflow = 0;
-    p.pad[0] = p.pad[1] = 0;
-    if constexpr (MODE == kChunkDense) {
-      double s = 0.0;
-      if (mx > -INFINITY) {
-        const float it = sp.inv_t;
-#pragma unroll
-        for (int i = 0; i < kVecPerThread; ++i) {
-          float sv = 0.f;  // one vector's EPV terms in fp32, then into the fp64 total
-#pragma unroll
-          for (int d = 0; d < 4; ++d) {
-#pragma unroll
-            for (int h = 0; h < Tr<E>::kPerDword; ++h)
-              sv += expf((Tr<E>::elem(regs[4 * i + d], h) - mx) * it);
-          }
-          s += (double)sv;
-        }
-      }
-      p.sum = block_sum_d(s, red);
-    } else {
-      int best = INT_MAX;
-#pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
-            const int idx = slot_index<E>(c0, i, d, h);
-            if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx < best) best = idx;
-          }
-        }
-      }
-      p.argmax = block_min_i(best, red);
-    }
-    if (tid == 0) *part = p;
+    for (int h = 0; h < Tr<E>::kPerDword; ++h) mx = fmaxf(mx, Tr<E>::elem(regs[j], h));
   }
+  mx = block_max_f(mx, red);
+  ChunkPart p;
+  p.vmax = mx;
+  p.argmax = -1;
+  p.sum = 0.0;
+  p.pad[0] = p.pad[1] = p.pad[2] = p.pad[3] = 0;
+  if constexpr (MODE == kChunkDense) {
+    double s = 0.0;
+    if (mx > -INFINITY) {
+      const float it = sp.inv_t;
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) {
+        float sv = 0.f;  // one vector's EPV terms in fp32, then into the fp64 total
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+          for (int h = 0; h < Tr<E>::kPerDword; ++h)
+            sv += expf((Tr<E>::elem(regs[4 * i + d], h) - mx) * it);
+        }
+        s += (double)sv;
+      }
+    }
+    p.sum = block_sum_d(s, red);
+  } else {
+    int best = INT_MAX;
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+          const int idx = slot_index<E>(c0, i, d, h);
+          if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx < best) best = idx;
+        }
+      }
+    }
+    p.argmax = block_min_i(best, red);
+  }
+  if (tid == 0) *part = p;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -542,8 +445,8 @@ __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_
 }
 
 // ------------------------------------------------------------------------------------------
-// k_row: one workgroup per row.  Produces RowStat (m, thr, S) and, for compact top-k rows,
-// the kept tokens sorted by vocabulary index.
+// k_row: one workgroup per row.  Produces RowStat (m, thr, S) from the chunk partials; top-k
+// above the compact limit and top-p select their thresholds by re-reading the row.
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
@@ -554,27 +457,23 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
   const E* row = row_ptr(dm, tgt, drf, r);
   const ChunkPart* parts = ws.parts + (size_t)r * dm.nchunks;
   __shared__ RedScratch red;
-  __shared__ unsigned long long s_bins[2048];  // radix bins; reused as kept-list storage
-  __shared__ uint2 s_c[kRowGatherCap];
+  __shared__ unsigned long long s_bins[2048];  // radix bins
   __shared__ float s_m;
-  __shared__ int s_argmax, s_total, s_overflow, s_nk;
+  __shared__ int s_argmax;
   __shared__ double s_S;
-  __shared__ int s_off[1];
 
   if (tid == 0) {
     float m = -INFINITY;
-    int am = INT_MAX, total = 0, ovf = 0;
+    int am = INT_MAX;
     for (int c = 0; c < dm.nchunks; ++c) {
       const ChunkPart p = parts[c];
       if (p.vmax > m) {
         m = p.vmax;
         am = p.argmax;
       }
-      total += p.count;
-      ovf |= p.overflow;
     }
     double S = 0.0;
-    if (!sp.greedy && !sp.compact) {
+    if (!sp.greedy) {
       for (int c = 0; c < dm.nchunks; ++c) {
         const ChunkPart p = parts[c];
         if (p.sum > 0.0) S += p.sum * exp((double)(p.vmax - m) / (double)sp.temperature);
@@ -582,10 +481,7 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
     }
     s_m = m;
     s_argmax = am;
-    s_total = total;
-    s_overflow = ovf;
     s_S = S;
-    s_off[0] = 0;
   }
   __syncthreads();
   const float m = s_m;
@@ -608,122 +504,11 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
   }
 
   const float it = sp.inv_t;
-  uint32_t lower_key = 0;       // exact top-k threshold key once known
-  bool have_topk_key = false;
-
-  if (sp.compact && !s_overflow && s_total <= kRowGatherCap) {
-    // gather the chunks' candidates (canonical keys) into LDS, chunk order
-    int off = 0;
-    for (int c = 0; c < dm.nchunks; ++c) {
-      const int cnt = parts[c].count;
-      const uint2* src = ws.cand + ((size_t)r * dm.nchunks + c) * kChunkCap;
-      for (int j = tid; j < cnt; j += kThreads) {
-        uint2 e = src[j];
-        e.y = Tr<E>::canon(e.y);
-        s_c[off + j] = e;
-      }
-      off += cnt;
-    }
-    const int tot = off;
-    __syncthreads();
-    // k-th largest key among the candidates = the row's k-th largest
-    uint32_t x = 0;
-    for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
-      const uint32_t cand = x | (1u << bit);
-      int local = 0;
-      for (int j = tid; j < tot; j += kThreads) local += (s_c[j].y >= cand);
-      if (block_sum_i(local, red) >= sp.top_k) x = cand;
-    }
-    lower_key = x;
-    have_topk_key = true;
-    // kept = candidates with key >= x, placed by their rank in index order
-    uint2* s_k = reinterpret_cast<uint2*>(s_bins);  // up to kKeptCap entries (8 KB)
-    int nk_local = 0;
-    for (int j = tid; j < tot; j += kThreads) nk_local += (s_c[j].y >= x);
-    const int nk = block_sum_i(nk_local, red);
-    if (nk <= kKeptCap) {
-      for (int j = tid; j < tot; j += kThreads) {
-        const uint2 e = s_c[j];
-        if (e.y < x) continue;
-        int rank = 0;
-        for (int i = 0; i < tot; ++i) rank += (s_c[i].y >= x) && (s_c[i].x < e.x);
-        s_k[rank] = e;
-      }
-      __syncthreads();
-      // exponentials in index order
-      double* s_e = reinterpret_cast<double*>(s_bins) + kKeptCap;  // second 8 KB
-      for (int j = tid; j < nk; j += kThreads)
-        s_e[j] = (double)expf((Tr<E>::key_to_float(s_k[j].y) - m) * it);
-      __syncthreads();
-      double part = 0.0;
-      for (int j = tid; j < nk; j += kThreads) part += s_e[j];
-      double S = block_sum_d(part, red);
-      float thr = Tr<E>::key_to_float(x);
-      int nkeep = nk;
-      if (sp.top_p < 1.0f) {
-        // order by (z descending, index ascending); s_c is free now
-        __syncthreads();
-        int* s_ord = reinterpret_cast<int*>(s_c);
-        for (int j = tid; j < nk; j += kThreads) {
-          const uint32_t kj = s_k[j].y;
-          int rank = 0;
-          for (int i = 0; i < nk; ++i) {
-            const uint32_t ki = s_k[i].y;
-            rank += (ki > kj) || (ki == kj && i < j);
-          }
-          s_ord[rank] = j;
-        }
-        __syncthreads();
-        if (tid == 0) {
-          const double P = (double)sp.top_p;
-          double cum = 0.0;
-          uint32_t tkey = s_k[s_ord[nk - 1]].y;
-          for (int q = 0; q < nk; ++q) {
-            const int j = s_ord[q];
-            cum += s_e[j] / S;
-            if (cum >= P) {
-              tkey = s_k[j].y;
-              break;
-            }
-          }
-          // keep z >= the boundary value, preserving index order
-          int w = 0;
-          double S2 = 0.0;
-          for (int j = 0; j < nk; ++j) {
-            if (s_k[j].y >= tkey) {
-              s_k[w] = s_k[j];
-              s_e[w] = s_e[j];
-              S2 += s_e[j];
-              ++w;
-            }
-          }
-          s_nk = w;
-          s_S = S2;
-          s_off[0] = (int)tkey;
-        }
-        __syncthreads();
-        nkeep = s_nk;
-        S = s_S;
-        thr = Tr<E>::key_to_float((uint32_t)s_off[0]);
-      }
-      uint2* dst = ws.kept + (size_t)r * kKeptCap;
-      for (int j = tid; j < nkeep; j += kThreads)
-        dst[j] = make_uint2(s_k[j].x, __float_as_uint(Tr<E>::key_to_float(s_k[j].y)));
-      if (tid == 0) {
-        out.thr = thr;
-        out.S = S;
-        out.nkept = nkeep;
-        out.kind = kRowCompact;
-        ws.rstat[r] = out;
-      }
-      return;
-    }
-    __syncthreads();
-  }
+  uint32_t lower_key = 0;  // selection threshold key (0: none)
 
   // Whole-row path: exact selections by re-reading the row.
   const bool topk_on = sp.top_k > 0 && sp.top_k < dm.V;
-  if (topk_on && !have_topk_key)
+  if (topk_on)
     lower_key = radix_select<E, VEC, false>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins, red);
   if (sp.top_p < 1.0f)
     lower_key =
@@ -1107,16 +892,14 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
 // Compact top-k path, two launches and no communication between workgroups inside a launch
 // (on this GPU an agent-scope release per workgroup, needed to publish partial results to
 // another workgroup, costs far more than the streaming itself).
-//   k_topk_row : one workgroup per row streams the row in chunk-sized register tiles; each
-//                tile's candidates (key >= tau, tau = the k-th largest of the 256 per-thread
-//                maxima, which never exceeds the tile's k-th largest) are appended to an LDS
-//                list; at the end one wave selects the row's k-th largest among them (the row's
-//                top-k set, ties included, is contained in the union of the tiles' candidate
-//                sets) and writes (m, thr, S) and the kept tokens.
+//   k_topk_row : one workgroup per row streams the row in register tiles and keeps, per wave,
+//                a list of candidates (every element >= a threshold that never exceeds the
+//                row's k-th largest); at the end one wave selects the row's k-th largest among
+//                them (the row's top-k set, ties included, is among the candidates) and writes
+//                (m, thr, S) and the kept tokens.
 //   k_seq_compact : one workgroup per sequence: accept tests, first rejection, final draw.
 // ------------------------------------------------------------------------------------------
-constexpr int kWaveCap = 128;      // candidates one wave may emit per tile
-constexpr int kRowCandCap = 1024;  // candidates one row may hold in LDS
+constexpr int kWaveListCap = 512;  // candidates one wave may hold for a row
 
 // Order-preserving barrier between lanes of one wave communicating through LDS.
 __device__ __forceinline__ void wave_lds_sync() {
@@ -1129,140 +912,275 @@ __device__ __forceinline__ unsigned long long lanes_below() {
   return (1ull << lane_id()) - 1ull;
 }
 
-struct TileLds {
-  uint32_t tmax[kThreads];
-  uint2 wl[4 * kWaveCap];  // per-wave candidate lists of the current tile
-  int wcnt[4];
-  uint32_t tau, bmax;
+struct alignas(16) RowLds {
+  uint32_t key[4][kWaveListCap];  // per-wave candidate lists: canonical keys ...
+  uint32_t idx[4][kWaveListCap];  // ... and vocabulary indices
+  float e[4][kWaveListCap];       // exp((z - m) / T) of each candidate (row merge)
+  RedScratch red;
+  uint32_t tmax[kThreads];        // per-thread maxima of tile 0
+  uint32_t tau;
+  int cnt[4];
+  int ovf[4];
+  int fallback;
 };
 
-// One tile [c0, c0 + clen) of the row: candidates appended to (s_key, s_idx) in (wave,
-// register, lane) order, so the list is identical on every run.  nrow, ovf and bmax are
-// updated identically in every thread.
-template <class E, bool VEC>
-__device__ void topk_tile(const E* __restrict__ row, int V, int k, int c0, int clen,
-                          TileLds& t, uint32_t* s_key, uint32_t* s_idx, int& nrow, int& ovf,
-                          uint32_t& bmax) {
-  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
-  uint32_t regs[kRegs];
-  load_chunk<E, VEC>(row, V, c0, clen, regs, Tr<E>::kKey0Pair);
-  uint32_t tm = 0;
-#pragma unroll
-  for (int j = 0; j < kRegs; ++j) {
-    regs[j] = Tr<E>::keys_of_dword(regs[j]);
-    tm = Tr<E>::dword_max(tm, regs[j]);
-  }
-  t.tmax[tid] = Tr<E>::dword_hmax(tm);
-  __syncthreads();
-  if (wv == 0) {
-    const uint32_t a0 = t.tmax[lane], a1 = t.tmax[lane + 64];
-    const uint32_t a2 = t.tmax[lane + 128], a3 = t.tmax[lane + 192];
-    uint32_t bm = max(max(a0, a1), max(a2, a3));
-    bm = wave_reduce(bm, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
-    uint32_t x = 0;
-    for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
-      const uint32_t cand = x | (1u << bit);
-      const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand)) +
-                      __popcll(__ballot(a2 >= cand)) + __popcll(__ballot(a3 >= cand));
-      if (cnt >= k) x = cand;
-    }
-    if (x < 1u) x = 1u;                              // key 0 marks slots past the row end
-    if (x == Tr<E>::kKeyPos0) x = Tr<E>::kKeyNeg0;  // -0 equals +0
-    if (lane == 0) {
-      t.tau = x;
-      t.bmax = bm;
+// One wave's candidate list (row w of RowLds); every field has the same value in all lanes.
+struct WaveList {
+  int w;
+  int count;
+  int ovf;
+  uint32_t tau;  // filter threshold on (non-canonical) keys
+};
+
+__device__ __forceinline__ void wl_push(RowLds& S, WaveList& L, bool hit, uint32_t idx,
+                                        uint32_t key) {
+  const unsigned long long m = __ballot(hit);
+  if (hit) {
+    const int pos = L.count + __popcll(m & lanes_below());
+    if (pos < kWaveListCap) {
+      S.key[L.w][pos] = key;
+      S.idx[L.w][pos] = idx;
     }
   }
-  __syncthreads();
-  const uint32_t tau = t.tau;
-  const unsigned long long below = lanes_below();
-  uint2* mine = t.wl + wv * kWaveCap;
-  int wcount = 0;  // same value in every lane of the wave
-  auto push = [&](bool hit, int idx, uint32_t key) {
-    const unsigned long long m = __ballot(hit);
-    if (hit) {
-      const int pos = wcount + __popcll(m & below);
-      if (pos < kWaveCap) mine[pos] = make_uint2((uint32_t)idx, key);
-    }
-    wcount += __popcll(m);
-  };
-  if constexpr (Tr<E>::kPerDword == 2) {
-    const uint32_t tm1 = tau - 1u;
-    const uint32_t tpair = tm1 | (tm1 << 16);
-#pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = regs[4 * i + d];
-        const bool any = Tr<E>::dword_max(w, tpair) != tpair;  // some half >= tau
-        if (__ballot(any)) {
-          const uint32_t k0 = w & 0xFFFFu, k1 = w >> 16;
-          push(any && k0 >= tau, slot_index<E>(c0, i, d, 0), k0);
-          push(any && k1 >= tau, slot_index<E>(c0, i, d, 1), k1);
-        }
-      }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const uint32_t w = regs[4 * i + d];
-        if (__ballot(w >= tau)) push(w >= tau, slot_index<E>(c0, i, d, 0), w);
-      }
-    }
-  }
-  if (lane == 0) t.wcnt[wv] = wcount;
-  __syncthreads();
-  int off = nrow, total = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int cw = t.wcnt[w];
-    ovf |= cw > kWaveCap;
-    const int cc = cw < kWaveCap ? cw : kWaveCap;
-    if (w < wv) off += cc;
-    total += cc;
-  }
-  const int cmine = t.wcnt[wv] < kWaveCap ? t.wcnt[wv] : kWaveCap;
-  for (int j = lane; j < cmine; j += 64) {
-    if (off + j < kRowCandCap) {
-      const uint2 e = mine[j];
-      s_idx[off + j] = e.x;
-      s_key[off + j] = Tr<E>::canon(e.y);
-    }
-  }
-  nrow += total;
-  ovf |= nrow > kRowCandCap;
-  bmax = t.bmax > bmax ? t.bmax : bmax;
-  __syncthreads();
+  L.count += __popcll(m);
 }
 
-// One wave: the row's k-th largest key among the `total` LDS candidates, then top-p on the
-// kept list if requested; writes RowStat and the kept list (candidate order).
+// Threshold on non-canonical keys equivalent to "value >= value of canonical key x".
 template <class E>
-__device__ void row_merge_lds(const Samp& sp, int r, const Workspace& ws, float m,
-                              const uint32_t* s_key, const uint32_t* s_idx, float* s_e,
-                              int total) {
+__device__ __forceinline__ uint32_t filter_tau(uint32_t x) {
+  if (x < 1u) x = 1u;                                 // key 0 marks slots past the row end
+  return x == Tr<E>::kKeyPos0 ? Tr<E>::kKeyNeg0 : x;  // -0 equals +0
+}
+
+// Raise the wave's tau to the k-th largest key of its list and drop the entries below it.
+// The wave's k-th largest never exceeds the row's, so the row's top-k set stays covered.
+template <class E>
+__device__ __forceinline__ void wl_raise(RowLds& S, WaveList& L, int k) {
   const int lane = lane_id();
+  if (L.count > kWaveListCap) L.ovf = 1;  // entries were lost: the row takes the fallback path
+  const int n = L.count < kWaveListCap ? L.count : kWaveListCap;
+  wave_lds_sync();
   uint32_t x = 0;
   for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
     const uint32_t cand = x | (1u << bit);
     int c = 0;
-    for (int e0 = 0; e0 < total; e0 += 64) {
-      const int e = e0 + lane;
-      c += __popcll(__ballot(e < total && s_key[e] >= cand));
+    for (int j0 = 0; j0 < n; j0 += 64) {
+      const int j = j0 + lane;
+      c += __popcll(__ballot(j < n && S.key[L.w][j] >= cand));
+    }
+    if (c >= k) x = cand;
+  }
+  int base = 0;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    const bool keep = j < n && S.key[L.w][j] >= x;
+    const uint32_t kk = keep ? S.key[L.w][j] : 0u, ii = keep ? S.idx[L.w][j] : 0u;
+    const unsigned long long m = __ballot(keep);
+    wave_lds_sync();
+    if (keep) {
+      const int pos = base + __popcll(m & lanes_below());
+      S.key[L.w][pos] = kk;
+      S.idx[L.w][pos] = ii;
+    }
+    base += __popcll(m);
+    wave_lds_sync();
+  }
+  L.count = base;
+  const uint32_t t = filter_tau<E>(x);
+  if (t > L.tau) L.tau = t;
+}
+
+// Per-lane select: lanes in `mask` take hi, the others lo (one v_cndmask_b32).  Written as asm
+// so that the compiler cannot fold a tree of these selects back into an indexed load, which
+// would move the whole register tile to scratch memory.
+__device__ __forceinline__ uint32_t lane_select(unsigned long long mask, uint32_t lo,
+                                                uint32_t hi) {
+  uint32_t out;
+  asm("v_cndmask_b32 %0, %1, %2, %3" : "=v"(out) : "v"(lo), "v"(hi), "s"(mask));
+  return out;
+}
+
+// regs[j] for a per-lane index j in [0, 64): a select tree on the bits of j (m[b] = the lanes
+// whose j has bit b set), depth first so that few partial results are live at once.  Every
+// lane may ask for a different register without leaving the register file.
+template <int N>
+__device__ __forceinline__ uint32_t sel_tree(const uint32_t (&r)[kRegs], int base,
+                                             const unsigned long long (&m)[6]) {
+  if constexpr (N == 1) {
+    return r[base];
+  } else {
+    constexpr int bit = N == 2 ? 0 : N == 4 ? 1 : N == 8 ? 2 : N == 16 ? 3 : N == 32 ? 4 : 5;
+    const uint32_t lo = sel_tree<N / 2>(r, base, m);
+    const uint32_t hi = sel_tree<N / 2>(r, base + N / 2, m);
+    return lane_select(m[bit], lo, hi);
+  }
+}
+
+__device__ __forceinline__ uint32_t reg_select(const uint32_t (&r)[kRegs], int j) {
+  unsigned long long m[6];
+#pragma unroll
+  for (int b = 0; b < 6; ++b) m[b] = __ballot((j >> b) & 1);
+  return sel_tree<kRegs>(r, 0, m);
+}
+
+// One register tile of a row for the top-k stream.  With VEC, raw buffer loads whose range
+// check returns 0 past the end of the row (so no register is rewritten after the loads); the
+// raw path treats such a 0 (+0.0) as below every positive tau, and tile_keys maps those slots
+// to key 0.  Without VEC, element loads with all-ones bits (key 0, and -1 read as signed) past
+// the end.
+template <class E, bool VEC>
+__device__ __forceinline__ void load_tile(const E* __restrict__ row, int V, int c0, int clen,
+                                          uint32_t (&regs)[kRegs]) {
+  if constexpr (VEC) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(row + c0), (short)0, clen * (int)sizeof(E), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kVecPerThread; ++i) {
+      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, threadIdx.x * 16,
+                                                         i * kThreads * 16, 2);
+      regs[4 * i + 0] = x.x;
+      regs[4 * i + 1] = x.y;
+      regs[4 * i + 2] = x.z;
+      regs[4 * i + 3] = x.w;
+    }
+  } else {
+    load_chunk<E, false>(row, V, c0, clen, regs, Tr<E>::kKey0Pair);
+  }
+}
+
+// Keys of register j of the tile (raw bits in regs); slots past the end of the row get key 0.
+// `valid` holds, per vector i, the lanes whose vector i lies inside the row.
+template <class E>
+__device__ __forceinline__ uint32_t tile_key(const uint32_t (&regs)[kRegs], int j,
+                                             const unsigned long long (&valid)[kVecPerThread]) {
+  return lane_select(valid[j >> 2], 0u, Tr<E>::keys_of_dword(regs[j]));
+}
+
+template <class E, bool VEC>
+__device__ __forceinline__ void tile_valid(int clen, unsigned long long (&valid)[kVecPerThread]) {
+  const int nvec = clen / Tr<E>::kEpv;  // clen is a multiple of the vector width with VEC
+#pragma unroll
+  for (int i = 0; i < kVecPerThread; ++i)
+    valid[i] = __ballot(!VEC || (int)threadIdx.x + kThreads * i < nvec);
+}
+
+// Candidates of one tile (raw bits in regs) into the wave's list.  KEYS: compare order-preserving
+// keys; otherwise compare raw bits, which is valid only while tau is a positive value (an element is >= tau
+// exactly when its bits, read as a signed integer, are >= the bits of tau; slots past the row
+// end read as 0 or -1, below the bits of any positive tau).  First a per-lane mask of the registers holding a
+// candidate, without branches; then one pass per candidate register of the busiest lane, each
+// lane taking its lowest remaining register.
+template <class E, bool KEYS>
+__device__ __forceinline__ void filter_tile(const uint32_t (&regs)[kRegs], int c0,
+                                            const unsigned long long (&valid)[kVecPerThread],
+                                            RowLds& S, WaveList& L, int k, int raise_at) {
+  // Register j has a candidate iff max(w, t) != t with t = tau - 1 (per 16-bit half for bf16;
+  // unsigned on keys, signed on raw bits).  The mask bits are shifted in, register j of each
+  // half-tile ending at bit 31 - (j mod 32); no compares into VCC and no per-bit constants.
+  uint32_t mlo = 0, mhi = 0;
+  if constexpr (Tr<E>::kPerDword == 2) {
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    const uint32_t tm1 = KEYS ? L.tau - 1u : (L.tau & 0x7FFFu) - 1u;
+    const uint32_t tpair = tm1 | (tm1 << 16);
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+      uint32_t mx;
+      if constexpr (KEYS)
+        mx = Tr<E>::dword_max(tile_key<E>(regs, j, valid), tpair);
+      else
+        mx = __builtin_bit_cast(uint32_t, __builtin_elementwise_max(
+                                              __builtin_bit_cast(s2, regs[j]),
+                                              __builtin_bit_cast(s2, tpair)));
+      const uint32_t bit = min(mx ^ tpair, 1u);
+      if (j < 32)
+        mlo = (mlo << 1) | bit;
+      else
+        mhi = (mhi << 1) | bit;
+    }
+  } else {
+    const uint32_t tm1 = KEYS ? L.tau - 1u : (L.tau & 0x7FFFFFFFu) - 1u;
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+      const uint32_t mx =
+          KEYS ? max(tile_key<E>(regs, j, valid), tm1) : (uint32_t)max((int)regs[j], (int)tm1);
+      const uint32_t bit = min(mx ^ tm1, 1u);
+      if (j < 32)
+        mlo = (mlo << 1) | bit;
+      else
+        mhi = (mhi << 1) | bit;
+    }
+  }
+  while (true) {
+    const bool has = (mlo | mhi) != 0u;
+    if (__ballot(has) == 0ull) break;
+    if (L.count > raise_at) wl_raise<E>(S, L, k);
+    const int j = mlo ? __builtin_clz(mlo) : (mhi ? 32 + __builtin_clz(mhi) : 0);
+    if (mlo)
+      mlo &= ~(0x80000000u >> j);
+    else
+      mhi &= ~(0x80000000u >> (j - 32));
+    const uint32_t w = reg_select(regs, j);
+    const int i = j >> 2, d = j & 3;
+    const uint32_t tau = L.tau;
+    if constexpr (Tr<E>::kPerDword == 2) {
+      const uint32_t k0 = Tr<E>::key_of_bits(w & 0xFFFFu);
+      const uint32_t k1 = Tr<E>::key_of_bits(w >> 16);
+      wl_push(S, L, has && k0 >= tau, slot_index<E>(c0, i, d, 0), Tr<E>::canon(k0));
+      wl_push(S, L, has && k1 >= tau, slot_index<E>(c0, i, d, 1), Tr<E>::canon(k1));
+    } else {
+      const uint32_t k0 = Tr<E>::key_of_bits(w);
+      wl_push(S, L, has && k0 >= tau, slot_index<E>(c0, i, d, 0), Tr<E>::canon(k0));
+    }
+  }
+}
+
+// One wave merges the row from the four wave lists: the row maximum (the largest candidate:
+// the maximum is >= every threshold used), the k-th largest key, top-p on the kept set if
+// requested; writes RowStat and the kept list (candidate order).  Returns 1, writing nothing,
+// when the kept set would not fit kKeptCap.
+template <class E>
+__device__ int row_merge_lists(const Samp& sp, int r, const Workspace& ws, RowLds& S) {
+  const int lane = lane_id();
+  int cnt[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) cnt[w] = S.cnt[w];
+  uint32_t first[4];  // the first 64 entries of each list stay in registers
+  uint32_t mk = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    first[w] = lane < cnt[w] ? S.key[w][lane] : 0u;
+    mk = first[w] > mk ? first[w] : mk;
+    for (int j = lane + 64; j < cnt[w]; j += 64) mk = S.key[w][j] > mk ? S.key[w][j] : mk;
+  }
+  mk = wave_reduce(mk, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  const float m = Tr<E>::key_to_float(mk);
+  uint32_t x = 0;
+  for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+    const uint32_t cand = x | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      c += __popcll(__ballot(first[w] >= cand));
+      for (int j0 = 64; j0 < cnt[w]; j0 += 64) {
+        const int j = j0 + lane;
+        c += __popcll(__ballot(j < cnt[w] && S.key[w][j] >= cand));
+      }
     }
     if (c >= sp.top_k) x = cand;
   }
   const float it = sp.inv_t;
   double part = 0.0;
-  for (int e = lane; e < total; e += 64) {
-    float ev = 0.0f;
-    if (s_key[e] >= x) ev = expf((Tr<E>::key_to_float(s_key[e]) - m) * it);
-    s_e[e] = ev;
-    part += (double)ev;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    for (int j = lane; j < cnt[w]; j += 64) {
+      const uint32_t kj = S.key[w][j];
+      const float ev = kj >= x ? expf((Tr<E>::key_to_float(kj) - m) * it) : 0.0f;
+      S.e[w][j] = ev;
+      part += (double)ev;
+    }
   }
-  double S = wave_reduce(part, [](double a, double b) { return a + b; });
+  double Ssum = wave_reduce(part, [](double a, double b) { return a + b; });
   uint32_t tkey = x;
   if (sp.top_p < 1.0f) {
     // For each kept entry, the mass of the kept entries ordered before it by (logit
@@ -1271,55 +1189,74 @@ __device__ void row_merge_lds(const Samp& sp, int r, const Workspace& ws, float 
     wave_lds_sync();
     const double P = (double)sp.top_p;
     uint32_t hit = 0;
-    for (int e = lane; e < total; e += 64) {
-      const uint32_t ke = s_key[e], ie = s_idx[e];
-      if (ke < x) continue;
-      double ex = 0.0;
-      for (int q = 0; q < total; ++q) {
-        const uint32_t kq = s_key[q];
-        if (kq >= x && (kq > ke || (kq == ke && s_idx[q] < ie))) ex += (double)s_e[q];
+    for (int w = 0; w < 4; ++w) {
+      for (int j = lane; j < cnt[w]; j += 64) {
+        const uint32_t ke = S.key[w][j], ie = S.idx[w][j];
+        if (ke < x) continue;
+        double ex = 0.0;
+        for (int w2 = 0; w2 < 4; ++w2) {
+          for (int q = 0; q < cnt[w2]; ++q) {
+            const uint32_t kq = S.key[w2][q];
+            if (kq >= x && (kq > ke || (kq == ke && S.idx[w2][q] < ie))) ex += (double)S.e[w2][q];
+          }
+        }
+        const double lo = ex / Ssum, hi = (ex + (double)S.e[w][j]) / Ssum;
+        if (hi >= P && lo < P) hit = ke;
       }
-      const double lo = ex / S, hi = (ex + (double)s_e[e]) / S;
-      if (hi >= P && lo < P) hit = ke;
     }
     hit = wave_reduce(hit, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
     if (hit != 0) tkey = hit;  // otherwise rounding left the total below P: keep everything
     part = 0.0;
-    for (int e = lane; e < total; e += 64)
-      if (s_key[e] >= tkey) part += (double)s_e[e];
-    S = wave_reduce(part, [](double a, double b) { return a + b; });
+    for (int w = 0; w < 4; ++w)
+      for (int j = lane; j < cnt[w]; j += 64)
+        if (S.key[w][j] >= tkey) part += (double)S.e[w][j];
+    Ssum = wave_reduce(part, [](double a, double b) { return a + b; });
   }
+  int nk = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    for (int j0 = 0; j0 < cnt[w]; j0 += 64) {
+      const int j = j0 + lane;
+      nk += __popcll(__ballot(j < cnt[w] && S.key[w][j] >= tkey));
+    }
+  if (nk > kKeptCap) return 1;
   uint2* dst = ws.kept + (size_t)r * kKeptCap;
   const unsigned long long below = lanes_below();
   int base = 0;
-  for (int e0 = 0; e0 < total; e0 += 64) {
-    const int e = e0 + lane;
-    const bool keep = e < total && s_key[e] >= tkey;
-    const unsigned long long mk = __ballot(keep);
-    if (keep)
-      dst[base + __popcll(mk & below)] =
-          make_uint2(s_idx[e], __float_as_uint(Tr<E>::key_to_float(s_key[e])));
-    base += __popcll(mk);
-  }
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    for (int j0 = 0; j0 < cnt[w]; j0 += 64) {
+      const int j = j0 + lane;
+      const bool keep = j < cnt[w] && S.key[w][j] >= tkey;
+      const unsigned long long mkp = __ballot(keep);
+      if (keep)
+        dst[base + __popcll(mkp & below)] =
+            make_uint2(S.idx[w][j], __float_as_uint(Tr<E>::key_to_float(S.key[w][j])));
+      base += __popcll(mkp);
+    }
   if (lane == 0) {
     RowStat rs;
     rs.m = m;
     rs.thr = Tr<E>::key_to_float(tkey);
-    rs.S = S;
+    rs.S = Ssum;
     rs.argmax = -1;
-    rs.nkept = base;
+    rs.nkept = nk;
     rs.kind = kRowCompact;
     rs.pad = 0;
     ws.rstat[r] = rs;
   }
+  return 0;
 }
 
-// Whole-row fallback (all threads) when the candidates do not fit in LDS: exact selections
-// by re-reading the row, 8-bit radix digits (2 KB of bins).  Writes a dense RowStat.
+// Whole-row fallback (all threads) when the candidates do not fit: the row maximum and exact
+// selections by re-reading the row, 8-bit radix digits (2 KB of bins).  Writes a dense RowStat.
 template <class E, bool VEC>
 __device__ void row_merge_block(const E* __restrict__ row, const Dims& dm, const Samp& sp, int r,
-                                const Workspace& ws, float m, unsigned long long* s_bins,
+                                const Workspace& ws, unsigned long long* s_bins,
                                 RedScratch& red) {
+  float mx = -INFINITY;
+  row_foreach<E, VEC>(row, dm.V, [&](int, float z, uint32_t) { mx = fmaxf(mx, z); });
+  const float m = block_max_f(mx, red);
   const float it = sp.inv_t;
   uint32_t key = radix_select<E, VEC, false, 8>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins,
                                                  red);
@@ -1340,31 +1277,75 @@ __device__ void row_merge_block(const E* __restrict__ row, const Dims& dm, const
   }
 }
 
+// One workgroup per row, the row streamed in register tiles.  Tile 0 sets tau = the k-th
+// largest of the 256 per-thread maxima (at most the tile's k-th largest, so at most the row's);
+// every tile appends its elements >= tau to the wave's list, and a wave raises tau to its own
+// list's k-th largest whenever the list grows long.  No barrier after tile 0.  At the end one
+// wave selects the row's k-th largest among the candidates (the row's top-k set, ties
+// included, is among them).
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt,
                                                        const E* __restrict__ drf, Dims dm,
                                                        Samp sp, Workspace ws) {
   const int r = blockIdx.x;
-  __shared__ TileLds t;
-  __shared__ uint32_t s_key[kRowCandCap];
-  __shared__ uint32_t s_idx[kRowCandCap];
-  __shared__ float s_e[kRowCandCap];
-  __shared__ unsigned long long s_bins[256];
-  __shared__ RedScratch red;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  __shared__ RowLds S;
   const E* row = row_ptr(dm, tgt, drf, r);
-  int nrow = 0, ovf = 0;
-  uint32_t bmax = 0;
+  const int k = sp.top_k;
+  const int raise_at = k + 128;  // a pass pushes at most 128, so lists stay within the cap
+  WaveList L{wv, 0, 0, 0u};
   for (int c = 0; c < dm.nchunks; ++c) {
     const int c0 = c * dm.chunk_elems;
-    topk_tile<E, VEC>(row, dm.V, sp.top_k, c0, min(dm.chunk_elems, dm.V - c0), t, s_key, s_idx,
-                      nrow, ovf, bmax);
+    const int clen = min(dm.chunk_elems, dm.V - c0);
+    uint32_t regs[kRegs];
+    load_tile<E, VEC>(row, dm.V, c0, clen, regs);
+    unsigned long long valid[kVecPerThread];
+    tile_valid<E, VEC>(clen, valid);
+    if (c == 0) {
+      uint32_t tm = 0;
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) tm = Tr<E>::dword_max(tm, tile_key<E>(regs, j, valid));
+      S.tmax[tid] = Tr<E>::dword_hmax(tm);
+      // Opaque to the compiler, so that it recomputes the keys in filter_tile rather than
+      // keeping all 64 of them live across the selection below.
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) asm volatile("" : "+v"(regs[j]));
+      __syncthreads();
+      if (wv == 0) {
+        const uint32_t a0 = S.tmax[lane], a1 = S.tmax[lane + 64];
+        const uint32_t a2 = S.tmax[lane + 128], a3 = S.tmax[lane + 192];
+        uint32_t x = 0;
+        for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+          const uint32_t cand = x | (1u << bit);
+          const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand)) +
+                          __popcll(__ballot(a2 >= cand)) + __popcll(__ballot(a3 >= cand));
+          if (cnt >= k) x = cand;
+        }
+        if (lane == 0) S.tau = filter_tau<E>(x);
+      }
+      __syncthreads();
+      L.tau = S.tau;
+      filter_tile<E, true>(regs, c0, valid, S, L, k, raise_at);
+    } else if (L.tau > Tr<E>::kKeyPos0) {
+      filter_tile<E, false>(regs, c0, valid, S, L, k, raise_at);
+    } else {
+      filter_tile<E, true>(regs, c0, valid, S, L, k, raise_at);
+    }
   }
-  const float m = Tr<E>::key_to_float(bmax);
-  if (!ovf) {
-    if (wave_id() == 0) row_merge_lds<E>(sp, r, ws, m, s_key, s_idx, s_e, nrow);
-  } else {
-    row_merge_block<E, VEC>(row, dm, sp, r, ws, m, s_bins, red);
+  if (lane == 0) {
+    S.cnt[wv] = L.count < kWaveListCap ? L.count : kWaveListCap;
+    S.ovf[wv] = L.ovf | (L.count > kWaveListCap);
   }
+  __syncthreads();
+  if (wv == 0) {
+    const int ovf = S.ovf[0] | S.ovf[1] | S.ovf[2] | S.ovf[3];
+    const int fb = ovf ? 1 : row_merge_lists<E>(sp, r, ws, S);
+    if (lane == 0) S.fallback = fb;
+  }
+  __syncthreads();
+  if (S.fallback)
+    row_merge_block<E, VEC>(row, dm, sp, r, ws,
+                            reinterpret_cast<unsigned long long*>(&S.key[0][0]), S.red);
 }
 
 // Final draw over a compact row, one wave.  Weights (q - p)_+ (or q for the bonus row, or q
