@@ -11,7 +11,8 @@ draft rows (spec_sample) beforehand.
 Prints one JSON line.  value = logit elements per second over the timed steps.  "roofline"
 covers the dominant kernel (the row-streaming kernel), timed with HIP events recorded on the
 library's stream around that kernel in every timed step.  "cpu_baseline" times the CPU oracle
-(numpy, float64, single process) on a bounded sample of the same workload.
+(numpy, float64, single process) on the same inputs: whole steps repeated for about 10 s.
+--workload tree_B32_N64_V32000_bf16 times greedy token-tree verification instead.
 """
 
 import argparse
@@ -63,27 +64,147 @@ def _traffic_from_profiles(kernel, workload):
     return float(fetch.group(1)) + float(write.group(1))
 
 
-def cpu_baseline(name, target, draft, budget_seqs):
-    """Time the CPU oracle on the first `budget_seqs` sequences of the same inputs."""
+def cpu_baseline(name, target, draft, seconds):
+    """Time the CPU oracle on the same inputs: whole steps (every sequence) repeated until
+    `seconds` have passed (at least one step)."""
     import numpy as np
     import oracle.spec_verify_oracle as O
     from workloads import synthetic as S
     cfg = S.WORKLOADS[name]
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
-    nseq = min(B, budget_seqs)
-    tf = target[:nseq].float().cpu().numpy()
-    df = draft[:nseq].float().cpu().numpy()
+    tf = target.float().cpu().numpy()
+    df = draft.float().cpu().numpy()
     T, k, P = np.float32(cfg["temperature"]), cfg["top_k"], np.float32(cfg["top_p"])
-    u_draw = S.philox_uniforms(101, (nseq, K))
+    u_draw = S.philox_uniforms(101, (B, K))
     drafts = np.stack([O.sample_rows(df[:, j], u_draw[:, j], T, k, P) for j in range(K)], axis=1)
-    u = S.philox_uniforms(102, (nseq, K + 1))
+    u = S.philox_uniforms(102, (B, K + 1))
+    reps = 0
     t0 = time.perf_counter()
-    O.spec_verify(tf, df, drafts, u, T, k, P, np.float32(cfg["lenience"]))
-    dt = time.perf_counter() - t0
-    elems = nseq * (2 * K + 1) * V
+    while True:
+        O.spec_verify(tf, df, drafts, u, T, k, P, np.float32(cfg["lenience"]))
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    elems = reps * B * (2 * K + 1) * V
     return {"value": elems / dt, "unit": "logit elems/s", "cores": 1, "kind": "oracle",
-            "sample": f"{nseq} of {B} sequences of one step ({elems} logits), "
-                      f"{dt:.2f} s, numpy float64, one process"}
+            "sample": f"{reps} whole steps ({B} sequences, {B * (2 * K + 1) * V} logits each), "
+                      f"{dt:.1f} s, numpy float64, one process"}
+
+
+def cpu_baseline_tree(logits, parent, tokens, max_depth, seconds):
+    """Time the CPU oracle's tree walk on the same inputs, whole steps repeated."""
+    import oracle.spec_verify_oracle as O
+    x = logits.float().cpu().numpy()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        O.tree_verify(x, parent, tokens, max_depth)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    B, N, V = x.shape
+    return {"value": reps * B * N * V / dt, "unit": "logit elems/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{reps} whole steps ({B} trees of {N} nodes, {B * N * V} logits each), "
+                      f"{dt:.1f} s, numpy float64, one process"}
+
+
+def _elapsed(hip, a, b):
+    f = ctypes.c_float()
+    hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
+    return f.value
+
+
+def bench_tree(args, name, cfg):
+    """Greedy token-tree verification: a step is one spec_verify_tree call over the batch.  The
+    logits (131 MB per set) would fit the 256 MB last-level cache, so the timed steps rotate
+    through 8 independently generated input sets."""
+    import numpy as np
+    import torch
+    import speculative_sampling_verification_amd as svm
+    from workloads import synthetic as S
+
+    B, N, V, D = cfg["B"], cfg["N"], cfg["V"], cfg["max_depth"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sets = []
+    for seed in range(1, 9):
+        logits, parent, tokens = S.workload_inputs(name, device=dev, seed=seed)
+        sets.append((logits, torch.from_numpy(np.asarray(parent, np.int32)).to(dev),
+                     torch.from_numpy(np.asarray(tokens, np.int32)).to(dev), parent, tokens))
+    out = svm.spec_verify_tree(sets[0][0], sets[0][1], sets[0][2], D)
+    torch.cuda.synchronize()
+    hip = _hip_runtime()
+
+    def new_event():
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    evs = [[new_event() for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.warmup):
+        s = sets[i % len(sets)]
+        svm.spec_verify_tree(s[0], s[1], s[2], D, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        svm.spec_verify_tree(s[0], s[1], s[2], D, out=out, events=evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    _copy_reference(args, dev)
+    kern_ms = [_elapsed(hip, e[0], e[1]) for e in evs]
+    step_ms = [_elapsed(hip, e[0], e[2]) for e in evs]
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    elems = B * N * V
+    logit_bytes = elems * sets[0][0].element_size()
+    ms_per_step = wall * 1e3 / args.steps
+    kern_avg = float(np.mean(kern_ms))
+    achieved = logit_bytes / (kern_avg * 1e-3) / 1e9
+    res = {
+        "metric": f"tree verify throughput: logit elems/s, greedy token tree B={B} N={N} V={V} "
+                  f"{cfg['dtype']}",
+        "value": elems / (ms_per_step * 1e-3),
+        "unit": "logit elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "N": N, "V": V, "max_depth": D,
+                   "planted": cfg["planted"], "input_sets": len(sets)},
+        "roofline": {"bound": "hbm", "kernel": "k_chunk", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": _traffic_from_profiles("k_chunk", name), "kernel_ms": kern_avg,
+                     "algorithmic_bytes_per_launch": logit_bytes},
+        "gpu_event_ms_per_step": float(np.median(step_ms)),
+        "mean_accepted_depth": float(out["num_accepted"].float().mean().item()),
+        "source_sha256_12": _source_tag(),
+    }
+    if not args.no_cpu_baseline:
+        s = sets[0]
+        res["cpu_baseline"] = cpu_baseline_tree(s[0], s[3], s[4], D, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+def _copy_reference(args, dev):
+    """A plain copy kernel of known size, for calibrating rocprofv3 byte counters."""
+    import torch
+    if args.copy_reference_mib > 0:
+        src = torch.empty(args.copy_reference_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
 
 def main():
@@ -92,8 +213,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: the metric one)")
-    ap.add_argument("--cpu-seqs", type=int, default=128,
-                    help="sequences of the step the CPU oracle is timed on")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU oracle timing budget: whole steps are repeated until it is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference-mib", type=int, default=512,
                     help="after the timed steps, copy a tensor of this size 3 times (a plain "
@@ -114,8 +235,8 @@ def main():
     name = args.workload or S.METRIC_WORKLOAD
     cfg = S.WORKLOADS[name]
     if cfg["gen"] == "tree":
-        raise SystemExit("bench.py times spec_verify workloads; the tree workload is covered "
-                         "by the tests")
+        bench_tree(args, name, cfg)
+        return
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -147,17 +268,9 @@ def main():
     wall = time.perf_counter() - t0
 
     def elapsed(a, b):
-        f = ctypes.c_float()
-        hip.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b))
-        return f.value
+        return _elapsed(hip, a, b)
 
-    if args.copy_reference_mib > 0:
-        src = torch.empty(args.copy_reference_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    _copy_reference(args, dev)
 
     kern_ms = [elapsed(e[0], e[1]) for e in evs]
     step_ms = [elapsed(e[0], e[2]) for e in evs]
@@ -177,7 +290,9 @@ def main():
     n = out["num_accepted"].cpu().numpy()
     a = out["accept_prob"].cpu().numpy()
     res = {
-        "metric": METRIC,
+        "metric": METRIC if name == S.METRIC_WORKLOAD else
+                  f"verify throughput: logit elems/s + % HBM peak, B={B} K={K} V={V} "
+                  f"{cfg['dtype']}",
         "value": elems / (ms_per_step * 1e-3),
         "unit": "logit elems/s",
         "n_gpus": 1,
@@ -206,7 +321,7 @@ def main():
         "source_sha256_12": _source_tag(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seqs)
+        res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

@@ -144,6 +144,19 @@ int spec_verify_tree(const void* target_logits, sv_dtype dtype, int B, int N, in
                      int32_t* out_tokens, int32_t* out_num_accepted, int32_t* out_last_node,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * spec_verify_tree with per-phase timing, for profiling.  `events` holds n_events >= 2 events
+ * created by the caller with hipEventCreate; the library records events[0] before its first
+ * kernel, events[1] after the row-streaming kernel (the per-row argmax, which reads every
+ * logit), and, if n_events >= 3, events[2] after its last kernel.  Results are identical to
+ * spec_verify_tree.
+ */
+int spec_verify_tree_profiled(const void* target_logits, sv_dtype dtype, int B, int N, int V,
+                              const int32_t* parent, const int32_t* node_tokens, int max_depth,
+                              int32_t* out_tokens, int32_t* out_num_accepted,
+                              int32_t* out_last_node, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, hipEvent_t* events, int n_events);
+
 /* Static string for a status code. */
 const char* spec_verify_status_string(int status);
 

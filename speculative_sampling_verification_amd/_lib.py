@@ -29,7 +29,8 @@ class SVSampling(ctypes.Structure):
 EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "spec_verify_profiled",
     "spec_sample_workspace_size", "spec_sample",
-    "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_status_string",
+    "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_tree_profiled",
+    "spec_verify_status_string",
 ]
 
 
@@ -55,6 +56,8 @@ def load(path=LIB_PATH):
     lib.spec_verify_tree_workspace_size.restype = sz
     lib.spec_verify_tree.argtypes = [vp, i32, i32, i32, i32, vp, vp, i32, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_tree.restype = i32
+    lib.spec_verify_tree_profiled.argtypes = lib.spec_verify_tree.argtypes + [vp, i32]
+    lib.spec_verify_tree_profiled.restype = i32
     lib.spec_verify_status_string.argtypes = [i32]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     return lib
@@ -206,8 +209,12 @@ def spec_sample(logits, uniforms, *, temperature=1.0, top_k=0, top_p=1.0, out=No
     return out
 
 
-def spec_verify_tree(target_logits, parent, node_tokens, max_depth, *, out=None, stream=None):
-    """Greedy tree verification: target_logits [B, N, V], parent / node_tokens [B, N] int32."""
+def spec_verify_tree(target_logits, parent, node_tokens, max_depth, *, out=None, stream=None,
+                     events=None):
+    """Greedy tree verification: target_logits [B, N, V], parent / node_tokens [B, N] int32.
+
+    ``events``: optional list of >= 2 hipEvent_t handles (ints) for per-phase timing.
+    """
     dev = target_logits.device
     B, N, V = target_logits.shape
     _need(target_logits, "target_logits", dev)
@@ -225,8 +232,13 @@ def spec_verify_tree(target_logits, parent, node_tokens, max_depth, *, out=None,
     if need == 0:
         raise SpecVerifyError("spec_verify_tree_workspace_size", 1)
     ws = workspace(dev, need)
-    _check("spec_verify_tree", _lib.spec_verify_tree(
-        _ptr(target_logits), dt, B, N, V, _ptr(parent), _ptr(node_tokens), int(max_depth),
-        _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["last_node"]), _ptr(ws),
-        ws.numel(), _stream(dev, stream)))
+    args = (_ptr(target_logits), dt, B, N, V, _ptr(parent), _ptr(node_tokens), int(max_depth),
+            _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["last_node"]), _ptr(ws),
+            ws.numel(), _stream(dev, stream))
+    if events is None:
+        _check("spec_verify_tree", _lib.spec_verify_tree(*args))
+    else:
+        arr = (ctypes.c_void_p * len(events))(*events)
+        _check("spec_verify_tree_profiled",
+               _lib.spec_verify_tree_profiled(*args, arr, len(events)))
     return out

@@ -171,7 +171,7 @@ int spec_verify_profiled(const void* target_logits, const void* draft_logits, sv
                          int32_t* out_num_accepted, float* out_accept_prob, float* out_q_draft,
                          float* out_p_draft, void* workspace, size_t workspace_bytes,
                          hipStream_t stream, hipEvent_t* events, int n_events) {
-  if (!out_num_accepted || !events) return SV_ERR_INVALID_ARG;
+  if (!out_num_accepted || !events || n_events < 2) return SV_ERR_INVALID_ARG;
   return verify_impl(target_logits, draft_logits, dtype, B, K, V, draft_rows, draft_tokens,
                      uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
                      out_q_draft, out_p_draft, workspace, workspace_bytes, stream, events,
@@ -198,10 +198,12 @@ size_t spec_verify_tree_workspace_size(int B, int N, int V, sv_dtype dtype) {
   return layout_tree(d, nullptr, nullptr);
 }
 
-int spec_verify_tree(const void* target_logits, sv_dtype dtype, int B, int N, int V,
-                     const int32_t* parent, const int32_t* node_tokens, int max_depth,
-                     int32_t* out_tokens, int32_t* out_num_accepted, int32_t* out_last_node,
-                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+int tree_impl(const void* target_logits, sv_dtype dtype, int B, int N, int V,
+              const int32_t* parent, const int32_t* node_tokens, int max_depth,
+              int32_t* out_tokens, int32_t* out_num_accepted, int32_t* out_last_node,
+              void* workspace, size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+              int n_events) {
   if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
   if (B < 1 || N < 1 || N > 2048 || V < 1 || max_depth < 0) return SV_ERR_INVALID_ARG;
   if ((long long)B * N > INT_MAX) return SV_ERR_INVALID_ARG;
@@ -218,8 +220,30 @@ int spec_verify_tree(const void* target_logits, sv_dtype dtype, int B, int N, in
   d.B = B;
   d.K = N;
   const hipError_t e = launch_tree(target_logits, dtype, d, parent, node_tokens, max_depth,
-                                   out_tokens, out_num_accepted, out_last_node, ws, stream);
+                                   out_tokens, out_num_accepted, out_last_node, ws, stream,
+                                   events, n_events);
   return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+}  // namespace
+
+int spec_verify_tree(const void* target_logits, sv_dtype dtype, int B, int N, int V,
+                     const int32_t* parent, const int32_t* node_tokens, int max_depth,
+                     int32_t* out_tokens, int32_t* out_num_accepted, int32_t* out_last_node,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return tree_impl(target_logits, dtype, B, N, V, parent, node_tokens, max_depth, out_tokens,
+                   out_num_accepted, out_last_node, workspace, workspace_bytes, stream, nullptr,
+                   0);
+}
+
+int spec_verify_tree_profiled(const void* target_logits, sv_dtype dtype, int B, int N, int V,
+                              const int32_t* parent, const int32_t* node_tokens, int max_depth,
+                              int32_t* out_tokens, int32_t* out_num_accepted,
+                              int32_t* out_last_node, void* workspace, size_t workspace_bytes,
+                              hipStream_t stream, hipEvent_t* events, int n_events) {
+  if (!events || n_events < 2) return SV_ERR_INVALID_ARG;
+  return tree_impl(target_logits, dtype, B, N, V, parent, node_tokens, max_depth, out_tokens,
+                   out_num_accepted, out_last_node, workspace, workspace_bytes, stream, events,
+                   n_events);
 }
 
 const char* spec_verify_status_string(int status) {

@@ -106,6 +106,6 @@ hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, con
 hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,
                        const int32_t* tokens, int max_depth, int32_t* out_tokens,
                        int32_t* out_n, int32_t* out_last, const Workspace& ws,
-                       hipStream_t stream);
+                       hipStream_t stream, hipEvent_t* events, int n_events);
 
 }  // namespace sv

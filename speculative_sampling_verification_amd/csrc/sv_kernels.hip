@@ -284,6 +284,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
     for (int h = 0; h < Tr<E>::kPerDword; ++h) mx = fmaxf(mx, Tr<E>::elem(regs[j], h));
   }
   mx = block_max_f(mx, red);
+  // Opaque to the compiler, so that the second pass decodes the elements again instead of
+  // keeping every decoded value live across the reduction.
+#pragma unroll
+  for (int j = 0; j < kRegs; ++j) asm volatile("" : "+v"(regs[j]));
   ChunkPart p;
   p.vmax = mx;
   p.argmax = -1;
@@ -1649,8 +1653,9 @@ hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, con
 hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,
                        const int32_t* tokens, int max_depth, int32_t* out_tokens,
                        int32_t* out_n, int32_t* out_last, const Workspace& ws,
-                       hipStream_t stream) {
+                       hipStream_t stream, hipEvent_t* ev, int nev) {
   (void)hipGetLastError();
+  if (ev && nev >= 1) (void)hipEventRecord(ev[0], stream);
   Samp sp{};
   sp.greedy = 1;
   const unsigned grid = (unsigned)((size_t)d.rows * d.nchunks);
@@ -1671,8 +1676,10 @@ hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int
       hipLaunchKernelGGL((k_chunk<float, false, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
                          stream, t, t, d, sp, ws);
   }
+  if (ev && nev >= 2) (void)hipEventRecord(ev[1], stream);
   hipLaunchKernelGGL(k_tree_walk, dim3(d.B), dim3(kSeqThreads), 0, stream, d, ws, parent, tokens,
                      max_depth, out_tokens, out_n, out_last);
+  if (ev && nev >= 3) (void)hipEventRecord(ev[2], stream);
   return hipGetLastError();
 }
 
