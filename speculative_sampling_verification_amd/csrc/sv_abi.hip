@@ -52,6 +52,7 @@ Samp make_samp(const sv_sampling* p, int V) {
   s.lenience = p->lenience;
   s.compact = !s.greedy && s.top_k > 0 && s.top_k <= kCompactMaxK;
   s.generic_trunc = !s.greedy && ((s.top_k > kCompactMaxK) || (s.top_p < 1.0f && !s.compact));
+  s.topp_hist = !s.greedy && s.top_k == 0 && s.top_p < 1.0f;
   return s;
 }
 
@@ -90,6 +91,10 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const size_t o_seq = c.take((size_t)d.B * sizeof(SeqState));
   const size_t o_fpart = c.take(s.greedy ? 0 : (size_t)d.B * nch * sizeof(double2));
   const size_t o_n = c.take((size_t)d.B * sizeof(int32_t));
+  const bool th = s.topp_hist != 0;
+  const size_t o_hist = c.take(th ? rows * nch * kHistBins * sizeof(unsigned long long) : 0);
+  const size_t o_tprow = c.take(th ? rows * sizeof(TopPRow) : 0);
+  const size_t o_tcand = c.take(th ? rows * kTopPCandCap * sizeof(uint2) : 0);
   if (ws) {
     ws->parts = s.compact ? nullptr : at<ChunkPart>(base, o_parts);
     ws->rstat = at<RowStat>(base, o_rstat);
@@ -97,6 +102,9 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
     ws->seq = at<SeqState>(base, o_seq);
     ws->fpart = s.greedy ? nullptr : at<double2>(base, o_fpart);
     ws->nbuf = at<int32_t>(base, o_n);
+    ws->hist = th ? at<unsigned long long>(base, o_hist) : nullptr;
+    ws->tprow = th ? at<TopPRow>(base, o_tprow) : nullptr;
+    ws->tcand = th ? at<uint2>(base, o_tcand) : nullptr;
   }
   return c.off;
 }

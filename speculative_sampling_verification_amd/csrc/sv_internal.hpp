@@ -27,6 +27,9 @@ constexpr int kVecPerThread = 16;    // 16-byte vectors each thread holds per ch
 constexpr int kCompactMaxK = 256;    // top-k <= this uses the compact candidate path
 constexpr int kKeptCap = 1024;       // kept tokens a compact row may hold
 constexpr int kSeqThreads = 64;      // one wave per sequence
+constexpr int kHistBins = 512;       // top-p mass histogram bins per chunk ...
+constexpr int kHistPerUnit = 8;      // ... on a grid of 1/8 of a unit of z / T
+constexpr int kTopPCandCap = 4096;   // boundary candidates a top-p row may hold
 
 // Row kinds written by k_row.
 enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
@@ -48,6 +51,15 @@ struct alignas(16) RowStat {
   int argmax;      // lowest index of the maximum (greedy rows)
   int nkept;       // number of kept tokens (compact rows), else -1
   int kind;        // RowKind
+  int pad;
+};
+
+// Top-p selection state of a row (histogram path): the boundary lies among the elements whose
+// grid edge floor(8 z / T) is in [e_lo, e_hi]; every element above e_hi is kept.
+struct alignas(16) TopPRow {
+  double mass_above;  // sum of exp((z - m) / T) over the elements above e_hi
+  int e_lo, e_hi;     // candidate edge range (e_lo = INT_MIN: open below)
+  int count;          // candidates appended (may exceed kTopPCandCap: the row falls back)
   int pad;
 };
 
@@ -78,6 +90,7 @@ struct Samp {
   int compact;      // compact top-k path
   int generic_trunc;// truncation that needs the row-pass selection (top-k > kCompactMaxK or top-p
                     // without a compact list)
+  int topp_hist;    // top-p without top-k: histogram, boundary candidates, exact selection
 };
 
 struct Workspace {
@@ -87,6 +100,9 @@ struct Workspace {
   SeqState* seq;     // [B]
   double2* fpart;    // [B][nchunks]  (residual mass, target mass)
   int32_t* nbuf;     // [B] accepted counts when the caller does not want them
+  unsigned long long* hist;  // [rows][nchunks][kHistBins] fixed-point mass   top-p histogram only
+  TopPRow* tprow;            // [rows]                                        top-p histogram only
+  uint2* tcand;              // [rows][kTopPCandCap] (index, bits)            top-p histogram only
 };
 
 inline int chunk_elems_for(sv_dtype dt) {

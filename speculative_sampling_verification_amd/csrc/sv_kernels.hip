@@ -260,7 +260,15 @@ __device__ __forceinline__ int slot_index(int c0, int i, int d, int h) {
 //   dense : vmax and sum exp((z - vmax) / T) over the chunk
 //   argmax: vmax and the lowest index holding it
 // ------------------------------------------------------------------------------------------
-template <class E, bool VEC, int MODE>
+// Grid edge of a logit for the top-p mass histogram: floor(8 z / T), clamped so that any finite
+// logit (and -inf) maps to an int.  Every kernel bins with this one function.
+__device__ __forceinline__ int topp_edge(float z, float it) {
+  float f = floorf(z * it * (float)kHistPerUnit);
+  f = fminf(fmaxf(f, -1073741824.0f), 1073741824.0f);
+  return (int)f;
+}
+
+template <class E, bool VEC, int MODE, bool HIST = false>
 __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
                                                     const E* __restrict__ drf, Dims dm, Samp sp,
                                                     Workspace ws) {
@@ -276,6 +284,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
   uint32_t regs[kRegs];
   ChunkPart* part = ws.parts + (size_t)r * dm.nchunks + c;
 
+  __shared__ unsigned long long s_hist[HIST ? kHistBins : 1];
+  if constexpr (HIST)
+    for (int j = tid; j < kHistBins; j += kThreads) s_hist[j] = 0ull;
   load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kNegInfPair);
   float mx = -INFINITY;
 #pragma unroll
@@ -295,21 +306,38 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
   p.pad[0] = p.pad[1] = p.pad[2] = p.pad[3] = 0;
   if constexpr (MODE == kChunkDense) {
     double s = 0.0;
+    const float it = sp.inv_t;
+    const int etop = topp_edge(mx, it);
     if (mx > -INFINITY) {
-      const float it = sp.inv_t;
 #pragma unroll
       for (int i = 0; i < kVecPerThread; ++i) {
         float sv = 0.f;  // one vector's EPV terms in fp32, then into the fp64 total
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
 #pragma unroll
-          for (int h = 0; h < Tr<E>::kPerDword; ++h)
-            sv += expf((Tr<E>::elem(regs[4 * i + d], h) - mx) * it);
+          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+            const float z = Tr<E>::elem(regs[4 * i + d], h);
+            const float e = expf((z - mx) * it);
+            sv += e;
+            if constexpr (HIST) {
+              // mass in 2^-40 fixed point relative to the chunk maximum, so that the bin sums
+              // are exact integer additions whatever their order
+              if (e > 0.0f) {
+                const int j = min(etop - topp_edge(z, it), kHistBins - 1);
+                atomicAdd(&s_hist[j], __float2ull_rz(e * 1099511627776.0f));
+              }
+            }
+          }
         }
         s += (double)sv;
       }
     }
-    p.sum = block_sum_d(s, red);
+    p.sum = block_sum_d(s, red);  // its barriers also order the histogram updates
+    if constexpr (HIST) {
+      unsigned long long* dst = ws.hist + ((size_t)r * dm.nchunks + c) * kHistBins;
+      for (int j = tid; j < kHistBins; j += kThreads) dst[j] = s_hist[j];
+      p.pad[0] = etop;
+    }
   } else {
     int best = INT_MAX;
 #pragma unroll
@@ -449,6 +477,308 @@ __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_
 }
 
 // ------------------------------------------------------------------------------------------
+// Top-p without top-k (the nucleus; Chen et al. notes, A2, and the Leviathan blog's standardised
+// sampling section: the smallest set of most probable tokens whose mass reaches P).
+//   k_chunk (HIST)  per chunk: a histogram of exp((z - chunk max) / T) in 2^-40 fixed point
+//                   over edges floor(8 z / T), 512 edges down from the chunk maximum's (the last
+//                   bin holds everything lower)
+//   k_row           merges the chunk histograms onto the row maximum's edges and finds the bin
+//                   where the mass, accumulated from the top, first reaches P * S; the elements
+//                   of that bin and its two neighbours are the candidates, everything above is
+//                   kept
+//   k_topp_cand     re-reads the rows and appends the candidates to a per-row list
+//   k_topp_select   sorts the candidates by logit (descending) and takes the exact boundary
+// The tokens in the last bin are at least 64 units of z / T below the maximum, where the mass of
+// any number of tokens that fits an int stays below 1 - P for every float P < 1, so the
+// boundary is never among them unless the candidate range is already open below.
+// ------------------------------------------------------------------------------------------
+__device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPart* parts,
+                           float m, double S, double* s_mass, const Workspace& ws) {
+  const int tid = threadIdx.x;
+  __shared__ RedScratch red;
+  int emt = INT_MIN;
+  for (int c = tid; c < dm.nchunks; c += kThreads)
+    if (parts[c].vmax > -INFINITY) emt = max(emt, parts[c].pad[0]);
+  const int em = block_max_i(emt, red);
+  const unsigned long long* hist = ws.hist + (size_t)r * dm.nchunks * kHistBins;
+  // row bin B holds the elements with edge em - B (B = kHistBins - 1: that edge and below);
+  // chunk c's bin j lands in row bin j + (em - edge of chunk c's maximum).  Chunks are added in
+  // order, one bin per thread and chunk (the shift is one-to-one below the last bin), so every
+  // bin's sum has a fixed order; the last bin's share is summed per thread and reduced.
+  constexpr int PT = kHistBins / kThreads;
+#pragma unroll
+  for (int i = 0; i < PT; ++i) s_mass[tid + i * kThreads] = 0.0;
+  double rest = 0.0;
+  unsigned long long hn[PT];
+  auto load_h = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+      hn[i] = c < dm.nchunks ? hist[(size_t)c * kHistBins + tid + i * kThreads] : 0ull;
+  };
+  load_h(0);
+  for (int c = 0; c < dm.nchunks; ++c) {
+    unsigned long long h[PT];
+#pragma unroll
+    for (int i = 0; i < PT; ++i) h[i] = hn[i];
+    load_h(c + 1);
+    const ChunkPart p = parts[c];
+    __syncthreads();
+    if (p.vmax > -INFINITY) {
+      const double sc = exp((double)(p.vmax - m) / (double)sp.temperature) * 0x1p-40;
+      const long long dc = (long long)em - p.pad[0];
+#pragma unroll
+      for (int i = 0; i < PT; ++i) {
+        const int j = tid + i * kThreads;
+        const double v = (double)h[i] * sc;
+        if (j == kHistBins - 1 || j + dc >= kHistBins - 1)
+          rest += v;
+        else
+          s_mass[j + dc] += v;
+      }
+    }
+  }
+  rest = block_sum_d(rest, red);
+  if (tid == 0) s_mass[kHistBins - 1] = rest;
+  __syncthreads();
+  if (tid < 64) {
+    constexpr int PER = kHistBins / 64;
+    const int lane = tid;
+    double v[PER];
+    double tot = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      v[i] = s_mass[lane * PER + i];
+      tot += v[i];
+    }
+    double inc = tot;  // inclusive scan over lanes, fixed order
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    double cum = __shfl_up(inc, 1);
+    if (lane == 0) cum = 0.0;
+    const double target = (double)sp.top_p * S;
+    int bstar = INT_MAX, last = -1;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      cum += v[i];
+      if (cum >= target && bstar == INT_MAX) bstar = lane * PER + i;
+      if (v[i] > 0.0) last = lane * PER + i;
+    }
+    bstar = wave_reduce(bstar, [](int a, int b) { return a < b ? a : b; });
+    last = wave_reduce(last, [](int a, int b) { return a > b ? a : b; });
+    if (bstar == INT_MAX) bstar = last < 0 ? 0 : last;  // rounding kept the total below P S
+    const int lo = bstar > 0 ? bstar - 1 : 0;
+    const int hi = bstar + 1 < kHistBins - 1 ? bstar + 1 : kHistBins - 1;
+    double above = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      if (lane * PER + i < lo) above += v[i];
+    above = wave_reduce(above, [](double a, double b) { return a + b; });
+    if (lane == 0) {
+      TopPRow t;
+      t.mass_above = above;
+      t.e_hi = em - lo;
+      t.e_lo = hi == kHistBins - 1 ? INT_MIN : em - hi;
+      t.count = 0;
+      t.pad = 0;
+      ws.tprow[r] = t;
+    }
+  }
+}
+
+// Candidates of the boundary bins, appended to the row's list (in no particular order:
+// k_topp_select's result does not depend on it).  A chunk gathers its candidates in LDS and
+// reserves room in the row's list with one atomic add.
+constexpr int kToppChunkCap = 2048;  // candidates one chunk may gather
+
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tgt,
+                                                        const E* __restrict__ drf, Dims dm,
+                                                        Samp sp, Workspace ws) {
+  const int bid = blockIdx.x;
+  const int r = bid / dm.nchunks;
+  const int c = bid - r * dm.nchunks;
+  const int tid = threadIdx.x;
+  const E* row = row_ptr(dm, tgt, drf, r);
+  const int c0 = c * dm.chunk_elems;
+  const int clen = min(dm.chunk_elems, dm.V - c0);
+  const int e_lo = ws.tprow[r].e_lo, e_hi = ws.tprow[r].e_hi;
+  const float it = sp.inv_t;
+  __shared__ uint2 s_c[kToppChunkCap];
+  __shared__ int s_n, s_base;
+  if (tid == 0) s_n = 0;
+  uint32_t regs[kRegs];
+  load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kNegInfPair);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kVecPerThread; ++i) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+      for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+        const float z = Tr<E>::elem(regs[4 * i + d], h);
+        const int e = topp_edge(z, it);
+        if (z > -INFINITY && e >= e_lo && e <= e_hi) {
+          const int pos = atomicAdd(&s_n, 1);
+          if (pos < kToppChunkCap)
+            s_c[pos] = make_uint2(slot_index<E>(c0, i, d, h), __float_as_uint(z));
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int n = s_n;
+  if (n == 0) return;
+  if (tid == 0)  // a chunk that overflowed its buffer pushes the row past the list capacity
+    s_base = atomicAdd(&ws.tprow[r].count, n <= kToppChunkCap ? n : kTopPCandCap + 1);
+  __syncthreads();
+  const int base = s_base;
+  uint2* list = ws.tcand + (size_t)r * kTopPCandCap;
+  if (n <= kToppChunkCap)
+    for (int j = tid; j < n && base + j < kTopPCandCap; j += kThreads) list[base + j] = s_c[j];
+}
+
+// Order-preserving key of a float (see Tr), with -0 merged into +0.
+__device__ __forceinline__ uint32_t float_key(float z) {
+  return Tr<float>::canon(Tr<float>::keys_of_dword(__float_as_uint(z)));
+}
+
+// Weight of a candidate in 2^-40 fixed point (integer sums: exact whatever their order).
+__device__ __forceinline__ unsigned long long topp_weight(uint32_t key, float m, float it) {
+  return __float2ull_rz(expf((Tr<float>::key_to_float(key) - m) * it) * 1099511627776.0f);
+}
+
+// The exact top-p threshold of a row among its boundary candidates: the largest key v such that
+// the mass above the candidate range plus the candidates' mass at keys >= v reaches P * S, by a
+// most-significant-digit-first selection on the candidates' keys (8-bit digits, mass-weighted
+// bins).  v is the key of the first candidate, in descending order, at which the running mass
+// reaches the target; every token at that logit or above is kept.  A row whose candidates
+// overflowed the list (or whose candidates' mass does not reach the target, from rounding)
+// takes the exact selection by re-reading the row.
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_topp_select(const E* __restrict__ tgt,
+                                                          const E* __restrict__ drf, Dims dm,
+                                                          Samp sp, Workspace ws) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  __shared__ unsigned long long s_buf[kTopPCandCap / 2];  // candidate keys; radix bins on fallback
+  __shared__ unsigned long long s_bins[256];
+  __shared__ RedScratch red;
+  __shared__ uint32_t s_prefix;
+  __shared__ unsigned long long s_need;
+  uint32_t* s_key = reinterpret_cast<uint32_t*>(s_buf);
+  RowStat rs = ws.rstat[r];
+  const TopPRow tr = ws.tprow[r];
+  const float m = rs.m;
+  const float it = sp.inv_t;
+  const double S = rs.S;
+  const int n = tr.count;
+  bool fallback = n > kTopPCandCap;
+  double Skept = 0.0;
+  float thr = -INFINITY;
+  if (!fallback) {
+    const uint2* list = ws.tcand + (size_t)r * kTopPCandCap;
+    unsigned long long tot = 0;
+    for (int i = tid; i < n; i += kThreads) {
+      const uint32_t key = float_key(__uint_as_float(list[i].y));
+      s_key[i] = key;
+      tot += topp_weight(key, m, it);
+    }
+    tot = wave_reduce(tot, [](unsigned long long x, unsigned long long y) { return x + y; });
+    if (lane_id() == 0) red.u[wave_id()] = tot;
+    if (tid == 0) s_prefix = 0u;
+    __syncthreads();
+    tot = red.u[0] + red.u[1] + red.u[2] + red.u[3];
+    const double rem = (double)sp.top_p * S - tr.mass_above;
+    unsigned long long need = 1ull;
+    if (rem > 0.0) {
+      const double q = ceil(rem * 1099511627776.0);
+      need = q < 1.8e19 ? (unsigned long long)q : ~0ull;
+      if (need == 0ull) need = 1ull;
+    }
+    if (need > tot) {  // the candidates' mass does not reach the target
+      if (tr.e_lo == INT_MIN) {
+        thr = -INFINITY;  // rounding: keep every token
+        Skept = tr.mass_above + (double)tot * 0x1p-40;
+      } else {
+        fallback = true;
+      }
+    } else {
+      if (tid == 0) s_need = need;
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int j = tid; j < 256; j += kThreads) s_bins[j] = 0ull;
+        __syncthreads();
+        const uint32_t prefix = s_prefix;
+        for (int i = tid; i < n; i += kThreads) {
+          const uint32_t key = s_key[i];
+          if (shift == 24 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
+            atomicAdd(&s_bins[(key >> shift) & 255u], topp_weight(key, m, it));
+        }
+        __syncthreads();
+        if (tid < 64) {  // digits from 255 down: lane L holds 255 - 4L - i, i = 0..3
+          const int L = tid;
+          unsigned long long bv[4], loc = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bv[i] = s_bins[255 - 4 * L - i];
+            loc += bv[i];
+          }
+          unsigned long long inc = loc;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long y = __shfl_up(inc, o);
+            if (L >= o) inc += y;
+          }
+          const unsigned long long want = s_need;
+          unsigned long long cum = inc - loc, before = 0;
+          int hit = -1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (hit < 0 && cum + bv[i] >= want) {
+              hit = i;
+              before = cum;
+            }
+            cum += bv[i];
+          }
+          const unsigned long long lanes = __ballot(hit >= 0);
+          if (lanes && L == __ffsll((long long)lanes) - 1) {
+            s_prefix = prefix | ((uint32_t)(255 - 4 * L - hit) << shift);
+            s_need = want - before;
+          }
+        }
+        __syncthreads();
+      }
+      const uint32_t v = s_prefix;
+      thr = Tr<float>::key_to_float(v);
+      unsigned long long own = 0;
+      for (int i = tid; i < n; i += kThreads)
+        if (s_key[i] >= v) own += topp_weight(s_key[i], m, it);
+      own = wave_reduce(own, [](unsigned long long x, unsigned long long y) { return x + y; });
+      __syncthreads();
+      if (lane_id() == 0) red.u[wave_id()] = own;
+      __syncthreads();
+      Skept = tr.mass_above + (double)(red.u[0] + red.u[1] + red.u[2] + red.u[3]) * 0x1p-40;
+    }
+  }
+  if (fallback) {
+    __syncthreads();
+    const E* row = row_ptr(dm, tgt, drf, r);
+    const uint32_t key =
+        radix_select<E, VEC, true>(row, dm.V, m, it, 0u, (double)sp.top_p, s_buf, red);
+    thr = Tr<E>::key_to_float(key);
+    Skept = dense_sum<E, VEC>(row, dm.V, m, it, thr, red);
+  }
+  if (tid == 0) {
+    rs.thr = thr;
+    rs.S = Skept;
+    rs.kind = kRowDense;
+    ws.rstat[r] = rs;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // k_row: one workgroup per row.  Produces RowStat (m, thr, S) from the chunk partials; top-k
 // above the compact limit and top-p select their thresholds by re-reading the row.
 // ------------------------------------------------------------------------------------------
@@ -466,26 +796,31 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
   __shared__ int s_argmax;
   __shared__ double s_S;
 
-  if (tid == 0) {
-    float m = -INFINITY;
-    int am = INT_MAX;
-    for (int c = 0; c < dm.nchunks; ++c) {
+  // Row maximum (and the lowest index holding it), then the normaliser, over the chunk
+  // partials: threads take chunks in a fixed order and combine in a fixed tree.
+  float mt = -INFINITY;
+  int at = INT_MAX;
+  for (int c = tid; c < dm.nchunks; c += kThreads) {
+    const ChunkPart p = parts[c];
+    if (p.vmax > mt) {  // chunks of one thread ascend, so the first maximum wins
+      mt = p.vmax;
+      at = p.argmax;
+    }
+  }
+  const float mrow = block_max_f(mt, red);
+  const int am = block_min_i(mt == mrow ? at : INT_MAX, red);
+  double st = 0.0;
+  if (!sp.greedy) {
+    for (int c = tid; c < dm.nchunks; c += kThreads) {
       const ChunkPart p = parts[c];
-      if (p.vmax > m) {
-        m = p.vmax;
-        am = p.argmax;
-      }
+      if (p.sum > 0.0) st += p.sum * exp((double)(p.vmax - mrow) / (double)sp.temperature);
     }
-    double S = 0.0;
-    if (!sp.greedy) {
-      for (int c = 0; c < dm.nchunks; ++c) {
-        const ChunkPart p = parts[c];
-        if (p.sum > 0.0) S += p.sum * exp((double)(p.vmax - m) / (double)sp.temperature);
-      }
-    }
-    s_m = m;
+  }
+  const double Srow = sp.greedy ? 0.0 : block_sum_d(st, red);
+  if (tid == 0) {
+    s_m = mrow;
     s_argmax = am;
-    s_S = S;
+    s_S = Srow;
   }
   __syncthreads();
   const float m = s_m;
@@ -508,6 +843,18 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
   }
 
   const float it = sp.inv_t;
+  if (sp.topp_hist) {
+    // top-p without top-k: locate the boundary bin of the merged mass histogram; the exact
+    // threshold is taken among the boundary candidates by k_topp_select
+    topp_range(dm, sp, r, parts, m, s_S, reinterpret_cast<double*>(s_bins), ws);
+    if (tid == 0) {
+      out.thr = -INFINITY;
+      out.S = s_S;
+      out.kind = kRowDense;
+      ws.rstat[r] = out;
+    }
+    return;
+  }
   uint32_t lower_key = 0;  // selection threshold key (0: none)
 
   // Whole-row path: exact selections by re-reading the row.
@@ -723,8 +1070,80 @@ __device__ __forceinline__ void load_vec_f(const E* row, int V, int e0, float (&
   }
 }
 
+// Weights of the final draw for one element pair, in fp32 with the normalisers' reciprocals
+// taken once per row: w = max(0, q - p) (the residual, Theorem 1) and q.  Sums over them run in
+// fp64 (per 16-byte vector in fp32 first).
+struct DrawRows {
+  RowStat rt, rd;
+  float inv_st, inv_sd;
+  bool resid;
+};
+
+__device__ __forceinline__ void draw_weights(float zt, float zd, const DrawRows& g, float it,
+                                             float& w, float& q) {
+  q = kept_exp(zt, g.rt, it) * g.inv_st;
+  w = q;
+  if (g.resid) w = fmaxf(q - kept_exp(zd, g.rd, it) * g.inv_sd, 0.0f);
+}
+
+__device__ __forceinline__ DrawRows draw_rows(const Dims& dm, const Workspace& ws, int b, int n) {
+  DrawRows g;
+  g.resid = n < dm.K;
+  g.rt = ws.rstat[target_row(dm, b, n)];
+  g.rd = g.resid ? ws.rstat[draft_row(dm, b, n)] : g.rt;
+  g.inv_st = (float)(1.0 / g.rt.S);
+  g.inv_sd = (float)(1.0 / g.rd.S);
+  return g;
+}
+
+// NV 16-byte vectors per thread from a row.  STRIDED: vector i of thread t at element
+// base + (t + 256 i) * EPV; otherwise a contiguous run, vector i at base + i * EPV.  With VEC the
+// loads are range-checked buffer loads, so no load sits behind a branch: elements at or past
+// `end` read as 0 and the caller must not use them.  Without VEC they read as -inf.  `end` must
+// be the same in every lane (it sets the buffer's range).
+template <class E, bool VEC, int NV, bool STRIDED>
+__device__ __forceinline__ void load_vecs(const E* __restrict__ row, int end, int base,
+                                          uint32_t (&regs)[4 * NV]) {
+  constexpr int EPV = Tr<E>::kEpv;
+  constexpr uint32_t kNegInf = Tr<E>::kNegInfPair;
+  const int t = STRIDED ? (int)threadIdx.x : 0;
+  if constexpr (VEC) {
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<E*>(row), (short)0, end * (int)sizeof(E), 0x00020000);
+    const int voff = (base + t * EPV) * (int)sizeof(E);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int step = STRIDED ? kThreads * EPV : EPV;
+      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i * step * (int)sizeof(E), 0);
+      regs[4 * i + 0] = x.x;
+      regs[4 * i + 1] = x.y;
+      regs[4 * i + 2] = x.z;
+      regs[4 * i + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int e = base + (t + (STRIDED ? kThreads * i : i)) * EPV;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+          const int idx = e + d * Tr<E>::kPerDword + h;
+          const uint32_t bits = idx < end ? Tr<E>::bits_of(row[idx])
+                                          : ((Tr<E>::kPerDword == 2) ? 0xFF80u : kNegInf);
+          w |= bits << (16 * h * (Tr<E>::kPerDword == 2));
+        }
+        regs[4 * i + d] = w;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // k_final_partial: grid = B x chunks; mass of the final weights per chunk (residual, target).
+// Both rows' chunks are loaded as register tiles up front.
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict__ tgt,
@@ -736,29 +1155,38 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
   if (!st.need_dense) return;
   __shared__ RedScratch red;
   const int n = st.n;
-  const bool resid = n < dm.K;
-  const RowStat rt = ws.rstat[target_row(dm, b, n)];
-  RowStat rd = rt;
+  const DrawRows g = draw_rows(dm, ws, b, n);
   const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
-  const E* drow = trow;
-  if (resid) {
-    rd = ws.rstat[draft_row(dm, b, n)];
-    drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
-  }
-  constexpr int EPV = Tr<E>::kEpv;
+  const E* drow = g.resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : trow;
   const int c0 = c * dm.chunk_elems;
-  const int clen = min(dm.chunk_elems, dm.V - c0);
-  const int nvec = (clen + EPV - 1) / EPV;
+  const int cend = min(c0 + dm.chunk_elems, dm.V);
   const float it = sp.inv_t;
+  constexpr int EPV = Tr<E>::kEpv;
+  constexpr int NV = 4;  // vectors per thread per step; many workgroups hide the load latency
   double W = 0.0, Q = 0.0;
-  for (int v = threadIdx.x; v < nvec; v += kThreads) {
-    float zt[EPV], zd[EPV];
-    load_vec_f<E, VEC>(trow, dm.V, c0 + v * EPV, zt);
-    if (resid) load_vec_f<E, VEC>(drow, dm.V, c0 + v * EPV, zd);
+#pragma unroll 1
+  for (int s = 0; s < kVecPerThread / NV; ++s) {
+    const int base = c0 + s * kThreads * NV * EPV;
+    uint32_t rt[4 * NV], rd[4 * NV];
+    load_vecs<E, VEC, NV, true>(trow, cend, base, rt);
+    if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, base, rd);
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      W += final_weight(zt[e], resid ? zd[e] : 0.f, rt, rd, resid, false, it);
-      Q += final_weight(zt[e], 0.f, rt, rd, false, true, it);
+    for (int i = 0; i < NV; ++i) {
+      float wv = 0.0f, qv = 0.0f;
+      const int e = base + ((int)threadIdx.x + kThreads * i) * EPV;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+          float w, q;
+          draw_weights(e < cend ? Tr<E>::elem(rt[4 * i + d], h) : -INFINITY,
+                       g.resid ? Tr<E>::elem(rd[4 * i + d], h) : 0.0f, g, it, w, q);
+          wv += w;
+          qv += q;
+        }
+      }
+      W += (double)wv;
+      Q += (double)qv;
     }
   }
   W = block_sum_d(W, red);
@@ -766,8 +1194,28 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
   if (threadIdx.x == 0) ws.fpart[(size_t)b * dm.nchunks + c] = make_double2(W, Q);
 }
 
+// Exclusive prefix of one double per thread over the workgroup, in thread order (fixed order:
+// a scan inside each wave, then the wave totals in order).  Also returns the total.
+__device__ double block_exclusive_d(double v, double& total, RedScratch& red) {
+  double x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(x, o);
+    if (lane_id() >= o) x += y;
+  }
+  __syncthreads();
+  if (lane_id() == 63) red.d[wave_id()] = x;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < wave_id(); ++w) base += red.d[w];
+  total = ((red.d[0] + red.d[1]) + red.d[2]) + red.d[3];
+  return base + (x - v);
+}
+
 // ------------------------------------------------------------------------------------------
-// k_final_pick: grid = B.  Chooses the chunk holding u*W, then scans it in index order.
+// k_final_pick: grid = B.  Chooses the chunk holding u*W (chunk totals scanned in order), then
+// the token inside it: every thread owns a contiguous run of the chunk, so one scan of the
+// threads' sums locates the run and the thread that owns it finds the index.
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ tgt,
@@ -780,116 +1228,139 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
   if (!st.need_dense) return;
   const int tid = threadIdx.x;
   __shared__ RedScratch red;
-  __shared__ double s_scan[kThreads];
-  __shared__ double s_before, s_target;
-  __shared__ int s_chunk, s_useq;
+  __shared__ int s_chunk, s_last, s_pick;
+  __shared__ double s_before;
   const int n = st.n;
   const int K = dm.K;
-  const bool resid = n < K;
+  const DrawRows g = draw_rows(dm, ws, b, n);
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
+  const E* drow = g.resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : trow;
   const double2* fp = ws.fpart + (size_t)b * dm.nchunks;
+  // chunk totals: thread t owns chunks [t * per, (t + 1) * per)
+  const int per = (dm.nchunks + kThreads - 1) / kThreads;
+  const int ca = min(dm.nchunks, tid * per), cb = min(dm.nchunks, ca + per);
+  double w_loc = 0.0, q_loc = 0.0;
+  for (int c = ca; c < cb; ++c) {
+    w_loc += fp[c].x;
+    q_loc += fp[c].y;
+  }
+  double Wt, Qt;
+  double w_ex = block_exclusive_d(w_loc, Wt, red);
+  const double q_ex = block_exclusive_d(q_loc, Qt, red);
+  const bool use_q = !(Wt > 0.0) || !g.resid;
+  const double W = use_q ? Qt : Wt;
+  if (use_q) w_ex = q_ex;
+  const double target = (double)uni[(size_t)b * (K + 1) + K] * W;
   if (tid == 0) {
-    double W = 0.0;
-    for (int c = 0; c < dm.nchunks; ++c) W += fp[c].x;
-    int useq = !(W > 0.0) || !resid;
-    if (useq) {
-      W = 0.0;
-      for (int c = 0; c < dm.nchunks; ++c) W += fp[c].y;
-    }
-    const double target = (double)uni[(size_t)b * (K + 1) + K] * W;
-    double cum = 0.0;
-    int ch = -1, lastpos = 0;
-    double before_last = 0.0;
-    for (int c = 0; c < dm.nchunks; ++c) {
-      const double v = useq ? fp[c].y : fp[c].x;
-      if (v > 0.0) {
-        lastpos = c;
-        before_last = cum;
-      }
-      if (cum + v > target) {
-        ch = c;
-        break;
-      }
-      cum += v;
-    }
-    if (ch < 0) {
-      ch = lastpos;
-      cum = before_last;
-    }
-    s_chunk = ch;
-    s_before = cum;
-    s_target = target;
-    s_useq = useq;
-    if (resid && !(useq == 0)) {
-      // residual had zero mass: q is used (reported)
+    s_chunk = INT_MAX;
+    s_last = -1;
+    s_pick = INT_MAX;
+    if (g.resid && use_q) {  // the residual had zero mass: q is used (reported)
       SeqState s2 = st;
       s2.fallback = 1;
       ws.seq[b] = s2;
     }
   }
   __syncthreads();
-  const int c = s_chunk;
-  const bool use_q = s_useq != 0;
-  const double target = s_target;
-  const RowStat rt = ws.rstat[target_row(dm, b, n)];
-  RowStat rd = rt;
-  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
-  const E* drow = trow;
-  if (resid) {
-    rd = ws.rstat[draft_row(dm, b, n)];
-    drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
+  {
+    double cum = w_ex;
+    int found = INT_MAX, lastc = -1;
+    for (int c = ca; c < cb; ++c) {
+      const double v = use_q ? fp[c].y : fp[c].x;
+      if (v > 0.0) lastc = c;
+      if (found == INT_MAX && cum + v > target) found = c;
+      cum += v;
+    }
+    if (found != INT_MAX) atomicMin(&s_chunk, found);
+    if (lastc >= 0) atomicMax(&s_last, lastc);
   }
+  __syncthreads();
+  const int c = s_chunk != INT_MAX ? s_chunk : s_last;
+  if (c >= ca && c < cb) {  // the owner of chunk c: the mass before it, as summed above
+    double cum = w_ex;
+    for (int cc = ca; cc < c; ++cc) cum += use_q ? fp[cc].y : fp[cc].x;
+    s_before = cum;
+  }
+  // the chunk: thread t owns elements [c0 + t * run, c0 + (t + 1) * run)
   constexpr int EPV = Tr<E>::kEpv;
   const int c0 = c * dm.chunk_elems;
   const int clen = min(dm.chunk_elems, dm.V - c0);
-  const int nvec = (clen + EPV - 1) / EPV;
+  const int run = kVecPerThread * EPV;  // chunk_elems / kThreads
+  const int e0 = c0 + tid * run;
+  const int cend = c0 + clen;  // uniform: the buffer range of the loads
+  const int e1 = min(cend, e0 + run);
   const float it = sp.inv_t;
-  double carry = s_before;
-  int pick = INT_MAX, lastpos = -1;
-  for (int v0 = 0; v0 < nvec; v0 += kThreads) {
-    const int v = v0 + tid;
-    double w[EPV];
-    double local = 0.0;
-    {
-      float zt[EPV], zd[EPV];
-      if (v < nvec) {
-        load_vec_f<E, VEC>(trow, dm.V, c0 + v * EPV, zt);
-        if (resid) load_vec_f<E, VEC>(drow, dm.V, c0 + v * EPV, zd);
-      }
+  constexpr int NV = 4;  // vectors per step of the run
+  double loc = 0.0;
+  int mylast = -1;
+#pragma unroll 1
+  for (int s = 0; s < kVecPerThread / NV; ++s) {
+    const int es = e0 + s * NV * EPV;
+    uint32_t rt[4 * NV], rd[4 * NV];
+    load_vecs<E, VEC, NV, false>(trow, cend, es, rt);
+    if (g.resid) load_vecs<E, VEC, NV, false>(drow, cend, es, rd);
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        w[e] = (v < nvec) ? final_weight(zt[e], resid ? zd[e] : 0.f, rt, rd, resid, use_q, it)
-                          : 0.0;
-        local += w[e];
-      }
-    }
-    // inclusive scan of `local` over the 256 threads (index order), fp64
-    s_scan[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < kThreads; off <<= 1) {
-      const double add = tid >= off ? s_scan[tid - off] : 0.0;
-      __syncthreads();
-      s_scan[tid] += add;
-      __syncthreads();
-    }
-    double cum = carry + (s_scan[tid] - local);
-    int mine = INT_MAX, mylast = -1;
+    for (int i = 0; i < NV; ++i) {
+      float vv = 0.0f;
+      const int e = es + i * EPV;
 #pragma unroll
-    for (int e = 0; e < EPV; ++e) {
-      if (w[e] > 0.0) mylast = c0 + v * EPV + e;
-      cum += w[e];
-      if (mine == INT_MAX && cum > target && w[e] > 0.0) mine = c0 + v * EPV + e;
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+          float w, q;
+          draw_weights(e < e1 ? Tr<E>::elem(rt[4 * i + d], h) : -INFINITY,
+                       g.resid ? Tr<E>::elem(rd[4 * i + d], h) : 0.0f, g, it, w, q);
+          const float v = use_q ? q : w;
+          vv += v;
+          if (v > 0.0f) mylast = e + d * Tr<E>::kPerDword + h;
+        }
+      }
+      loc += (double)vv;
     }
-    const double round_total = s_scan[kThreads - 1];
-    const int got = block_min_i(mine, red);
-    const int lp = block_max_i(mylast, red);
-    if (lp > lastpos) lastpos = lp;
-    if (got != INT_MAX) {
-      pick = got;
-      break;
-    }
-    carry += round_total;
   }
-  if (tid == 0) out_tokens[(size_t)b * (K + 1) + n] = pick != INT_MAX ? pick : lastpos;
+  double tot;
+  const double ex = block_exclusive_d(loc, tot, red);  // its barriers also publish s_before
+  double cum = s_before + ex;
+  if (cum + loc > target) {  // this thread's run holds the first index past the target
+    int hit = INT_MAX;
+#pragma unroll 1
+    for (int s = 0; s < kVecPerThread / NV && hit == INT_MAX; ++s) {
+      const int es = e0 + s * NV * EPV;
+      uint32_t rt[4 * NV], rd[4 * NV];
+      load_vecs<E, VEC, NV, false>(trow, cend, es, rt);
+      if (g.resid) load_vecs<E, VEC, NV, false>(drow, cend, es, rd);
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int e = es + i * EPV;
+        float wv[EPV];
+        float vv = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+            float w, q;
+            draw_weights(e < e1 ? Tr<E>::elem(rt[4 * i + d], h) : -INFINITY,
+                         g.resid ? Tr<E>::elem(rd[4 * i + d], h) : 0.0f, g, it, w, q);
+            wv[d * Tr<E>::kPerDword + h] = use_q ? q : w;
+            vv += wv[d * Tr<E>::kPerDword + h];
+          }
+        }
+        // the vector's elements one by one only where the running sum crosses the target
+        if (hit == INT_MAX && cum + (double)vv > target) {
+#pragma unroll
+          for (int x = 0; x < EPV; ++x) {
+            cum += (double)wv[x];
+            if (hit == INT_MAX && wv[x] > 0.0f && cum > target) hit = e + x;
+          }
+        } else {
+          cum += (double)vv;
+        }
+      }
+    }
+    if (hit != INT_MAX) atomicMin(&s_pick, hit);
+  }
+  const int lp = block_max_i(mylast, red);
+  if (tid == 0) out_tokens[(size_t)b * (K + 1) + n] = s_pick != INT_MAX ? s_pick : lp;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1608,11 +2079,20 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
   if (sp.greedy)
     hipLaunchKernelGGL((k_chunk<E, VEC, kChunkArgmax>), dim3(grid_chunks), dim3(kThreads), 0, st,
                        t, d, dm, sp, ws);
+  else if (sp.topp_hist)
+    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkDense, true>), dim3(grid_chunks), dim3(kThreads), 0,
+                       st, t, d, dm, sp, ws);
   else
     hipLaunchKernelGGL((k_chunk<E, VEC, kChunkDense>), dim3(grid_chunks), dim3(kThreads), 0, st,
                        t, d, dm, sp, ws);
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
+  if (sp.topp_hist) {
+    hipLaunchKernelGGL((k_topp_cand<E, VEC>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm,
+                       sp, ws);
+    hipLaunchKernelGGL((k_topp_select<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm,
+                       sp, ws);
+  }
   hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
   if (!sp.greedy) {
     hipLaunchKernelGGL((k_final_partial<E, VEC>), dim3((unsigned)((size_t)dm.B * dm.nchunks)),

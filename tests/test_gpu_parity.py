@@ -88,6 +88,26 @@ def test_topp_bf16_small():
     verify_case(t, d, dict(temperature=0.8, top_p=0.9), seed=11)
 
 
+def test_topp_boundary_candidate_overflow():
+    _announce("bf16 logits on 4 levels, top-p 0.9: boundary bin overflows -> row-pass selection")
+    g = torch.Generator().manual_seed(23)
+    t = torch.randint(0, 4, (3, 3, 40000), generator=g).float().to(torch.bfloat16)
+    d = torch.randint(0, 4, (3, 2, 40000), generator=g).float().to(torch.bfloat16)
+    verify_case(t, d, dict(temperature=1.0, top_p=0.9), seed=23)
+
+
+@pytest.mark.parametrize("P,T", [(0.01, 1.0), (0.9999, 1.0), (0.95, 0.05), (0.5, 3.0)])
+def test_topp_extremes(P, T):
+    _announce(f"fp32 top-p {P} T={T}, rows with -inf entries and far outliers, V=70000")
+    t, d = S.zipf_logits(3, 2, 70000, 1.1, 2.0, "f32", seed=24)
+    t[:, :, ::97] = -float("inf")
+    d[:, :, 5::89] = -float("inf")
+    t[0, 0, 123] = 60.0
+    t[1, 1, 17] = -1.0e4
+    d[2, 0, 999] = 45.0
+    verify_case(t, d, dict(temperature=T, top_p=P), seed=24)
+
+
 # ------------------------------------------------------------------ layouts and edge cases
 def test_unaligned_vocab_scalar_path():
     _announce("unaligned rows: bf16 V=50001 top-k 50, fp32 V=1001 dense")
