@@ -104,6 +104,13 @@ struct Tr<float> {
   __device__ static uint32_t canon(uint32_t key) { return key == kKeyNeg0 ? kKeyPos0 : key; }
 };
 
+// e^x in fp32 for x <= 0 (every weight here is exp((z - m) / T) with z <= m): the hardware
+// base-2 exponential of x * log2(e).  Every fp32 weight in the library goes through this one
+// function, so the normalisers and the weights they normalise agree.
+__device__ __forceinline__ float fast_exp(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
 constexpr int kRegs = kVecPerThread * 4;  // 32-bit registers per thread holding one chunk
 
 // ------------------------------------------------------------------------------------------
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
 #pragma unroll
           for (int h = 0; h < Tr<E>::kPerDword; ++h) {
             const float z = Tr<E>::elem(regs[4 * i + d], h);
-            const float e = expf((z - mx) * it);
+            const float e = fast_exp((z - mx) * it);
             sv += e;
             if constexpr (HIST) {
               // mass in 2^-40 fixed point relative to the chunk maximum, so that the bin sums
@@ -390,7 +397,7 @@ template <class E, bool VEC>
 __device__ double dense_sum(const E* row, int V, float m, float it, float thr, RedScratch& red) {
   double s = 0.0;
   row_foreach<E, VEC>(row, V, [&](int, float z, uint32_t) {
-    if (z >= thr) s += (double)expf((z - m) * it);
+    if (z >= thr) s += (double)fast_exp((z - m) * it);
   });
   return block_sum_d(s, red);
 }
@@ -425,7 +432,7 @@ __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_
       if (key < lower) return;
       if (L > 0 && (hshift >= 32 ? 0u : (key >> hshift)) != prefix) return;
       unsigned long long w = 1ull;
-      if constexpr (MASS) w = (unsigned long long)rintf(expf((z - m) * it) * 0x1p40f);
+      if constexpr (MASS) w = (unsigned long long)rintf(fast_exp((z - m) * it) * 0x1p40f);
       if (w) atomicAdd(&s_bins[(key >> shift) & (uint32_t)(nb - 1)], w);
     });
     __syncthreads();
@@ -647,7 +654,7 @@ __device__ __forceinline__ uint32_t float_key(float z) {
 
 // Weight of a candidate in 2^-40 fixed point (integer sums: exact whatever their order).
 __device__ __forceinline__ unsigned long long topp_weight(uint32_t key, float m, float it) {
-  return __float2ull_rz(expf((Tr<float>::key_to_float(key) - m) * it) * 1099511627776.0f);
+  return __float2ull_rz(fast_exp((Tr<float>::key_to_float(key) - m) * it) * 1099511627776.0f);
 }
 
 // The exact top-p threshold of a row among its boundary candidates: the largest key v such that
@@ -877,7 +884,7 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
 
 // Unnormalised weight of a logit in a row's kept set: exp((z - m) / T) in fp32.
 __device__ __forceinline__ float kept_exp(float z, const RowStat& rs, float it) {
-  return z >= rs.thr ? expf((z - rs.m) * it) : 0.0f;
+  return z >= rs.thr ? fast_exp((z - rs.m) * it) : 0.0f;
 }
 
 template <class E>
@@ -996,7 +1003,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
     }
     for (int j = lane; j < nk; j += kSeqThreads) {
       const uint2 e = kept[j];
-      const double q = (double)expf((__uint_as_float(e.y) - rt.m) * it) / rt.S;
+      const double q = (double)fast_exp((__uint_as_float(e.y) - rt.m) * it) / rt.S;
       double w = q;
       if (resid) {
         const double p = (double)kept_exp(load_logit(drow, (int)e.x), rd, it) / rd.S;
@@ -1143,7 +1150,6 @@ __device__ __forceinline__ void load_vecs(const E* __restrict__ row, int end, in
 
 // ------------------------------------------------------------------------------------------
 // k_final_partial: grid = B x chunks; mass of the final weights per chunk (residual, target).
-// Both rows' chunks are loaded as register tiles up front.
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict__ tgt,
@@ -1162,25 +1168,24 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
   const int cend = min(c0 + dm.chunk_elems, dm.V);
   const float it = sp.inv_t;
   constexpr int EPV = Tr<E>::kEpv;
-  constexpr int NV = 4;  // vectors per thread per step; many workgroups hide the load latency
+  // steps of NV vectors per thread of both rows; the next step's loads are issued before a
+  // step is summed
+  constexpr int NV = EPV == 8 ? 2 : 4;
+  constexpr int NS = kVecPerThread / NV;
+  constexpr int STEP = kThreads * NV * EPV;
   double W = 0.0, Q = 0.0;
-#pragma unroll 1
-  for (int s = 0; s < kVecPerThread / NV; ++s) {
-    const int base = c0 + s * kThreads * NV * EPV;
-    uint32_t rt[4 * NV], rd[4 * NV];
-    load_vecs<E, VEC, NV, true>(trow, cend, base, rt);
-    if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, base, rd);
+  auto sum_step = [&](const uint32_t(&xt)[4 * NV], const uint32_t(&xd)[4 * NV], int s) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       float wv = 0.0f, qv = 0.0f;
-      const int e = base + ((int)threadIdx.x + kThreads * i) * EPV;
+      const int e = c0 + s * STEP + ((int)threadIdx.x + kThreads * i) * EPV;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
 #pragma unroll
         for (int h = 0; h < Tr<E>::kPerDword; ++h) {
           float w, q;
-          draw_weights(e < cend ? Tr<E>::elem(rt[4 * i + d], h) : -INFINITY,
-                       g.resid ? Tr<E>::elem(rd[4 * i + d], h) : 0.0f, g, it, w, q);
+          draw_weights(e < cend ? Tr<E>::elem(xt[4 * i + d], h) : -INFINITY,
+                       g.resid ? Tr<E>::elem(xd[4 * i + d], h) : 0.0f, g, it, w, q);
           wv += w;
           qv += q;
         }
@@ -1188,6 +1193,19 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
       W += (double)wv;
       Q += (double)qv;
     }
+  };
+  uint32_t at[4 * NV], ad[4 * NV], bt[4 * NV], bd[4 * NV];
+  load_vecs<E, VEC, NV, true>(trow, cend, c0, at);
+  if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, c0, ad);
+#pragma unroll 1
+  for (int s = 0; s < NS; s += 2) {
+    load_vecs<E, VEC, NV, true>(trow, cend, c0 + (s + 1) * STEP, bt);
+    if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, c0 + (s + 1) * STEP, bd);
+    sum_step(at, ad, s);
+    // past the chunk's last step this loads nothing: the buffer range check covers it
+    load_vecs<E, VEC, NV, true>(trow, cend, c0 + (s + 2) * STEP, at);
+    if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, c0 + (s + 2) * STEP, ad);
+    sum_step(bt, bd, s + 1);
   }
   W = block_sum_d(W, red);
   Q = block_sum_d(Q, red);
@@ -1212,10 +1230,18 @@ __device__ double block_exclusive_d(double v, double& total, RedScratch& red) {
   return base + (x - v);
 }
 
+// Mass of chunk c: the residual's, or q's.
+__device__ __forceinline__ double chunk_mass(const double2* fp, int c, bool use_q) {
+  return use_q ? fp[c].y : fp[c].x;
+}
+
 // ------------------------------------------------------------------------------------------
-// k_final_pick: grid = B.  Chooses the chunk holding u*W (chunk totals scanned in order), then
-// the token inside it: every thread owns a contiguous run of the chunk, so one scan of the
-// threads' sums locates the run and the thread that owns it finds the index.
+// k_final_pick: grid = B.  Chooses the chunk holding u*W from the chunk totals (scanned in
+// order), then the token inside it in three steps, all in index order: the chunk is loaded as
+// a register tile (thread t, vector i covers elements c0 + (t + 256 i) * EPV ...), so vector
+// row i (all threads' vector i) precedes row i + 1; the row sums locate the vector row, a
+// workgroup scan over the row's vectors locates the vector, and its owner finds the index.
+// With a single chunk the chunk pass is skipped and the totals come from the tile itself.
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ tgt,
@@ -1226,141 +1252,188 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
   const int b = blockIdx.x;
   const SeqState st = ws.seq[b];
   if (!st.need_dense) return;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  constexpr int EPV = Tr<E>::kEpv;
+  constexpr int NR = kVecPerThread;  // vector rows of a chunk
   __shared__ RedScratch red;
-  __shared__ int s_chunk, s_last, s_pick;
+  __shared__ float s_vw[NR][kThreads], s_vq[NR][kThreads];  // per-vector sums
+  __shared__ double s_rw[NR], s_rq[NR];                       // per-row sums
+  __shared__ int s_chunk, s_last, s_t, s_tl;
   __shared__ double s_before;
   const int n = st.n;
   const int K = dm.K;
   const DrawRows g = draw_rows(dm, ws, b, n);
-  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
-  const E* drow = g.resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : trow;
-  const double2* fp = ws.fpart + (size_t)b * dm.nchunks;
-  // chunk totals: thread t owns chunks [t * per, (t + 1) * per)
-  const int per = (dm.nchunks + kThreads - 1) / kThreads;
-  const int ca = min(dm.nchunks, tid * per), cb = min(dm.nchunks, ca + per);
-  double w_loc = 0.0, q_loc = 0.0;
-  for (int c = ca; c < cb; ++c) {
-    w_loc += fp[c].x;
-    q_loc += fp[c].y;
-  }
-  double Wt, Qt;
-  double w_ex = block_exclusive_d(w_loc, Wt, red);
-  const double q_ex = block_exclusive_d(q_loc, Qt, red);
-  const bool use_q = !(Wt > 0.0) || !g.resid;
-  const double W = use_q ? Qt : Wt;
-  if (use_q) w_ex = q_ex;
-  const double target = (double)uni[(size_t)b * (K + 1) + K] * W;
-  if (tid == 0) {
-    s_chunk = INT_MAX;
-    s_last = -1;
-    s_pick = INT_MAX;
-    if (g.resid && use_q) {  // the residual had zero mass: q is used (reported)
-      SeqState s2 = st;
-      s2.fallback = 1;
-      ws.seq[b] = s2;
+  const double u = (double)uni[(size_t)b * (K + 1) + K];
+  const bool single = dm.nchunks == 1;
+  bool use_q = !g.resid;
+  double target = 0.0;
+  int c = 0;
+  if (!single) {
+    const double2* fp = ws.fpart + (size_t)b * dm.nchunks;
+    // chunk totals: thread t owns chunks [t * per, (t + 1) * per)
+    const int per = (dm.nchunks + kThreads - 1) / kThreads;
+    const int ca = min(dm.nchunks, tid * per), cb = min(dm.nchunks, ca + per);
+    double w_loc = 0.0, q_loc = 0.0;
+    for (int cc = ca; cc < cb; ++cc) {
+      w_loc += chunk_mass(fp, cc, false);
+      q_loc += chunk_mass(fp, cc, true);
     }
-  }
-  __syncthreads();
-  {
+    double Wt, Qt;
+    double w_ex = block_exclusive_d(w_loc, Wt, red);
+    const double q_ex = block_exclusive_d(q_loc, Qt, red);
+    use_q = !(Wt > 0.0) || !g.resid;
+    if (use_q) w_ex = q_ex;
+    target = u * (use_q ? Qt : Wt);
+    if (tid == 0) {
+      s_chunk = INT_MAX;
+      s_last = -1;
+    }
+    __syncthreads();
     double cum = w_ex;
     int found = INT_MAX, lastc = -1;
-    for (int c = ca; c < cb; ++c) {
-      const double v = use_q ? fp[c].y : fp[c].x;
-      if (v > 0.0) lastc = c;
-      if (found == INT_MAX && cum + v > target) found = c;
+    for (int cc = ca; cc < cb; ++cc) {
+      const double v = chunk_mass(fp, cc, use_q);
+      if (v > 0.0) lastc = cc;
+      if (found == INT_MAX && cum + v > target) found = cc;
       cum += v;
     }
     if (found != INT_MAX) atomicMin(&s_chunk, found);
     if (lastc >= 0) atomicMax(&s_last, lastc);
+    __syncthreads();
+    c = s_chunk != INT_MAX ? s_chunk : s_last;
+    if (c >= ca && c < cb) {  // the owner of chunk c: the mass before it, as summed above
+      double cb4 = w_ex;
+      for (int cc = ca; cc < c; ++cc) cb4 += chunk_mass(fp, cc, use_q);
+      s_before = cb4;
+    }
   }
-  __syncthreads();
-  const int c = s_chunk != INT_MAX ? s_chunk : s_last;
-  if (c >= ca && c < cb) {  // the owner of chunk c: the mass before it, as summed above
-    double cum = w_ex;
-    for (int cc = ca; cc < c; ++cc) cum += use_q ? fp[cc].y : fp[cc].x;
-    s_before = cum;
-  }
-  // the chunk: thread t owns elements [c0 + t * run, c0 + (t + 1) * run)
-  constexpr int EPV = Tr<E>::kEpv;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
+  const E* drow = g.resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : trow;
   const int c0 = c * dm.chunk_elems;
-  const int clen = min(dm.chunk_elems, dm.V - c0);
-  const int run = kVecPerThread * EPV;  // chunk_elems / kThreads
-  const int e0 = c0 + tid * run;
-  const int cend = c0 + clen;  // uniform: the buffer range of the loads
-  const int e1 = min(cend, e0 + run);
+  const int cend = min(c0 + dm.chunk_elems, dm.V);
   const float it = sp.inv_t;
-  constexpr int NV = 4;  // vectors per step of the run
-  double loc = 0.0;
-  int mylast = -1;
+  // per-vector sums of the chunk
+  constexpr int NV = 4;
 #pragma unroll 1
-  for (int s = 0; s < kVecPerThread / NV; ++s) {
-    const int es = e0 + s * NV * EPV;
+  for (int s = 0; s < NR / NV; ++s) {
+    const int base = c0 + s * kThreads * NV * EPV;
     uint32_t rt[4 * NV], rd[4 * NV];
-    load_vecs<E, VEC, NV, false>(trow, cend, es, rt);
-    if (g.resid) load_vecs<E, VEC, NV, false>(drow, cend, es, rd);
+    load_vecs<E, VEC, NV, true>(trow, cend, base, rt);
+    if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, base, rd);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-      float vv = 0.0f;
-      const int e = es + i * EPV;
+      const int e = base + (tid + kThreads * i) * EPV;
+      float wv = 0.0f, qv = 0.0f;
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
 #pragma unroll
         for (int h = 0; h < Tr<E>::kPerDword; ++h) {
           float w, q;
-          draw_weights(e < e1 ? Tr<E>::elem(rt[4 * i + d], h) : -INFINITY,
+          draw_weights(e < cend ? Tr<E>::elem(rt[4 * i + d], h) : -INFINITY,
                        g.resid ? Tr<E>::elem(rd[4 * i + d], h) : 0.0f, g, it, w, q);
-          const float v = use_q ? q : w;
-          vv += v;
-          if (v > 0.0f) mylast = e + d * Tr<E>::kPerDword + h;
+          wv += w;
+          qv += q;
         }
       }
-      loc += (double)vv;
+      s_vw[s * NV + i][tid] = wv;
+      s_vq[s * NV + i][tid] = qv;
     }
   }
-  double tot;
-  const double ex = block_exclusive_d(loc, tot, red);  // its barriers also publish s_before
-  double cum = s_before + ex;
-  if (cum + loc > target) {  // this thread's run holds the first index past the target
-    int hit = INT_MAX;
-#pragma unroll 1
-    for (int s = 0; s < kVecPerThread / NV && hit == INT_MAX; ++s) {
-      const int es = e0 + s * NV * EPV;
-      uint32_t rt[4 * NV], rd[4 * NV];
-      load_vecs<E, VEC, NV, false>(trow, cend, es, rt);
-      if (g.resid) load_vecs<E, VEC, NV, false>(drow, cend, es, rd);
+  __syncthreads();
+  // row sums: wave w takes rows w, w + 4, ... (fixed order inside each row)
+  for (int i = wv; i < NR; i += 4) {
+    double sw = 0.0, sq = 0.0;
 #pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int e = es + i * EPV;
-        float wv[EPV];
-        float vv = 0.0f;
+    for (int j = 0; j < kThreads / 64; ++j) {
+      sw += (double)s_vw[i][lane * (kThreads / 64) + j];
+      sq += (double)s_vq[i][lane * (kThreads / 64) + j];
+    }
+    sw = wave_reduce(sw, [](double x, double y) { return x + y; });
+    sq = wave_reduce(sq, [](double x, double y) { return x + y; });
+    if (lane == 0) {
+      s_rw[i] = sw;
+      s_rq[i] = sq;
+    }
+  }
+  __syncthreads();
+  double before = 0.0;
+  if (single) {
+    double Wt = 0.0, Qt = 0.0;
+    for (int i = 0; i < NR; ++i) {
+      Wt += s_rw[i];
+      Qt += s_rq[i];
+    }
+    use_q = !(Wt > 0.0) || !g.resid;
+    target = u * (use_q ? Qt : Wt);
+  } else {
+    before = s_before;
+  }
+  if (tid == 0 && g.resid && use_q) {  // the residual had zero mass: q is used (reported)
+    SeqState s2 = st;
+    s2.fallback = 1;
+    ws.seq[b] = s2;
+  }
+  const float(*sv)[kThreads] = use_q ? s_vq : s_vw;
+  const double* rs = use_q ? s_rq : s_rw;
+  // the vector row
+  int ri = -1, rlast = -1;
+  double cum = before, cum_last = before;
+  for (int i = 0; i < NR; ++i) {
+    if (rs[i] > 0.0) {
+      rlast = i;
+      cum_last = cum;
+    }
+    if (ri < 0 && cum + rs[i] > target) {
+      ri = i;
+      break;
+    }
+    cum += rs[i];
+  }
+  const bool clamp = ri < 0;  // rounding left u*W at or past the total: the last positive
+  if (clamp) {
+    ri = rlast < 0 ? 0 : rlast;
+    cum = cum_last;
+  }
+  // the vector inside row ri
+  const double v = (double)sv[ri][tid];
+  double rtot;
+  const double vex = block_exclusive_d(v, rtot, red);
+  if (tid == 0) {
+    s_t = INT_MAX;
+    s_tl = -1;
+  }
+  __syncthreads();
+  if (v > 0.0) {
+    atomicMax(&s_tl, tid);
+    if (!clamp && cum + vex + v > target) atomicMin(&s_t, tid);
+  }
+  __syncthreads();
+  int tt = s_t;
+  const bool last = clamp || tt == INT_MAX;  // fall back to the last positive vector
+  if (last) tt = s_tl;
+  if (tid == (tt < 0 ? 0 : tt)) {
+    int pick = -1;
+    if (tt >= 0) {
+      const int e = c0 + (tt + kThreads * ri) * EPV;
+      float zt[EPV], zd[EPV];
+      load_vec_f<E, VEC>(trow, cend, e, zt);
+      if (g.resid) load_vec_f<E, VEC>(drow, cend, e, zd);
+      double run = cum + vex;
+      int lastpos = -1;
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
-            float w, q;
-            draw_weights(e < e1 ? Tr<E>::elem(rt[4 * i + d], h) : -INFINITY,
-                         g.resid ? Tr<E>::elem(rd[4 * i + d], h) : 0.0f, g, it, w, q);
-            wv[d * Tr<E>::kPerDword + h] = use_q ? q : w;
-            vv += wv[d * Tr<E>::kPerDword + h];
-          }
-        }
-        // the vector's elements one by one only where the running sum crosses the target
-        if (hit == INT_MAX && cum + (double)vv > target) {
-#pragma unroll
-          for (int x = 0; x < EPV; ++x) {
-            cum += (double)wv[x];
-            if (hit == INT_MAX && wv[x] > 0.0f && cum > target) hit = e + x;
-          }
-        } else {
-          cum += (double)vv;
-        }
+      for (int x = 0; x < EPV; ++x) {
+        float w, q;
+        draw_weights(zt[x], g.resid ? zd[x] : 0.0f, g, it, w, q);
+        const float wx = use_q ? q : w;
+        if (wx > 0.0f) lastpos = e + x;
+        run += (double)wx;
+        if (!last && pick < 0 && wx > 0.0f && run > target) pick = e + x;
       }
+      if (pick < 0) pick = lastpos;
     }
-    if (hit != INT_MAX) atomicMin(&s_pick, hit);
+    if (pick < 0) pick = c0;  // no positive weight in the chunk (cannot happen for a valid row)
+    out_tokens[(size_t)b * (K + 1) + n] = pick;
   }
-  const int lp = block_max_i(mylast, red);
-  if (tid == 0) out_tokens[(size_t)b * (K + 1) + n] = s_pick != INT_MAX ? s_pick : lp;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1650,7 +1723,7 @@ __device__ int row_merge_lists(const Samp& sp, int r, const Workspace& ws, RowLd
   for (int w = 0; w < 4; ++w) {
     for (int j = lane; j < cnt[w]; j += 64) {
       const uint32_t kj = S.key[w][j];
-      const float ev = kj >= x ? expf((Tr<E>::key_to_float(kj) - m) * it) : 0.0f;
+      const float ev = kj >= x ? fast_exp((Tr<E>::key_to_float(kj) - m) * it) : 0.0f;
       S.e[w][j] = ev;
       part += (double)ev;
     }
@@ -1845,7 +1918,7 @@ __device__ int final_draw_compact_wave(const E* __restrict__ tgt, const E* __res
   double Wp = 0.0;
   for (int e = lane; e < nk; e += 64) {
     const uint2 v = kept[e];
-    const double q = (double)expf((__uint_as_float(v.y) - rt.m) * it) / rt.S;
+    const double q = (double)fast_exp((__uint_as_float(v.y) - rt.m) * it) / rt.S;
     double w = q;
     if (resid) {
       const float zd = Tr<E>::to_float(Tr<E>::bits_of(drow[v.x]));
@@ -1860,7 +1933,7 @@ __device__ int final_draw_compact_wave(const E* __restrict__ tgt, const E* __res
   if (!(W > 0.0)) {  // empty residual: draw from q
     double Qp = 0.0;
     for (int e = lane; e < nk; e += 64) {
-      const double q = (double)expf((__uint_as_float(kept[e].y) - rt.m) * it) / rt.S;
+      const double q = (double)fast_exp((__uint_as_float(kept[e].y) - rt.m) * it) / rt.S;
       s_w[e] = q;
       Qp += q;
     }
@@ -2095,8 +2168,9 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
   }
   hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
   if (!sp.greedy) {
-    hipLaunchKernelGGL((k_final_partial<E, VEC>), dim3((unsigned)((size_t)dm.B * dm.nchunks)),
-                       dim3(kThreads), 0, st, t, d, dm, sp, ws);
+    if (dm.nchunks > 1)
+      hipLaunchKernelGGL((k_final_partial<E, VEC>), dim3((unsigned)((size_t)dm.B * dm.nchunks)),
+                         dim3(kThreads), 0, st, t, d, dm, sp, ws);
     hipLaunchKernelGGL((k_final_pick<E, VEC>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm, sp,
                        ws, uni, out_tokens);
   }
