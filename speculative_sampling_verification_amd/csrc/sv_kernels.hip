@@ -1461,8 +1461,10 @@ __device__ __forceinline__ unsigned long long lanes_below() {
 }
 
 struct alignas(16) RowLds {
-  uint32_t key[4][kWaveListCap];  // per-wave candidate lists: canonical keys ...
-  uint32_t idx[4][kWaveListCap];  // ... and vocabulary indices
+  // per-wave candidate lists: canonical keys and vocabulary indices; entries kWaveListCap ..
+  // kWaveListCap + 63 are per-lane sinks for the stores of lanes without a candidate
+  uint32_t key[4][kWaveListCap + 64];
+  uint32_t idx[4][kWaveListCap + 64];
   float e[4][kWaveListCap];       // exp((z - m) / T) of each candidate (row merge)
   RedScratch red;
   uint32_t tmax[kThreads];        // per-thread maxima of tile 0
@@ -1480,17 +1482,21 @@ struct WaveList {
   uint32_t tau;  // filter threshold on (non-canonical) keys
 };
 
-__device__ __forceinline__ void wl_push(RowLds& S, WaveList& L, bool hit, uint32_t idx,
-                                        uint32_t key) {
-  const unsigned long long m = __ballot(hit);
-  if (hit) {
-    const int pos = L.count + __popcll(m & lanes_below());
-    if (pos < kWaveListCap) {
-      S.key[L.w][pos] = key;
-      S.idx[L.w][pos] = idx;
-    }
-  }
-  L.count += __popcll(m);
+// Appends up to two entries per lane (h0: (i0, k0), h1: (i1, k1)) in (lane, half) order, with
+// no branch: a lane without an entry stores to its sink slot.
+__device__ __forceinline__ void wl_push(RowLds& S, WaveList& L, bool h0, uint32_t i0, uint32_t k0,
+                                        bool h1, uint32_t i1, uint32_t k1) {
+  const unsigned long long m0 = __ballot(h0), m1 = __ballot(h1);
+  const unsigned long long below = lanes_below();
+  const int pos = L.count + __popcll(m0 & below) + __popcll(m1 & below);
+  const int sink = kWaveListCap + lane_id();
+  const int p0 = (h0 && pos < kWaveListCap) ? pos : sink;
+  const int p1 = (h1 && pos + (int)h0 < kWaveListCap) ? pos + (int)h0 : sink;
+  S.key[L.w][p0] = k0;
+  S.idx[L.w][p0] = i0;
+  S.key[L.w][p1] = k1;
+  S.idx[L.w][p1] = i1;
+  L.count += __popcll(m0) + __popcll(m1);
 }
 
 // Threshold on non-canonical keys equivalent to "value >= value of canonical key x".
@@ -1674,11 +1680,12 @@ __device__ __forceinline__ void filter_tile(const uint32_t (&regs)[kRegs], int c
     if constexpr (Tr<E>::kPerDword == 2) {
       const uint32_t k0 = Tr<E>::key_of_bits(w & 0xFFFFu);
       const uint32_t k1 = Tr<E>::key_of_bits(w >> 16);
-      wl_push(S, L, has && k0 >= tau, slot_index<E>(c0, i, d, 0), Tr<E>::canon(k0));
-      wl_push(S, L, has && k1 >= tau, slot_index<E>(c0, i, d, 1), Tr<E>::canon(k1));
+      wl_push(S, L, has && k0 >= tau, slot_index<E>(c0, i, d, 0), Tr<E>::canon(k0),
+              has && k1 >= tau, slot_index<E>(c0, i, d, 1), Tr<E>::canon(k1));
     } else {
       const uint32_t k0 = Tr<E>::key_of_bits(w);
-      wl_push(S, L, has && k0 >= tau, slot_index<E>(c0, i, d, 0), Tr<E>::canon(k0));
+      wl_push(S, L, has && k0 >= tau, slot_index<E>(c0, i, d, 0), Tr<E>::canon(k0), false, 0u,
+              0u);
     }
   }
 }
