@@ -35,6 +35,10 @@ __all__ = [
     "spec_verify",
     "sample_rows",
     "tree_verify",
+    "kl_divergence",
+    "mentored_solve",
+    "mentored_verify_sequence",
+    "mentored_spec_verify",
     "expected_tokens_per_call",
     "walltime_speedup",
     "ops_factor",
@@ -347,6 +351,184 @@ def sample_rows(logits, u, temperature=1.0, top_k=0, top_p=1.0):
     for r in range(R):
         prob = row_distribution(logits[r], temperature, top_k, top_p)
         out[r] = inverse_cdf(prob, float(u[r]))
+    return out
+
+
+# ---------------------------------------------------------------------------------------------
+# Mentored decoding: the optimal lossy variant (page "推测解码的一种最优有损变体", sections 导师解码
+# and 解决优化问题).  For one position with target q and draft p (the page's letters: p draft,
+# q target, the same as here), choose the accept probabilities r and the replacement law s
+# that maximise the chance of accepting the draft token, sum_i p_i r_i, subject to a bound D on
+# the divergence of the emitted law pi_i = p_i r_i + s_i (1 - sum_j p_j r_j) from q.  The page
+# states the optimum's form: r_i = min(1, q_i / (alpha p_i)) and
+# s_i = max(0, q_i / beta - p_i) / (1 - sum_j p_j r_j), alpha in ]0, 1], beta fixed by alpha,
+# the divergence decreasing in alpha, so alpha is found by bisection; and its speed-ups: the
+# draft token is accepted without solving when u < min(1, q_x / p_x) (r_x is never smaller),
+# and directly when the divergence of p itself is within D.
+#
+# Readings (the page's displays of the problem and of the algorithm are missing):
+#   * the divergence is KL(q || pi) = sum_{q_i > 0} q_i ln(q_i / pi_i): the page's list of
+#     precomputed sums (prefix sums of q_i ln(q_i / p_i) over tokens ordered by q_i / p_i)
+#     evaluates exactly this, and with every draft accepted (pi = p) it is the KL(q, p) of the
+#     page's direct-accept rule;
+#   * trivial case KL(q || p) <= D: every draft token is accepted (r = 1, no replacement);
+#   * otherwise alpha = the upper end after 50 bisection steps on [0, 1] of the condition
+#     KL(q || pi_alpha) <= D (which holds at alpha = 1, where the rule is the lossless one);
+#     D = 0 is the lossless rule, alpha = 1, without bisection;
+#   * beta solves sum_i max(0, q_i / beta - p_i) = 1 - sum_i min(p_i, q_i / alpha), so that pi
+#     sums to 1; no replacement is needed when that residual mass is 0;
+#   * the replacement token is drawn like the lossless one: inverse CDF in vocabulary index
+#     order over the weights max(0, q_i / beta - p_i), with the final uniform.
+# ---------------------------------------------------------------------------------------------
+MENTORED_BISECTION_STEPS = 50
+
+
+def kl_divergence(q, pi):
+    """KL(q || pi) = sum over q_i > 0 of q_i ln(q_i / pi_i); +inf if pi_i = 0 < q_i."""
+    q = np.asarray(q, dtype=np.float64)
+    pi = np.asarray(pi, dtype=np.float64)
+    sup = q > 0
+    if np.any(pi[sup] <= 0):
+        return np.inf
+    return float(np.sum(q[sup] * np.log(q[sup] / pi[sup])))
+
+
+def _mentored_beta(q, p, R):
+    """beta with sum_i max(0, q_i / beta - p_i) = R > 0: tokens by q_i / p_i descending; with the
+    m largest ratios in play, beta = (sum of their q) / (R + sum of their p), valid once it is
+    at least the next ratio."""
+    sup = np.nonzero(q > 0)[0]
+    with np.errstate(divide="ignore"):
+        ratio = np.where(p[sup] > 0, q[sup] / np.where(p[sup] > 0, p[sup], 1.0), np.inf)
+    order = np.argsort(-ratio, kind="stable")
+    Qm = 0.0
+    Pm = 0.0
+    beta = np.inf
+    for pos, t in enumerate(order):
+        Qm += q[sup[t]]
+        Pm += p[sup[t]]
+        beta = Qm / (R + Pm)
+        nxt = ratio[order[pos + 1]] if pos + 1 < order.size else -np.inf
+        if beta >= nxt:
+            break
+    return beta
+
+
+def _mentored_pi(q, p, alpha):
+    """(pi, beta, weights of the replacement) for r_i = min(1, q_i / (alpha p_i))."""
+    acc = np.minimum(p, q / alpha)  # p_i r_i
+    R = 1.0 - float(np.sum(acc))
+    if R <= 0.0:
+        return acc, np.inf, np.zeros_like(q)
+    beta = _mentored_beta(q, p, R)
+    w = np.maximum(0.0, q / beta - p)
+    return acc + w, beta, w
+
+
+def mentored_solve(q, p, D):
+    """Optimum for one position.  Returns a dict: trivial (every draft accepted), alpha, beta,
+    r (accept probabilities), w (replacement weights, unnormalised), kl (of the emitted law)."""
+    q = np.asarray(q, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    if kl_divergence(q, p) <= D:
+        return {"trivial": True, "alpha": 0.0, "beta": np.inf, "r": np.ones_like(q),
+                "w": np.zeros_like(q), "kl": kl_divergence(q, p)}
+    lo, hi = 0.0, 1.0
+    # D = 0 is the lossless rule itself (alpha = 1); no bisection, whose comparisons near
+    # KL = 0 would only see rounding
+    for _ in range(MENTORED_BISECTION_STEPS if D > 0 else 0):
+        mid = 0.5 * (lo + hi)
+        pi, _, _ = _mentored_pi(q, p, mid)
+        if kl_divergence(q, pi) <= D:
+            hi = mid
+        else:
+            lo = mid
+    alpha = hi
+    pi, beta, w = _mentored_pi(q, p, alpha)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(p > 0, np.minimum(1.0, q / (alpha * np.where(p > 0, p, 1.0))),
+                     np.where(q > 0, 1.0, 0.0))
+    return {"trivial": False, "alpha": alpha, "beta": beta, "r": r, "w": w,
+            "kl": kl_divergence(q, pi)}
+
+
+def mentored_verify_sequence(q_rows, p_rows, drafts, u, D):
+    """One sequence under mentored decoding: position k accepts x~_k iff u_k < r_{x~_k};
+    n = first rejection; the token at n < K is drawn from the replacement weights, the bonus at
+    n = K from q_K.  Every position is solved here so that a = r at the draft token is reported
+    for all of them (the page's speed-up, no solve when u_k < min(1, q/p), changes no
+    decision).  Returns the same dict as verify_sequence plus alpha and beta per position."""
+    q_rows = [np.asarray(r, dtype=np.float64) for r in q_rows]
+    p_rows = [np.asarray(r, dtype=np.float64) for r in p_rows]
+    K = len(drafts)
+    V = q_rows[0].size
+    q_x = np.zeros(K)
+    p_x = np.zeros(K)
+    a = np.zeros(K)
+    sols = []
+    for k in range(K):
+        x = int(drafts[k])
+        sol = mentored_solve(q_rows[k], p_rows[k], D)
+        sols.append(sol)
+        if 0 <= x < V:
+            q_x[k] = q_rows[k][x]
+            p_x[k] = p_rows[k][x]
+            a[k] = sol["r"][x] if (q_x[k] > 0 or p_x[k] > 0) else 0.0
+    n = K
+    for k in range(K):
+        if not (float(u[k]) < a[k]):
+            n = k
+            break
+    fell_back = False
+    if n < K:
+        w = sols[n]["w"]
+        if not np.sum(w) > 0:  # nothing to replace with (rounding): draw from q
+            w, fell_back = q_rows[n], True
+    else:
+        w = q_rows[K]
+    tok = inverse_cdf(w, float(u[K]))
+    margin = inverse_cdf_margin(w, float(u[K]), tok)
+    tokens = np.full(K + 1, -1, dtype=np.int64)
+    tokens[:n] = np.asarray(drafts[:n], dtype=np.int64)
+    tokens[n] = tok
+    return {"tokens": tokens, "n": n, "a": a, "q_x": q_x, "p_x": p_x, "fallback": fell_back,
+            "weights": w, "draw_margin": margin,
+            "alpha": np.array([s["alpha"] for s in sols]),
+            "beta": np.array([s["beta"] for s in sols])}
+
+
+def mentored_spec_verify(target_logits, draft_logits, drafts, uniforms, temperature=1.0,
+                         top_k=0, top_p=1.0, D=0.0):
+    """Batch mentored verification; same inputs and outputs as spec_verify (plus alpha, beta
+    [B, K])."""
+    target_logits = np.asarray(target_logits)
+    draft_logits = np.asarray(draft_logits)
+    drafts = np.asarray(drafts)
+    uniforms = np.asarray(uniforms)
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    out = {
+        "tokens": np.full((B, K + 1), -1, dtype=np.int64),
+        "n": np.zeros(B, dtype=np.int64),
+        "a": np.zeros((B, K)),
+        "q_x": np.zeros((B, K)),
+        "p_x": np.zeros((B, K)),
+        "fallback": np.zeros(B, dtype=bool),
+        "draw_margin": np.zeros(B),
+        "alpha": np.zeros((B, K)),
+        "beta": np.zeros((B, K)),
+        "topp_margin_t": np.full((B, K + 1), np.inf),
+        "topp_margin_d": np.full((B, K), np.inf),
+    }
+    for b in range(B):
+        q_rows = [row_distribution(target_logits[b, k], temperature, top_k, top_p)
+                  for k in range(K + 1)]
+        p_rows = [row_distribution(draft_logits[b, k], temperature, top_k, top_p)
+                  for k in range(K)]
+        r = mentored_verify_sequence(q_rows, p_rows, list(drafts[b]), list(uniforms[b]), D)
+        for key in ("tokens", "n", "a", "q_x", "p_x", "fallback", "draw_margin", "alpha",
+                    "beta"):
+            out[key][b] = r[key]
     return out
 
 
