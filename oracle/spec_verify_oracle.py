@@ -374,7 +374,9 @@ def sample_rows(logits, u, temperature=1.0, top_k=0, top_p=1.0):
 #   * trivial case KL(q || p) <= D: every draft token is accepted (r = 1, no replacement);
 #   * otherwise alpha = the upper end after 50 bisection steps on [0, 1] of the condition
 #     KL(q || pi_alpha) <= D (which holds at alpha = 1, where the rule is the lossless one);
-#     D = 0 is the lossless rule, alpha = 1, without bisection;
+#     D = 0 is the lossless rule, alpha = 1, without bisection and without the trivial-case
+#     test (KL(q || p) <= 0 holds only for q = p, where the lossless rule accepts every draft
+#     token anyway, so the test could only ever fire on rounding);
 #   * beta solves sum_i max(0, q_i / beta - p_i) = 1 - sum_i min(p_i, q_i / alpha), so that pi
 #     sums to 1; no replacement is needed when that residual mass is 0;
 #   * the replacement token is drawn like the lossless one: inverse CDF in vocabulary index
@@ -430,7 +432,7 @@ def mentored_solve(q, p, D):
     r (accept probabilities), w (replacement weights, unnormalised), kl (of the emitted law)."""
     q = np.asarray(q, dtype=np.float64)
     p = np.asarray(p, dtype=np.float64)
-    if kl_divergence(q, p) <= D:
+    if D > 0 and kl_divergence(q, p) <= D:
         return {"trivial": True, "alpha": 0.0, "beta": np.inf, "r": np.ones_like(q),
                 "w": np.zeros_like(q), "kl": kl_divergence(q, p)}
     lo, hi = 0.0, 1.0
