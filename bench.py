@@ -8,10 +8,12 @@ A step is one spec_verify call over the whole batch: every target row (B*(K+1)) 
 Inputs are resident in HBM before the timed region; draft tokens are drawn on the GPU from the
 draft rows (spec_sample) beforehand.
 
-Prints one JSON line.  value = logit elements per second over the timed steps.  "roofline"
-covers the dominant kernel (the row-streaming kernel), timed with HIP events recorded on the
-library's stream around that kernel in every timed step.  "cpu_baseline" times the CPU oracle
-(numpy, float64, single process) on the same inputs: whole steps repeated for about 10 s.
+Prints one JSON line.  value = logit elements per second over the timed steps, which carry no
+instrumentation.  "roofline" covers the dominant kernel (the row-streaming kernel), timed with
+HIP events recorded on the library's stream around that kernel in a second pass of as many
+steps (ms_per_step_with_phase_events is that pass's rate: each event record leaves the GPU
+idle for a few microseconds).  "cpu_baseline" times the CPU oracle (numpy, float64, single
+process) on the same inputs: whole steps repeated for about 10 s.
 --workload tree_B32_N64_V32000_bf16 times greedy token-tree verification instead.
 """
 
@@ -38,11 +40,25 @@ def _hip_runtime():
     paths = [l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l]
     hip = ctypes.CDLL(paths[0])
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
     hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                         ctypes.c_void_p]
     hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
     return hip
+
+
+# Events only time the work (they are read after a full synchronisation), so they skip the
+# system-scope fence of a recorded event: with it, each record writes back and invalidates the
+# caches and leaves the GPU idle for several microseconds between kernels.
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def _new_event(hip, fence=False):
+    e = ctypes.c_void_p()
+    flags = 0 if fence else HIP_EVENT_DISABLE_SYSTEM_FENCE
+    assert hip.hipEventCreateWithFlags(ctypes.byref(e), flags) == 0
+    return e.value
 
 
 def _source_tag():
@@ -64,9 +80,11 @@ def _traffic_from_profiles(kernel, workload):
     return float(fetch.group(1)) + float(write.group(1))
 
 
-def cpu_baseline(name, target, draft, seconds):
+def cpu_baseline(name, target, draft, seconds, mentor_kl=0.0):
     """Time the CPU oracle on the same inputs: whole steps (every sequence) repeated until
-    `seconds` have passed (at least one step)."""
+    `seconds` have passed (at least one step).  Mentored decoding, whose oracle solves every
+    position over the full vocabulary, is timed on groups of 4 sequences instead, until the
+    budget is spent."""
     import numpy as np
     import oracle.spec_verify_oracle as O
     from workloads import synthetic as S
@@ -78,6 +96,21 @@ def cpu_baseline(name, target, draft, seconds):
     u_draw = S.philox_uniforms(101, (B, K))
     drafts = np.stack([O.sample_rows(df[:, j], u_draw[:, j], T, k, P) for j in range(K)], axis=1)
     u = S.philox_uniforms(102, (B, K + 1))
+    if mentor_kl > 0:
+        seqs = 0
+        t0 = time.perf_counter()
+        while True:
+            sl = slice(seqs % B, seqs % B + 4)
+            O.mentored_spec_verify(tf[sl], df[sl], drafts[sl], u[sl], T, k, P,
+                                   np.float32(mentor_kl))
+            seqs += tf[sl].shape[0]
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                break
+        return {"value": seqs * (2 * K + 1) * V / dt, "unit": "logit elems/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"{seqs} sequences in groups of 4 ({(2 * K + 1) * V} logits each), "
+                          f"{dt:.1f} s, numpy float64, one process"}
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -139,9 +172,7 @@ def bench_tree(args, name, cfg):
     hip = _hip_runtime()
 
     def new_event():
-        e = ctypes.c_void_p()
-        assert hip.hipEventCreate(ctypes.byref(e)) == 0
-        return e.value
+        return _new_event(hip, args.fenced_events)
 
     evs = [[new_event() for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.warmup):
@@ -151,9 +182,16 @@ def bench_tree(args, name, cfg):
     t0 = time.perf_counter()
     for i in range(args.steps):
         s = sets[i % len(sets)]
-        svm.spec_verify_tree(s[0], s[1], s[2], D, out=out, events=evs[i])
+        svm.spec_verify_tree(s[0], s[1], s[2], D, out=out)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same steps again with per-phase events, for the kernel durations
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % len(sets)]
+        svm.spec_verify_tree(s[0], s[1], s[2], D, out=out, events=evs[i])
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t0
     _copy_reference(args, dev)
     kern_ms = [_elapsed(hip, e[0], e[1]) for e in evs]
     step_ms = [_elapsed(hip, e[0], e[2]) for e in evs]
@@ -186,7 +224,9 @@ def bench_tree(args, name, cfg):
                      "traffic": _traffic_from_profiles("k_chunk", name), "kernel_ms": kern_avg,
                      "algorithmic_bytes_per_launch": logit_bytes},
         "gpu_event_ms_per_step": float(np.median(step_ms)),
+        "ms_per_step_with_phase_events": wall_ev * 1e3 / args.steps,
         "mean_accepted_depth": float(out["num_accepted"].float().mean().item()),
+        "timing_events": "system fence" if args.fenced_events else "no system fence",
         "source_sha256_12": _source_tag(),
     }
     if not args.no_cpu_baseline:
@@ -216,6 +256,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU oracle timing budget: whole steps are repeated until it is spent")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fenced-events", action="store_true",
+                    help="record the per-step timing events with the default system-scope "
+                         "fence (costs idle time between kernels)")
+    ap.add_argument("--mentor-kl", type=float, default=0.0,
+                    help="KL bound D > 0: mentored decoding (top-k workloads)")
+    ap.add_argument("--no-probs", action="store_true",
+                    help="do not request per-position accept probabilities (mentored decoding "
+                         "then solves only the positions its shortcut cannot accept)")
     ap.add_argument("--copy-reference-mib", type=int, default=512,
                     help="after the timed steps, copy a tensor of this size 3 times (a plain "
                          "copy kernel of known size for calibrating rocprofv3 byte counters); "
@@ -242,7 +290,7 @@ def main():
     torch.cuda.set_device(dev)
     target, draft = S.workload_inputs(name, device=dev, seed=1)
     kw = dict(temperature=cfg["temperature"], top_k=cfg["top_k"], top_p=cfg["top_p"],
-              lenience=cfg["lenience"])
+              lenience=cfg["lenience"], mentor_kl=args.mentor_kl, want_probs=not args.no_probs)
     u_draw = torch.from_numpy(S.philox_uniforms(2, (B * K,))).to(dev)
     drafts = svm.spec_sample(draft.view(B * K, V), u_draw, temperature=cfg["temperature"],
                              top_k=cfg["top_k"], top_p=cfg["top_p"]).view(B, K)
@@ -253,9 +301,7 @@ def main():
     hip = _hip_runtime()
 
     def new_event():
-        e = ctypes.c_void_p()
-        assert hip.hipEventCreate(ctypes.byref(e)) == 0
-        return e.value
+        return _new_event(hip, args.fenced_events)
 
     evs = [[new_event() for _ in range(3)] for _ in range(args.steps)]
     for _ in range(args.warmup):
@@ -263,9 +309,16 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        svm.spec_verify(target, draft, drafts, u, out=out, events=evs[i], **kw)
+        svm.spec_verify(target, draft, drafts, u, out=out, **kw)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the same steps again with per-phase events (each record idles the GPU for a few
+    # microseconds, so they stay out of the throughput loop), for the kernel durations
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        svm.spec_verify(target, draft, drafts, u, out=out, events=evs[i], **kw)
+    torch.cuda.synchronize()
+    wall_ev = time.perf_counter() - t0
 
     def elapsed(a, b):
         return _elapsed(hip, a, b)
@@ -288,11 +341,13 @@ def main():
     dominant = "k_topk_row" if 0 < cfg["top_k"] <= 256 and cfg["temperature"] > 0 else "k_chunk"
     traffic = _traffic_from_profiles(dominant, name)
     n = out["num_accepted"].cpu().numpy()
-    a = out["accept_prob"].cpu().numpy()
+    a = out["accept_prob"].cpu().numpy() if "accept_prob" in out else None
+    mentored = args.mentor_kl > 0
     res = {
-        "metric": METRIC if name == S.METRIC_WORKLOAD else
+        "metric": METRIC if name == S.METRIC_WORKLOAD and not mentored else
                   f"verify throughput: logit elems/s + % HBM peak, B={B} K={K} V={V} "
-                  f"{cfg['dtype']}",
+                  f"{cfg['dtype']}" + (f", mentored decoding D={args.mentor_kl}"
+                                       if mentored else ""),
         "value": elems / (ms_per_step * 1e-3),
         "unit": "logit elems/s",
         "n_gpus": 1,
@@ -305,7 +360,8 @@ def main():
         "dtype": {2: "bf16", 4: "f32"}[esz],
         "data": "synthetic",
         "config": {"workload": name, "B": B, "K": K, "V": V, "temperature": cfg["temperature"],
-                   "top_k": cfg["top_k"], "top_p": cfg["top_p"], "lenience": cfg["lenience"]},
+                   "top_k": cfg["top_k"], "top_p": cfg["top_p"], "lenience": cfg["lenience"],
+                   "mentor_kl": args.mentor_kl, "accept_probs_requested": not args.no_probs},
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "kernel_ms": kern_avg,
@@ -315,13 +371,16 @@ def main():
         "step_frac_hbm_peak": logit_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "gpu_event_ms_per_step": float(np.median(step_ms)),
         "gpu_region_ms_per_step": gpu_region_ms / args.steps,
-        "mean_accept_prob": float(a.mean()) if a.size else None,
+        "ms_per_step_with_phase_events": wall_ev * 1e3 / args.steps,
+        "mean_accept_prob": float(a.mean()) if a is not None and a.size else None,
         "mean_tokens_per_call": float(n.mean() + 1.0),
         "accepted_hist": np.bincount(n, minlength=K + 1).tolist(),
+        "timing_events": "system fence" if args.fenced_events else "no system fence",
         "source_sha256_12": _source_tag(),
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seconds,
+                                           args.mentor_kl)
     print(json.dumps(res), flush=True)
 
 

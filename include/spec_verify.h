@@ -21,6 +21,14 @@
  *      that a call yields up to K+1 tokens).  The draw is the inverse CDF in vocabulary index
  *      order with u[b,K]: the smallest i whose cumulative weight exceeds u * (total weight).
  *
+ * Mentored decoding (sv_sampling.mentor_kl = D > 0) replaces steps 2 and 4 per position: over
+ * the target's kept tokens, r_i = min(1, q_i / (alpha p_i)) and replacement weights
+ * w_i = max(0, q_i / beta - p_i), where beta makes sum_i (p_i r_i + w_i) = 1 and alpha is the
+ * upper end of 50 bisection steps on [0, 1] for KL(q || p r + w) <= D; if KL(q || p) <= D
+ * every draft token with p > 0 is accepted.  a_k = r at the draft token; the token at n < K is
+ * drawn from w (from q if w has no mass).  A position whose target or draft row has more than
+ * 1024 kept tokens (ties at the top-k boundary) uses the lossless rule.
+ *
  * spec_verify_tree is the greedy exact-match rule for a token tree laid out in BFS order (the
  * REST article, section on retrieval-based speculative decoding): a node is accepted iff its
  * parent is accepted and its token equals the argmax of the parent's target row.
@@ -68,6 +76,12 @@ typedef struct {
   int32_t top_k;     /* >= 0.  0, or >= V, = off */
   float top_p;       /* in (0, 1].  1 = off */
   float lenience;    /* in (0, 1].  1 = the lossless rule; < 1 = App. F of the Leviathan blog */
+  float mentor_kl;   /* >= 0, finite.  0 = off; D > 0 = mentored decoding with KL bound D (the
+                        community blog on an optimal lossy variant of speculative decoding, its
+                        sections on mentored decoding and on solving the optimisation problem).
+                        D > 0 with K > 0 requires lenience 1 and, unless temperature is 0, a
+                        top-k of 1..256 (top-p may be combined with it); otherwise
+                        SV_ERR_INVALID_ARG.  At temperature 0 the rule equals the lossless one. */
 } sv_sampling;
 
 /* Bytes of workspace spec_verify needs for these sizes and parameters (0 on invalid input). */

@@ -23,7 +23,8 @@ SV_DTYPE_BF16 = 1
 
 class SVSampling(ctypes.Structure):
     _fields_ = [("temperature", ctypes.c_float), ("top_k", ctypes.c_int32),
-                ("top_p", ctypes.c_float), ("lenience", ctypes.c_float)]
+                ("top_p", ctypes.c_float), ("lenience", ctypes.c_float),
+                ("mentor_kl", ctypes.c_float)]
 
 
 EXPORTS = [
@@ -110,8 +111,9 @@ def _need(t, name, device, dtype=None, shape=None):
         raise ValueError(f"{name} must be contiguous")
 
 
-def sampling(temperature=1.0, top_k=0, top_p=1.0, lenience=1.0):
-    return SVSampling(float(temperature), int(top_k), float(top_p), float(lenience))
+def sampling(temperature=1.0, top_k=0, top_p=1.0, lenience=1.0, mentor_kl=0.0):
+    return SVSampling(float(temperature), int(top_k), float(top_p), float(lenience),
+                      float(mentor_kl))
 
 
 _workspaces = {}
@@ -133,13 +135,16 @@ def _stream(device, stream):
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperature=1.0, top_k=0,
-                top_p=1.0, lenience=1.0, out=None, want_probs=True, stream=None, events=None):
+                top_p=1.0, lenience=1.0, mentor_kl=0.0, out=None, want_probs=True, stream=None,
+                events=None):
     """Verify-and-resample for a batch (see include/spec_verify.h).
 
     target_logits [B, K+1, V], draft_logits [B, K or K+1, V] (bf16 or fp32, same dtype),
     draft_tokens [B, K] int32, uniforms [B, K+1] float32, all on one GPU.
     Returns a dict: tokens [B, K+1], num_accepted [B], and if want_probs accept_prob / q_draft /
     p_draft [B, K].  ``out`` may hold preallocated tensors under the same keys.
+    ``mentor_kl`` > 0 selects mentored decoding with that KL bound (needs lenience 1 and, for
+    temperature > 0, top_k in 1..256).
     ``events``: optional list of >= 2 hipEvent_t handles (ints) for per-phase timing.
     """
     dev = target_logits.device
@@ -170,7 +175,7 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
     for k in ("accept_prob", "q_draft", "p_draft"):
         if k in out:
             _need(out[k], f"out {k}", dev, torch.float32, (B, K))
-    samp = sampling(temperature, top_k, top_p, lenience)
+    samp = sampling(temperature, top_k, top_p, lenience, mentor_kl)
     need = _lib.spec_verify_workspace_size(B, K, V, dt, ctypes.byref(samp))
     if need == 0:
         raise SpecVerifyError("spec_verify_workspace_size", 1)

@@ -39,7 +39,19 @@ bool valid_params(const sv_sampling* p) {
   if (p->top_k < 0) return false;
   if (!(p->top_p > 0.0f && p->top_p <= 1.0f)) return false;
   if (!(p->lenience > 0.0f && p->lenience <= 1.0f)) return false;
+  if (!(p->mentor_kl >= 0.0f) || !std::isfinite(p->mentor_kl)) return false;
   return true;
+}
+
+Samp make_samp(const sv_sampling* p, int V);
+
+// Mentored decoding with draft tokens to verify needs the lossless comparison (lenience 1) and,
+// for sampled rows, the compact top-k lists.
+bool valid_mentor(const sv_sampling* p, int V, int K) {
+  if (p->mentor_kl == 0.0f || K == 0) return true;
+  if (p->lenience != 1.0f) return false;
+  const Samp s = make_samp(p, V);
+  return s.greedy || s.compact;
 }
 
 Samp make_samp(const sv_sampling* p, int V) {
@@ -53,6 +65,8 @@ Samp make_samp(const sv_sampling* p, int V) {
   s.compact = !s.greedy && s.top_k > 0 && s.top_k <= kCompactMaxK;
   s.generic_trunc = !s.greedy && ((s.top_k > kCompactMaxK) || (s.top_p < 1.0f && !s.compact));
   s.topp_hist = !s.greedy && s.top_k == 0 && s.top_p < 1.0f;
+  s.mentor_d = (double)p->mentor_kl;
+  s.mentor = s.compact && p->mentor_kl > 0.0f;  // greedy rows: the lossless rule is the optimum
   return s;
 }
 
@@ -95,6 +109,8 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const size_t o_hist = c.take(th ? rows * nch * kHistBins * sizeof(unsigned long long) : 0);
   const size_t o_tprow = c.take(th ? rows * sizeof(TopPRow) : 0);
   const size_t o_tcand = c.take(th ? rows * kTopPCandCap * sizeof(uint2) : 0);
+  const bool me = s.mentor && d.K > 0;
+  const size_t o_ment = c.take(me ? (size_t)d.B * d.K * sizeof(MentorSol) : 0);
   if (ws) {
     ws->parts = s.compact ? nullptr : at<ChunkPart>(base, o_parts);
     ws->rstat = at<RowStat>(base, o_rstat);
@@ -105,6 +121,7 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
     ws->hist = th ? at<unsigned long long>(base, o_hist) : nullptr;
     ws->tprow = th ? at<TopPRow>(base, o_tprow) : nullptr;
     ws->tcand = th ? at<uint2>(base, o_tcand) : nullptr;
+    ws->ment = me ? at<MentorSol>(base, o_ment) : nullptr;
   }
   return c.off;
 }
@@ -133,6 +150,7 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
   if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
   if (!valid_params(params)) return SV_ERR_INVALID_ARG;
   if (K > 0 && draft_rows != K && draft_rows != K + 1) return SV_ERR_INVALID_ARG;
+  if (V < 1 || !valid_mentor(params, V, K)) return SV_ERR_INVALID_ARG;
   Dims d{};
   if (!make_dims(B, K, V, K > 0 ? draft_rows : 0, dtype, &d)) return SV_ERR_INVALID_ARG;
   if (!target || !uniforms || !out_tokens) return SV_ERR_INVALID_ARG;
@@ -157,6 +175,7 @@ extern "C" {
 
 size_t spec_verify_workspace_size(int B, int K, int V, sv_dtype dtype, const sv_sampling* params) {
   if (!valid_dtype(dtype) || !valid_params(params)) return 0;
+  if (V < 1 || K < 0 || !valid_mentor(params, V, K)) return 0;
   Dims d{};
   if (!make_dims(B, K, V, K, dtype, &d)) return 0;
   return layout_verify(d, make_samp(params, V), nullptr, nullptr);

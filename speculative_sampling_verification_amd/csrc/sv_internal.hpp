@@ -30,6 +30,7 @@ constexpr int kSeqThreads = 64;      // one wave per sequence
 constexpr int kHistBins = 512;       // top-p mass histogram bins per chunk ...
 constexpr int kHistPerUnit = 8;      // ... on a grid of 1/8 of a unit of z / T
 constexpr int kTopPCandCap = 4096;   // boundary candidates a top-p row may hold
+constexpr int kMentorBisectionSteps = 50;  // bisection steps on alpha (mentored decoding)
 
 // Row kinds written by k_row.
 enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
@@ -63,6 +64,25 @@ struct alignas(16) TopPRow {
   int pad;
 };
 
+// How a draft position is decided under mentored decoding.
+enum MentorMode : int {
+  kMentorLossless = 0,  // a row of the pair has no kept list: the lossless rule
+  kMentorShortcut = 1,  // u < min(1, q/p): accepted without solving (r is never smaller)
+  kMentorTrivial = 2,   // KL(q || p) <= D: every draft token with p > 0 is accepted
+  kMentorSolved = 3,    // alpha and beta solved
+  kMentorDeferred = 4   // kept list longer than the first pass holds: solved by the second
+};
+
+// Per-position result of the mentored solve (k_mentor), read by the accept scan and the draw.
+struct alignas(16) MentorSol {
+  double a;           // accept probability of the draft token
+  double qx, px;      // q and p of the draft token (fp64 normalisers below)
+  double alpha, beta; // solved parameters (kMentorSolved; beta = inf: no replacement mass)
+  double st, sd;      // sum over the target / draft kept set of exp(z/T - m/T), in fp64
+  int mode;           // MentorMode
+  int pad;
+};
+
 struct alignas(16) SeqState {
   int n;           // accepted drafts
   int need_dense;  // 1 if the final draw runs in k_final_partial / k_final_pick
@@ -91,6 +111,8 @@ struct Samp {
   int generic_trunc;// truncation that needs the row-pass selection (top-k > kCompactMaxK or top-p
                     // without a compact list)
   int topp_hist;    // top-p without top-k: histogram, boundary candidates, exact selection
+  int mentor;       // mentored decoding (KL bound > 0, compact rows, K > 0)
+  double mentor_d;  // the KL bound D
 };
 
 struct Workspace {
@@ -103,6 +125,7 @@ struct Workspace {
   unsigned long long* hist;  // [rows][nchunks][kHistBins] fixed-point mass   top-p histogram only
   TopPRow* tprow;            // [rows]                                        top-p histogram only
   uint2* tcand;              // [rows][kTopPCandCap] (index, bits)            top-p histogram only
+  MentorSol* ment;           // [B][K]                                        mentored only
 };
 
 inline int chunk_elems_for(sv_dtype dt) {

@@ -922,26 +922,32 @@ __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ 
       const int x = o.drafts[(size_t)b * K + k];
       const RowStat rt = ws.rstat[target_row(dm, b, k)];
       const RowStat rd = ws.rstat[draft_row(dm, b, k)];
-      double q = 0.0, p = 0.0;
-      if (x >= 0 && x < V) {
-        if (sp.greedy) {
-          q = (x == rt.argmax) ? 1.0 : 0.0;
-          p = (x == rd.argmax) ? 1.0 : 0.0;
-        } else {
-          const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
-          const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
-          const float zt = Tr<E>::to_float(Tr<E>::bits_of(trow[x]));
-          const float zd = Tr<E>::to_float(Tr<E>::bits_of(drow[x]));
-          if (zt >= rt.thr) q = exp(((double)zt - (double)rt.m) / T) / rt.S;
-          if (zd >= rd.thr) p = exp(((double)zd - (double)rd.m) / T) / rd.S;
-        }
-      }
-      double a;
-      if (p > 0.0) {
-        a = q / ((double)sp.lenience * p);
-        a = a < 1.0 ? a : 1.0;
+      double q = 0.0, p = 0.0, a;
+      const MentorSol* ms = sp.mentor ? ws.ment + (size_t)b * K + k : nullptr;
+      if (ms && ms->mode != kMentorLossless) {  // mentored decoding: r at the draft token
+        q = ms->qx;
+        p = ms->px;
+        a = ms->a;
       } else {
-        a = q > 0.0 ? 1.0 : 0.0;
+        if (x >= 0 && x < V) {
+          if (sp.greedy) {
+            q = (x == rt.argmax) ? 1.0 : 0.0;
+            p = (x == rd.argmax) ? 1.0 : 0.0;
+          } else {
+            const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
+            const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
+            const float zt = Tr<E>::to_float(Tr<E>::bits_of(trow[x]));
+            const float zd = Tr<E>::to_float(Tr<E>::bits_of(drow[x]));
+            if (zt >= rt.thr) q = exp(((double)zt - (double)rt.m) / T) / rt.S;
+            if (zd >= rd.thr) p = exp(((double)zd - (double)rd.m) / T) / rd.S;
+          }
+        }
+        if (p > 0.0) {
+          a = q / ((double)sp.lenience * p);
+          a = a < 1.0 ? a : 1.0;
+        } else {
+          a = q > 0.0 ? 1.0 : 0.0;
+        }
       }
       rej = !((double)o.uni[(size_t)b * (K + 1) + k] < a);
       if (o.a) o.a[(size_t)b * K + k] = (float)a;
@@ -1903,6 +1909,32 @@ __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt
                             reinterpret_cast<unsigned long long*>(&S.key[0][0]), S.red);
 }
 
+// Inverse-CDF pick over weights staged in LDS by one wave (s_idx / s_w, nk entries, total W):
+// the smallest index whose cumulative weight in index order exceeds u * W; the largest index of
+// positive weight if rounding leaves none.
+__device__ int pick_staged_wave(int nk, double W, double u, const uint32_t* s_idx,
+                                const double* s_w) {
+  wave_lds_sync();
+  const double target = u * W;
+  uint32_t pick = 0xFFFFFFFFu;
+  int lastpos = -1;
+  for (int e = lane_id(); e < nk; e += 64) {
+    const uint32_t ie = s_idx[e];
+    const double we = s_w[e];
+    double pre = 0.0;
+    for (int j = 0; j < nk; ++j)
+      if (s_idx[j] <= ie) pre += s_w[j];
+    if (we > 0.0) {
+      if (pre > target && ie < pick) pick = ie;
+      if ((int)ie > lastpos) lastpos = (int)ie;
+    }
+  }
+  pick = wave_reduce(pick, [](uint32_t a, uint32_t c) { return a < c ? a : c; });
+  lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
+  wave_lds_sync();
+  return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
+}
+
 // Final draw over a compact row, one wave.  Weights (q - p)_+ (or q for the bonus row, or q
 // when the residual is empty); the token is the smallest index whose cumulative weight in
 // index order exceeds u * W.  Entries are staged in LDS (s_idx / s_w).
@@ -1946,25 +1978,424 @@ __device__ int final_draw_compact_wave(const E* __restrict__ tgt, const E* __res
     }
     W = wave_reduce(Qp, [](double a, double c) { return a + c; });
   }
+  return pick_staged_wave(nk, W, u, s_idx, s_w);
+}
+
+// ------------------------------------------------------------------------------------------
+// Mentored decoding (community blog on an optimal lossy variant of speculative decoding,
+// sections on mentored decoding and on solving the optimisation problem).  Per draft position,
+// over the target's kept tokens (q_i > 0): r_i = min(1, q_i / (alpha p_i)) and replacement
+// weights w_i = max(0, q_i / beta - p_i), beta making the emitted law pi = p r + w sum to 1,
+// alpha the smallest value on the grid of 50 halvings of [0, 1] with KL(q || pi) <= D.
+//
+// With the tokens sorted by ratio q_i / p_i (decreasing), and ia = #{ratio >= alpha}, the
+// active set of the replacement is a prefix of m tokens (all with ratio > beta >= alpha), and
+//   sum_i p_i r_i = P[ia] + (Q[n] - Q[ia]) / alpha,   beta = Q[m] / (R + P[m]),
+//   KL = Q[m] ln beta + (L[ia] - L[m]) + (Q[n] - Q[ia]) ln alpha
+// with prefix sums Q, P, L of q, p and q ln(q / p) in that order: pi_i = q_i / beta on the
+// prefix, p_i up to ia, q_i / alpha after it.  These are the precomputed sums the blog lists.
+// m is the first prefix length whose beta reaches the next ratio; that condition, once met,
+// holds for every longer prefix (beta of a longer prefix lies between the shorter one's beta
+// and the added ratio), so both ia and m are binary searches.
+//
+// The grid point is found by multisection: KL decreases in alpha, so the smallest grid point
+// with KL <= D is the one bisection reaches; each round evaluates 64 evenly spaced grid points
+// of the current interval in parallel, one per lane, and keeps the sub-interval in front of
+// the first point that satisfies the bound (9 rounds instead of 50 dependent steps).
+// ------------------------------------------------------------------------------------------
+template <int CAP>
+struct MentorLds {
+  double r[CAP];                // ratios, sorted in decreasing order (-1: no entry)
+  double q[CAP], p[CAP];        // by kept-list position
+  double qc[CAP + 1], pc[CAP + 1], lc[CAP + 1];  // prefix sums, sorted order
+  uint16_t pos[CAP];            // kept-list position of each sorted entry
+};
+
+constexpr int kMentorSmallCap = 256;  // kept tokens the first mentored pass holds in LDS
+
+// q_i or p_i of a kept logit in fp64, evaluated as exp(z/T - m/T) / S (the order the
+// probabilities are defined in: scale by the temperature, subtract the maximum, normalise).
+__device__ __forceinline__ double prob64(float z, float m, double T, double S) {
+  return exp((double)z / T - (double)m / T) / S;
+}
+
+// Does (ra, pa) precede (rb, pb) in decreasing ratio order (ties: lower kept position first)?
+__device__ __forceinline__ bool ratio_before(double ra, uint32_t pa, double rb, uint32_t pb) {
+  return ra > rb || (ra == rb && pa < pb);
+}
+
+// KL(q || pi_alpha) of one lane's alpha, from the sorted ratios and prefix sums; beta out.
+// ia and m (-1 when R <= 0, where no prefix is active) are returned for reuse: both are
+// monotone in alpha, so when they agree at the two ends of an interval they hold inside it,
+// and `hint` (ia >= 0) skips the searches.
+template <int CAP>
+__device__ double mentor_kl_at(const MentorLds<CAP>& L, int nsup, int ninf, double alpha,
+                               int hint_ia, int hint_m, int& ia_out, int& m_out,
+                               double& beta) {
+  int ia = hint_ia;
+  if (ia < 0) {  // ia = #{ratio >= alpha}
+    int lo = 0, hi = nsup;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L.r[mid] >= alpha)
+        lo = mid + 1;
+      else
+        hi = mid;
+    }
+    ia = lo;
+  }
+  ia_out = ia;
+  const double qn = L.qc[nsup];
+  const double qlo = qn - L.qc[ia];
+  const double R = 1.0 - (L.pc[ia] + qlo / alpha);
+  const double lna = log(alpha);
+  if (!(R > 0.0)) {  // no replacement mass: pi = p r
+    m_out = -1;
+    beta = INFINITY;
+    return ninf > 0 ? INFINITY : L.lc[ia] + qlo * lna;
+  }
+  // m = the first prefix length with Q[m] / (R + P[m]) >= the next ratio (the full support
+  // always qualifies)
+  int m = hint_ia >= 0 ? hint_m : -1;
+  if (m < 0) {
+    int lo = 1, hi = nsup;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (L.qc[mid] / (R + L.pc[mid]) >= L.r[mid])
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    m = lo;
+  }
+  m_out = m;
+  beta = L.qc[m] / (R + L.pc[m]);
+  const double lnb = log(beta);
+  if (m <= ia) return L.qc[m] * lnb + (L.lc[ia] - L.lc[m]) + qlo * lna;
+  // rounding put tokens with ratio < alpha into the active prefix: their pi_i is
+  // q_i / alpha + q_i / beta - p_i
+  double odd = 0.0;
+  for (int j = ia; j < m; ++j) {
+    const int e = L.pos[j];
+    const double q = L.q[e];
+    odd += q * log(q / (q / alpha + (q / beta - L.p[e])));
+  }
+  return L.qc[ia] * lnb + odd + (qn - L.qc[m]) * lna;
+}
+
+// Solve of draft position `pos` (= b * K + k) by one wave.  CAP = kMentorSmallCap: positions
+// whose target row keeps more tokens are marked kMentorDeferred and left to the CAP = kKeptCap
+// pass.
+template <class E, int CAP>
+__device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
+                                  const Dims& dm, const Samp& sp, const Workspace& ws,
+                                  const int32_t* __restrict__ drafts,
+                                  const float* __restrict__ uni, int need_all, int pos,
+                                  MentorLds<CAP>& L) {
+  const int lane = lane_id();
+  const int K = dm.K;
+  const int b = pos / K;
+  const int k = pos - b * K;
+  MentorSol* out = ws.ment + pos;
+  const int ti = target_row(dm, b, k), di = draft_row(dm, b, k);
+  const RowStat rt = ws.rstat[ti], rd = ws.rstat[di];
+  MentorSol sol;
+  sol.a = 0.0;
+  sol.qx = 0.0;
+  sol.px = 0.0;
+  sol.alpha = 1.0;
+  sol.beta = INFINITY;
+  sol.st = 0.0;
+  sol.sd = 0.0;
+  sol.mode = kMentorLossless;
+  sol.pad = 0;
+  if (rt.kind != kRowCompact || rd.kind != kRowCompact) {
+    if (lane == 0) *out = sol;
+    return;
+  }
+  const int n = rt.nkept;
+  if (n > CAP) {  // only in the small pass: the kKeptCap pass holds any kept list
+    sol.mode = kMentorDeferred;
+    if (lane == 0) *out = sol;
+    return;
+  }
+  const double T = (double)sp.temperature;
+  const double D = sp.mentor_d;
+  const uint2* kt = ws.kept + (size_t)ti * kKeptCap;
+  const uint2* kd = ws.kept + (size_t)di * kKeptCap;
+
+  // fp64 normalisers over the kept sets
+  double st = 0.0, sd = 0.0;
+  for (int e = lane; e < n; e += 64)
+    st += exp((double)__uint_as_float(kt[e].y) / T - (double)rt.m / T);
+  for (int e = lane; e < rd.nkept; e += 64)
+    sd += exp((double)__uint_as_float(kd[e].y) / T - (double)rd.m / T);
+  st = wave_reduce(st, [](double a, double c) { return a + c; });
+  sd = wave_reduce(sd, [](double a, double c) { return a + c; });
+  sol.st = st;
+  sol.sd = sd;
+
+  // the draft token and the lossless acceptance min(1, q/p), a lower bound of r at it
+  const E* trow = row_ptr(dm, tgt, drf, ti);
+  const E* drow = row_ptr(dm, tgt, drf, di);
+  const int x = drafts[(size_t)b * K + k];
+  double qx = 0.0, px = 0.0;
+  if (x >= 0 && x < dm.V) {
+    const float zt = load_logit(trow, x);
+    const float zd = load_logit(drow, x);
+    if (zt >= rt.thr) qx = prob64(zt, rt.m, T, st);
+    if (zd >= rd.thr) px = prob64(zd, rd.m, T, sd);
+  }
+  sol.qx = qx;
+  sol.px = px;
+  const double a0 = px > 0.0 ? fmin(1.0, qx / px) : (qx > 0.0 ? 1.0 : 0.0);
+  const double u = (double)uni[(size_t)b * (K + 1) + k];
+  if (!need_all && u < a0) {
+    sol.a = a0;
+    sol.mode = kMentorShortcut;
+    if (lane == 0) *out = sol;
+    return;
+  }
+
+  // entries of the target support: q, p, ratio; KL(q || p)
+  double klp = 0.0;
+  int nsup = 0;
+  double my_r = -1.0;  // ratio of this lane's entry (the only one when n <= 64)
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const int e = e0 + lane;
+    bool sup = false;
+    if (e < n) {
+      const uint2 v = kt[e];
+      const double q = prob64(__uint_as_float(v.y), rt.m, T, st);
+      const float zd = load_logit(drow, (int)v.x);
+      const double p = zd >= rd.thr ? prob64(zd, rd.m, T, sd) : 0.0;
+      sup = q > 0.0;
+      my_r = !sup ? -1.0 : (p > 0.0 ? q / p : INFINITY);
+      L.q[e] = q;
+      L.p[e] = p;
+      L.r[e] = my_r;
+      L.pos[e] = (uint16_t)e;
+      if (sup) klp += p > 0.0 ? q * log(q / p) : INFINITY;
+    }
+    nsup += __popcll(__ballot(sup));
+  }
+  klp = wave_reduce(klp, [](double a, double c) { return a + c; });
+  if (klp <= D) {
+    sol.a = (qx > 0.0 || px > 0.0) ? 1.0 : 0.0;
+    sol.alpha = 0.0;
+    sol.mode = kMentorTrivial;
+    if (lane == 0) *out = sol;
+    return;
+  }
+
+  // sort (ratio, position) into decreasing ratio order (ties: lower position first)
+  if (n <= 64) {
+    // one entry per lane: its rank from the other lanes' ratios, read lane by lane
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const double rj = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_r), j),
+                                         __builtin_amdgcn_readlane(__double2loint(my_r), j));
+      rank += ratio_before(rj, (uint32_t)j, my_r, (uint32_t)lane) ? 1 : 0;
+    }
+    wave_lds_sync();
+    if (lane < n) {
+      L.r[rank] = my_r;
+      L.pos[rank] = (uint16_t)lane;
+    }
+  } else {  // bitonic sort over a power-of-two span
+    int N = 2;
+    while (N < n) N <<= 1;
+    for (int e = n + lane; e < N; e += 64) {
+      L.r[e] = -1.0;
+      L.pos[e] = 0xFFFFu;
+    }
+    for (int size = 2; size <= N; size <<= 1)
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        wave_lds_sync();
+        for (int t = lane; t < (N >> 1); t += 64) {
+          const int i = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
+          const int l = i + stride;
+          const double ri = L.r[i], rl = L.r[l];
+          const uint32_t pi = L.pos[i], pl = L.pos[l];
+          const bool swap = (i & size) == 0 ? ratio_before(rl, pl, ri, pi)
+                                            : ratio_before(ri, pi, rl, pl);
+          if (swap) {
+            L.r[i] = rl;
+            L.r[l] = ri;
+            L.pos[i] = (uint16_t)pl;
+            L.pos[l] = (uint16_t)pi;
+          }
+        }
+      }
+  }
   wave_lds_sync();
-  const double target = u * W;
-  uint32_t pick = 0xFFFFFFFFu;
-  int lastpos = -1;
-  for (int e = lane; e < nk; e += 64) {
-    const uint32_t ie = s_idx[e];
-    const double we = s_w[e];
-    double pre = 0.0;
-    for (int j = 0; j < nk; ++j)
-      if (s_idx[j] <= ie) pre += s_w[j];
-    if (we > 0.0) {
-      if (pre > target && ie < pick) pick = ie;
-      if ((int)ie > lastpos) lastpos = (int)ie;
+
+  // prefix sums over the nsup support entries in sorted order: each lane a contiguous segment
+  const int seg = (nsup + 63) >> 6;
+  const int j0 = lane * seg, j1 = min(nsup, j0 + seg);
+  double aq = 0.0, ap = 0.0, al = 0.0;
+  for (int j = j0; j < j1; ++j) {
+    const int e = L.pos[j];
+    const double r = L.r[j];
+    aq += L.q[e];
+    ap += L.p[e];
+    if (r != INFINITY) al += L.q[e] * log(r);
+  }
+  double iq = aq, ip = ap, il = al;  // inclusive scans over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double tq = __shfl_up(iq, o), tp = __shfl_up(ip, o), tl = __shfl_up(il, o);
+    if (lane >= o) {
+      iq += tq;
+      ip += tp;
+      il += tl;
     }
   }
-  pick = wave_reduce(pick, [](uint32_t a, uint32_t c) { return a < c ? a : c; });
-  lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
+  double cq = __shfl_up(iq, 1), cp = __shfl_up(ip, 1), cl = __shfl_up(il, 1);
+  if (lane == 0) {
+    cq = 0.0;
+    cp = 0.0;
+    cl = 0.0;
+    L.qc[0] = 0.0;
+    L.pc[0] = 0.0;
+    L.lc[0] = 0.0;
+  }
+  for (int j = j0; j < j1; ++j) {
+    const int e = L.pos[j];
+    const double r = L.r[j];
+    cq += L.q[e];
+    cp += L.p[e];
+    if (r != INFINITY) cl += L.q[e] * log(r);
+    L.qc[j + 1] = cq;
+    L.pc[j + 1] = cp;
+    L.lc[j + 1] = cl;
+  }
   wave_lds_sync();
-  return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
+  int ninf = 0;
+  for (int c0 = 0; c0 < nsup; c0 += 64)
+    ninf += __popcll(__ballot(c0 + lane < nsup && L.r[c0 + lane] == INFINITY));
+
+  // multisection on the grid of 2^-kMentorBisectionSteps: (lo, hi] holds the answer, hi
+  // satisfies the bound (hi = 1 is taken to, as bisection never tests it)
+  const double grid = ldexp(1.0, -kMentorBisectionSteps);
+  double lo = 0.0, hi = 1.0;
+  int ia_lo = -1, m_lo = -1, ia_hi = -1, m_hi = -1;  // -1: not known at that end
+  while (hi - lo > grid) {
+    const double w = hi - lo;
+    const double step = fmax(w * (1.0 / 64.0), grid);
+    const double pt = lo + (double)(lane + 1) * step;
+    const bool same = ia_lo >= 0 && ia_lo == ia_hi && m_lo == m_hi;
+    bool ok = true;  // points at or beyond hi
+    int ia = -1, m = -1;
+    if (pt < hi) {
+      double bt;
+      ok = mentor_kl_at(L, nsup, ninf, pt, same ? ia_lo : -1, m_lo, ia, m, bt) <= D;
+    }
+    const unsigned long long okm = __ballot(ok);
+    const int f = __ffsll((long long)okm) - 1;  // lane 63's point is hi at the latest
+    const double nhi = lo + (double)(f + 1) * step;
+    const int ia_f = __shfl(ia, f), m_f = __shfl(m, f);
+    const int ia_p = __shfl(ia, f > 0 ? f - 1 : 0), m_p = __shfl(m, f > 0 ? f - 1 : 0);
+    if (nhi < hi) {  // lane f's point was evaluated
+      ia_hi = ia_f;
+      m_hi = m_f;
+    }
+    if (f > 0) {
+      ia_lo = ia_p;
+      m_lo = m_p;
+    }
+    lo = lo + (double)f * step;
+    hi = nhi;
+  }
+  double beta = INFINITY;
+  {
+    int ia, m;
+    (void)mentor_kl_at(L, nsup, ninf, hi, -1, -1, ia, m, beta);
+  }
+  sol.alpha = hi;
+  sol.beta = beta;
+  sol.a = px > 0.0 ? fmin(1.0, qx / (hi * px)) : (qx > 0.0 ? 1.0 : 0.0);
+  sol.mode = kMentorSolved;
+  if (lane == 0) *out = sol;
+}
+
+// First pass: one 64-thread block per draft position, kept lists up to kMentorSmallCap.
+template <class E>
+__global__ __launch_bounds__(64) void k_mentor(const E* __restrict__ tgt,
+                                               const E* __restrict__ drf, Dims dm, Samp sp,
+                                               Workspace ws, const int32_t* __restrict__ drafts,
+                                               const float* __restrict__ uni, int need_all) {
+  __shared__ MentorLds<kMentorSmallCap> L;
+  mentor_solve_wave<E, kMentorSmallCap>(tgt, drf, dm, sp, ws, drafts, uni, need_all,
+                                        (int)blockIdx.x, L);
+}
+
+// Second pass over the deferred positions (kept lists up to kKeptCap): a grid-stride loop of
+// a few blocks, since such positions are rare (ties at the top-k boundary).
+template <class E>
+__global__ __launch_bounds__(64) void k_mentor_large(const E* __restrict__ tgt,
+                                                     const E* __restrict__ drf, Dims dm, Samp sp,
+                                                     Workspace ws,
+                                                     const int32_t* __restrict__ drafts,
+                                                     const float* __restrict__ uni,
+                                                     int need_all) {
+  __shared__ MentorLds<kKeptCap> L;
+  const int npos = dm.B * dm.K;
+  const int G = (int)gridDim.x;
+  // block g owns positions g, g + G, ...; their modes are read 64 at a time, one per lane
+  for (int base = blockIdx.x; base < npos; base += 64 * G) {
+    const int mine = base + lane_id() * G;
+    unsigned long long def = __ballot(mine < npos && ws.ment[mine].mode == kMentorDeferred);
+    while (def) {
+      const int j = __ffsll((long long)def) - 1;
+      def &= def - 1;
+      mentor_solve_wave<E, kKeptCap>(tgt, drf, dm, sp, ws, drafts, uni, need_all, base + j * G,
+                                     L);
+      wave_lds_sync();  // LDS reuse by the next position
+    }
+  }
+}
+
+// Final draw of a mentored position n < K, one wave: weights max(0, q_i / beta - p_i) over the
+// target's kept tokens (q if they have no mass), fp64 with the solve's normalisers.
+template <class E>
+__device__ int mentor_draw_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
+                                const Dims& dm, const Samp& sp, const Workspace& ws, int b, int n,
+                                const MentorSol& ms, double u, uint32_t* s_idx, double* s_w) {
+  const int lane = lane_id();
+  const RowStat rt = ws.rstat[target_row(dm, b, n)];
+  const RowStat rd = ws.rstat[draft_row(dm, b, n)];
+  const int nk = rt.nkept;
+  const uint2* kept = ws.kept + (size_t)target_row(dm, b, n) * kKeptCap;
+  const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
+  const double T = (double)sp.temperature;
+  const bool solved = ms.mode == kMentorSolved;
+  double Wp = 0.0;
+  for (int e = lane; e < nk; e += 64) {
+    const uint2 v = kept[e];
+    double w = 0.0;
+    if (solved) {
+      const double q = prob64(__uint_as_float(v.y), rt.m, T, ms.st);
+      const float zd = load_logit(drow, (int)v.x);
+      const double p = zd >= rd.thr ? prob64(zd, rd.m, T, ms.sd) : 0.0;
+      w = q / ms.beta - p;
+      w = w > 0.0 ? w : 0.0;
+    }
+    s_idx[e] = v.x;
+    s_w[e] = w;
+    Wp += w;
+  }
+  double W = wave_reduce(Wp, [](double a, double c) { return a + c; });
+  if (!(W > 0.0)) {  // no replacement mass: draw from q
+    double Qp = 0.0;
+    for (int e = lane; e < nk; e += 64) {
+      const double q = prob64(__uint_as_float(kept[e].y), rt.m, T, ms.st);
+      s_w[e] = q;
+      Qp += q;
+    }
+    W = wave_reduce(Qp, [](double a, double c) { return a + c; });
+  }
+  return pick_staged_wave(nk, W, u, s_idx, s_w);
 }
 
 // Final draw over a full row pair (all threads): totals, then a scan in index order.
@@ -2053,7 +2484,12 @@ __global__ __launch_bounds__(kThreads) void k_seq_compact(const E* __restrict__ 
       s_n = n;
       s_kind = rt.kind;
     }
-    if (rt.kind == kRowCompact) {
+    const MentorSol* ms = (sp.mentor && n < K) ? ws.ment + (size_t)b * K + n : nullptr;
+    if (ms && ms->mode != kMentorLossless) {  // both rows compact: a wave draw
+      const MentorSol sol = *ms;
+      const int tok = mentor_draw_wave<E>(tgt, drf, dm, sp, ws, b, n, sol, u, s_idx, s_w);
+      if (lane_id() == 0) o.tokens[(size_t)b * (K + 1) + n] = tok;
+    } else if (rt.kind == kRowCompact) {
       const int tok = final_draw_compact_wave<E>(tgt, drf, dm, sp, ws, b, n, u, s_idx, s_w);
       if (lane_id() == 0) o.tokens[(size_t)b * (K + 1) + n] = tok;
     }
@@ -2151,6 +2587,14 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_topk_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
                        ws);
     if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
+    if (sp.mentor && dm.K > 0) {
+      const int need_all = out_a != nullptr ? 1 : 0;
+      const int npos = dm.B * dm.K;
+      hipLaunchKernelGGL((k_mentor<E>), dim3(npos), dim3(64), 0, st, t, d, dm, sp, ws, drafts,
+                         uni, need_all);
+      hipLaunchKernelGGL((k_mentor_large<E>), dim3(npos < 128 ? npos : 128), dim3(64), 0, st, t,
+                         d, dm, sp, ws, drafts, uni, need_all);
+    }
     hipLaunchKernelGGL((k_seq_compact<E, VEC>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm, sp,
                        ws, o);
     if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);

@@ -44,7 +44,9 @@ def run_gpu(target, draft, drafts, u, params, device="cuda"):
     uu = torch.from_numpy(np.ascontiguousarray(u)).to(device)
     out = svm.spec_verify(t, d, x, uu, temperature=params["temperature"],
                           top_k=params.get("top_k", 0), top_p=params.get("top_p", 1.0),
-                          lenience=params.get("lenience", 1.0))
+                          lenience=params.get("lenience", 1.0),
+                          mentor_kl=params.get("mentor_kl", 0.0),
+                          want_probs=params.get("want_probs", True))
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in out.items()}
 
@@ -55,6 +57,43 @@ def run_oracle(target, draft, drafts, u, params):
     return O.spec_verify(tf, df, drafts, u, np.float32(params["temperature"]),
                          params.get("top_k", 0), np.float32(params.get("top_p", 1.0)),
                          np.float32(params.get("lenience", 1.0)))
+
+
+def run_oracle_mentored(target, draft, drafts, u, params):
+    tf = target.float().cpu().numpy()
+    df = draft.float().cpu().numpy()
+    return O.mentored_spec_verify(tf, df, drafts, u, np.float32(params["temperature"]),
+                                  params.get("top_k", 0), np.float32(params.get("top_p", 1.0)),
+                                  np.float32(params["mentor_kl"]))
+
+
+def oracle_mentored_weights(target, draft, o, params, b):
+    """The oracle's final-draw weights for sequence b under mentored decoding."""
+    tf = target.float().cpu().numpy()
+    n = int(o["n"][b])
+    K = tf.shape[1] - 1
+    T, k, P = np.float32(params["temperature"]), params.get("top_k", 0), np.float32(
+        params.get("top_p", 1.0))
+    q = O.row_distribution(tf[b, n], T, k, P)
+    if n == K:
+        return q
+    p = O.row_distribution(draft.float().cpu().numpy()[b, n], T, k, P)
+    w = O.mentored_solve(q, p, np.float32(params["mentor_kl"]))["w"]
+    return w if np.sum(w) > 0 else q
+
+
+def verify_mentored_case(target, draft, params, seed=0, max_flip_frac=0.02, drafts=None,
+                         u=None):
+    """Parity of mentored decoding (params["mentor_kl"] > 0) against the oracle; returns
+    (flips, gpu results, oracle results)."""
+    d0, u0 = make_inputs(target, draft, params, seed)
+    drafts = d0 if drafts is None else drafts
+    u = u0 if u is None else u
+    g = run_gpu(target, draft, drafts, u, params)
+    o = run_oracle_mentored(target, draft, drafts, u, params)
+    flips = compare_with_draw_flips(
+        g, o, u, lambda b: oracle_mentored_weights(target, draft, o, params, b), max_flip_frac)
+    return flips, g, o
 
 
 def compare(g, o, u, max_flip_frac=0.02):

@@ -59,6 +59,22 @@ def test_workspace_sizes(svl):
     assert L.spec_verify_workspace_size(2, 1, 100, 1, _samp(svl, top_p=0.0)) == 0
     assert L.spec_sample_workspace_size(10, 100, 0, _samp(svl)) == \
         L.spec_verify_workspace_size(10, 0, 100, 0, _samp(svl))
+    # mentored decoding: a segment of per-position solutions; needs lenience 1 and compact
+    # top-k lists (1..256) unless greedy; ignored without draft tokens
+    ment = L.spec_verify_workspace_size(256, 7, 128256, 1,
+                                        _samp(svl, temperature=0.7, top_k=50, mentor_kl=0.1))
+    assert ment > big
+    for bad in (dict(temperature=0.7, mentor_kl=0.1), dict(temperature=0.7, top_k=300,
+                                                            mentor_kl=0.1),
+                dict(temperature=0.7, top_k=50, lenience=0.5, mentor_kl=0.1),
+                dict(temperature=0.7, top_k=50, mentor_kl=-0.1),
+                dict(temperature=0.7, top_k=50, mentor_kl=float("inf")),
+                dict(temperature=0.7, top_k=50, mentor_kl=float("nan"))):
+        assert L.spec_verify_workspace_size(256, 7, 128256, 1, _samp(svl, **bad)) == 0, bad
+    assert L.spec_verify_workspace_size(256, 7, 128256, 1,
+                                        _samp(svl, temperature=0.0, mentor_kl=0.1)) == greedy
+    assert L.spec_verify_workspace_size(256, 0, 128256, 1,
+                                        _samp(svl, temperature=0.7, mentor_kl=0.1)) > 0
     assert L.spec_verify_tree_workspace_size(32, 64, 32000, 1) > 0
     assert L.spec_verify_tree_workspace_size(32, 4096, 32000, 1) == 0
 
@@ -92,6 +108,11 @@ def test_bad_arguments_are_rejected_on_the_host(svl):
                 svl.sampling(1.0, 0, 1.01, 1.0), svl.sampling(1.0, 0, 1.0, 0.0),
                 svl.sampling(1.0, 0, 1.0, 1.5), svl.sampling(float("inf"), 0, 1.0, 1.0)):
         assert _verify(svl, p=bad) == INVALID
+    # mentored decoding needs top-k lists (1..256) and lenience 1
+    for bad in (svl.sampling(1.0, 0, 1.0, 1.0, 0.1), svl.sampling(1.0, 10, 1.0, 0.5, 0.1),
+                svl.sampling(1.0, 10, 1.0, 1.0, -0.1)):
+        assert _verify(svl, p=bad) == INVALID
+    assert _verify(svl, p=svl.sampling(1.0, 10, 1.0, 1.0, 0.1)) == WS
     assert _verify(svl) == WS  # valid arguments but no workspace
     assert _verify(svl, ws=None, wsb=1 << 40) == WS
     # rows * chunks must fit in int32
