@@ -70,7 +70,7 @@ enum MentorMode : int {
   kMentorShortcut = 1,  // u < min(1, q/p): accepted without solving (r is never smaller)
   kMentorTrivial = 2,   // KL(q || p) <= D: every draft token with p > 0 is accepted
   kMentorSolved = 3,    // alpha and beta solved
-  kMentorDeferred = 4   // kept list longer than the first pass holds: solved by the second
+  kMentorDeferred = 4   // kept list longer than k_mentor holds: solved in k_seq_compact
 };
 
 // Per-position result of the mentored solve (k_mentor), read by the accept scan and the draw.

@@ -2024,6 +2024,21 @@ __device__ __forceinline__ bool ratio_before(double ra, uint32_t pa, double rb, 
   return ra > rb || (ra == rb && pa < pb);
 }
 
+// m = the first prefix length with Q[m] / (R + P[m]) >= the next ratio (the full support
+// always qualifies); R > 0.
+template <int CAP>
+__device__ int mentor_m_search(const MentorLds<CAP>& L, int nsup, double R) {
+  int lo = 1, hi = nsup;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (L.qc[mid] / (R + L.pc[mid]) >= L.r[mid])
+      hi = mid;
+    else
+      lo = mid + 1;
+  }
+  return lo;
+}
+
 // KL(q || pi_alpha) of one lane's alpha, from the sorted ratios and prefix sums; beta out.
 // ia and m (-1 when R <= 0, where no prefix is active) are returned for reuse: both are
 // monotone in alpha, so when they agree at the two ends of an interval they hold inside it,
@@ -2054,20 +2069,8 @@ __device__ double mentor_kl_at(const MentorLds<CAP>& L, int nsup, int ninf, doub
     beta = INFINITY;
     return ninf > 0 ? INFINITY : L.lc[ia] + qlo * lna;
   }
-  // m = the first prefix length with Q[m] / (R + P[m]) >= the next ratio (the full support
-  // always qualifies)
   int m = hint_ia >= 0 ? hint_m : -1;
-  if (m < 0) {
-    int lo = 1, hi = nsup;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (L.qc[mid] / (R + L.pc[mid]) >= L.r[mid])
-        hi = mid;
-      else
-        lo = mid + 1;
-    }
-    m = lo;
-  }
+  if (m < 0) m = mentor_m_search(L, nsup, R);
   m_out = m;
   beta = L.qc[m] / (R + L.pc[m]);
   const double lnb = log(beta);
@@ -2084,8 +2087,8 @@ __device__ double mentor_kl_at(const MentorLds<CAP>& L, int nsup, int ninf, doub
 }
 
 // Solve of draft position `pos` (= b * K + k) by one wave.  CAP = kMentorSmallCap: positions
-// whose target row keeps more tokens are marked kMentorDeferred and left to the CAP = kKeptCap
-// pass.
+// whose target row keeps more tokens are marked kMentorDeferred and solved with CAP = kKeptCap
+// by the sequence's block of k_seq_compact.
 template <class E, int CAP>
 __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
                                   const Dims& dm, const Samp& sp, const Workspace& ws,
@@ -2124,6 +2127,15 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   const uint2* kt = ws.kept + (size_t)ti * kKeptCap;
   const uint2* kd = ws.kept + (size_t)di * kKeptCap;
 
+  // the draft token's logits, loaded first so that their latency overlaps the sums below
+  const E* trow = row_ptr(dm, tgt, drf, ti);
+  const E* drow = row_ptr(dm, tgt, drf, di);
+  const int x = drafts[(size_t)b * K + k];
+  const double u = (double)uni[(size_t)b * (K + 1) + k];
+  const bool x_in = x >= 0 && x < dm.V;
+  const float zt_x = x_in ? load_logit(trow, x) : -INFINITY;
+  const float zd_x = x_in ? load_logit(drow, x) : -INFINITY;
+
   // fp64 normalisers over the kept sets
   double st = 0.0, sd = 0.0;
   for (int e = lane; e < n; e += 64)
@@ -2135,21 +2147,15 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   sol.st = st;
   sol.sd = sd;
 
-  // the draft token and the lossless acceptance min(1, q/p), a lower bound of r at it
-  const E* trow = row_ptr(dm, tgt, drf, ti);
-  const E* drow = row_ptr(dm, tgt, drf, di);
-  const int x = drafts[(size_t)b * K + k];
+  // q and p of the draft token and the lossless acceptance min(1, q/p), a lower bound of r
   double qx = 0.0, px = 0.0;
-  if (x >= 0 && x < dm.V) {
-    const float zt = load_logit(trow, x);
-    const float zd = load_logit(drow, x);
-    if (zt >= rt.thr) qx = prob64(zt, rt.m, T, st);
-    if (zd >= rd.thr) px = prob64(zd, rd.m, T, sd);
+  if (x_in) {
+    if (zt_x >= rt.thr) qx = prob64(zt_x, rt.m, T, st);
+    if (zd_x >= rd.thr) px = prob64(zd_x, rd.m, T, sd);
   }
   sol.qx = qx;
   sol.px = px;
   const double a0 = px > 0.0 ? fmin(1.0, qx / px) : (qx > 0.0 ? 1.0 : 0.0);
-  const double u = (double)uni[(size_t)b * (K + 1) + k];
   if (!need_all && u < a0) {
     sol.a = a0;
     sol.mode = kMentorShortcut;
@@ -2279,7 +2285,14 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   // satisfies the bound (hi = 1 is taken to, as bisection never tests it)
   const double grid = ldexp(1.0, -kMentorBisectionSteps);
   double lo = 0.0, hi = 1.0;
-  int ia_lo = -1, m_lo = -1, ia_hi = -1, m_hi = -1;  // -1: not known at that end
+  // ia and m at the two ends (-1: not known).  Near alpha = 0 every ratio is >= alpha, no q
+  // mass is scaled (R = 1 - P[nsup]), so ia and m take their limits there.
+  int ia_lo = nsup, m_lo = -1, ia_hi = -1, m_hi = -1;
+  {
+    const double R0 = 1.0 - L.pc[nsup];
+    if (R0 > 0.0) m_lo = mentor_m_search(L, nsup, R0);
+  }
+  double beta_hi = -1.0;  // beta at hi once a lane has evaluated it
   while (hi - lo > grid) {
     const double w = hi - lo;
     const double step = fmax(w * (1.0 / 64.0), grid);
@@ -2287,18 +2300,19 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
     const bool same = ia_lo >= 0 && ia_lo == ia_hi && m_lo == m_hi;
     bool ok = true;  // points at or beyond hi
     int ia = -1, m = -1;
-    if (pt < hi) {
-      double bt;
-      ok = mentor_kl_at(L, nsup, ninf, pt, same ? ia_lo : -1, m_lo, ia, m, bt) <= D;
-    }
+    double bt = -1.0;
+    if (pt < hi) ok = mentor_kl_at(L, nsup, ninf, pt, same ? ia_lo : -1, m_lo, ia, m, bt) <= D;
     const unsigned long long okm = __ballot(ok);
     const int f = __ffsll((long long)okm) - 1;  // lane 63's point is hi at the latest
     const double nhi = lo + (double)(f + 1) * step;
-    const int ia_f = __shfl(ia, f), m_f = __shfl(m, f);
-    const int ia_p = __shfl(ia, f > 0 ? f - 1 : 0), m_p = __shfl(m, f > 0 ? f - 1 : 0);
+    const int fp = f > 0 ? f - 1 : 0;
+    const int ia_f = __builtin_amdgcn_readlane(ia, f), m_f = __builtin_amdgcn_readlane(m, f);
+    const int ia_p = __builtin_amdgcn_readlane(ia, fp), m_p = __builtin_amdgcn_readlane(m, fp);
     if (nhi < hi) {  // lane f's point was evaluated
       ia_hi = ia_f;
       m_hi = m_f;
+      beta_hi = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(bt), f),
+                                 __builtin_amdgcn_readlane(__double2loint(bt), f));
     }
     if (f > 0) {
       ia_lo = ia_p;
@@ -2307,8 +2321,8 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
     lo = lo + (double)f * step;
     hi = nhi;
   }
-  double beta = INFINITY;
-  {
+  double beta = beta_hi;
+  if (beta < 0.0) {  // hi = 1, never evaluated
     int ia, m;
     (void)mentor_kl_at(L, nsup, ninf, hi, -1, -1, ia, m, beta);
   }
@@ -2328,32 +2342,6 @@ __global__ __launch_bounds__(64) void k_mentor(const E* __restrict__ tgt,
   __shared__ MentorLds<kMentorSmallCap> L;
   mentor_solve_wave<E, kMentorSmallCap>(tgt, drf, dm, sp, ws, drafts, uni, need_all,
                                         (int)blockIdx.x, L);
-}
-
-// Second pass over the deferred positions (kept lists up to kKeptCap): a grid-stride loop of
-// a few blocks, since such positions are rare (ties at the top-k boundary).
-template <class E>
-__global__ __launch_bounds__(64) void k_mentor_large(const E* __restrict__ tgt,
-                                                     const E* __restrict__ drf, Dims dm, Samp sp,
-                                                     Workspace ws,
-                                                     const int32_t* __restrict__ drafts,
-                                                     const float* __restrict__ uni,
-                                                     int need_all) {
-  __shared__ MentorLds<kKeptCap> L;
-  const int npos = dm.B * dm.K;
-  const int G = (int)gridDim.x;
-  // block g owns positions g, g + G, ...; their modes are read 64 at a time, one per lane
-  for (int base = blockIdx.x; base < npos; base += 64 * G) {
-    const int mine = base + lane_id() * G;
-    unsigned long long def = __ballot(mine < npos && ws.ment[mine].mode == kMentorDeferred);
-    while (def) {
-      const int j = __ffsll((long long)def) - 1;
-      def &= def - 1;
-      mentor_solve_wave<E, kKeptCap>(tgt, drf, dm, sp, ws, drafts, uni, need_all, base + j * G,
-                                     L);
-      wave_lds_sync();  // LDS reuse by the next position
-    }
-  }
 }
 
 // Final draw of a mentored position n < K, one wave: weights max(0, q_i / beta - p_i) over the
@@ -2466,17 +2454,47 @@ __device__ int final_draw_dense_block(const E* __restrict__ trow, const E* __res
   return pick != INT_MAX ? pick : lastpos;
 }
 
-template <class E, bool VEC>
+// LDS of k_seq_compact: the final draw's staging, or (mentored decoding) the solve of the
+// positions whose kept lists were too long for k_mentor.
+template <bool MENTOR>
+struct SeqCompactLds {
+  union {
+    struct {
+      double w[kKeptCap];
+      uint32_t idx[kKeptCap];
+    } draw;
+    MentorLds<MENTOR ? kKeptCap : 1> ment;
+  };
+};
+
+template <class E, bool VEC, bool MENTOR>
 __global__ __launch_bounds__(kThreads) void k_seq_compact(const E* __restrict__ tgt,
                                                           const E* __restrict__ drf, Dims dm,
                                                           Samp sp, Workspace ws, Outs o) {
   const int b = blockIdx.x;
   const int K = dm.K;
-  __shared__ double s_w[kKeptCap];
-  __shared__ uint32_t s_idx[kKeptCap];
+  __shared__ SeqCompactLds<MENTOR> S;
+  double* s_w = S.draw.w;
+  uint32_t* s_idx = S.draw.idx;
   __shared__ int s_n, s_kind;
   __shared__ RedScratch red;
   const double u = (double)o.uni[(size_t)b * (K + 1) + K];
+  if constexpr (MENTOR) {
+    if (wave_id() == 0) {  // deferred mentored solves of this sequence, one at a time
+      for (int k0 = 0; k0 < K; k0 += 64) {
+        const int k = k0 + lane_id();
+        unsigned long long def =
+            __ballot(k < K && ws.ment[(size_t)b * K + k].mode == kMentorDeferred);
+        while (def) {
+          const int j = __ffsll((long long)def) - 1;
+          def &= def - 1;
+          mentor_solve_wave<E, kKeptCap>(tgt, drf, dm, sp, ws, o.drafts, o.uni,
+                                         o.a != nullptr ? 1 : 0, b * K + k0 + j, S.ment);
+          wave_lds_sync();  // the solution's store and the LDS reuse below
+        }
+      }
+    }
+  }
   if (wave_id() == 0) {
     const int n = seq_accept_wave<E>(tgt, drf, dm, sp, ws, o, b);
     const RowStat rt = ws.rstat[target_row(dm, b, n)];
@@ -2589,14 +2607,14 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
     if (sp.mentor && dm.K > 0) {
       const int need_all = out_a != nullptr ? 1 : 0;
-      const int npos = dm.B * dm.K;
-      hipLaunchKernelGGL((k_mentor<E>), dim3(npos), dim3(64), 0, st, t, d, dm, sp, ws, drafts,
-                         uni, need_all);
-      hipLaunchKernelGGL((k_mentor_large<E>), dim3(npos < 128 ? npos : 128), dim3(64), 0, st, t,
-                         d, dm, sp, ws, drafts, uni, need_all);
+      hipLaunchKernelGGL((k_mentor<E>), dim3(dm.B * dm.K), dim3(64), 0, st, t, d, dm, sp, ws,
+                         drafts, uni, need_all);
+      hipLaunchKernelGGL((k_seq_compact<E, VEC, true>), dim3(dm.B), dim3(kThreads), 0, st, t, d,
+                         dm, sp, ws, o);
+    } else {
+      hipLaunchKernelGGL((k_seq_compact<E, VEC, false>), dim3(dm.B), dim3(kThreads), 0, st, t, d,
+                         dm, sp, ws, o);
     }
-    hipLaunchKernelGGL((k_seq_compact<E, VEC>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm, sp,
-                       ws, o);
     if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);
     return hipGetLastError();
   }

@@ -124,6 +124,18 @@ def test_mentored_out_of_range_draft_tokens():
     assert g["accept_prob"][0, 0] == 0.0
 
 
+def test_mentored_long_kept_lists():
+    _announce("mentored: kept lists of 246-298 tokens (ties at top-k 230) take the second "
+              "solve, fp32 B=6 K=3 V=20000")
+    t, d = S.zipf_logits(6, 3, 20000, 1.1, 1.0, "f32", seed=53)
+    t, d = (t * 2).round() / 2, (d * 2).round() / 2
+    params = dict(temperature=1.0, top_k=230, mentor_kl=0.05)
+    flips, g, o = verify_mentored_case(t, d, params, seed=53)
+    drafts, u = make_inputs(t, d, params, 53)
+    short = run_gpu(t, d, drafts, u, dict(params, want_probs=False))
+    np.testing.assert_array_equal(g["tokens"], short["tokens"])
+
+
 def test_mentored_tie_overflow_rows_use_lossless_rule():
     _announce("mentored: rows whose top-k ties overflow the kept lists use the lossless rule")
     g = torch.Generator().manual_seed(50)
