@@ -15,7 +15,9 @@ restated here in the q=target / p=draft convention.
 Where the pages leave a step open, the reading used is stated next to the step.
 
 Pinning status: every public function here is pinned by tests under ``tests/`` that compare it
-with closed forms, brute force, library routines or values printed on the pages.
+with closed forms, brute force, library routines or values printed on the pages (the REST tree
+builder against a worked example built from the prefixes the REST article names, and brute
+force over random candidate sets).
 ``expected_tokens_per_call`` and ``walltime_speedup`` / ``ops_factor`` are pinned to the values
 printed on the Leviathan page (App. E figures); no function is "parity unpinned".
 """
@@ -35,6 +37,8 @@ __all__ = [
     "spec_verify",
     "sample_rows",
     "tree_verify",
+    "rest_trie",
+    "rest_build_tree",
     "kl_divergence",
     "mentored_solve",
     "mentored_verify_sequence",
@@ -581,6 +585,84 @@ def tree_verify(target_logits, parent, node_tokens, max_depth):
         n_acc[b] = len(path)
         last[b] = best
     return {"tokens": tokens, "n": n_acc, "last_node": last}
+
+
+# ---------------------------------------------------------------------------------------------
+# REST draft-tree construction (REST article, section "REST: 基于检索的投机解码"): the
+# continuations retrieved for the context are the candidate sequences; every prefix of a
+# candidate may follow the context, so the candidates are put in a trie (prefix tree) whose
+# node weights are the number of candidates carrying that node's prefix; the draft is the
+# subtree of the highest-weight nodes, and its breadth-first traversal is the pseudo-sequence
+# fed to the target with a tree-attention mask that restores each token's own ancestry.
+#
+# Readings (the page gives no algorithm text and its figure is missing):
+#   * candidates [M, L] of token ids; a candidate ends at its first negative entry; duplicate
+#     candidates count once each;
+#   * node 0 is the root (the context's last token, carried by the caller; written as -1);
+#     every other node is a distinct non-empty prefix, its weight the number of candidates
+#     that start with it, its "first candidate" the lowest candidate index that does;
+#   * the subtree keeps the N - 1 non-root nodes that come first in the order (weight
+#     descending, depth ascending, first candidate ascending) -- a parent always precedes its
+#     children in that order, so the kept set is a subtree;
+#   * breadth-first order: the root, then level by level, children of earlier nodes first and
+#     siblings by (weight descending, first candidate ascending);
+#   * outputs in that order: parent index (-1 for the root), token, depth, weight, and the
+#     mask M[i, j] = 1 iff node j is node i or one of its ancestors; unused slots (fewer than
+#     N nodes) hold -1 and zero mask rows.
+# ---------------------------------------------------------------------------------------------
+def rest_trie(candidates):
+    """Trie of the candidate sequences: dict prefix (tuple of tokens) -> (weight, first
+    candidate index), for every non-empty prefix of every candidate."""
+    nodes = {}
+    for c, cand in enumerate(np.asarray(candidates, dtype=np.int64)):
+        prefix = ()
+        for tok in cand:
+            if tok < 0:
+                break
+            prefix = prefix + (int(tok),)
+            w, first = nodes.get(prefix, (0, c))
+            nodes[prefix] = (w + 1, first)
+    return nodes
+
+
+def rest_build_tree(candidates, N):
+    """Draft tree of at most N nodes (root included) from candidates [M, L].  Returns a dict
+    with parent, tokens, depth, weight [N] (int64), mask [N, N] (uint8) and n_nodes."""
+    nodes = rest_trie(candidates)
+    order = sorted(nodes, key=lambda pre: (-nodes[pre][0], len(pre), nodes[pre][1]))
+    kept = set(order[: max(N - 1, 0)])
+    # breadth-first traversal of the kept subtree
+    children = {}
+    for pre in kept:
+        children.setdefault(pre[:-1], []).append(pre)
+    for kids in children.values():
+        kids.sort(key=lambda pre: (-nodes[pre][0], nodes[pre][1]))
+    bfs = [()]
+    head = 0
+    while head < len(bfs):
+        bfs.extend(children.get(bfs[head], []))
+        head += 1
+    index = {pre: i for i, pre in enumerate(bfs)}
+    parent = np.full(N, -1, dtype=np.int64)
+    tokens = np.full(N, -1, dtype=np.int64)
+    depth = np.full(N, -1, dtype=np.int64)
+    weight = np.full(N, -1, dtype=np.int64)
+    mask = np.zeros((N, N), dtype=np.uint8)
+    n_nodes = min(len(bfs), N)
+    for i, pre in enumerate(bfs[:n_nodes]):
+        depth[i] = len(pre)
+        if i == 0:
+            weight[i] = int(sum(1 for cand in np.asarray(candidates) if len(cand) and cand[0] >= 0))
+        else:
+            parent[i] = index[pre[:-1]]
+            tokens[i] = pre[-1]
+            weight[i] = nodes[pre][0]
+        j = i
+        while j >= 0:
+            mask[i, j] = 1
+            j = int(parent[j])
+    return {"parent": parent, "tokens": tokens, "depth": depth, "weight": weight,
+            "mask": mask, "n_nodes": n_nodes}
 
 
 # ---------------------------------------------------------------------------------------------
