@@ -14,7 +14,8 @@ HIP events recorded on the library's stream around that kernel in a second pass 
 steps (ms_per_step_with_phase_events is that pass's rate: each event record leaves the GPU
 idle for a few microseconds).  "cpu_baseline" times the CPU oracle (numpy, float64, single
 process) on the same inputs: whole steps repeated for about 10 s.
---workload tree_B32_N64_V32000_bf16 times greedy token-tree verification instead.
+--workload tree_B32_N64_V32000_bf16 times greedy token-tree verification instead, and
+--workload rest_B32_M64_L8_N64 the REST draft-tree construction.
 """
 
 import argparse
@@ -235,6 +236,87 @@ def bench_tree(args, name, cfg):
     print(json.dumps(res), flush=True)
 
 
+def bench_rest(args, name, cfg):
+    """REST draft-tree construction: a step is one spec_build_tree call over the batch (one
+    workgroup per sequence; latency-bound: the data are a few hundred KB)."""
+    import numpy as np
+    import torch
+    import speculative_sampling_verification_amd as svm
+    from workloads import synthetic as S
+
+    B, M, L, N = cfg["B"], cfg["M"], cfg["L"], cfg["N"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cands = S.workload_inputs(name, device=dev, seed=1)
+    out = svm.spec_build_tree(cands, N)
+    torch.cuda.synchronize()
+    hip = _hip_runtime()
+    hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    evs = [[_new_event(hip, args.fenced_events) for _ in range(2)] for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        svm.spec_build_tree(cands, N, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        svm.spec_build_tree(cands, N, out=out)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for i in range(args.steps):
+        hip.hipEventRecord(ctypes.c_void_p(evs[i][0]), stream)
+        svm.spec_build_tree(cands, N, out=out)
+        hip.hipEventRecord(ctypes.c_void_p(evs[i][1]), stream)
+    torch.cuda.synchronize()
+    kern_ms = [_elapsed(hip, e[0], e[1]) for e in evs]
+    for row in evs:
+        for e in row:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    ms_per_step = wall * 1e3 / args.steps
+    kern_avg = float(np.mean(kern_ms))
+    nbytes = B * M * L * 4 + B * N * 4 * 4 + B * 4 + B * N * N
+    achieved = nbytes / (kern_avg * 1e-3) / 1e9
+    res = {
+        "metric": f"REST draft-tree build: trees/s, B={B} candidates M={M} of L={L} tokens, "
+                  f"N={N} nodes",
+        "value": B / (ms_per_step * 1e-3),
+        "unit": "trees/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int32",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "M": M, "L": L, "N": N},
+        "roofline": {"bound": "hbm", "kernel": "k_rest_tree", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "kernel_ms": kern_avg,
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "note": "latency-bound: one workgroup per sequence, B workgroups"},
+        "mean_nodes": float(out["num_nodes"].float().mean().item()),
+        "timing_events": "system fence" if args.fenced_events else "no system fence",
+        "source_sha256_12": _source_tag(),
+    }
+    if not args.no_cpu_baseline:
+        import oracle.spec_verify_oracle as O
+        c = cands.cpu().numpy()
+        done = 0
+        t0 = time.perf_counter()
+        while True:
+            O.rest_build_tree(c[done % B], N)
+            done += 1
+            dt = time.perf_counter() - t0
+            if dt >= args.cpu_seconds:
+                break
+        res["cpu_baseline"] = {"value": done / dt, "unit": "trees/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"{done} trees of the same batch, {dt:.1f} s, one "
+                                         "process"}
+    print(json.dumps(res), flush=True)
+
+
 def _copy_reference(args, dev):
     """A plain copy kernel of known size, for calibrating rocprofv3 byte counters."""
     import torch
@@ -284,6 +366,9 @@ def main():
     cfg = S.WORKLOADS[name]
     if cfg["gen"] == "tree":
         bench_tree(args, name, cfg)
+        return
+    if cfg["gen"] == "rest":
+        bench_rest(args, name, cfg)
         return
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     dev = torch.device("cuda:0")

@@ -171,6 +171,33 @@ int spec_verify_tree_profiled(const void* target_logits, sv_dtype dtype, int B, 
                               int32_t* out_last_node, void* workspace, size_t workspace_bytes,
                               hipStream_t stream, hipEvent_t* events, int n_events);
 
+/*
+ * Draft tree of a REST step (REST article, section on retrieval-based speculative decoding):
+ * the candidate continuations retrieved for each sequence are put in a trie whose node weight
+ * is the number of candidates starting with that node's prefix; the N-1 nodes first in the
+ * order (weight descending, depth ascending, lowest candidate index carrying the prefix
+ * ascending) form a subtree (a parent always precedes its children in that order), which is
+ * laid out breadth-first -- children of earlier nodes first, siblings in the same order -- as
+ * the pseudo-sequence that spec_verify_tree takes.
+ *
+ *   candidates [B, M, L] int32, device: token ids; a candidate ends at its first negative
+ *               entry; duplicates count once each.  1 <= M <= 128, 1 <= L <= 32.
+ *   N          nodes per tree, root included, 1 <= N <= 256.
+ *   out_parent [B, N] int32: parent's index (-1 for node 0, the root = the context's last
+ *               token, carried by the caller; -1 in unused slots)
+ *   out_tokens [B, N] int32: token of each node (-1 for the root and unused slots)
+ *   out_num_nodes [B] int32: nodes used, 1 + min(N - 1, distinct non-empty prefixes)
+ *   out_depth  [B, N] int32 or NULL: prefix length (0 for the root, -1 unused)
+ *   out_weight [B, N] int32 or NULL: candidates carrying the prefix (root: non-empty
+ *               candidates; -1 unused)
+ *   out_mask   [B, N, N] uint8 or NULL: tree attention, 1 iff node j is node i or one of its
+ *               ancestors (0 in unused rows and columns)
+ * No workspace; deterministic.  Argument errors return SV_ERR_INVALID_ARG before any launch.
+ */
+int spec_build_tree(const int32_t* candidates, int B, int M, int L, int N, int32_t* out_parent,
+                    int32_t* out_tokens, int32_t* out_num_nodes, int32_t* out_depth,
+                    int32_t* out_weight, uint8_t* out_mask, hipStream_t stream);
+
 /* Static string for a status code. */
 const char* spec_verify_status_string(int status);
 

@@ -31,7 +31,7 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "spec_verify_profiled",
     "spec_sample_workspace_size", "spec_sample",
     "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_tree_profiled",
-    "spec_verify_status_string",
+    "spec_build_tree", "spec_verify_status_string",
 ]
 
 
@@ -59,6 +59,8 @@ def load(path=LIB_PATH):
     lib.spec_verify_tree.restype = i32
     lib.spec_verify_tree_profiled.argtypes = lib.spec_verify_tree.argtypes + [vp, i32]
     lib.spec_verify_tree_profiled.restype = i32
+    lib.spec_build_tree.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.spec_build_tree.restype = i32
     lib.spec_verify_status_string.argtypes = [i32]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     return lib
@@ -246,4 +248,29 @@ def spec_verify_tree(target_logits, parent, node_tokens, max_depth, *, out=None,
         arr = (ctypes.c_void_p * len(events))(*events)
         _check("spec_verify_tree_profiled",
                _lib.spec_verify_tree_profiled(*args, arr, len(events)))
+    return out
+
+
+def spec_build_tree(candidates, N, *, want_mask=True, out=None, stream=None):
+    """REST draft tree from candidates [B, M, L] int32 (a candidate ends at its first negative
+    entry): returns parent, tokens, depth, weight [B, N], num_nodes [B] and, if want_mask,
+    mask [B, N, N] uint8 (see include/spec_verify.h)."""
+    dev = candidates.device
+    _need(candidates, "candidates", dev, torch.int32)
+    if candidates.dim() != 3:
+        raise ValueError("candidates must be [B, M, L]")
+    B, M, L = candidates.shape
+    out = dict(out or {})
+    for k in ("parent", "tokens", "depth", "weight"):
+        out.setdefault(k, torch.empty((B, N), dtype=torch.int32, device=dev))
+        _need(out[k], f"out {k}", dev, torch.int32, (B, N))
+    out.setdefault("num_nodes", torch.empty((B,), dtype=torch.int32, device=dev))
+    _need(out["num_nodes"], "out num_nodes", dev, torch.int32, (B,))
+    if want_mask:
+        out.setdefault("mask", torch.empty((B, N, N), dtype=torch.uint8, device=dev))
+        _need(out["mask"], "out mask", dev, torch.uint8, (B, N, N))
+    _check("spec_build_tree", _lib.spec_build_tree(
+        _ptr(candidates), B, M, L, int(N), _ptr(out["parent"]), _ptr(out["tokens"]),
+        _ptr(out["num_nodes"]), _ptr(out["depth"]), _ptr(out["weight"]), _ptr(out.get("mask")),
+        _stream(dev, stream)))
     return out

@@ -273,6 +273,18 @@ int spec_verify_tree_profiled(const void* target_logits, sv_dtype dtype, int B, 
                    n_events);
 }
 
+int spec_build_tree(const int32_t* candidates, int B, int M, int L, int N, int32_t* out_parent,
+                    int32_t* out_tokens, int32_t* out_num_nodes, int32_t* out_depth,
+                    int32_t* out_weight, uint8_t* out_mask, hipStream_t stream) {
+  if (B < 1 || M < 1 || M > kRestMaxM || L < 1 || L > kRestMaxL || N < 1 || N > kRestMaxN)
+    return SV_ERR_INVALID_ARG;
+  if ((long long)B * M * L > INT_MAX || (long long)B * N * N > INT_MAX) return SV_ERR_INVALID_ARG;
+  if (!candidates || !out_parent || !out_tokens || !out_num_nodes) return SV_ERR_INVALID_ARG;
+  const hipError_t e = launch_rest_tree(candidates, B, M, L, N, out_parent, out_tokens,
+                                        out_num_nodes, out_depth, out_weight, out_mask, stream);
+  return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
 const char* spec_verify_status_string(int status) {
   switch (status) {
     case SV_OK: return "ok";

@@ -31,6 +31,9 @@ constexpr int kHistBins = 512;       // top-p mass histogram bins per chunk ...
 constexpr int kHistPerUnit = 8;      // ... on a grid of 1/8 of a unit of z / T
 constexpr int kTopPCandCap = 4096;   // boundary candidates a top-p row may hold
 constexpr int kMentorBisectionSteps = 50;  // bisection steps on alpha (mentored decoding)
+constexpr int kRestMaxM = 128;  // candidates per sequence (REST tree builder)
+constexpr int kRestMaxL = 32;   // tokens per candidate
+constexpr int kRestMaxN = 256;  // tree nodes, root included
 
 // Row kinds written by k_row.
 enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
@@ -142,6 +145,9 @@ hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, con
                          int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
                          float* out_p, const Workspace& ws, hipStream_t stream,
                          hipEvent_t* events, int n_events);
+hipError_t launch_rest_tree(const int32_t* cands, int B, int M, int L, int N, int32_t* parent,
+                            int32_t* tokens, int32_t* n_nodes, int32_t* depth, int32_t* weight,
+                            uint8_t* mask, hipStream_t stream);
 hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,
                        const int32_t* tokens, int max_depth, int32_t* out_tokens,
                        int32_t* out_n, int32_t* out_last, const Workspace& ws,

@@ -136,6 +136,23 @@ def test_tree_bad_arguments(svl):
     assert call() == 3
 
 
+def test_build_tree_bad_arguments(svl):
+    L = svl.lib()
+    dummy = ctypes.c_void_p(4096)
+
+    def call(B=2, M=4, L_=4, N=8, cands=dummy, out=dummy):
+        return L.spec_build_tree(cands, B, M, L_, N, out, dummy, dummy, None, None, None, None)
+    assert call(B=0) == 1
+    assert call(M=0) == 1
+    assert call(M=129) == 1
+    assert call(L_=0) == 1
+    assert call(L_=33) == 1
+    assert call(N=0) == 1
+    assert call(N=257) == 1
+    assert call(cands=None) == 1
+    assert call(out=None) == 1
+
+
 def test_python_binding_rejects_bad_tensors(svl):
     import torch
     t = torch.zeros((2, 3, 10))

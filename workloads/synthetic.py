@@ -18,6 +18,12 @@ Recipes (all noise is i.i.d. per element and fresh for every row):
   tokens are uniform over the vocabulary; logits N(0,1).  ``planted`` raises, for each
   internal node with probability 0.8, the logit of one random child's token to the row
   maximum + 1, so that accepted paths are non-trivial.
+* ``rest``    (REST draft-tree construction, B=32 sequences x M=64 retrieved candidates of up
+  to L=8 tokens, trees of N=64 nodes, token ids < 32000): per sequence, candidates are walks of
+  a random order-1 chain from one start token; each token's successors are ``branch`` random
+  token ids with probabilities proportional to 1/rank^s, drawn once per token, so that
+  candidates share prefixes as retrieved continuations do; lengths are uniform in
+  [L/2, L] (-1 after the end).
 * uniforms: numpy Philox(seed) raw 64-bit words w -> float32((w >> 40) * 2^-24), which lies
   in [0, 1 - 2^-24] and converts exactly.
 
@@ -47,6 +53,8 @@ WORKLOADS = {
     "tree_B32_N64_V32000_bf16": dict(
         B=32, N=64, V=32000, dtype="bf16", gen="tree", max_depth=6, branch_max=4,
         planted=True),
+    "rest_B32_M64_L8_N64": dict(
+        B=32, M=64, L=8, N=64, V=32000, gen="rest", branch=4, s=1.2),
 }
 
 METRIC_WORKLOAD = "zipf_B256_K7_V128256_bf16_topk50"
@@ -155,6 +163,26 @@ def tree_inputs(B, N, V, max_depth=6, branch_max=4, planted=True, dtype="bf16", 
     return logits.to(torch_dtype(dtype)).contiguous(), parent, tokens
 
 
+def rest_candidates(B, M, L, V, branch=4, s=1.2, seed=0):
+    """candidates [B, M, L] int32 for the REST tree builder (recipe in the module header)."""
+    rng = np.random.Generator(np.random.Philox(int(seed) + 11))
+    probs = 1.0 / np.arange(1, branch + 1, dtype=np.float64) ** s
+    probs /= probs.sum()
+    out = np.full((B, M, L), -1, dtype=np.int32)
+    for b in range(B):
+        succ = {}
+        start = int(rng.integers(0, V))
+        for m in range(M):
+            n = int(rng.integers((L + 1) // 2, L + 1))
+            cur = start
+            for t in range(n):
+                if cur not in succ:
+                    succ[cur] = rng.integers(0, V, size=branch)
+                cur = int(succ[cur][int(rng.choice(branch, p=probs))])
+                out[b, m, t] = cur
+    return out
+
+
 def workload_inputs(name, device="cpu", seed=0, **override):
     """Logits (+ tree structure) for a named workload; sizes may be overridden for tests."""
     cfg = dict(WORKLOADS[name])
@@ -168,6 +196,9 @@ def workload_inputs(name, device="cpu", seed=0, **override):
     if cfg["gen"] == "tree":
         return tree_inputs(cfg["B"], cfg["N"], cfg["V"], cfg["max_depth"], cfg["branch_max"],
                            cfg["planted"], cfg["dtype"], device, seed)
+    if cfg["gen"] == "rest":
+        c = rest_candidates(cfg["B"], cfg["M"], cfg["L"], cfg["V"], cfg["branch"], cfg["s"], seed)
+        return torch.from_numpy(c).to(device)
     raise KeyError(name)
 
 
