@@ -39,6 +39,8 @@ __all__ = [
     "tree_verify",
     "rest_trie",
     "rest_build_tree",
+    "philox4x64",
+    "philox_uniforms",
     "kl_divergence",
     "mentored_solve",
     "mentored_verify_sequence",
@@ -663,6 +665,53 @@ def rest_build_tree(candidates, N):
             j = int(parent[j])
     return {"parent": parent, "tokens": tokens, "depth": depth, "weight": weight,
             "mask": mask, "n_nodes": n_nodes}
+
+
+# ---------------------------------------------------------------------------------------------
+# Counter-based uniforms: Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
+# as easy as 1, 2, 3", SC 2011), the generator the verify step's uniforms come from.  A block
+# is a function of a 256-bit counter and a 128-bit key alone: ten rounds, each multiplying
+# counter words 0 and 2 by two fixed 64-bit constants, xoring the high halves with the other
+# two words and the round key, and permuting; the key advances by two Weyl constants per
+# round.  The constants below are the published ones.
+#
+# Readings: word i of a stream (key, counter c) is word i mod 4 of the block at counter
+# c + floor(i / 4) (the counter as a 256-bit little-endian integer); a word w becomes the
+# float32 uniform (w >> 40) * 2^-24 in [0, 1 - 2^-24], exact in float32.
+# ---------------------------------------------------------------------------------------------
+PHILOX_M0 = 0xD2E7470EE14C6C93
+PHILOX_M1 = 0xCA5A826395121157
+PHILOX_W0 = 0x9E3779B97F4A7C15
+PHILOX_W1 = 0xBB67AE8584CAA73B
+_MASK64 = (1 << 64) - 1
+
+
+def philox4x64(counter, key, rounds=10):
+    """One Philox4x64 block: counter = 4 ints (64-bit words), key = 2 ints; returns 4 ints."""
+    x0, x1, x2, x3 = (int(v) & _MASK64 for v in counter)
+    k0, k1 = (int(v) & _MASK64 for v in key)
+    for _ in range(rounds):
+        p0 = PHILOX_M0 * x0
+        p1 = PHILOX_M1 * x2
+        hi0, lo0 = p0 >> 64, p0 & _MASK64
+        hi1, lo1 = p1 >> 64, p1 & _MASK64
+        x0, x1, x2, x3 = hi1 ^ x1 ^ k0, lo1, hi0 ^ x3 ^ k1, lo0
+        k0 = (k0 + PHILOX_W0) & _MASK64
+        k1 = (k1 + PHILOX_W1) & _MASK64
+    return [x0, x1, x2, x3]
+
+
+def philox_uniforms(key, counter, n):
+    """n float32 uniforms of the stream (key = (k0, k1), counter = 256-bit start, an int)."""
+    out = np.empty(int(n), dtype=np.float32)
+    for blk in range((int(n) + 3) // 4):
+        c = (int(counter) + blk) & ((1 << 256) - 1)
+        words = philox4x64([(c >> (64 * j)) & _MASK64 for j in range(4)], key)
+        for j, w in enumerate(words):
+            i = 4 * blk + j
+            if i < n:
+                out[i] = np.float32((w >> 40) * 2.0 ** -24)
+    return out
 
 
 # ---------------------------------------------------------------------------------------------
