@@ -317,6 +317,72 @@ def bench_rest(args, name, cfg):
     print(json.dumps(res), flush=True)
 
 
+def bench_pipeline(args, name, cfg):
+    """The draft -> verify hand-off with every uniform made on the GPU: a step draws the
+    draft tokens from the draft rows (Philox uniforms, spec_sample) and verifies them (Philox
+    uniforms, spec_verify); each step takes fresh counters."""
+    import numpy as np
+    import torch
+    import speculative_sampling_verification_amd as svm
+    from workloads import synthetic as S
+
+    B, K, V = cfg["B"], cfg["K"], cfg["V"]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    target, draft = S.workload_inputs(name, device=dev, seed=1)
+    kw = dict(temperature=cfg["temperature"], top_k=cfg["top_k"], top_p=cfg["top_p"])
+    key = (0x5EED, 0xC0FFEE)
+    nb_d, nb_v = (B * K + 3) // 4, (B * (K + 1) + 3) // 4
+    u_d = torch.empty(B * K, dtype=torch.float32, device=dev)
+    u_v = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
+    drafts = torch.empty((B, K), dtype=torch.int32, device=dev)
+    out = None
+
+    def step(i):
+        nonlocal out
+        c = i * (nb_d + nb_v)
+        svm.spec_philox_uniform(key, c, B * K, out=u_d)
+        svm.spec_sample(draft.view(B * K, V), u_d, out=drafts.view(B * K), **kw)
+        svm.spec_philox_uniform(key, c + nb_d, B * (K + 1), out=u_v.view(-1))
+        out = svm.spec_verify(target, draft, drafts, u_v, out=out, lenience=cfg["lenience"],
+                              **kw)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    elems = B * (2 * K + 1) * V + B * K * V
+    n = out["num_accepted"].cpu().numpy()
+    res = {
+        "metric": f"draft sampling + verify with device uniforms: logit elems/s, B={B} K={K} "
+                  f"V={V} {cfg['dtype']}",
+        "value": elems / (ms_per_step * 1e-3),
+        "unit": "logit elems/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg["dtype"],
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "K": K, "V": V, "temperature": cfg["temperature"],
+                   "top_k": cfg["top_k"], "top_p": cfg["top_p"], "lenience": cfg["lenience"],
+                   "pipeline": "philox -> spec_sample(draft rows) -> philox -> spec_verify"},
+        "roofline": None,
+        "logits_read_per_step": elems,
+        "mean_tokens_per_call": float(n.mean() + 1.0),
+        "source_sha256_12": _source_tag(),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def _copy_reference(args, dev):
     """A plain copy kernel of known size, for calibrating rocprofv3 byte counters."""
     import torch
@@ -341,6 +407,9 @@ def main():
     ap.add_argument("--fenced-events", action="store_true",
                     help="record the per-step timing events with the default system-scope "
                          "fence (costs idle time between kernels)")
+    ap.add_argument("--pipeline", action="store_true",
+                    help="time the draft -> verify hand-off with device uniforms instead: "
+                         "Philox, draft sampling, Philox, verify")
     ap.add_argument("--mentor-kl", type=float, default=0.0,
                     help="KL bound D > 0: mentored decoding (top-k workloads)")
     ap.add_argument("--no-probs", action="store_true",
@@ -369,6 +438,9 @@ def main():
         return
     if cfg["gen"] == "rest":
         bench_rest(args, name, cfg)
+        return
+    if args.pipeline:
+        bench_pipeline(args, name, cfg)
         return
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     dev = torch.device("cuda:0")

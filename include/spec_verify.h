@@ -198,6 +198,19 @@ int spec_build_tree(const int32_t* candidates, int B, int M, int L, int N, int32
                     int32_t* out_tokens, int32_t* out_num_nodes, int32_t* out_depth,
                     int32_t* out_weight, uint8_t* out_mask, hipStream_t stream);
 
+/*
+ * Uniforms for the accept tests and draws, generated on the device (the draft -> verify
+ * hand-off then needs no host data): Philox4x64-10 (Salmon et al., "Parallel random numbers:
+ * as easy as 1, 2, 3", SC 2011) with key (key0, key1).  out[i] = (w_i >> 40) * 2^-24 in
+ * [0, 1 - 2^-24], where w_i is word i mod 4 of the Philox block at the 256-bit counter
+ * counter + floor(i / 4).  Disjoint counter ranges give independent streams, e.g. counter =
+ * step * ceil(n / 4).
+ *   n >= 0 (n <= 2^40); out: device float[n] (may be NULL when n == 0).
+ * Argument errors return SV_ERR_INVALID_ARG before any launch.
+ */
+int spec_philox_uniform(uint64_t key0, uint64_t key1, uint64_t counter, int64_t n, float* out,
+                        hipStream_t stream);
+
 /* Static string for a status code. */
 const char* spec_verify_status_string(int status);
 

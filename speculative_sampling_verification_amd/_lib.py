@@ -31,7 +31,7 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "spec_verify_profiled",
     "spec_sample_workspace_size", "spec_sample",
     "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_tree_profiled",
-    "spec_build_tree", "spec_verify_status_string",
+    "spec_build_tree", "spec_philox_uniform", "spec_verify_status_string",
 ]
 
 
@@ -61,6 +61,9 @@ def load(path=LIB_PATH):
     lib.spec_verify_tree_profiled.restype = i32
     lib.spec_build_tree.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.spec_build_tree.restype = i32
+    u64 = ctypes.c_uint64
+    lib.spec_philox_uniform.argtypes = [u64, u64, u64, ctypes.c_int64, vp, vp]
+    lib.spec_philox_uniform.restype = i32
     lib.spec_verify_status_string.argtypes = [i32]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     return lib
@@ -272,5 +275,21 @@ def spec_build_tree(candidates, N, *, want_mask=True, out=None, stream=None):
     _check("spec_build_tree", _lib.spec_build_tree(
         _ptr(candidates), B, M, L, int(N), _ptr(out["parent"]), _ptr(out["tokens"]),
         _ptr(out["num_nodes"]), _ptr(out["depth"]), _ptr(out["weight"]), _ptr(out.get("mask")),
+        _stream(dev, stream)))
+    return out
+
+
+def spec_philox_uniform(key, counter, n, *, device=None, out=None, stream=None):
+    """n float32 uniforms of the Philox4x64-10 stream (key = (k0, k1), 64-bit start counter)
+    generated on the GPU (see include/spec_verify.h)."""
+    if out is None:
+        out = torch.empty((int(n),), dtype=torch.float32, device=device or "cuda")
+    dev = out.device
+    _need(out, "out", dev, torch.float32)
+    if out.numel() < n:
+        raise ValueError("out is too small")
+    k0, k1 = (int(k) & (2**64 - 1) for k in key)
+    _check("spec_philox_uniform", _lib.spec_philox_uniform(
+        k0, k1, int(counter) & (2**64 - 1), int(n), _ptr(out) if n else None,
         _stream(dev, stream)))
     return out

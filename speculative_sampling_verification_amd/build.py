@@ -7,7 +7,7 @@ import sys
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
-SOURCES = ["sv_kernels.hip", "sv_rest.hip", "sv_abi.hip"]
+SOURCES = ["sv_kernels.hip", "sv_rest.hip", "sv_rng.hip", "sv_abi.hip"]
 LIB_NAME = "libspecverify.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 

@@ -285,6 +285,14 @@ int spec_build_tree(const int32_t* candidates, int B, int M, int L, int N, int32
   return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
+int spec_philox_uniform(uint64_t key0, uint64_t key1, uint64_t counter, int64_t n, float* out,
+                        hipStream_t stream) {
+  if (n < 0 || n > kPhiloxMaxN || (n > 0 && !out)) return SV_ERR_INVALID_ARG;
+  if (n == 0) return SV_OK;
+  const hipError_t e = launch_philox_uniform(key0, key1, counter, n, out, stream);
+  return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
 const char* spec_verify_status_string(int status) {
   switch (status) {
     case SV_OK: return "ok";

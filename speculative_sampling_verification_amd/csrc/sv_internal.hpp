@@ -34,6 +34,7 @@ constexpr int kMentorBisectionSteps = 50;  // bisection steps on alpha (mentored
 constexpr int kRestMaxM = 128;  // candidates per sequence (REST tree builder)
 constexpr int kRestMaxL = 32;   // tokens per candidate
 constexpr int kRestMaxN = 256;  // tree nodes, root included
+constexpr int64_t kPhiloxMaxN = (int64_t)1 << 40;  // uniforms per spec_philox_uniform call
 
 // Row kinds written by k_row.
 enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
@@ -145,6 +146,8 @@ hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, con
                          int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
                          float* out_p, const Workspace& ws, hipStream_t stream,
                          hipEvent_t* events, int n_events);
+hipError_t launch_philox_uniform(uint64_t key0, uint64_t key1, uint64_t counter, int64_t n,
+                                 float* out, hipStream_t stream);
 hipError_t launch_rest_tree(const int32_t* cands, int B, int M, int L, int N, int32_t* parent,
                             int32_t* tokens, int32_t* n_nodes, int32_t* depth, int32_t* weight,
                             uint8_t* mask, hipStream_t stream);

@@ -153,6 +153,14 @@ def test_build_tree_bad_arguments(svl):
     assert call(out=None) == 1
 
 
+def test_philox_arguments(svl):
+    L = svl.lib()
+    assert L.spec_philox_uniform(1, 2, 3, 0, None, None) == 0  # nothing to do, nothing launched
+    assert L.spec_philox_uniform(1, 2, 3, -1, ctypes.c_void_p(4096), None) == 1
+    assert L.spec_philox_uniform(1, 2, 3, 8, None, None) == 1
+    assert L.spec_philox_uniform(1, 2, 3, (1 << 40) + 1, ctypes.c_void_p(4096), None) == 1
+
+
 def test_python_binding_rejects_bad_tensors(svl):
     import torch
     t = torch.zeros((2, 3, 10))

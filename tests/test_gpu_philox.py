@@ -1,0 +1,81 @@
+"""Device Philox4x64-10 uniforms (spec_philox_uniform, through the C ABI) against the oracle's
+philox_uniforms, bit-exact; and the draft -> verify hand-off with every uniform made on the
+GPU, against the oracle fed with its own Philox uniforms."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.spec_verify_oracle as O
+from workloads import synthetic as S
+
+from parity import compare_with_draw_flips, oracle_final_weights, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def svm():
+    import speculative_sampling_verification_amd as m
+    return m
+
+
+@pytest.mark.parametrize("key,counter,n", [((0, 0), 0, 1), ((5, 7), 0, 17),
+                                           ((2**64 - 1, 3), 2**64 - 3, 40),
+                                           ((123, 456), 10**12, 4096)])
+def test_matches_oracle(svm, key, counter, n):
+    _announce(f"philox key={key} counter={counter} n={n}")
+    g = svm.spec_philox_uniform(key, counter, n).cpu().numpy()
+    np.testing.assert_array_equal(g, O.philox_uniforms(key, counter, n))
+
+
+def test_unaligned_output_and_empty(svm):
+    _announce("philox into an unaligned view; n = 0")
+    buf = torch.zeros(64, dtype=torch.float32, device="cuda")
+    view = buf[1:40]
+    svm.spec_philox_uniform((9, 9), 3, 39, out=view)
+    np.testing.assert_array_equal(view.cpu().numpy(), O.philox_uniforms((9, 9), 3, 39))
+    assert buf[0].item() == 0.0 and (buf[40:] == 0).all().item()
+    assert svm.spec_philox_uniform((1, 1), 0, 0).numel() == 0
+
+
+def test_large_stream(svm):
+    _announce("philox n = 2^22: sampled words against the oracle, moments")
+    n = 1 << 22
+    g = svm.spec_philox_uniform((77, 88), 1000, n).cpu().numpy()
+    rng = np.random.default_rng(0)
+    for blk in rng.choice(n // 4, size=64, replace=False):
+        blk = int(blk)
+        np.testing.assert_array_equal(g[4 * blk: 4 * blk + 4],
+                                      O.philox_uniforms((77, 88), 1000 + blk, 4))
+    gd = g.astype(np.float64)
+    assert abs(gd.mean() - 0.5) < 1e-3 and abs(gd.var() - 1 / 12) < 1e-3
+    assert gd.min() >= 0.0 and gd.max() < 1.0
+
+
+def test_device_handoff_end_to_end(svm):
+    _announce("draft sampling and verify with device uniforms, B=16 K=4 V=20000 top-k 50")
+    B, K, V = 16, 4, 20000
+    t, d = S.zipf_logits(B, K, V, 1.1, 1.0, "bf16", seed=61)
+    params = dict(temperature=0.8, top_k=50)
+    key = (2024, 12)
+    td, dd = t.cuda(), d.cuda()
+    u_draw = svm.spec_philox_uniform(key, 0, B * K)
+    u_ver = svm.spec_philox_uniform(key, (B * K + 3) // 4, B * (K + 1)).view(B, K + 1)
+    drafts = svm.spec_sample(dd.view(B * K, V), u_draw, **params).view(B, K)
+    out = svm.spec_verify(td, dd, drafts, u_ver, **params)
+    torch.cuda.synchronize()
+    g = {k: v.cpu().numpy() for k, v in out.items()}
+    # the oracle makes the same uniforms itself, samples the drafts and verifies
+    uo_draw = O.philox_uniforms(key, 0, B * K).reshape(B, K)
+    uo_ver = O.philox_uniforms(key, (B * K + 3) // 4, B * (K + 1)).reshape(B, K + 1)
+    df = d.float().numpy()
+    drafts_o = np.stack([O.sample_rows(df[:, k], uo_draw[:, k], np.float32(0.8), 50, 1.0)
+                         for k in range(K)], axis=1)
+    np.testing.assert_array_equal(drafts.cpu().numpy(), drafts_o)
+    o = run_oracle(t, d, drafts_o, uo_ver, params)
+    compare_with_draw_flips(g, o, uo_ver, lambda b: oracle_final_weights(t, d, o, params, b))
