@@ -48,6 +48,8 @@ __all__ = [
     "expected_tokens_per_call",
     "walltime_speedup",
     "ops_factor",
+    "acceptance_rate",
+    "optimal_gamma",
 ]
 
 
@@ -735,3 +737,25 @@ def walltime_speedup(alpha, K, c):
 
 def ops_factor(alpha, K, c_hat):
     return (K * float(c_hat) + K + 1.0) / expected_tokens_per_call(alpha, K)
+
+
+def acceptance_rate(q, p, lenience=1.0):
+    """beta = probability that a draft token x ~ p is accepted at one position:
+    sum_x p(x) min(1, q(x) / (l p(x))) = sum_x min(p(x), q(x) / l); for l = 1 this is
+    sum min(p, q) = 1 - D_LK(p, q), the total-variation distance the Leviathan blog calls D_LK
+    (section 方法细节, the exact characterisation of the acceptance rate; alpha = E(beta))."""
+    q = np.asarray(q, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    return float(np.sum(np.minimum(p, q / float(lenience))))
+
+
+def optimal_gamma(alpha, c, max_gamma):
+    """The number of draft tokens in 1..max_gamma with the largest wall-clock factor
+    (Leviathan blog, FAQ on choosing gamma: maximise the factor numerically); the smallest
+    such gamma on ties."""
+    best, best_g = -np.inf, 1
+    for g in range(1, int(max_gamma) + 1):
+        v = walltime_speedup(alpha, g, c)
+        if v > best:
+            best, best_g = v, g
+    return best_g
