@@ -317,6 +317,30 @@ def bench_rest(args, name, cfg):
     print(json.dumps(res), flush=True)
 
 
+def _analytics(svm, target, draft, kw, K, measured_tokens):
+    """Acceptance rates of the batch on the GPU (beta = sum min(p, q/l) per position, alpha =
+    their mean) and the blog's analytics for this K: expected tokens per call (compare with the
+    measured mean, which assumes i.i.d. positions), wall-clock factor and optimal gamma for a
+    draft costing c = 5% of the target."""
+    import torch
+    args = dict(temperature=kw["temperature"], top_k=kw["top_k"], top_p=kw["top_p"],
+                lenience=kw["lenience"])
+    beta = svm.spec_acceptance_rate(target, draft, **args)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(10):
+        svm.spec_acceptance_rate(target, draft, out=beta, **args)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / 10
+    alpha = float(beta.double().mean().item())
+    return {"alpha_mean_beta": alpha,
+            "expected_tokens_per_call": svm.expected_tokens(alpha, K),
+            "measured_tokens_per_call": measured_tokens,
+            "walltime_speedup_c0.05": svm.walltime_speedup(alpha, K, 0.05),
+            "optimal_gamma_c0.05": svm.optimal_gamma(alpha, 0.05, 64),
+            "acceptance_rate_ms_per_call": ms}
+
+
 def bench_pipeline(args, name, cfg):
     """The draft -> verify hand-off with every uniform made on the GPU: a step draws the
     draft tokens from the draft rows (Philox uniforms, spec_sample) and verifies them (Philox
@@ -535,6 +559,8 @@ def main():
         "timing_events": "system fence" if args.fenced_events else "no system fence",
         "source_sha256_12": _source_tag(),
     }
+    if args.mentor_kl == 0.0:
+        res["analytics"] = _analytics(svm, target, draft, kw, K, float(n.mean() + 1.0))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seconds,
                                            args.mentor_kl)

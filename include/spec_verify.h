@@ -172,6 +172,35 @@ int spec_verify_tree_profiled(const void* target_logits, sv_dtype dtype, int B, 
                               hipStream_t stream, hipEvent_t* events, int n_events);
 
 /*
+ * Acceptance rate of every draft position (Leviathan blog, section on the method's theory:
+ * beta = 1 - D_LK(p, q) = sum_x min(p(x), q(x)) is the probability that a draft token x ~ p is
+ * accepted, alpha = E(beta); with lenience l the test compares against q/l and
+ * beta = sum_x min(p(x), q(x)/l)).  Same logits, sizes and sampling parameters as spec_verify
+ * (mentor_kl must be 0), no draft tokens or uniforms; K >= 1.
+ *   out_beta [B, K] float, device.
+ * Workspace: spec_verify_workspace_size(B, K, V, dtype, params) bytes.
+ */
+int spec_acceptance_rate(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                         int B, int K, int V, int draft_rows, const sv_sampling* params,
+                         float* out_beta, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * Host-side analytics of the same blog (section on the method's theory; FAQ on choosing
+ * gamma), for an i.i.d. acceptance rate alpha in [0, 1] and gamma draft tokens per call:
+ *   expected tokens per target call  (1 - alpha^(gamma+1)) / (1 - alpha)  (gamma + 1 at 1)
+ *   wall-clock factor                 expected tokens / (gamma * c + 1), c = draft/target cost
+ *   operations factor                 (gamma * c_hat + gamma + 1) / expected tokens
+ *   optimal gamma                     the gamma in 1..max_gamma with the largest wall-clock
+ *                                     factor (the smallest on ties)
+ * Out-of-range arguments give NaN (-1 for the optimal gamma).  No GPU work.
+ */
+double spec_expected_tokens(double alpha, int gamma);
+double spec_walltime_speedup(double alpha, int gamma, double c);
+double spec_ops_factor(double alpha, int gamma, double c_hat);
+int spec_optimal_gamma(double alpha, double c, int max_gamma);
+
+/*
  * Draft tree of a REST step (REST article, section on retrieval-based speculative decoding):
  * the candidate continuations retrieved for each sequence are put in a trie whose node weight
  * is the number of candidates starting with that node's prefix; the N-1 nodes first in the

@@ -4,8 +4,10 @@ The computation lives in libspecverify.so (HIP kernels for gfx950 behind a C ABI
 include/spec_verify.h); this package is its thin Python binding.
 """
 
-from ._lib import (SpecVerifyError, spec_build_tree, spec_philox_uniform,  # noqa: F401
-                   spec_sample, spec_verify, spec_verify_tree, status_string)
+from ._lib import (SpecVerifyError, expected_tokens, ops_factor, optimal_gamma,  # noqa: F401
+                   spec_acceptance_rate, spec_build_tree, spec_philox_uniform, spec_sample,
+                   spec_verify, spec_verify_tree, status_string, walltime_speedup)
 
 __all__ = ["spec_verify", "spec_sample", "spec_verify_tree", "spec_build_tree",
-           "spec_philox_uniform", "SpecVerifyError", "status_string"]
+           "spec_philox_uniform", "spec_acceptance_rate", "expected_tokens", "walltime_speedup",
+           "ops_factor", "optimal_gamma", "SpecVerifyError", "status_string"]

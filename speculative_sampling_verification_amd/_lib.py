@@ -31,7 +31,9 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "spec_verify_profiled",
     "spec_sample_workspace_size", "spec_sample",
     "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_tree_profiled",
-    "spec_build_tree", "spec_philox_uniform", "spec_verify_status_string",
+    "spec_build_tree", "spec_philox_uniform", "spec_acceptance_rate", "spec_expected_tokens",
+    "spec_walltime_speedup", "spec_ops_factor", "spec_optimal_gamma",
+    "spec_verify_status_string",
 ]
 
 
@@ -64,6 +66,17 @@ def load(path=LIB_PATH):
     u64 = ctypes.c_uint64
     lib.spec_philox_uniform.argtypes = [u64, u64, u64, ctypes.c_int64, vp, vp]
     lib.spec_philox_uniform.restype = i32
+    lib.spec_acceptance_rate.argtypes = [vp, vp, i32, i32, i32, i32, i32, psamp, vp, vp, sz, vp]
+    lib.spec_acceptance_rate.restype = i32
+    dbl = ctypes.c_double
+    lib.spec_expected_tokens.argtypes = [dbl, i32]
+    lib.spec_expected_tokens.restype = dbl
+    lib.spec_walltime_speedup.argtypes = [dbl, i32, dbl]
+    lib.spec_walltime_speedup.restype = dbl
+    lib.spec_ops_factor.argtypes = [dbl, i32, dbl]
+    lib.spec_ops_factor.restype = dbl
+    lib.spec_optimal_gamma.argtypes = [dbl, dbl, i32]
+    lib.spec_optimal_gamma.restype = i32
     lib.spec_verify_status_string.argtypes = [i32]
     lib.spec_verify_status_string.restype = ctypes.c_char_p
     return lib
@@ -293,3 +306,44 @@ def spec_philox_uniform(key, counter, n, *, device=None, out=None, stream=None):
         k0, k1, int(counter) & (2**64 - 1), int(n), _ptr(out) if n else None,
         _stream(dev, stream)))
     return out
+
+
+def spec_acceptance_rate(target_logits, draft_logits, *, temperature=1.0, top_k=0, top_p=1.0,
+                         lenience=1.0, out=None, stream=None):
+    """beta [B, K] = sum_x min(p(x), q(x) / l) per draft position (see include/spec_verify.h)."""
+    dev = target_logits.device
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    _need(target_logits, "target_logits", dev)
+    dt = _dtype_code(target_logits)
+    _need(draft_logits, "draft_logits", dev, target_logits.dtype)
+    if draft_logits.dim() != 3 or draft_logits.shape[0] != B or draft_logits.shape[2] != V:
+        raise ValueError("draft_logits must be [B, K or K+1, V]")
+    if out is None:
+        out = torch.empty((B, K), dtype=torch.float32, device=dev)
+    _need(out, "out", dev, torch.float32, (B, K))
+    samp = sampling(temperature, top_k, top_p, lenience)
+    need = _lib.spec_verify_workspace_size(B, K, V, dt, ctypes.byref(samp))
+    if need == 0:
+        raise SpecVerifyError("spec_verify_workspace_size", 1)
+    ws = workspace(dev, need)
+    _check("spec_acceptance_rate", _lib.spec_acceptance_rate(
+        _ptr(target_logits), _ptr(draft_logits), dt, B, K, V, draft_logits.shape[1],
+        ctypes.byref(samp), _ptr(out), _ptr(ws), ws.numel(), _stream(dev, stream)))
+    return out
+
+
+def expected_tokens(alpha, gamma):
+    return _lib.spec_expected_tokens(float(alpha), int(gamma))
+
+
+def walltime_speedup(alpha, gamma, c):
+    return _lib.spec_walltime_speedup(float(alpha), int(gamma), float(c))
+
+
+def ops_factor(alpha, gamma, c_hat):
+    return _lib.spec_ops_factor(float(alpha), int(gamma), float(c_hat))
+
+
+def optimal_gamma(alpha, c, max_gamma):
+    return _lib.spec_optimal_gamma(float(alpha), float(c), int(max_gamma))

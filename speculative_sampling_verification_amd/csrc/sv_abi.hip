@@ -165,7 +165,8 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
   layout_verify(d, s, workspace, &ws);
   if (!out_n) out_n = ws.nbuf;
   const hipError_t e = launch_verify(target, draft, dtype, d, s, drafts, uniforms, out_tokens,
-                                     out_n, out_a, out_q, out_p, ws, stream, events, n_events);
+                                     out_n, out_a, out_q, out_p, nullptr, ws, stream, events,
+                                     n_events);
   return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
@@ -271,6 +272,59 @@ int spec_verify_tree_profiled(const void* target_logits, sv_dtype dtype, int B, 
   return tree_impl(target_logits, dtype, B, N, V, parent, node_tokens, max_depth, out_tokens,
                    out_num_accepted, out_last_node, workspace, workspace_bytes, stream, events,
                    n_events);
+}
+
+int spec_acceptance_rate(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                         int B, int K, int V, int draft_rows, const sv_sampling* params,
+                         float* out_beta, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
+  if (!valid_params(params) || params->mentor_kl != 0.0f) return SV_ERR_INVALID_ARG;
+  if (K < 1 || (draft_rows != K && draft_rows != K + 1)) return SV_ERR_INVALID_ARG;
+  if (!target_logits || !draft_logits || !out_beta) return SV_ERR_INVALID_ARG;
+  Dims d{};
+  if (!make_dims(B, K, V, draft_rows, dtype, &d)) return SV_ERR_INVALID_ARG;
+  const Samp s = make_samp(params, V);
+  const size_t need = layout_verify(d, s, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+  d.vec = ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target_logits) &&
+          aligned16(draft_logits);
+  Workspace ws{};
+  layout_verify(d, s, workspace, &ws);
+  const hipError_t e = launch_verify(target_logits, draft_logits, dtype, d, s, nullptr, nullptr,
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, out_beta, ws,
+                                     stream, nullptr, 0);
+  return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
+}
+
+double spec_expected_tokens(double alpha, int gamma) {
+  if (!(alpha >= 0.0 && alpha <= 1.0) || gamma < 0) return NAN;
+  if (alpha == 1.0) return (double)gamma + 1.0;
+  return (1.0 - std::pow(alpha, gamma + 1)) / (1.0 - alpha);
+}
+
+double spec_walltime_speedup(double alpha, int gamma, double c) {
+  if (!(c >= 0.0)) return NAN;
+  return spec_expected_tokens(alpha, gamma) / ((double)gamma * c + 1.0);
+}
+
+double spec_ops_factor(double alpha, int gamma, double c_hat) {
+  if (!(c_hat >= 0.0)) return NAN;
+  return ((double)gamma * c_hat + (double)gamma + 1.0) / spec_expected_tokens(alpha, gamma);
+}
+
+int spec_optimal_gamma(double alpha, double c, int max_gamma) {
+  if (!(alpha >= 0.0 && alpha <= 1.0) || !(c >= 0.0) || max_gamma < 1) return -1;
+  int best_g = 1;
+  double best = -INFINITY;
+  for (int g = 1; g <= max_gamma; ++g) {
+    const double v = spec_walltime_speedup(alpha, g, c);
+    if (v > best) {
+      best = v;
+      best_g = g;
+    }
+  }
+  return best_g;
 }
 
 int spec_build_tree(const int32_t* candidates, int B, int M, int L, int N, int32_t* out_parent,

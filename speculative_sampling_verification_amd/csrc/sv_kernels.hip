@@ -2591,13 +2591,72 @@ __global__ __launch_bounds__(kSeqThreads) void k_tree_walk(Dims dm, Workspace ws
 }
 
 // ------------------------------------------------------------------------------------------
+// Acceptance rate of every draft position (Leviathan blog, section 方法细节: the acceptance
+// rate of one position is beta = 1 - D_LK(p, q) = sum_x min(p(x), q(x)), alpha = E(beta);
+// with lenience l the accept test compares against q/l, so beta = sum_x min(p(x), q(x)/l)).
+// One workgroup per position: greedy rows compare their argmaxes; two compact rows sum over
+// the target's kept list in one wave; otherwise both full rows are streamed.
+// ------------------------------------------------------------------------------------------
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_beta(const E* __restrict__ tgt,
+                                                   const E* __restrict__ drf, Dims dm, Samp sp,
+                                                   Workspace ws, float* __restrict__ out_beta) {
+  __shared__ RedScratch red;
+  const int pos = blockIdx.x;
+  const int b = pos / dm.K, k = pos - b * dm.K;
+  const RowStat rt = ws.rstat[target_row(dm, b, k)];
+  const RowStat rd = ws.rstat[draft_row(dm, b, k)];
+  const float it = sp.inv_t;
+  const double inv_l = 1.0 / (double)sp.lenience;
+  if (rt.kind == kRowGreedy) {  // one-hot rows: min(p, q/l) = 1 at a shared argmax
+    if (threadIdx.x == 0) out_beta[pos] = rt.argmax == rd.argmax ? 1.0f : 0.0f;
+    return;
+  }
+  const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
+  if (rt.kind == kRowCompact && rd.kind == kRowCompact) {
+    if (wave_id() != 0) return;
+    const uint2* kept = ws.kept + (size_t)target_row(dm, b, k) * kKeptCap;
+    double acc = 0.0;
+    for (int e = lane_id(); e < rt.nkept; e += 64) {
+      const uint2 v = kept[e];
+      const double q = (double)kept_exp(__uint_as_float(v.y), rt, it) / rt.S;
+      const double p = (double)kept_exp(load_logit(drow, (int)v.x), rd, it) / rd.S;
+      acc += p < q * inv_l ? p : q * inv_l;
+    }
+    acc = wave_reduce(acc, [](double a, double c) { return a + c; });
+    if (lane_id() == 0) out_beta[pos] = (float)acc;
+    return;
+  }
+  constexpr int EPV = Tr<E>::kEpv;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
+  const int nvec = (dm.V + EPV - 1) / EPV;
+  double acc = 0.0;
+  for (int v = threadIdx.x; v < nvec; v += kThreads) {
+    float zt[EPV], zd[EPV];
+    load_vec_f<E, VEC>(trow, dm.V, v * EPV, zt);
+    load_vec_f<E, VEC>(drow, dm.V, v * EPV, zd);
+    double part = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) {
+      const double q = (double)kept_exp(zt[e], rt, it) / rt.S * inv_l;
+      const double p = (double)kept_exp(zd[e], rd, it) / rd.S;
+      part += p < q ? p : q;
+    }
+    acc += part;
+  }
+  acc = block_sum_d(acc, red);
+  if (threadIdx.x == 0) out_beta[pos] = (float)acc;
+}
+
+// ------------------------------------------------------------------------------------------
 // Launch helpers
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC>
 hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& sp,
                            const int32_t* drafts, const float* uni, int32_t* out_tokens,
                            int32_t* out_n, float* out_a, float* out_q, float* out_p,
-                           const Workspace& ws, hipStream_t st, hipEvent_t* ev, int nev) {
+                           float* out_beta, const Workspace& ws, hipStream_t st,
+                           hipEvent_t* ev, int nev) {
   if (ev && nev >= 1) (void)hipEventRecord(ev[0], st);
   const unsigned grid_chunks = (unsigned)((size_t)dm.rows * dm.nchunks);
   const Outs o{drafts, uni, out_tokens, out_n, out_a, out_q, out_p};
@@ -2605,6 +2664,11 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_topk_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
                        ws);
     if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
+    if (out_beta) {  // acceptance rates only
+      hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm,
+                         sp, ws, out_beta);
+      return hipGetLastError();
+    }
     if (sp.mentor && dm.K > 0) {
       const int need_all = out_a != nullptr ? 1 : 0;
       hipLaunchKernelGGL((k_mentor<E>), dim3(dm.B * dm.K), dim3(64), 0, st, t, d, dm, sp, ws,
@@ -2635,6 +2699,11 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_topp_select<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm,
                        sp, ws);
   }
+  if (out_beta) {  // acceptance rates only
+    hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm, sp,
+                       ws, out_beta);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
   if (!sp.greedy) {
     if (dm.nchunks > 1)
@@ -2652,7 +2721,7 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
 hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, const Dims& d,
                          const Samp& s, const int32_t* drafts, const float* uniforms,
                          int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
-                         float* out_p, const Workspace& ws, hipStream_t stream,
+                         float* out_p, float* out_beta, const Workspace& ws, hipStream_t stream,
                          hipEvent_t* events, int n_events) {
   (void)hipGetLastError();  // clear a stale error so the status reflects these launches
   if (dt == SV_DTYPE_BF16) {
@@ -2660,17 +2729,19 @@ hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, con
     auto dr = static_cast<const uint16_t*>(draft);
     if (d.vec)
       return launch_verify_t<uint16_t, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
-                                             out_a, out_q, out_p, ws, stream, events, n_events);
+                                             out_a, out_q, out_p, out_beta, ws, stream, events,
+                                             n_events);
     return launch_verify_t<uint16_t, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
-                                            out_a, out_q, out_p, ws, stream, events, n_events);
+                                            out_a, out_q, out_p, out_beta, ws, stream, events,
+                                            n_events);
   }
   auto t = static_cast<const float*>(target);
   auto dr = static_cast<const float*>(draft);
   if (d.vec)
     return launch_verify_t<float, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
-                                        out_q, out_p, ws, stream, events, n_events);
+                                        out_q, out_p, out_beta, ws, stream, events, n_events);
   return launch_verify_t<float, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
-                                       out_q, out_p, ws, stream, events, n_events);
+                                       out_q, out_p, out_beta, ws, stream, events, n_events);
 }
 
 hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,

@@ -1,0 +1,85 @@
+"""GPU acceptance rates (spec_acceptance_rate, through the C ABI): beta = sum min(p, q/l) per
+draft position against the oracle's acceptance_rate on its own row distributions, 1e-5
+absolute; and alpha = mean beta against the accept decisions of spec_verify."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.spec_verify_oracle as O
+from workloads import synthetic as S
+
+from parity import make_inputs, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def svm():
+    import speculative_sampling_verification_amd as m
+    return m
+
+
+def _check(svm, t, d, params, atol=1e-5):
+    g = svm.spec_acceptance_rate(t.cuda(), d.cuda(), **params).cpu().numpy()
+    torch.cuda.synchronize()
+    B, K1, V = t.shape
+    tf, df = t.float().numpy(), d.float().numpy()
+    T = np.float32(params.get("temperature", 1.0))
+    k = params.get("top_k", 0)
+    P = np.float32(params.get("top_p", 1.0))
+    lenience = np.float32(params.get("lenience", 1.0))
+    for b in range(B):
+        for j in range(K1 - 1):
+            dt, dd = {}, {}
+            q = O.row_distribution(tf[b, j], T, k, P, diagnostics=dt)
+            p = O.row_distribution(df[b, j], T, k, P, diagnostics=dd)
+            if min(dt["topp_margin"], dd["topp_margin"]) < 1e-6:
+                continue  # a top-p boundary within rounding: either kept set is correct
+            o = O.acceptance_rate(q, p, lenience)
+            assert abs(g[b, j] - o) <= atol, (b, j, g[b, j], o)
+    return g
+
+
+def test_topk_compact(svm):
+    _announce("acceptance rate, zipf bf16 top-k 50 T=0.7 B=8 K=7 V=128256")
+    t, d = S.zipf_logits(8, 7, 128256, 1.1, 1.0, "bf16", seed=71)
+    _check(svm, t, d, dict(temperature=0.7, top_k=50))
+
+
+def test_dense_topp_lenience_greedy(svm):
+    _announce("acceptance rate: dense fp32, top-p 0.9, lenience 0.3, greedy; V=40000")
+    t, d = S.zipf_logits(4, 3, 40000, 1.1, 2.0, "f32", seed=72)
+    _check(svm, t, d, dict(temperature=1.0))
+    _check(svm, t, d, dict(temperature=1.0, top_p=0.9))
+    _check(svm, t, d, dict(temperature=0.8, top_k=300, lenience=0.3))
+    t2, d2 = S.normal_logits(6, 4, 5000, 3.0, 0.9, 0.4, "bf16", seed=73)
+    g = _check(svm, t2, d2, dict(temperature=0.0))
+    assert set(np.unique(g)) <= {0.0, 1.0}
+
+
+def test_tie_overflow_rows(svm):
+    _announce("acceptance rate: tie overflow of the kept lists (whole-row path)")
+    gen = torch.Generator().manual_seed(74)
+    t = torch.randint(0, 4, (2, 3, 30000), generator=gen).float().to(torch.bfloat16)
+    d = torch.randint(0, 4, (2, 2, 30000), generator=gen).float().to(torch.bfloat16)
+    _check(svm, t, d, dict(temperature=1.0, top_k=50))
+
+
+def test_alpha_matches_accept_decisions(svm):
+    _announce("alpha = mean beta against the accept probabilities of verified drafts")
+    t, d = S.zipf_logits(64, 4, 8000, 1.1, 1.0, "bf16", seed=75)
+    params = dict(temperature=0.9, top_k=40)
+    beta = svm.spec_acceptance_rate(t.cuda(), d.cuda(), **params).cpu().numpy()
+    drafts, u = make_inputs(t, d, params, 75)
+    g = run_gpu(t, d, drafts, u, params)
+    # E[a_k] over x ~ p equals beta_k; 256 draws: the means agree to a few standard errors
+    a = g["accept_prob"].astype(np.float64)
+    se = a.std() / np.sqrt(a.size)
+    assert abs(a.mean() - beta.mean()) < 4 * se + 1e-6
+    alpha = float(beta.mean())
+    assert abs(svm.expected_tokens(alpha, 4) - O.expected_tokens_per_call(alpha, 4)) < 1e-12
