@@ -1918,6 +1918,26 @@ __device__ int pick_staged_wave(int nk, double W, double u, const uint32_t* s_id
   const double target = u * W;
   uint32_t pick = 0xFFFFFFFFu;
   int lastpos = -1;
+  if (nk <= 64) {  // one entry per lane: the other entries are read lane by lane
+    const int lane = lane_id();
+    const uint32_t ie = lane < nk ? s_idx[lane] : 0xFFFFFFFFu;
+    const double we = lane < nk ? s_w[lane] : 0.0;
+    double pre = 0.0;
+    for (int j = 0; j < nk; ++j) {  // the same order of additions as the general loop below
+      const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)ie, j);
+      const double wj = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(we), j),
+                                         __builtin_amdgcn_readlane(__double2loint(we), j));
+      if (ij <= ie) pre += wj;
+    }
+    if (lane < nk && we > 0.0) {
+      if (pre > target) pick = ie;
+      lastpos = (int)ie;
+    }
+    pick = wave_reduce(pick, [](uint32_t a, uint32_t c) { return a < c ? a : c; });
+    lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
+    wave_lds_sync();
+    return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
+  }
   for (int e = lane_id(); e < nk; e += 64) {
     const uint32_t ie = s_idx[e];
     const double we = s_w[e];
@@ -2466,6 +2486,7 @@ struct SeqCompactLds {
     MentorLds<MENTOR ? kKeptCap : 1> ment;
   };
 };
+
 
 template <class E, bool VEC, bool MENTOR>
 __global__ __launch_bounds__(kThreads) void k_seq_compact(const E* __restrict__ tgt,
