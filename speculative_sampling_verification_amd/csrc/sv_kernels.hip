@@ -2669,6 +2669,52 @@ __global__ __launch_bounds__(kThreads) void k_beta(const E* __restrict__ tgt,
   if (threadIdx.x == 0) out_beta[pos] = (float)acc;
 }
 
+// Dense rows (no kept lists): one workgroup per (position, chunk) sums min(p, q/l) over the
+// chunk into the chunk-partials array, which k_row has finished with; k_beta_merge adds the
+// chunks of each position in order.
+template <class E, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_beta_partial(const E* __restrict__ tgt,
+                                                           const E* __restrict__ drf, Dims dm,
+                                                           Samp sp, Workspace ws) {
+  __shared__ RedScratch red;
+  const int pos = blockIdx.x / dm.nchunks;
+  const int c = blockIdx.x - pos * dm.nchunks;
+  const int b = pos / dm.K, k = pos - b * dm.K;
+  const RowStat rt = ws.rstat[target_row(dm, b, k)];
+  const RowStat rd = ws.rstat[draft_row(dm, b, k)];
+  const float it = sp.inv_t;
+  const double inv_l = 1.0 / (double)sp.lenience;
+  constexpr int EPV = Tr<E>::kEpv;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
+  const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
+  const int e0 = c * dm.chunk_elems;
+  const int e1 = min(dm.V, e0 + dm.chunk_elems);
+  // fp32 per element with the normalisers folded into one factor per row, fp64 across vectors
+  const float ft = (float)(inv_l / rt.S), fd = (float)(1.0 / rd.S);
+  double acc = 0.0;
+  for (int e = e0 + threadIdx.x * EPV; e < e1; e += kThreads * EPV) {
+    float zt[EPV], zd[EPV];
+    load_vec_f<E, VEC>(trow, dm.V, e, zt);
+    load_vec_f<E, VEC>(drow, dm.V, e, zd);
+    float part = 0.0f;
+#pragma unroll
+    for (int j = 0; j < EPV; ++j)
+      part += fminf(kept_exp(zd[j], rd, it) * fd, kept_exp(zt[j], rt, it) * ft);
+    acc += (double)part;
+  }
+  acc = block_sum_d(acc, red);
+  if (threadIdx.x == 0) ws.parts[(size_t)pos * dm.nchunks + c].sum = acc;
+}
+
+__global__ __launch_bounds__(kThreads) void k_beta_merge(Dims dm, Workspace ws,
+                                                         float* __restrict__ out_beta) {
+  const int pos = blockIdx.x * kThreads + threadIdx.x;
+  if (pos >= dm.B * dm.K) return;
+  double acc = 0.0;
+  for (int c = 0; c < dm.nchunks; ++c) acc += ws.parts[(size_t)pos * dm.nchunks + c].sum;
+  out_beta[pos] = (float)acc;
+}
+
 // ------------------------------------------------------------------------------------------
 // Launch helpers
 // ------------------------------------------------------------------------------------------
@@ -2721,8 +2767,16 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
                        sp, ws);
   }
   if (out_beta) {  // acceptance rates only
-    hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm, sp,
-                       ws, out_beta);
+    if (sp.greedy) {
+      hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm,
+                         sp, ws, out_beta);
+    } else {
+      const int npos = dm.B * dm.K;
+      hipLaunchKernelGGL((k_beta_partial<E, VEC>), dim3((unsigned)((size_t)npos * dm.nchunks)),
+                         dim3(kThreads), 0, st, t, d, dm, sp, ws);
+      hipLaunchKernelGGL(k_beta_merge, dim3((npos + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                         st, dm, ws, out_beta);
+    }
     return hipGetLastError();
   }
   hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
