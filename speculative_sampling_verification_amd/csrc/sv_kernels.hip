@@ -1912,31 +1912,42 @@ __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt
 // Inverse-CDF pick over weights staged in LDS by one wave (s_idx / s_w, nk entries, total W):
 // the smallest index whose cumulative weight in index order exceeds u * W; the largest index of
 // positive weight if rounding leaves none.
+// The same pick over at most 64 entries held one per lane (lane e: index ie, weight we; lanes
+// >= nk hold none): each lane reads the others' entries in order, adding in the order of the
+// general loop of pick_staged_wave, so both give the same token.
+__device__ int pick_lanes(int nk, uint32_t ie, double we, double W, double u) {
+  const int lane = lane_id();
+  const double target = u * W;
+  double pre = 0.0;
+  for (int j = 0; j < nk; ++j) {
+    const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)ie, j);
+    const double wj = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(we), j),
+                                       __builtin_amdgcn_readlane(__double2loint(we), j));
+    if (ij <= ie) pre += wj;
+  }
+  uint32_t pick = 0xFFFFFFFFu;
+  int lastpos = -1;
+  if (lane < nk && we > 0.0) {
+    if (pre > target) pick = ie;
+    lastpos = (int)ie;
+  }
+  pick = wave_reduce(pick, [](uint32_t a, uint32_t c) { return a < c ? a : c; });
+  lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
+  return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
+}
+
 __device__ int pick_staged_wave(int nk, double W, double u, const uint32_t* s_idx,
                                 const double* s_w) {
   wave_lds_sync();
   const double target = u * W;
   uint32_t pick = 0xFFFFFFFFu;
   int lastpos = -1;
-  if (nk <= 64) {  // one entry per lane: the other entries are read lane by lane
+  if (nk <= 64) {  // one entry per lane
     const int lane = lane_id();
-    const uint32_t ie = lane < nk ? s_idx[lane] : 0xFFFFFFFFu;
-    const double we = lane < nk ? s_w[lane] : 0.0;
-    double pre = 0.0;
-    for (int j = 0; j < nk; ++j) {  // the same order of additions as the general loop below
-      const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)ie, j);
-      const double wj = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(we), j),
-                                         __builtin_amdgcn_readlane(__double2loint(we), j));
-      if (ij <= ie) pre += wj;
-    }
-    if (lane < nk && we > 0.0) {
-      if (pre > target) pick = ie;
-      lastpos = (int)ie;
-    }
-    pick = wave_reduce(pick, [](uint32_t a, uint32_t c) { return a < c ? a : c; });
-    lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
+    const int tok = pick_lanes(nk, lane < nk ? s_idx[lane] : 0xFFFFFFFFu,
+                               lane < nk ? s_w[lane] : 0.0, W, u);
     wave_lds_sync();
-    return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
+    return tok;
   }
   for (int e = lane_id(); e < nk; e += 64) {
     const uint32_t ie = s_idx[e];
@@ -1953,6 +1964,25 @@ __device__ int pick_staged_wave(int nk, double W, double u, const uint32_t* s_id
   lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
   wave_lds_sync();
   return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
+}
+
+// Final draw over at most 64 kept tokens held one per lane (lane e < nk: index ie, target logit
+// zt, draft logit zd): weights and order of additions as in final_draw_compact_wave.
+__device__ int draw_small_wave(int nk, uint32_t ie, float zt, float zd, const RowStat& rt,
+                               const RowStat& rd, bool resid, float it, double u) {
+  const bool has = lane_id() < nk;
+  const double q = has ? (double)fast_exp((zt - rt.m) * it) / rt.S : 0.0;
+  double w = q;
+  if (resid) {
+    const double p = has ? (double)kept_exp(zd, rd, it) / rd.S : 0.0;
+    w = q - p > 0.0 ? q - p : 0.0;
+  }
+  double W = wave_reduce(w, [](double a, double c) { return a + c; });
+  if (!(W > 0.0)) {  // empty residual: draw from q
+    w = q;
+    W = wave_reduce(q, [](double a, double c) { return a + c; });
+  }
+  return pick_lanes(nk, has ? ie : 0xFFFFFFFFu, w, W, u);
 }
 
 // Final draw over a compact row, one wave.  Weights (q - p)_+ (or q for the bonus row, or q
@@ -1974,6 +2004,17 @@ __device__ int final_draw_compact_wave(const E* __restrict__ tgt, const E* __res
     drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
   }
   const float it = sp.inv_t;
+  if (nk <= 64) {
+    uint32_t ie = 0xFFFFFFFFu;
+    float zt = 0.0f, zd = 0.0f;
+    if (lane < nk) {
+      const uint2 v = kept[lane];
+      ie = v.x;
+      zt = __uint_as_float(v.y);
+      if (resid) zd = Tr<E>::to_float(Tr<E>::bits_of(drow[v.x]));
+    }
+    return draw_small_wave(nk, ie, zt, zd, rt, rd, resid, it, u);
+  }
   double Wp = 0.0;
   for (int e = lane; e < nk; e += 64) {
     const uint2 v = kept[e];
