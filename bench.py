@@ -317,11 +317,12 @@ def bench_rest(args, name, cfg):
     print(json.dumps(res), flush=True)
 
 
-def _analytics(svm, target, draft, kw, K, measured_tokens):
+def _analytics(svm, target, draft, kw, K, measured_tokens, step_inputs):
     """Acceptance rates of the batch on the GPU (beta = sum min(p, q/l) per position, alpha =
     their mean) and the blog's analytics for this K: expected tokens per call (compare with the
     measured mean, which assumes i.i.d. positions), wall-clock factor and optimal gamma for a
-    draft costing c = 5% of the target."""
+    draft costing c = 5% of the target.  Also the time of a verify step that returns the rates
+    too (spec_verify_rates), against the separate acceptance-rate call."""
     import torch
     args = dict(temperature=kw["temperature"], top_k=kw["top_k"], top_p=kw["top_p"],
                 lenience=kw["lenience"])
@@ -332,13 +333,23 @@ def _analytics(svm, target, draft, kw, K, measured_tokens):
         svm.spec_acceptance_rate(target, draft, out=beta, **args)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / 10
+    drafts, u = step_inputs
+    out = svm.spec_verify(target, draft, drafts, u, want_rates=True, **args)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(20):
+        svm.spec_verify(target, draft, drafts, u, want_rates=True, out=out, **args)
+    torch.cuda.synchronize()
+    ms_both = (time.perf_counter() - t0) * 1e3 / 20
+    assert torch.equal(out["rate"], beta), "rates of spec_verify_rates differ"
     alpha = float(beta.double().mean().item())
     return {"alpha_mean_beta": alpha,
             "expected_tokens_per_call": svm.expected_tokens(alpha, K),
             "measured_tokens_per_call": measured_tokens,
             "walltime_speedup_c0.05": svm.walltime_speedup(alpha, K, 0.05),
             "optimal_gamma_c0.05": svm.optimal_gamma(alpha, 0.05, 64),
-            "acceptance_rate_ms_per_call": ms}
+            "acceptance_rate_ms_per_call": ms,
+            "verify_with_rates_ms_per_step": ms_both}
 
 
 def bench_pipeline(args, name, cfg):
@@ -560,7 +571,8 @@ def main():
         "source_sha256_12": _source_tag(),
     }
     if args.mentor_kl == 0.0:
-        res["analytics"] = _analytics(svm, target, draft, kw, K, float(n.mean() + 1.0))
+        res["analytics"] = _analytics(svm, target, draft, kw, K, float(n.mean() + 1.0),
+                                      (drafts, u))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seconds,
                                            args.mentor_kl)

@@ -186,6 +186,22 @@ int spec_acceptance_rate(const void* target_logits, const void* draft_logits, sv
                          hipStream_t stream);
 
 /*
+ * spec_verify and spec_acceptance_rate in one call: the verify step's results, identical to
+ * spec_verify's, plus out_beta [B, K] float (device), identical to spec_acceptance_rate's on
+ * the same logits and parameters.  The rates come from the row summaries the verify step makes
+ * anyway, so the logits are streamed once; a serving loop can track alpha = mean beta (and the
+ * draft length that maximises the wall-clock factor below) at no second pass.
+ * K >= 1, out_beta non-NULL and mentor_kl == 0, else SV_ERR_INVALID_ARG.  Workspace:
+ * spec_verify_workspace_size(B, K, V, dtype, params) bytes.
+ */
+int spec_verify_rates(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                      int B, int K, int V, int draft_rows, const int32_t* draft_tokens,
+                      const float* uniforms, const sv_sampling* params, int32_t* out_tokens,
+                      int32_t* out_num_accepted, float* out_accept_prob, float* out_q_draft,
+                      float* out_p_draft, float* out_beta, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Host-side analytics of the same blog (section on the method's theory; FAQ on choosing
  * gamma), for an i.i.d. acceptance rate alpha in [0, 1] and gamma draft tokens per call:
  *   expected tokens per target call  (1 - alpha^(gamma+1)) / (1 - alpha)  (gamma + 1 at 1)

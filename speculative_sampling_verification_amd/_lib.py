@@ -31,7 +31,8 @@ EXPORTS = [
     "spec_verify_workspace_size", "spec_verify", "spec_verify_profiled",
     "spec_sample_workspace_size", "spec_sample",
     "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_tree_profiled",
-    "spec_build_tree", "spec_philox_uniform", "spec_acceptance_rate", "spec_expected_tokens",
+    "spec_build_tree", "spec_philox_uniform", "spec_acceptance_rate", "spec_verify_rates",
+    "spec_expected_tokens",
     "spec_walltime_speedup", "spec_ops_factor", "spec_optimal_gamma",
     "spec_verify_status_string",
 ]
@@ -51,6 +52,9 @@ def load(path=LIB_PATH):
     lib.spec_verify.restype = i32
     lib.spec_verify_profiled.argtypes = lib.spec_verify.argtypes + [vp, i32]
     lib.spec_verify_profiled.restype = i32
+    lib.spec_verify_rates.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, psamp, vp, vp, vp,
+                                      vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_rates.restype = i32
     lib.spec_sample_workspace_size.argtypes = [i32, i32, i32, psamp]
     lib.spec_sample_workspace_size.restype = sz
     lib.spec_sample.argtypes = [vp, i32, i32, i32, vp, psamp, vp, vp, sz, vp]
@@ -153,8 +157,8 @@ def _stream(device, stream):
 
 
 def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperature=1.0, top_k=0,
-                top_p=1.0, lenience=1.0, mentor_kl=0.0, out=None, want_probs=True, stream=None,
-                events=None):
+                top_p=1.0, lenience=1.0, mentor_kl=0.0, out=None, want_probs=True,
+                want_rates=False, stream=None, events=None):
     """Verify-and-resample for a batch (see include/spec_verify.h).
 
     target_logits [B, K+1, V], draft_logits [B, K or K+1, V] (bf16 or fp32, same dtype),
@@ -163,6 +167,8 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
     p_draft [B, K].  ``out`` may hold preallocated tensors under the same keys.
     ``mentor_kl`` > 0 selects mentored decoding with that KL bound (needs lenience 1 and, for
     temperature > 0, top_k in 1..256).
+    ``want_rates``: also return rate [B, K], the acceptance rate sum_x min(p, q/l) of each
+    position (spec_verify_rates: the same results plus the rates, one pass over the logits).
     ``events``: optional list of >= 2 hipEvent_t handles (ints) for per-phase timing.
     """
     dev = target_logits.device
@@ -193,6 +199,12 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
     for k in ("accept_prob", "q_draft", "p_draft"):
         if k in out:
             _need(out[k], f"out {k}", dev, torch.float32, (B, K))
+    if want_rates:
+        if events is not None:
+            raise ValueError("want_rates and events cannot be combined")
+        if "rate" not in out:
+            out["rate"] = torch.empty((B, K), dtype=torch.float32, device=dev)
+        _need(out["rate"], "out rate", dev, torch.float32, (B, K))
     samp = sampling(temperature, top_k, top_p, lenience, mentor_kl)
     need = _lib.spec_verify_workspace_size(B, K, V, dt, ctypes.byref(samp))
     if need == 0:
@@ -203,7 +215,10 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
             _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out.get("accept_prob")),
             _ptr(out.get("q_draft")), _ptr(out.get("p_draft")), _ptr(ws), ws.numel(),
             _stream(dev, stream)]
-    if events is None:
+    if want_rates:
+        _check("spec_verify_rates", _lib.spec_verify_rates(*args[:15], _ptr(out["rate"]),
+                                                           *args[15:]))
+    elif events is None:
         _check("spec_verify", _lib.spec_verify(*args))
     else:
         arr = (ctypes.c_void_p * len(events))(*events)

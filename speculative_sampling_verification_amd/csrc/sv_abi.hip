@@ -145,8 +145,8 @@ namespace {
 int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, int K, int V,
                 int draft_rows, const int32_t* drafts, const float* uniforms,
                 const sv_sampling* params, int32_t* out_tokens, int32_t* out_n, float* out_a,
-                float* out_q, float* out_p, void* workspace, size_t workspace_bytes,
-                hipStream_t stream, hipEvent_t* events, int n_events) {
+                float* out_q, float* out_p, float* out_beta, void* workspace,
+                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int n_events) {
   if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
   if (!valid_params(params)) return SV_ERR_INVALID_ARG;
   if (K > 0 && draft_rows != K && draft_rows != K + 1) return SV_ERR_INVALID_ARG;
@@ -165,8 +165,8 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
   layout_verify(d, s, workspace, &ws);
   if (!out_n) out_n = ws.nbuf;
   const hipError_t e = launch_verify(target, draft, dtype, d, s, drafts, uniforms, out_tokens,
-                                     out_n, out_a, out_q, out_p, nullptr, ws, stream, events,
-                                     n_events);
+                                     out_n, out_a, out_q, out_p, out_beta, false, ws, stream,
+                                     events, n_events);
   return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
@@ -190,7 +190,22 @@ int spec_verify(const void* target_logits, const void* draft_logits, sv_dtype dt
   if (!out_num_accepted) return SV_ERR_INVALID_ARG;
   return verify_impl(target_logits, draft_logits, dtype, B, K, V, draft_rows, draft_tokens,
                      uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
-                     out_q_draft, out_p_draft, workspace, workspace_bytes, stream, nullptr, 0);
+                     out_q_draft, out_p_draft, nullptr, workspace, workspace_bytes, stream,
+                     nullptr, 0);
+}
+
+int spec_verify_rates(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                      int B, int K, int V, int draft_rows, const int32_t* draft_tokens,
+                      const float* uniforms, const sv_sampling* params, int32_t* out_tokens,
+                      int32_t* out_num_accepted, float* out_accept_prob, float* out_q_draft,
+                      float* out_p_draft, float* out_beta, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (!out_num_accepted || !out_beta || K < 1) return SV_ERR_INVALID_ARG;
+  if (params && params->mentor_kl != 0.0f) return SV_ERR_INVALID_ARG;
+  return verify_impl(target_logits, draft_logits, dtype, B, K, V, draft_rows, draft_tokens,
+                     uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
+                     out_q_draft, out_p_draft, out_beta, workspace, workspace_bytes, stream,
+                     nullptr, 0);
 }
 
 int spec_verify_profiled(const void* target_logits, const void* draft_logits, sv_dtype dtype,
@@ -202,7 +217,7 @@ int spec_verify_profiled(const void* target_logits, const void* draft_logits, sv
   if (!out_num_accepted || !events || n_events < 2) return SV_ERR_INVALID_ARG;
   return verify_impl(target_logits, draft_logits, dtype, B, K, V, draft_rows, draft_tokens,
                      uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
-                     out_q_draft, out_p_draft, workspace, workspace_bytes, stream, events,
+                     out_q_draft, out_p_draft, nullptr, workspace, workspace_bytes, stream, events,
                      n_events);
 }
 
@@ -214,8 +229,8 @@ int spec_sample(const void* logits, sv_dtype dtype, int R, int V, const float* u
                 const sv_sampling* params, int32_t* out_tokens, void* workspace,
                 size_t workspace_bytes, hipStream_t stream) {
   return verify_impl(logits, nullptr, dtype, R, 0, V, 0, nullptr, uniforms, params, out_tokens,
-                     nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
-                     nullptr, 0);
+                     nullptr, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                     stream, nullptr, 0);
 }
 
 size_t spec_verify_tree_workspace_size(int B, int N, int V, sv_dtype dtype) {
@@ -292,8 +307,8 @@ int spec_acceptance_rate(const void* target_logits, const void* draft_logits, sv
   Workspace ws{};
   layout_verify(d, s, workspace, &ws);
   const hipError_t e = launch_verify(target_logits, draft_logits, dtype, d, s, nullptr, nullptr,
-                                     nullptr, nullptr, nullptr, nullptr, nullptr, out_beta, ws,
-                                     stream, nullptr, 0);
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, out_beta, true,
+                                     ws, stream, nullptr, 0);
   return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 

@@ -144,8 +144,8 @@ size_t layout_tree(const Dims& d, void* base, Workspace* ws);
 hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, const Dims& d,
                          const Samp& s, const int32_t* drafts, const float* uniforms,
                          int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
-                         float* out_p, float* out_beta, const Workspace& ws, hipStream_t stream,
-                         hipEvent_t* events, int n_events);
+                         float* out_p, float* out_beta, bool rates_only, const Workspace& ws,
+                         hipStream_t stream, hipEvent_t* events, int n_events);
 hipError_t launch_philox_uniform(uint64_t key0, uint64_t key1, uint64_t counter, int64_t n,
                                  float* out, hipStream_t stream);
 hipError_t launch_rest_tree(const int32_t* cands, int B, int M, int L, int N, int32_t* parent,

@@ -2763,7 +2763,7 @@ template <class E, bool VEC>
 hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& sp,
                            const int32_t* drafts, const float* uni, int32_t* out_tokens,
                            int32_t* out_n, float* out_a, float* out_q, float* out_p,
-                           float* out_beta, const Workspace& ws, hipStream_t st,
+                           float* out_beta, bool rates_only, const Workspace& ws, hipStream_t st,
                            hipEvent_t* ev, int nev) {
   if (ev && nev >= 1) (void)hipEventRecord(ev[0], st);
   const unsigned grid_chunks = (unsigned)((size_t)dm.rows * dm.nchunks);
@@ -2772,10 +2772,10 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_topk_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
                        ws);
     if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
-    if (out_beta) {  // acceptance rates only
+    if (out_beta) {  // acceptance rates from the row summaries (read-only for the steps below)
       hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm,
                          sp, ws, out_beta);
-      return hipGetLastError();
+      if (rates_only) return hipGetLastError();
     }
     if (sp.mentor && dm.K > 0) {
       const int need_all = out_a != nullptr ? 1 : 0;
@@ -2807,7 +2807,7 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_topp_select<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm,
                        sp, ws);
   }
-  if (out_beta) {  // acceptance rates only
+  if (out_beta) {  // acceptance rates; the chunk partials are free once k_row has run
     if (sp.greedy) {
       hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm,
                          sp, ws, out_beta);
@@ -2818,7 +2818,7 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
       hipLaunchKernelGGL(k_beta_merge, dim3((npos + kThreads - 1) / kThreads), dim3(kThreads), 0,
                          st, dm, ws, out_beta);
     }
-    return hipGetLastError();
+    if (rates_only) return hipGetLastError();
   }
   hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
   if (!sp.greedy) {
@@ -2837,27 +2837,27 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
 hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, const Dims& d,
                          const Samp& s, const int32_t* drafts, const float* uniforms,
                          int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
-                         float* out_p, float* out_beta, const Workspace& ws, hipStream_t stream,
-                         hipEvent_t* events, int n_events) {
+                         float* out_p, float* out_beta, bool rates_only, const Workspace& ws,
+                         hipStream_t stream, hipEvent_t* events, int n_events) {
   (void)hipGetLastError();  // clear a stale error so the status reflects these launches
   if (dt == SV_DTYPE_BF16) {
     auto t = static_cast<const uint16_t*>(target);
     auto dr = static_cast<const uint16_t*>(draft);
     if (d.vec)
       return launch_verify_t<uint16_t, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
-                                             out_a, out_q, out_p, out_beta, ws, stream, events,
+                                             out_a, out_q, out_p, out_beta, rates_only, ws, stream, events,
                                              n_events);
     return launch_verify_t<uint16_t, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
-                                            out_a, out_q, out_p, out_beta, ws, stream, events,
+                                            out_a, out_q, out_p, out_beta, rates_only, ws, stream, events,
                                             n_events);
   }
   auto t = static_cast<const float*>(target);
   auto dr = static_cast<const float*>(draft);
   if (d.vec)
     return launch_verify_t<float, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
-                                        out_q, out_p, out_beta, ws, stream, events, n_events);
+                                        out_q, out_p, out_beta, rates_only, ws, stream, events, n_events);
   return launch_verify_t<float, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
-                                       out_q, out_p, out_beta, ws, stream, events, n_events);
+                                       out_q, out_p, out_beta, rates_only, ws, stream, events, n_events);
 }
 
 hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,

@@ -119,6 +119,28 @@ def test_bad_arguments_are_rejected_on_the_host(svl):
     assert _verify(svl, B=2**30, K=3, V=10**6) == INVALID
 
 
+def _verify_rates(svl, **over):
+    L = svl.lib()
+    dummy = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation
+    a = dict(t=dummy, d=dummy, dt=1, B=2, K=3, V=100, dr=3, x=dummy, u=dummy,
+             p=svl.sampling(1.0, 0, 1.0, 1.0), ot=dummy, on=dummy, beta=dummy, ws=dummy, wsb=0)
+    a.update(over)
+    return L.spec_verify_rates(a["t"], a["d"], a["dt"], a["B"], a["K"], a["V"], a["dr"], a["x"],
+                               a["u"], ctypes.byref(a["p"]), a["ot"], a["on"], None, None, None,
+                               a["beta"], a["ws"], a["wsb"], None)
+
+
+def test_verify_rates_bad_arguments(svl):
+    INVALID, WS = 1, 3
+    assert _verify_rates(svl, beta=None) == INVALID
+    assert _verify_rates(svl, K=0) == INVALID
+    assert _verify_rates(svl, on=None) == INVALID
+    # acceptance rates are defined for the lossless rule only
+    assert _verify_rates(svl, p=svl.sampling(1.0, 10, 1.0, 1.0, 0.1)) == INVALID
+    assert _verify_rates(svl, B=0) == INVALID
+    assert _verify_rates(svl) == WS  # valid arguments but no workspace
+
+
 def test_tree_bad_arguments(svl):
     L = svl.lib()
     dummy = ctypes.c_void_p(4096)

@@ -83,3 +83,28 @@ def test_alpha_matches_accept_decisions(svm):
     assert abs(a.mean() - beta.mean()) < 4 * se + 1e-6
     alpha = float(beta.mean())
     assert abs(svm.expected_tokens(alpha, 4) - O.expected_tokens_per_call(alpha, 4)) < 1e-12
+
+
+@pytest.mark.parametrize("name,params,shape,V,dtype", [
+    ("compact top-k 50 bf16", dict(temperature=0.7, top_k=50), (16, 7), 50000, "bf16"),
+    ("dense fp32", dict(temperature=1.0), (6, 3), 40000, "f32"),
+    ("top-p 0.9 fp32", dict(temperature=1.0, top_p=0.9), (6, 3), 40000, "f32"),
+    ("top-k 300 lenience 0.3", dict(temperature=0.8, top_k=300, lenience=0.3), (6, 3), 40000,
+     "f32"),
+    ("greedy bf16", dict(temperature=0.0), (8, 4), 32000, "bf16"),
+])
+def test_verify_with_rates_equals_the_two_calls(svm, name, params, shape, V, dtype):
+    _announce(f"spec_verify_rates = spec_verify + spec_acceptance_rate: {name}")
+    B, K = shape
+    t, d = S.zipf_logits(B, K, V, 1.1, 1.0, dtype, seed=76)
+    drafts, u = make_inputs(t, d, params, 76)
+    tc, dc = t.cuda(), d.cuda()
+    x, uu = torch.from_numpy(drafts).cuda(), torch.from_numpy(u).cuda()
+    both = svm.spec_verify(tc, dc, x, uu, want_rates=True, **params)
+    plain = svm.spec_verify(tc, dc, x, uu, **params)
+    rate = svm.spec_acceptance_rate(tc, dc, **params)
+    torch.cuda.synchronize()
+    for k, v in plain.items():
+        np.testing.assert_array_equal(both[k].cpu().numpy(), v.cpu().numpy(), err_msg=k)
+    np.testing.assert_array_equal(both["rate"].cpu().numpy(), rate.cpu().numpy())
+    assert both["rate"].shape == (B, K)
