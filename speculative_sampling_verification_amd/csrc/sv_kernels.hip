@@ -198,6 +198,17 @@ __device__ __forceinline__ int draft_row(const Dims& dm, int b, int k) {
   return b * dm.rows_per_seq + dm.K + 1 + k;
 }
 
+// Work item of workgroup b out of n.  Workgroups go to the eight XCDs round-robin (workgroup b
+// to XCD b mod 8); this gives each XCD one contiguous range of items, taken in order, instead
+// of every eighth item (measured: 1-2% less time for k_topk_row and k_topp_cand, but 3% more
+// for k_chunk, which keeps the plain order).  Items past the last
+// multiple of 8 keep their index, so the map is a bijection on [0, n).
+__device__ __forceinline__ int xcd_contiguous(int b, int n) {
+  const int q = n >> 3;
+  if (b >= (q << 3)) return b;
+  return (b & 7) * q + (b >> 3);
+}
+
 // Load this thread's share of one chunk: vector i of thread t covers elements
 // c0 + (t + 256 i) * EPV ... + EPV - 1.  Slots past the row end hold `fill`.
 template <class E, bool VEC>
@@ -279,7 +290,7 @@ template <class E, bool VEC, int MODE, bool HIST = false>
 __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
                                                     const E* __restrict__ drf, Dims dm, Samp sp,
                                                     Workspace ws) {
-  const int bid = blockIdx.x;
+  const int bid = blockIdx.x;  // (the XCD-contiguous order measured slower here)
   const int r = bid / dm.nchunks;
   const int c = bid - r * dm.nchunks;
   const E* row = row_ptr(dm, tgt, drf, r);
@@ -604,7 +615,7 @@ template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tgt,
                                                         const E* __restrict__ drf, Dims dm,
                                                         Samp sp, Workspace ws) {
-  const int bid = blockIdx.x;
+  const int bid = xcd_contiguous((int)blockIdx.x, dm.rows * dm.nchunks);
   const int r = bid / dm.nchunks;
   const int c = bid - r * dm.nchunks;
   const int tid = threadIdx.x;
@@ -1161,8 +1172,9 @@ template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict__ tgt,
                                                             const E* __restrict__ drf, Dims dm,
                                                             Samp sp, Workspace ws) {
-  const int b = blockIdx.x / dm.nchunks;
-  const int c = blockIdx.x - b * dm.nchunks;
+  const int bid = xcd_contiguous((int)blockIdx.x, dm.B * dm.nchunks);
+  const int b = bid / dm.nchunks;
+  const int c = bid - b * dm.nchunks;
   const SeqState st = ws.seq[b];
   if (!st.need_dense) return;
   __shared__ RedScratch red;
@@ -1848,7 +1860,7 @@ template <class E, bool VEC>
 __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt,
                                                        const E* __restrict__ drf, Dims dm,
                                                        Samp sp, Workspace ws) {
-  const int r = blockIdx.x;
+  const int r = xcd_contiguous((int)blockIdx.x, dm.rows);
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   __shared__ RowLds S;
   const E* row = row_ptr(dm, tgt, drf, r);
