@@ -2080,6 +2080,7 @@ template <int CAP>
 struct MentorLds {
   double r[CAP];                // ratios, sorted in decreasing order (-1: no entry)
   double q[CAP], p[CAP];        // by kept-list position
+  double lq[CAP];               // q ln(q / p) by kept-list position (0 where p = 0)
   double qc[CAP + 1], pc[CAP + 1], lc[CAP + 1];  // prefix sums, sorted order
   uint16_t pos[CAP];            // kept-list position of each sorted entry
 };
@@ -2209,10 +2210,13 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   const float zt_x = x_in ? load_logit(trow, x) : -INFINITY;
   const float zd_x = x_in ? load_logit(drow, x) : -INFINITY;
 
-  // fp64 normalisers over the kept sets
+  // fp64 normalisers over the kept sets; the target's terms are kept for q below
   double st = 0.0, sd = 0.0;
-  for (int e = lane; e < n; e += 64)
-    st += exp((double)__uint_as_float(kt[e].y) / T - (double)rt.m / T);
+  for (int e = lane; e < n; e += 64) {
+    const double ex = exp((double)__uint_as_float(kt[e].y) / T - (double)rt.m / T);
+    L.q[e] = ex;
+    st += ex;
+  }
   for (int e = lane; e < rd.nkept; e += 64)
     sd += exp((double)__uint_as_float(kd[e].y) / T - (double)rd.m / T);
   st = wave_reduce(st, [](double a, double c) { return a + c; });
@@ -2245,16 +2249,18 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
     bool sup = false;
     if (e < n) {
       const uint2 v = kt[e];
-      const double q = prob64(__uint_as_float(v.y), rt.m, T, st);
+      const double q = L.q[e] / st;  // = prob64 of the target logit (same exponential)
       const float zd = load_logit(drow, (int)v.x);
       const double p = zd >= rd.thr ? prob64(zd, rd.m, T, sd) : 0.0;
       sup = q > 0.0;
       my_r = !sup ? -1.0 : (p > 0.0 ? q / p : INFINITY);
+      const double lq = sup && p > 0.0 ? q * log(my_r) : 0.0;
       L.q[e] = q;
       L.p[e] = p;
       L.r[e] = my_r;
+      L.lq[e] = lq;
       L.pos[e] = (uint16_t)e;
-      if (sup) klp += p > 0.0 ? q * log(q / p) : INFINITY;
+      if (sup) klp += p > 0.0 ? lq : INFINITY;
     }
     nsup += __popcll(__ballot(sup));
   }
@@ -2269,13 +2275,10 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
 
   // sort (ratio, position) into decreasing ratio order (ties: lower position first)
   if (n <= 64) {
-    // one entry per lane: its rank from the other lanes' ratios, read lane by lane
+    // one entry per lane: its rank from the other entries' ratios (broadcast LDS reads)
+    wave_lds_sync();
     int rank = 0;
-    for (int j = 0; j < n; ++j) {
-      const double rj = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(my_r), j),
-                                         __builtin_amdgcn_readlane(__double2loint(my_r), j));
-      rank += ratio_before(rj, (uint32_t)j, my_r, (uint32_t)lane) ? 1 : 0;
-    }
+    for (int j = 0; j < n; ++j) rank += ratio_before(L.r[j], (uint32_t)j, my_r, (uint32_t)lane);
     wave_lds_sync();
     if (lane < n) {
       L.r[rank] = my_r;
@@ -2315,10 +2318,9 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   double aq = 0.0, ap = 0.0, al = 0.0;
   for (int j = j0; j < j1; ++j) {
     const int e = L.pos[j];
-    const double r = L.r[j];
     aq += L.q[e];
     ap += L.p[e];
-    if (r != INFINITY) al += L.q[e] * log(r);
+    al += L.lq[e];
   }
   double iq = aq, ip = ap, il = al;  // inclusive scans over lanes
 #pragma unroll
@@ -2341,10 +2343,9 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   }
   for (int j = j0; j < j1; ++j) {
     const int e = L.pos[j];
-    const double r = L.r[j];
     cq += L.q[e];
     cp += L.p[e];
-    if (r != INFINITY) cl += L.q[e] * log(r);
+    cl += L.lq[e];
     L.qc[j + 1] = cq;
     L.pc[j + 1] = cp;
     L.lc[j + 1] = cl;
@@ -2354,10 +2355,18 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   for (int c0 = 0; c0 < nsup; c0 += 64)
     ninf += __popcll(__ballot(c0 + lane < nsup && L.r[c0 + lane] == INFINITY));
 
-  // multisection on the grid of 2^-kMentorBisectionSteps: (lo, hi] holds the answer, hi
-  // satisfies the bound (hi = 1 is taken to, as bisection never tests it)
+  // Search on the grid of 2^-kMentorBisectionSteps, in grid units: (LO, HI] holds the answer
+  // and HI satisfies the bound (HI = 1 is taken to, as bisection never tests it).  Each round
+  // evaluates up to 64 grid points inside (LO, HI), one per lane, and keeps HI = the smallest
+  // point that satisfies the bound and LO = the largest point below it that does not (KL
+  // decreases in alpha, so this is the interval bisection would narrow to).  The first round,
+  // and any round without the KL values at both ends, spreads all 64 points evenly; later
+  // rounds spread 16 points evenly (at least a 16-fold cut) and put 48 at a spacing of 1/2048
+  // of the interval around the point where the straight line through the two ends' KL values
+  // meets D, which is where the answer lies once the interval is short.
   const double grid = ldexp(1.0, -kMentorBisectionSteps);
-  double lo = 0.0, hi = 1.0;
+  double LO = 0.0, HI = ldexp(1.0, kMentorBisectionSteps);  // integers, exact in fp64
+  double kl_lo = NAN, kl_hi = NAN;
   // ia and m at the two ends (-1: not known).  Near alpha = 0 every ratio is >= alpha, no q
   // mass is scaled (R = 1 - P[nsup]), so ia and m take their limits there.
   int ia_lo = nsup, m_lo = -1, ia_hi = -1, m_hi = -1;
@@ -2365,35 +2374,80 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
     const double R0 = 1.0 - L.pc[nsup];
     if (R0 > 0.0) m_lo = mentor_m_search(L, nsup, R0);
   }
-  double beta_hi = -1.0;  // beta at hi once a lane has evaluated it
-  while (hi - lo > grid) {
-    const double w = hi - lo;
-    const double step = fmax(w * (1.0 / 64.0), grid);
-    const double pt = lo + (double)(lane + 1) * step;
+  double beta_hi = -1.0;  // beta at HI once a lane has evaluated it
+  while (HI - LO > 1.0) {
+    const double W = HI - LO;
+    // both ends evaluated, KL finite at LO (KL at HI is <= D)
+    const bool interp = kl_lo == kl_lo && kl_hi == kl_hi && kl_lo < INFINITY;
+    double idx;
+    if (!interp || lane < 16) {
+      idx = LO + fmax(floor(W / (interp ? 16.0 : 64.0)), 1.0) * (double)(lane + 1);
+    } else {
+      const double c = LO + floor((kl_lo - D) / (kl_lo - kl_hi) * W);
+      idx = c + fmax(floor(W * (1.0 / 2048.0)), 1.0) * (double)(lane - 40);
+    }
+    const bool inside = idx > LO && idx < HI;
     const bool same = ia_lo >= 0 && ia_lo == ia_hi && m_lo == m_hi;
-    bool ok = true;  // points at or beyond hi
     int ia = -1, m = -1;
-    double bt = -1.0;
-    if (pt < hi) ok = mentor_kl_at(L, nsup, ninf, pt, same ? ia_lo : -1, m_lo, ia, m, bt) <= D;
-    const unsigned long long okm = __ballot(ok);
-    const int f = __ffsll((long long)okm) - 1;  // lane 63's point is hi at the latest
-    const double nhi = lo + (double)(f + 1) * step;
-    const int fp = f > 0 ? f - 1 : 0;
-    const int ia_f = __builtin_amdgcn_readlane(ia, f), m_f = __builtin_amdgcn_readlane(m, f);
-    const int ia_p = __builtin_amdgcn_readlane(ia, fp), m_p = __builtin_amdgcn_readlane(m, fp);
-    if (nhi < hi) {  // lane f's point was evaluated
-      ia_hi = ia_f;
-      m_hi = m_f;
-      beta_hi = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(bt), f),
-                                 __builtin_amdgcn_readlane(__double2loint(bt), f));
+    double bt = -1.0, kl = NAN;
+    if (inside) kl = mentor_kl_at(L, nsup, ninf, idx * grid, same ? ia_lo : -1, m_lo, ia, m, bt);
+    const bool ok = inside && kl <= D;
+    // The points rise with the lane inside each group (lanes 0-63, or 0-15 and 16-63), so the
+    // new ends come from ballots: HI from each group's first satisfying lane, LO from each
+    // group's last failing lane before that (and below the new HI).
+    const unsigned long long okm = __ballot(ok), failm = __ballot(inside && !ok);
+    const unsigned long long groups[2] = {interp ? 0xFFFFull : ~0ull,
+                                          interp ? ~0xFFFFull : 0ull};
+    double nhi = HI;
+    int fh = -1;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const unsigned long long gm = okm & groups[g];
+      if (gm) {
+        const int f = __ffsll((long long)gm) - 1;
+        const double v = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(idx), f),
+                                          __builtin_amdgcn_readlane(__double2loint(idx), f));
+        if (v < nhi) {
+          nhi = v;
+          fh = f;
+        }
+      }
     }
-    if (f > 0) {
-      ia_lo = ia_p;
-      m_lo = m_p;
+    double nlo = LO;
+    int fl = -1;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const unsigned long long okg = okm & groups[g];
+      unsigned long long gm = failm & groups[g];
+      if (okg) gm &= (1ull << (__ffsll((long long)okg) - 1)) - 1ull;  // lanes before the first ok
+      if (gm) {
+        const int l = 63 - __clzll((long long)gm);
+        const double v = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(idx), l),
+                                          __builtin_amdgcn_readlane(__double2loint(idx), l));
+        if (v > nlo && v < nhi) {
+          nlo = v;
+          fl = l;
+        }
+      }
     }
-    lo = lo + (double)f * step;
-    hi = nhi;
+    if (fh >= 0) {  // the lane holding the new HI
+      ia_hi = __builtin_amdgcn_readlane(ia, fh);
+      m_hi = __builtin_amdgcn_readlane(m, fh);
+      beta_hi = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(bt), fh),
+                                 __builtin_amdgcn_readlane(__double2loint(bt), fh));
+      kl_hi = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(kl), fh),
+                               __builtin_amdgcn_readlane(__double2loint(kl), fh));
+    }
+    if (fl >= 0) {  // the lane holding the new LO
+      ia_lo = __builtin_amdgcn_readlane(ia, fl);
+      m_lo = __builtin_amdgcn_readlane(m, fl);
+      kl_lo = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(kl), fl),
+                               __builtin_amdgcn_readlane(__double2loint(kl), fl));
+    }
+    LO = nlo;
+    HI = nhi;
   }
+  const double hi = HI * grid;
   double beta = beta_hi;
   if (beta < 0.0) {  // hi = 1, never evaluated
     int ia, m;
