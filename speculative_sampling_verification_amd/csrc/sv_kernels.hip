@@ -2098,11 +2098,10 @@ __device__ __forceinline__ bool ratio_before(double ra, uint32_t pa, double rb, 
   return ra > rb || (ra == rb && pa < pb);
 }
 
-// m = the first prefix length with Q[m] / (R + P[m]) >= the next ratio (the full support
-// always qualifies); R > 0.
+// m = the first prefix length with Q[m] / (R + P[m]) >= the next ratio, searched in [lo, hi]
+// (hi qualifies: the full support always does); R > 0.
 template <int CAP>
-__device__ int mentor_m_search(const MentorLds<CAP>& L, int nsup, double R) {
-  int lo = 1, hi = nsup;
+__device__ int mentor_m_search(const MentorLds<CAP>& L, int lo, int hi, double R) {
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
     if (L.qc[mid] / (R + L.pc[mid]) >= L.r[mid])
@@ -2114,16 +2113,17 @@ __device__ int mentor_m_search(const MentorLds<CAP>& L, int nsup, double R) {
 }
 
 // KL(q || pi_alpha) of one lane's alpha, from the sorted ratios and prefix sums; beta out.
-// ia and m (-1 when R <= 0, where no prefix is active) are returned for reuse: both are
-// monotone in alpha, so when they agree at the two ends of an interval they hold inside it,
-// and `hint` (ia >= 0) skips the searches.
+// ia and m (-1 when R <= 0, where no prefix is active) are returned for reuse: ia falls and m
+// rises with alpha, so when they agree at the two ends of an interval they hold inside it,
+// and `hint` (ia >= 0) skips the searches; otherwise the searches run between the values at
+// the ends, ia in [ia_min, ia_max] and m in [m_min, m_max].
 template <int CAP>
 __device__ double mentor_kl_at(const MentorLds<CAP>& L, int nsup, int ninf, double alpha,
-                               int hint_ia, int hint_m, int& ia_out, int& m_out,
-                               double& beta) {
+                               int hint_ia, int hint_m, int ia_min, int ia_max, int m_min,
+                               int m_max, int& ia_out, int& m_out, double& beta) {
   int ia = hint_ia;
   if (ia < 0) {  // ia = #{ratio >= alpha}
-    int lo = 0, hi = nsup;
+    int lo = ia_min, hi = ia_max;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
       if (L.r[mid] >= alpha)
@@ -2144,7 +2144,7 @@ __device__ double mentor_kl_at(const MentorLds<CAP>& L, int nsup, int ninf, doub
     return ninf > 0 ? INFINITY : L.lc[ia] + qlo * lna;
   }
   int m = hint_ia >= 0 ? hint_m : -1;
-  if (m < 0) m = mentor_m_search(L, nsup, R);
+  if (m < 0) m = mentor_m_search(L, m_min, m_max, R);
   m_out = m;
   beta = L.qc[m] / (R + L.pc[m]);
   const double lnb = log(beta);
@@ -2372,7 +2372,7 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   int ia_lo = nsup, m_lo = -1, ia_hi = -1, m_hi = -1;
   {
     const double R0 = 1.0 - L.pc[nsup];
-    if (R0 > 0.0) m_lo = mentor_m_search(L, nsup, R0);
+    if (R0 > 0.0) m_lo = mentor_m_search(L, 1, nsup, R0);
   }
   double beta_hi = -1.0;  // beta at HI once a lane has evaluated it
   while (HI - LO > 1.0) {
@@ -2390,7 +2390,14 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
     const bool same = ia_lo >= 0 && ia_lo == ia_hi && m_lo == m_hi;
     int ia = -1, m = -1;
     double bt = -1.0, kl = NAN;
-    if (inside) kl = mentor_kl_at(L, nsup, ninf, idx * grid, same ? ia_lo : -1, m_lo, ia, m, bt);
+    // ia between its values at HI and LO; m between those at LO and HI where known
+    int ia_min = ia_hi >= 0 ? ia_hi : 0, ia_max = ia_lo >= 0 ? ia_lo : nsup;
+    int m_min = m_lo >= 1 ? m_lo : 1, m_max = m_hi >= 1 ? m_hi : nsup;
+    if (ia_min > ia_max) ia_min = 0, ia_max = nsup;  // (rounding at the ends: search it all)
+    if (m_min > m_max) m_min = 1, m_max = nsup;
+    if (inside)
+      kl = mentor_kl_at(L, nsup, ninf, idx * grid, same ? ia_lo : -1, m_lo, ia_min, ia_max,
+                        m_min, m_max, ia, m, bt);
     const bool ok = inside && kl <= D;
     // The points rise with the lane inside each group (lanes 0-63, or 0-15 and 16-63), so the
     // new ends come from ballots: HI from each group's first satisfying lane, LO from each
@@ -2451,7 +2458,7 @@ __device__ void mentor_solve_wave(const E* __restrict__ tgt, const E* __restrict
   double beta = beta_hi;
   if (beta < 0.0) {  // hi = 1, never evaluated
     int ia, m;
-    (void)mentor_kl_at(L, nsup, ninf, hi, -1, -1, ia, m, beta);
+    (void)mentor_kl_at(L, nsup, ninf, hi, -1, -1, 0, nsup, 1, nsup, ia, m, beta);
   }
   sol.alpha = hi;
   sol.beta = beta;
