@@ -94,6 +94,11 @@ bool make_dims(int B, int K, int V, int draft_rows, sv_dtype dt, Dims* d) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Logit pointers must be aligned to their element size (any 16-byte phase is handled).
+bool elem_aligned(const void* p, sv_dtype dt) {
+  return p == nullptr || (reinterpret_cast<uintptr_t>(p) % esize(dt)) == 0;
+}
+
 }  // namespace
 
 size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
@@ -155,6 +160,8 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
   if (!make_dims(B, K, V, K > 0 ? draft_rows : 0, dtype, &d)) return SV_ERR_INVALID_ARG;
   if (!target || !uniforms || !out_tokens) return SV_ERR_INVALID_ARG;
   if (K > 0 && (!draft || !drafts)) return SV_ERR_INVALID_ARG;
+  if (!elem_aligned(target, dtype) || (K > 0 && !elem_aligned(draft, dtype)))
+    return SV_ERR_INVALID_ARG;
   if (events && n_events < 2) return SV_ERR_INVALID_ARG;
   const Samp s = make_samp(params, V);
   const size_t need = layout_verify(d, s, nullptr, nullptr);
@@ -252,6 +259,7 @@ int tree_impl(const void* target_logits, sv_dtype dtype, int B, int N, int V,
   if ((long long)B * N > INT_MAX) return SV_ERR_INVALID_ARG;
   if (!target_logits || !parent || !node_tokens || !out_tokens || !out_num_accepted)
     return SV_ERR_INVALID_ARG;
+  if (!elem_aligned(target_logits, dtype)) return SV_ERR_INVALID_ARG;
   Dims d{};
   if (!make_dims(B * N, 0, V, 0, dtype, &d)) return SV_ERR_INVALID_ARG;
   const size_t need = layout_tree(d, nullptr, nullptr);
@@ -297,6 +305,8 @@ int spec_acceptance_rate(const void* target_logits, const void* draft_logits, sv
   if (!valid_params(params) || params->mentor_kl != 0.0f) return SV_ERR_INVALID_ARG;
   if (K < 1 || (draft_rows != K && draft_rows != K + 1)) return SV_ERR_INVALID_ARG;
   if (!target_logits || !draft_logits || !out_beta) return SV_ERR_INVALID_ARG;
+  if (!elem_aligned(target_logits, dtype) || !elem_aligned(draft_logits, dtype))
+    return SV_ERR_INVALID_ARG;
   Dims d{};
   if (!make_dims(B, K, V, draft_rows, dtype, &d)) return SV_ERR_INVALID_ARG;
   const Samp s = make_samp(params, V);

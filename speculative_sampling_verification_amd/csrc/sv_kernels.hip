@@ -43,7 +43,6 @@ struct Tr<uint16_t> {
   static constexpr uint32_t kKeyPos0 = 0x8000u;
   static constexpr uint32_t kKeyNeg0 = 0x7FFFu;
   static constexpr uint32_t kNegInfPair = 0xFF80FF80u;  // two -inf
-  static constexpr uint32_t kKey0Pair = 0xFFFFFFFFu;    // bits whose keys are 0 (never kept)
 
   __device__ static float elem(uint32_t w, int h) {
     return __uint_as_float(h ? (w & 0xFFFF0000u) : (w << 16));
@@ -84,7 +83,6 @@ struct Tr<float> {
   static constexpr uint32_t kKeyPos0 = 0x80000000u;
   static constexpr uint32_t kKeyNeg0 = 0x7FFFFFFFu;
   static constexpr uint32_t kNegInfPair = 0xFF800000u;
-  static constexpr uint32_t kKey0Pair = 0xFFFFFFFFu;
 
   __device__ static float elem(uint32_t w, int) { return __uint_as_float(w); }
   __device__ static uint32_t bits_of(float v) { return __float_as_uint(v); }
@@ -168,14 +166,6 @@ __device__ int block_max_i(int v, RedScratch& s) {
   int a = s.i[0] > s.i[1] ? s.i[0] : s.i[1];
   int b = s.i[2] > s.i[3] ? s.i[2] : s.i[3];
   return a > b ? a : b;
-}
-
-__device__ int block_sum_i(int v, RedScratch& s) {
-  v = wave_reduce(v, [](int a, int b) { return a + b; });
-  __syncthreads();
-  if (lane_id() == 0) s.i[wave_id()] = v;
-  __syncthreads();
-  return s.i[0] + s.i[1] + s.i[2] + s.i[3];
 }
 
 // ------------------------------------------------------------------------------------------
@@ -417,15 +407,21 @@ __device__ double dense_sum(const E* row, int V, float m, float it, float thr, R
 // canonical keys, restricted to keys >= lower.  MASS: weight = exp((z - m) / T) in 2^-40 fixed
 // point (integer atomics, deterministic), target = ceil(P * total); else weight 1, target = k.
 // Digits of D bits, most significant first (the last one may be narrower); s_bins holds 2^D.
+// Scratch of radix_select, one copy per kernel whatever the instantiations it uses.
+__shared__ unsigned long long g_radix_tot[kThreads];
+__shared__ unsigned long long g_radix_target, g_radix_above;
+__shared__ uint32_t g_radix_prefix;
+
 template <class E, bool VEC, bool MASS, int D = (Tr<E>::kKeyBits == 16 ? 8 : 11)>
 __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_t lower,
-                                 double P_or_k, unsigned long long* s_bins, RedScratch& red) {
+                                 double P_or_k, unsigned long long* s_bins) {
   constexpr int KB = Tr<E>::kKeyBits;
   constexpr int NLEV = (KB + D - 1) / D;
   const int tid = threadIdx.x;
-  __shared__ unsigned long long s_tot[kThreads];
-  __shared__ unsigned long long s_target, s_above;
-  __shared__ uint32_t s_prefix;
+  unsigned long long* s_tot = g_radix_tot;
+  unsigned long long& s_target = g_radix_target;
+  unsigned long long& s_above = g_radix_above;
+  uint32_t& s_prefix = g_radix_prefix;
   if (tid == 0) {
     s_above = 0;
     s_prefix = 0;
@@ -784,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void k_topp_select(const E* __restrict__ 
     __syncthreads();
     const E* row = row_ptr(dm, tgt, drf, r);
     const uint32_t key =
-        radix_select<E, VEC, true>(row, dm.V, m, it, 0u, (double)sp.top_p, s_buf, red);
+        radix_select<E, VEC, true>(row, dm.V, m, it, 0u, (double)sp.top_p, s_buf);
     thr = Tr<E>::key_to_float(key);
     Skept = dense_sum<E, VEC>(row, dm.V, m, it, thr, red);
   }
@@ -878,10 +874,10 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
   // Whole-row path: exact selections by re-reading the row.
   const bool topk_on = sp.top_k > 0 && sp.top_k < dm.V;
   if (topk_on)
-    lower_key = radix_select<E, VEC, false>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins, red);
+    lower_key = radix_select<E, VEC, false>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins);
   if (sp.top_p < 1.0f)
     lower_key =
-        radix_select<E, VEC, true>(row, dm.V, m, it, lower_key, (double)sp.top_p, s_bins, red);
+        radix_select<E, VEC, true>(row, dm.V, m, it, lower_key, (double)sp.top_p, s_bins);
   const bool trunc = topk_on || sp.top_p < 1.0f;
   const float thr = (trunc && lower_key) ? Tr<E>::key_to_float(lower_key) : -INFINITY;
   double S = trunc ? dense_sum<E, VEC>(row, dm.V, m, it, thr, red) : s_S;
@@ -1595,29 +1591,23 @@ __device__ __forceinline__ uint32_t reg_select(const uint32_t (&r)[kRegs], int j
   return sel_tree<kRegs>(r, 0, m);
 }
 
-// One register tile of a row for the top-k stream.  With VEC, raw buffer loads whose range
-// check returns 0 past the end of the row (so no register is rewritten after the loads); the
-// raw path treats such a 0 (+0.0) as below every positive tau, and tile_keys maps those slots
-// to key 0.  Without VEC, element loads with all-ones bits (key 0, and -1 read as signed) past
-// the end.
-template <class E, bool VEC>
-__device__ __forceinline__ void load_tile(const E* __restrict__ row, int V, int c0, int clen,
+// One register tile of the 16-byte aligned part of a row for the top-k stream: raw buffer loads
+// over [c0, c0 + clen) whose range check returns 0 past its end (clen <= 0: nothing is read),
+// so no register is rewritten after the loads; the raw path treats such a 0 (+0.0) as below
+// every positive tau, and tile_key maps those slots to key 0.
+template <class E>
+__device__ __forceinline__ void load_tile(const E* __restrict__ row, int c0, int clen,
                                           uint32_t (&regs)[kRegs]) {
-  if constexpr (VEC) {
-    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<E*>(row + c0), (short)0, clen * (int)sizeof(E), 0x00020000);
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<E*>(row + c0), (short)0, (clen > 0 ? clen : 0) * (int)sizeof(E), 0x00020000);
 #pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, threadIdx.x * 16,
-                                                         i * kThreads * 16, 2);
-      regs[4 * i + 0] = x.x;
-      regs[4 * i + 1] = x.y;
-      regs[4 * i + 2] = x.z;
-      regs[4 * i + 3] = x.w;
-    }
-  } else {
-    load_chunk<E, false>(row, V, c0, clen, regs, Tr<E>::kKey0Pair);
+  for (int i = 0; i < kVecPerThread; ++i) {
+    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, threadIdx.x * 16, i * kThreads * 16, 2);
+    regs[4 * i + 0] = x.x;
+    regs[4 * i + 1] = x.y;
+    regs[4 * i + 2] = x.z;
+    regs[4 * i + 3] = x.w;
   }
 }
 
@@ -1629,18 +1619,17 @@ __device__ __forceinline__ uint32_t tile_key(const uint32_t (&regs)[kRegs], int 
   return lane_select(valid[j >> 2], 0u, Tr<E>::keys_of_dword(regs[j]));
 }
 
-template <class E, bool VEC>
+template <class E>
 __device__ __forceinline__ void tile_valid(int clen, unsigned long long (&valid)[kVecPerThread]) {
-  const int nvec = clen / Tr<E>::kEpv;  // clen is a multiple of the vector width with VEC
+  const int nvec = clen / Tr<E>::kEpv;  // clen is a multiple of the vector width (or <= 0)
 #pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i)
-    valid[i] = __ballot(!VEC || (int)threadIdx.x + kThreads * i < nvec);
+  for (int i = 0; i < kVecPerThread; ++i) valid[i] = __ballot((int)threadIdx.x + kThreads * i < nvec);
 }
 
 // Candidates of one tile (raw bits in regs) into the wave's list.  KEYS: compare order-preserving
 // keys; otherwise compare raw bits, which is valid only while tau is a positive value (an element is >= tau
 // exactly when its bits, read as a signed integer, are >= the bits of tau; slots past the row
-// end read as 0 or -1, below the bits of any positive tau).  First a per-lane mask of the registers holding a
+// end read as 0, below the bits of any positive tau).  First a per-lane mask of the registers holding a
 // candidate, without branches; then one pass per candidate register of the busiest lane, each
 // lane taking its lowest remaining register.
 template <class E, bool KEYS>
@@ -1831,10 +1820,9 @@ __device__ void row_merge_block(const E* __restrict__ row, const Dims& dm, const
   row_foreach<E, VEC>(row, dm.V, [&](int, float z, uint32_t) { mx = fmaxf(mx, z); });
   const float m = block_max_f(mx, red);
   const float it = sp.inv_t;
-  uint32_t key = radix_select<E, VEC, false, 8>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins,
-                                                 red);
+  uint32_t key = radix_select<E, VEC, false, 8>(row, dm.V, m, it, 0u, (double)sp.top_k, s_bins);
   if (sp.top_p < 1.0f)
-    key = radix_select<E, VEC, true, 8>(row, dm.V, m, it, key, (double)sp.top_p, s_bins, red);
+    key = radix_select<E, VEC, true, 8>(row, dm.V, m, it, key, (double)sp.top_p, s_bins);
   const float thr = Tr<E>::key_to_float(key);
   const double S = dense_sum<E, VEC>(row, dm.V, m, it, thr, red);
   if (threadIdx.x == 0) {
@@ -1850,30 +1838,42 @@ __device__ void row_merge_block(const E* __restrict__ row, const Dims& dm, const
   }
 }
 
-// One workgroup per row, the row streamed in register tiles.  Tile 0 sets tau = the k-th
-// largest of the 256 per-thread maxima (at most the tile's k-th largest, so at most the row's);
-// every tile appends its elements >= tau to the wave's list, and a wave raises tau to its own
-// list's k-th largest whenever the list grows long.  No barrier after tile 0.  At the end one
-// wave selects the row's k-th largest among the candidates (the row's top-k set, ties
-// included, is among them).
-template <class E, bool VEC>
+// One workgroup per row, the row streamed in register tiles of 16-byte vectors.  A row need not
+// start on a 16-byte boundary (e.g. an odd bf16 vocabulary): the vectors cover the aligned
+// interior [h, h + nin) of the row, and the at most 2 (EPV - 1) elements before and after it
+// (the fringe) are loaded one by one and appended to wave 0's list whatever their value.
+// Tile 0 sets tau = the k-th largest of the 256 per-thread maxima (at most the tile's k-th
+// largest, so at most the row's); every tile appends its elements >= tau to the wave's list,
+// and a wave raises tau to its own list's k-th largest whenever the list grows long.  No
+// barrier after tile 0.  At the end one wave selects the row's k-th largest among the
+// candidates (the row's top-k set, ties included, is among them).
+template <class E>
 __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt,
                                                        const E* __restrict__ drf, Dims dm,
                                                        Samp sp, Workspace ws) {
+  constexpr int EPV = Tr<E>::kEpv;
   const int r = xcd_contiguous((int)blockIdx.x, dm.rows);
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   __shared__ RowLds S;
   const E* row = row_ptr(dm, tgt, drf, r);
+  const int V = dm.V;
+  // elements before the first 16-byte boundary, the aligned interior, where the tail starts
+  const int h = min(V, (int)(((16u - ((uint32_t)reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) /
+                             sizeof(E)));
+  const int nin = (V - h) / EPV * EPV;
+  const int tail = h + nin;
+  const E* inner = row + h;
+  const int ntiles = max(1, (nin + dm.chunk_elems - 1) / dm.chunk_elems);
   const int k = sp.top_k;
   const int raise_at = k + 128;  // a pass pushes at most 128, so lists stay within the cap
   WaveList L{wv, 0, 0, 0u};
-  for (int c = 0; c < dm.nchunks; ++c) {
+  for (int c = 0; c < ntiles; ++c) {
     const int c0 = c * dm.chunk_elems;
-    const int clen = min(dm.chunk_elems, dm.V - c0);
+    const int clen = min(dm.chunk_elems, nin - c0);
     uint32_t regs[kRegs];
-    load_tile<E, VEC>(row, dm.V, c0, clen, regs);
+    load_tile<E>(inner, c0, clen, regs);
     unsigned long long valid[kVecPerThread];
-    tile_valid<E, VEC>(clen, valid);
+    tile_valid<E>(clen, valid);
     if (c == 0) {
       uint32_t tm = 0;
 #pragma unroll
@@ -1898,12 +1898,19 @@ __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt
       }
       __syncthreads();
       L.tau = S.tau;
-      filter_tile<E, true>(regs, c0, valid, S, L, k, raise_at);
+      filter_tile<E, true>(regs, h + c0, valid, S, L, k, raise_at);
     } else if (L.tau > Tr<E>::kKeyPos0) {
-      filter_tile<E, false>(regs, c0, valid, S, L, k, raise_at);
+      filter_tile<E, false>(regs, h + c0, valid, S, L, k, raise_at);
     } else {
-      filter_tile<E, true>(regs, c0, valid, S, L, k, raise_at);
+      filter_tile<E, true>(regs, h + c0, valid, S, L, k, raise_at);
     }
+  }
+  if (wv == 0 && nin < V) {  // the fringe, one element per lane
+    if (L.count > raise_at) wl_raise<E>(S, L, k);
+    const int f = lane < h ? lane : tail + (lane - h);
+    uint32_t key = 0u;
+    if (lane < V - nin) key = Tr<E>::key_of_bits(Tr<E>::bits_of(row[f]));
+    wl_push(S, L, key != 0u, (uint32_t)f, Tr<E>::canon(key), false, 0u, 0u);
   }
   if (lane == 0) {
     S.cnt[wv] = L.count < kWaveListCap ? L.count : kWaveListCap;
@@ -1916,9 +1923,13 @@ __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt
     if (lane == 0) S.fallback = fb;
   }
   __syncthreads();
-  if (S.fallback)
-    row_merge_block<E, VEC>(row, dm, sp, r, ws,
-                            reinterpret_cast<unsigned long long*>(&S.key[0][0]), S.red);
+  if (S.fallback) {
+    unsigned long long* bins = reinterpret_cast<unsigned long long*>(&S.key[0][0]);
+    if (nin == V)  // the whole row is 16-byte aligned
+      row_merge_block<E, true>(row, dm, sp, r, ws, bins, S.red);
+    else
+      row_merge_block<E, false>(row, dm, sp, r, ws, bins, S.red);
+  }
 }
 
 // Inverse-CDF pick over weights staged in LDS by one wave (s_idx / s_w, nk entries, total W):
@@ -2842,8 +2853,7 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
   const unsigned grid_chunks = (unsigned)((size_t)dm.rows * dm.nchunks);
   const Outs o{drafts, uni, out_tokens, out_n, out_a, out_q, out_p};
   if (sp.compact) {
-    hipLaunchKernelGGL((k_topk_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
-                       ws);
+    hipLaunchKernelGGL((k_topk_row<E>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
     if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
     if (out_beta) {  // acceptance rates from the row summaries (read-only for the steps below)
       hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm,

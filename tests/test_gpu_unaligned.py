@@ -1,0 +1,101 @@
+"""GPU parity on rows that do not start on a 16-byte boundary: vocabularies whose row length is
+not a multiple of 16 bytes (e.g. V = 50257 in bf16) and logit tensors that begin a few
+elements into their allocation.  The top-k stream loads the aligned interior of each row in
+vectors and the few elements around it one by one; these tests compare it, through the C ABI,
+with the oracle on the same logits (same bar as tests/parity.py).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from workloads import synthetic as S
+
+from parity import (compare_with_draw_flips, make_inputs, oracle_final_weights, run_oracle,
+                    verify_case)
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module")
+def svm():
+    import speculative_sampling_verification_amd as m
+    return m
+
+
+def _offset_copy(x, offset):
+    """A contiguous device copy of x that starts `offset` elements into its allocation."""
+    flat = torch.empty(x.numel() + offset, dtype=x.dtype, device="cuda")
+    view = flat[offset:].view(x.shape)
+    view.copy_(x.cuda())
+    return view
+
+
+def _run(svm, t, d, drafts, u, params):
+    x = torch.from_numpy(np.ascontiguousarray(drafts)).cuda()
+    uu = torch.from_numpy(np.ascontiguousarray(u)).cuda()
+    out = svm.spec_verify(t, d, x, uu, temperature=params["temperature"],
+                          top_k=params.get("top_k", 0), top_p=params.get("top_p", 1.0))
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+@pytest.mark.parametrize("V,dtype,k", [(50257, "bf16", 50), (32001, "bf16", 256),
+                                       (40001, "f32", 40), (1003, "f32", 7)])
+def test_odd_vocabulary(V, dtype, k):
+    _announce(f"unaligned rows: V={V} {dtype} top-k {k}")
+    t, d = S.zipf_logits(8, 3, V, 1.1, 1.0, dtype, seed=V % 97)
+    verify_case(t, d, dict(temperature=0.8, top_k=k), seed=V % 89)
+
+
+@pytest.mark.parametrize("offset", [1, 3, 7])
+def test_tensor_offset_bf16(svm, offset):
+    _announce(f"logit tensors starting {offset} elements into their allocation, bf16 top-k 30")
+    t, d = S.zipf_logits(6, 4, 20000, 1.1, 1.0, "bf16", seed=60 + offset)
+    params = dict(temperature=0.9, top_k=30)
+    drafts, u = make_inputs(t, d, params, 60 + offset)
+    g = _run(svm, _offset_copy(t, offset), _offset_copy(d, offset + 2), drafts, u, params)
+    o = run_oracle(t, d, drafts, u, params)
+    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+
+
+@pytest.mark.parametrize("V,offset", [(5, 3), (9, 1), (17, 6)])
+def test_tiny_rows_all_fringe(svm, V, offset):
+    _announce(f"rows shorter than two vectors: V={V} bf16 offset {offset} top-k 3")
+    t, d = S.normal_logits(5, 3, V, 2.0, 1.0, 0.5, "bf16", seed=70 + V)
+    params = dict(temperature=1.0, top_k=3)
+    drafts, u = make_inputs(t, d, params, 70 + V)
+    g = _run(svm, _offset_copy(t, offset), _offset_copy(d, offset), drafts, u, params)
+    o = run_oracle(t, d, drafts, u, params)
+    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+
+
+def test_tie_overflow_unaligned(svm):
+    _announce("unaligned rows whose top-k ties overflow the lists (whole-row path), V=30001")
+    gen = torch.Generator().manual_seed(80)
+    t = torch.randint(0, 4, (3, 3, 30001), generator=gen).float().to(torch.bfloat16)
+    d = torch.randint(0, 4, (3, 2, 30001), generator=gen).float().to(torch.bfloat16)
+    verify_case(t, d, dict(temperature=1.0, top_k=50), seed=80)
+
+
+def test_sample_matches_verify_bonus_draw_unaligned(svm):
+    _announce("spec_sample on unaligned rows equals the oracle's draw")
+    import oracle.spec_verify_oracle as O
+    R, V = 40, 50257
+    t, _ = S.zipf_logits(R, 0, V, 1.1, 1.0, "bf16", seed=81)
+    rows = t[:, 0].contiguous()
+    u = S.philox_uniforms(82, (R,))
+    g = svm.spec_sample(_offset_copy(rows, 5), torch.from_numpy(u).cuda(), temperature=0.7,
+                        top_k=50).cpu().numpy()
+    o = O.sample_rows(rows.float().numpy(), u, np.float32(0.7), 50, np.float32(1.0))
+    flips = 0
+    for r in range(R):
+        if g[r] != o[r]:
+            q = O.row_distribution(rows[r].float().numpy(), np.float32(0.7), 50, np.float32(1.0))
+            assert O.inverse_cdf_margin(q, float(u[r]), int(g[r])) < 1e-6, r
+            flips += 1
+    assert flips <= 1
