@@ -139,13 +139,19 @@ def sampling(temperature=1.0, top_k=0, top_p=1.0, lenience=1.0, mentor_kl=0.0):
 
 
 _workspaces = {}
+_outgrown = []  # replaced workspaces, kept alive: a captured HIP graph may still use them
 
 
-def workspace(device, nbytes):
-    """A cached uint8 device buffer of at least nbytes (grown on demand, never shrunk)."""
-    key = (device.type, device.index)
+def workspace(device, nbytes, stream=None):
+    """A cached uint8 device buffer of at least nbytes, one per (device, stream): calls that
+    share a workspace must be ordered on one stream.  Grown on demand; a buffer it replaces is
+    never freed, so work already captured in a HIP graph keeps valid memory."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    key = (device.type, device.index, s.cuda_stream)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
+        if buf is not None:
+            _outgrown.append(buf)
         buf = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _workspaces[key] = buf
     return buf
@@ -209,7 +215,7 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
     need = _lib.spec_verify_workspace_size(B, K, V, dt, ctypes.byref(samp))
     if need == 0:
         raise SpecVerifyError("spec_verify_workspace_size", 1)
-    ws = workspace(dev, need)
+    ws = workspace(dev, need, stream)
     args = [_ptr(target_logits), _ptr(draft_logits) if K > 0 else None, dt, B, K, V, draft_rows,
             _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms), ctypes.byref(samp),
             _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out.get("accept_prob")),
@@ -240,7 +246,7 @@ def spec_sample(logits, uniforms, *, temperature=1.0, top_k=0, top_p=1.0, out=No
     need = _lib.spec_sample_workspace_size(R, V, dt, ctypes.byref(samp))
     if need == 0:
         raise SpecVerifyError("spec_sample_workspace_size", 1)
-    ws = workspace(dev, need)
+    ws = workspace(dev, need, stream)
     _check("spec_sample", _lib.spec_sample(_ptr(logits), dt, R, V, _ptr(uniforms),
                                            ctypes.byref(samp), _ptr(out), _ptr(ws), ws.numel(),
                                            _stream(dev, stream)))
@@ -269,7 +275,7 @@ def spec_verify_tree(target_logits, parent, node_tokens, max_depth, *, out=None,
     need = _lib.spec_verify_tree_workspace_size(B, N, V, dt)
     if need == 0:
         raise SpecVerifyError("spec_verify_tree_workspace_size", 1)
-    ws = workspace(dev, need)
+    ws = workspace(dev, need, stream)
     args = (_ptr(target_logits), dt, B, N, V, _ptr(parent), _ptr(node_tokens), int(max_depth),
             _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out["last_node"]), _ptr(ws),
             ws.numel(), _stream(dev, stream))
@@ -341,7 +347,7 @@ def spec_acceptance_rate(target_logits, draft_logits, *, temperature=1.0, top_k=
     need = _lib.spec_verify_workspace_size(B, K, V, dt, ctypes.byref(samp))
     if need == 0:
         raise SpecVerifyError("spec_verify_workspace_size", 1)
-    ws = workspace(dev, need)
+    ws = workspace(dev, need, stream)
     _check("spec_acceptance_rate", _lib.spec_acceptance_rate(
         _ptr(target_logits), _ptr(draft_logits), dt, B, K, V, draft_logits.shape[1],
         ctypes.byref(samp), _ptr(out), _ptr(ws), ws.numel(), _stream(dev, stream)))

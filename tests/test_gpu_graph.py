@@ -149,3 +149,53 @@ def test_spec_sample_graph_replays(svm):
         torch.cuda.synchronize()
         np.testing.assert_array_equal(got.cpu().numpy(), ref.cpu().numpy(),
                                       err_msg=f"replay {rep}")
+
+
+def test_graph_replay_after_the_workspace_grew(svm):
+    _announce("graph replay after a larger call replaced the stream's cached workspace")
+    shape, V, params = (8, 5), 32000, dict(temperature=0.7, top_k=50)
+    static = [h.cuda() for h in _fresh(700, shape, V, "bf16", "zipf")]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        out = svm.spec_verify(*static, **params)  # allocates side's workspace
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        svm.spec_verify(*static, out=out, **params)
+    # a larger call on the same stream replaces its cached workspace; the replaced buffer must
+    # stay allocated for the graph
+    big = [h.cuda() for h in _fresh(701, (64, 8), 128256, "bf16", "zipf")]
+    with torch.cuda.stream(side):
+        svm.spec_verify(*big, **params)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        _copy_in(static, _fresh(702 + rep, shape, V, "bf16", "zipf"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {k: v.clone() for k, v in out.items()}
+        ref = svm.spec_verify(*static, **params)
+        torch.cuda.synchronize()
+        for k in ref:
+            np.testing.assert_array_equal(got[k].cpu().numpy(), ref[k].cpu().numpy(),
+                                          err_msg=f"replay {rep}: {k}")
+
+
+def test_two_streams_at_once(svm):
+    _announce("spec_verify on two streams at once (one workspace per stream)")
+    params = dict(temperature=0.8, top_k=40)
+    a = [h.cuda() for h in _fresh(800, (32, 6), 50000, "bf16", "zipf")]
+    b = [h.cuda() for h in _fresh(801, (32, 6), 50000, "bf16", "zipf")]
+    ref_a = {k: v.cpu() for k, v in svm.spec_verify(*a, **params).items()}
+    ref_b = {k: v.cpu() for k, v in svm.spec_verify(*b, **params).items()}
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa = svm.spec_verify(*a, **params)
+        with torch.cuda.stream(s2):
+            ob = svm.spec_verify(*b, **params)
+        torch.cuda.synchronize()
+        for k in ref_a:
+            np.testing.assert_array_equal(oa[k].cpu().numpy(), ref_a[k].numpy(), err_msg=k)
+            np.testing.assert_array_equal(ob[k].cpu().numpy(), ref_b[k].numpy(), err_msg=k)
