@@ -37,8 +37,8 @@
  *   - Tensor pointers are caller-owned DEVICE memory, row-major and contiguous along V.
  *     Scalars and sv_sampling are host values.  Logit pointers must be aligned to their
  *     element size (else SV_ERR_INVALID_ARG); rows may start at any such offset and V may be
- *     any size (rows whose start or length is not a multiple of 16 bytes take slower
- *     element-wise loads in the dense and top-p kernels; the top-k kernel is not affected).
+ *     any size (on rows whose start or length is not a multiple of 16 bytes, the final draw of
+ *     dense rows and the dense acceptance rates use element-wise loads).
  *   - The library allocates nothing and never synchronises.  All work is enqueued on
  *     `stream`; outputs are valid once the caller synchronises with that stream.
  *   - Arguments are checked on the host before anything is enqueued; on an error status

@@ -77,7 +77,11 @@ bool make_dims(int B, int K, int V, int draft_rows, sv_dtype dt, Dims* d) {
   const long long rows = (long long)B * rps;
   if (rows > INT_MAX) return false;
   const int ce = chunk_elems_for(dt);
-  const long long nch = ((long long)V + ce - 1) / ce;
+  // chunks of a row counted from the 16-byte boundary at or before its start (the chunked
+  // kernels' frame): up to EPV - 1 more elements than V; set_alignment narrows it to V's
+  // chunks when every row is aligned
+  const int epv = 16 / (int)esize(dt);
+  const long long nch = ((long long)V + epv - 1 + ce - 1) / ce;
   if (rows * nch > (long long)INT_MAX) return false;
   if ((long long)B * nch > (long long)INT_MAX) return false;
   d->B = B;
@@ -93,6 +97,13 @@ bool make_dims(int B, int K, int V, int draft_rows, sv_dtype dt, Dims* d) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Records whether every row starts on a 16-byte boundary (16-byte loads in every kernel) and
+// then counts the chunks of V alone.
+void set_alignment(Dims* d, bool aligned) {
+  d->vec = aligned ? 1 : 0;
+  if (aligned) d->nchunks = (d->V + d->chunk_elems - 1) / d->chunk_elems;
+}
 
 // Logit pointers must be aligned to their element size (any 16-byte phase is handled).
 bool elem_aligned(const void* p, sv_dtype dt) {
@@ -166,8 +177,8 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
   const Samp s = make_samp(params, V);
   const size_t need = layout_verify(d, s, nullptr, nullptr);
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
-  d.vec = ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target) &&
-          (K == 0 || aligned16(draft));
+  set_alignment(&d, ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target) &&
+                        (K == 0 || aligned16(draft)));
   Workspace ws{};
   layout_verify(d, s, workspace, &ws);
   if (!out_n) out_n = ws.nbuf;
@@ -264,7 +275,7 @@ int tree_impl(const void* target_logits, sv_dtype dtype, int B, int N, int V,
   if (!make_dims(B * N, 0, V, 0, dtype, &d)) return SV_ERR_INVALID_ARG;
   const size_t need = layout_tree(d, nullptr, nullptr);
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
-  d.vec = ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target_logits);
+  set_alignment(&d, ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target_logits));
   Workspace ws{};
   layout_tree(d, workspace, &ws);
   // the walk kernel reads B and the node count from Dims
@@ -312,8 +323,8 @@ int spec_acceptance_rate(const void* target_logits, const void* draft_logits, sv
   const Samp s = make_samp(params, V);
   const size_t need = layout_verify(d, s, nullptr, nullptr);
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
-  d.vec = ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target_logits) &&
-          aligned16(draft_logits);
+  set_alignment(&d, ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target_logits) &&
+                        aligned16(draft_logits));
   Workspace ws{};
   layout_verify(d, s, workspace, &ws);
   const hipError_t e = launch_verify(target_logits, draft_logits, dtype, d, s, nullptr, nullptr,

@@ -199,62 +199,66 @@ __device__ __forceinline__ int xcd_contiguous(int b, int n) {
   return (b & 7) * q + (b >> 3);
 }
 
-// Load this thread's share of one chunk: vector i of thread t covers elements
-// c0 + (t + 256 i) * EPV ... + EPV - 1.  Slots past the row end hold `fill`.
-template <class E, bool VEC>
-__device__ __forceinline__ void load_chunk(const E* __restrict__ row, int V, int c0, int clen,
-                                           uint32_t (&regs)[kRegs], uint32_t fill) {
+// Elements of a row before its first 16-byte boundary (the row's 16-byte phase).
+template <class E>
+__device__ __forceinline__ int row_phase(const E* row) {
+  return (int)(((uint32_t)reinterpret_cast<uintptr_t>(row) & 15u) / sizeof(E));
+}
+
+// Load this thread's share of chunk c of a row, the chunks counted from the 16-byte boundary at
+// or before the row start (the row's frame: frame index a holds element a - ph, ph = the row's
+// phase), so that every load is an aligned 16-byte vector: vector i of thread t covers frame
+// indices c*CH + (t + 256 i) * EPV .. + EPV - 1.  The loads are range-checked raw buffer loads
+// over the chunk's part of the frame, rounded up to whole vectors: the first and last vector of a
+// row may take a few bytes of the neighbouring rows (the same 16-byte blocks, never another
+// page); those slots, and slots past the row end, get `fill`.  Returns ph: the element index of
+// slot_index(c0, ...) is then slot_index(c * CH - ph, ...).
+template <class E>
+__device__ __forceinline__ int load_chunk_frame(const E* __restrict__ row, int V, int c, int ce,
+                                                uint32_t (&regs)[kRegs], uint32_t fill) {
   constexpr int EPV = Tr<E>::kEpv;
   const int tid = threadIdx.x;
-  if constexpr (VEC) {
-    // Raw buffer loads over [c0, c0 + clen): one per-lane offset register, the per-vector
-    // offsets in scalar registers, and the hardware range check returns 0 past the end
-    // instead of touching memory.  Logits are read exactly once, so the loads are
-    // non-temporal (cache policy bit 1) and do not displace the small per-row summaries.
-    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<E*>(row + c0), (short)0, clen * (int)sizeof(E), 0x00020000);
-    const int nvec = clen / EPV;  // clen is a multiple of EPV when VEC
+  const int ph = row_phase(row);
+  const int fl = V + ph;  // frame length
+  const int c0 = c * ce;
+  const int flen = max(0, min(ce, fl - c0));
+  const int bytes = min(ce * (int)sizeof(E), (flen * (int)sizeof(E) + 15) & ~15);
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  // Logits are read exactly once, so the loads are non-temporal (cache policy bit 1).
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<E*>(row - ph + c0), (short)0, bytes, 0x00020000);
 #pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, i * kThreads * 16, 2);
-      regs[4 * i + 0] = x.x;
-      regs[4 * i + 1] = x.y;
-      regs[4 * i + 2] = x.z;
-      regs[4 * i + 3] = x.w;
-    }
-    if (nvec < kThreads * kVecPerThread) {  // ragged last tile: slots past the end get `fill`
+  for (int i = 0; i < kVecPerThread; ++i) {
+    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, i * kThreads * 16, 2);
+    regs[4 * i + 0] = x.x;
+    regs[4 * i + 1] = x.y;
+    regs[4 * i + 2] = x.z;
+    regs[4 * i + 3] = x.w;
+  }
+  // slots outside [ph, fl): whole vectors past the end, and the row's first and last vector
 #pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) {
-        if (tid + kThreads * i >= nvec) {
-          regs[4 * i + 0] = fill;
-          regs[4 * i + 1] = fill;
-          regs[4 * i + 2] = fill;
-          regs[4 * i + 3] = fill;
+  for (int i = 0; i < kVecPerThread; ++i) {
+    const int a0 = c0 + (tid + kThreads * i) * EPV;
+    if (a0 >= ph && a0 + EPV <= fl) continue;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      uint32_t w = regs[4 * i + d];
+#pragma unroll
+      for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+        const int a = a0 + d * Tr<E>::kPerDword + h;
+        if (a < ph || a >= fl) {
+          if constexpr (Tr<E>::kPerDword == 2) {
+            const uint32_t m = 0xFFFFu << (16 * h);
+            w = (w & ~m) | (fill & m);
+          } else {
+            w = fill;
+          }
         }
       }
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
-      const int e0 = c0 + (tid + kThreads * i) * EPV;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
-          const int idx = e0 + d * Tr<E>::kPerDword + h;
-          uint32_t bits;
-          if (idx < V)
-            bits = Tr<E>::bits_of(row[idx]);
-          else
-            bits = (Tr<E>::kPerDword == 2) ? (fill & 0xFFFFu) : fill;
-          w |= bits << (16 * h * (Tr<E>::kPerDword == 2));
-        }
-        regs[4 * i + d] = w;
-      }
+      regs[4 * i + d] = w;
     }
   }
+  return ph;
 }
 
 // Element index of slot (vector i, register d, half h) of this thread in chunk starting at c0.
@@ -276,7 +280,7 @@ __device__ __forceinline__ int topp_edge(float z, float it) {
   return (int)f;
 }
 
-template <class E, bool VEC, int MODE, bool HIST = false>
+template <class E, int MODE, bool HIST = false>
 __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
                                                     const E* __restrict__ drf, Dims dm, Samp sp,
                                                     Workspace ws) {
@@ -284,8 +288,6 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
   const int r = bid / dm.nchunks;
   const int c = bid - r * dm.nchunks;
   const E* row = row_ptr(dm, tgt, drf, r);
-  const int c0 = c * dm.chunk_elems;
-  const int clen = min(dm.chunk_elems, dm.V - c0);
   const int tid = threadIdx.x;
   __shared__ RedScratch red;
 
@@ -295,7 +297,9 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
   __shared__ unsigned long long s_hist[HIST ? kHistBins : 1];
   if constexpr (HIST)
     for (int j = tid; j < kHistBins; j += kThreads) s_hist[j] = 0ull;
-  load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kNegInfPair);
+  // element index of the chunk's first slot (negative for a row's first chunk when unaligned)
+  const int c0 = c * dm.chunk_elems -
+                 load_chunk_frame<E>(row, dm.V, c, dm.chunk_elems, regs, Tr<E>::kNegInfPair);
   float mx = -INFINITY;
 #pragma unroll
   for (int j = 0; j < kRegs; ++j) {
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
 #pragma unroll
         for (int h = 0; h < Tr<E>::kPerDword; ++h) {
           const int idx = slot_index<E>(c0, i, d, h);
-          if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx < best) best = idx;
+          if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx >= 0 && idx < best) best = idx;
         }
       }
     }
@@ -607,7 +611,7 @@ __device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPar
 // reserves room in the row's list with one atomic add.
 constexpr int kToppChunkCap = 2048;  // candidates one chunk may gather
 
-template <class E, bool VEC>
+template <class E>
 __global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tgt,
                                                         const E* __restrict__ drf, Dims dm,
                                                         Samp sp, Workspace ws) {
@@ -616,15 +620,14 @@ __global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tg
   const int c = bid - r * dm.nchunks;
   const int tid = threadIdx.x;
   const E* row = row_ptr(dm, tgt, drf, r);
-  const int c0 = c * dm.chunk_elems;
-  const int clen = min(dm.chunk_elems, dm.V - c0);
   const int e_lo = ws.tprow[r].e_lo, e_hi = ws.tprow[r].e_hi;
   const float it = sp.inv_t;
   __shared__ uint2 s_c[kToppChunkCap];
   __shared__ int s_n, s_base;
   if (tid == 0) s_n = 0;
   uint32_t regs[kRegs];
-  load_chunk<E, VEC>(row, dm.V, c0, clen, regs, Tr<E>::kNegInfPair);
+  const int c0 = c * dm.chunk_elems -
+                 load_chunk_frame<E>(row, dm.V, c, dm.chunk_elems, regs, Tr<E>::kNegInfPair);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
@@ -2874,18 +2877,18 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     return hipGetLastError();
   }
   if (sp.greedy)
-    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkArgmax>), dim3(grid_chunks), dim3(kThreads), 0, st,
-                       t, d, dm, sp, ws);
+    hipLaunchKernelGGL((k_chunk<E, kChunkArgmax>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d,
+                       dm, sp, ws);
   else if (sp.topp_hist)
-    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkDense, true>), dim3(grid_chunks), dim3(kThreads), 0,
-                       st, t, d, dm, sp, ws);
-  else
-    hipLaunchKernelGGL((k_chunk<E, VEC, kChunkDense>), dim3(grid_chunks), dim3(kThreads), 0, st,
+    hipLaunchKernelGGL((k_chunk<E, kChunkDense, true>), dim3(grid_chunks), dim3(kThreads), 0, st,
                        t, d, dm, sp, ws);
+  else
+    hipLaunchKernelGGL((k_chunk<E, kChunkDense>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d,
+                       dm, sp, ws);
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
   hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
   if (sp.topp_hist) {
-    hipLaunchKernelGGL((k_topp_cand<E, VEC>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm,
+    hipLaunchKernelGGL((k_topp_cand<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm,
                        sp, ws);
     hipLaunchKernelGGL((k_topp_select<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm,
                        sp, ws);
@@ -2954,20 +2957,12 @@ hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int
   const unsigned grid = (unsigned)((size_t)d.rows * d.nchunks);
   if (dt == SV_DTYPE_BF16) {
     auto t = static_cast<const uint16_t*>(target);
-    if (d.vec)
-      hipLaunchKernelGGL((k_chunk<uint16_t, true, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
-                         stream, t, t, d, sp, ws);
-    else
-      hipLaunchKernelGGL((k_chunk<uint16_t, false, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
-                         stream, t, t, d, sp, ws);
+    hipLaunchKernelGGL((k_chunk<uint16_t, kChunkArgmax>), dim3(grid), dim3(kThreads), 0, stream,
+                       t, t, d, sp, ws);
   } else {
     auto t = static_cast<const float*>(target);
-    if (d.vec)
-      hipLaunchKernelGGL((k_chunk<float, true, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
-                         stream, t, t, d, sp, ws);
-    else
-      hipLaunchKernelGGL((k_chunk<float, false, kChunkArgmax>), dim3(grid), dim3(kThreads), 0,
-                         stream, t, t, d, sp, ws);
+    hipLaunchKernelGGL((k_chunk<float, kChunkArgmax>), dim3(grid), dim3(kThreads), 0, stream, t,
+                       t, d, sp, ws);
   }
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], stream);
   hipLaunchKernelGGL(k_tree_walk, dim3(d.B), dim3(kSeqThreads), 0, stream, d, ws, parent, tokens,

@@ -1,8 +1,9 @@
 """GPU parity on rows that do not start on a 16-byte boundary: vocabularies whose row length is
 not a multiple of 16 bytes (e.g. V = 50257 in bf16) and logit tensors that begin a few
 elements into their allocation.  The top-k stream loads the aligned interior of each row in
-vectors and the few elements around it one by one; these tests compare it, through the C ABI,
-with the oracle on the same logits (same bar as tests/parity.py).
+vectors and the few elements around it one by one; the chunked kernels count their chunks from
+the 16-byte boundary before each row and mask what lies outside it.  These tests compare the
+result, through the C ABI, with the oracle on the same logits (same bar as tests/parity.py).
 """
 
 import numpy as np
@@ -99,3 +100,70 @@ def test_sample_matches_verify_bonus_draw_unaligned(svm):
             assert O.inverse_cdf_margin(q, float(u[r]), int(g[r])) < 1e-6, r
             flips += 1
     assert flips <= 1
+
+
+DENSE_CASES = [
+    ("dense T=1 bf16", dict(temperature=1.0), 50257, "bf16"),
+    ("top-p 0.9 fp32", dict(temperature=1.0, top_p=0.9), 40001, "f32"),
+    ("top-p 0.8 bf16", dict(temperature=0.9, top_p=0.8), 32769, "bf16"),
+    ("top-k 300 + top-p 0.9 fp32", dict(temperature=1.0, top_k=300, top_p=0.9), 20003, "f32"),
+    ("greedy bf16", dict(temperature=0.0), 32001, "bf16"),
+]
+
+
+@pytest.mark.parametrize("name,params,V,dtype", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_paths_odd_vocabulary(name, params, V, dtype):
+    _announce(f"unaligned rows, {name}, V={V}")
+    t, d = S.zipf_logits(6, 3, V, 1.1, 1.0, dtype, seed=V % 101)
+    verify_case(t, d, params, seed=V % 83)
+
+
+@pytest.mark.parametrize("name,params,V,dtype", DENSE_CASES, ids=[c[0] for c in DENSE_CASES])
+def test_dense_paths_tensor_offset(svm, name, params, V, dtype):
+    _announce(f"logit tensors starting inside their allocation, {name}, V={V}")
+    t, d = S.zipf_logits(4, 3, V, 1.1, 1.0, dtype, seed=V % 103)
+    drafts, u = make_inputs(t, d, params, V % 79)
+    g = _run(svm, _offset_copy(t, 3), _offset_copy(d, 1), drafts, u, params)
+    o = run_oracle(t, d, drafts, u, params)
+    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+
+
+def test_tree_unaligned(svm):
+    _announce("greedy tree verify on unaligned rows, V=32001, offset 5")
+    import oracle.spec_verify_oracle as O
+    B, N, V = 4, 24, 32001
+    t, _ = S.normal_logits(B, N - 1, V, 3.0, 0.8, 1.5, "bf16", seed=90)
+    g = torch.Generator().manual_seed(90)
+    parent = torch.full((B, N), -1, dtype=torch.int32)
+    for i in range(1, N):
+        parent[:, i] = torch.randint(0, i, (B,), generator=g, dtype=torch.int32)
+    am = t.float().argmax(dim=2).to(torch.int32)
+    tok = torch.randint(0, V, (B, N), generator=g, dtype=torch.int32)
+    for i in range(1, N):
+        p = parent[:, i].long()
+        tok[:, i] = torch.where(torch.rand(B, generator=g) < 0.7, am[torch.arange(B), p],
+                                tok[:, i])
+    out = svm.spec_verify_tree(_offset_copy(t, 5), parent.cuda(), tok.cuda(), 10)
+    torch.cuda.synchronize()
+    o = O.tree_verify(t.float().numpy(), parent.numpy(), tok.numpy(), 10)
+    np.testing.assert_array_equal(out["num_accepted"].cpu().numpy(), o["n"])
+    np.testing.assert_array_equal(out["tokens"].cpu().numpy(), o["tokens"])
+    np.testing.assert_array_equal(out["last_node"].cpu().numpy(), o["last_node"])
+
+
+def test_acceptance_rate_unaligned(svm):
+    _announce("acceptance rates on unaligned rows, dense fp32 V=40001 and top-k bf16 V=50257")
+    import oracle.spec_verify_oracle as O
+    for V, dtype, params in ((40001, "f32", dict(temperature=1.0)),
+                             (50257, "bf16", dict(temperature=0.7, top_k=50))):
+        t, d = S.zipf_logits(3, 3, V, 1.1, 1.0, dtype, seed=V % 71)
+        beta = svm.spec_acceptance_rate(_offset_copy(t, 1), _offset_copy(d, 2),
+                                        **params).cpu().numpy()
+        tf, df = t.float().numpy(), d.float().numpy()
+        T = np.float32(params["temperature"])
+        k = params.get("top_k", 0)
+        for b in range(3):
+            for j in range(3):
+                q = O.row_distribution(tf[b, j], T, k, np.float32(1.0))
+                p = O.row_distribution(df[b, j], T, k, np.float32(1.0))
+                assert abs(beta[b, j] - O.acceptance_rate(q, p, np.float32(1.0))) <= 1e-5
