@@ -355,7 +355,9 @@ def _analytics(svm, target, draft, kw, K, measured_tokens, step_inputs):
 def bench_pipeline(args, name, cfg):
     """The draft -> verify hand-off with every uniform made on the GPU: a step draws the
     draft tokens from the draft rows (Philox uniforms, spec_sample) and verifies them (Philox
-    uniforms, spec_verify); each step takes fresh counters."""
+    uniforms, spec_verify); each step takes fresh counters.  By default the verify step takes
+    the draft rows' summaries from the sampling call (spec_verify_presampled), so every logit
+    is streamed once; --no-presampled streams the draft rows again in spec_verify."""
     import numpy as np
     import torch
     import speculative_sampling_verification_amd as svm
@@ -372,15 +374,17 @@ def bench_pipeline(args, name, cfg):
     u_v = torch.empty((B, K + 1), dtype=torch.float32, device=dev)
     drafts = torch.empty((B, K), dtype=torch.int32, device=dev)
     out = None
+    presampled = not args.no_presampled
+    summary = svm.sample_summary(B * K, V, draft.dtype, device=dev, **kw) if presampled else None
 
     def step(i):
         nonlocal out
         c = i * (nb_d + nb_v)
         svm.spec_philox_uniform(key, c, B * K, out=u_d)
-        svm.spec_sample(draft.view(B * K, V), u_d, out=drafts.view(B * K), **kw)
+        svm.spec_sample(draft.view(B * K, V), u_d, out=drafts.view(B * K), summary=summary, **kw)
         svm.spec_philox_uniform(key, c + nb_d, B * (K + 1), out=u_v.view(-1))
         out = svm.spec_verify(target, draft, drafts, u_v, out=out, lenience=cfg["lenience"],
-                              **kw)
+                              presampled=summary, **kw)
 
     for i in range(args.warmup):
         step(i)
@@ -391,7 +395,7 @@ def bench_pipeline(args, name, cfg):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    elems = B * (2 * K + 1) * V + B * K * V
+    elems = B * (2 * K + 1) * V + (0 if presampled else B * K * V)
     n = out["num_accepted"].cpu().numpy()
     res = {
         "metric": f"draft sampling + verify with device uniforms: logit elems/s, B={B} K={K} "
@@ -409,7 +413,8 @@ def bench_pipeline(args, name, cfg):
         "data": "synthetic",
         "config": {"workload": name, "B": B, "K": K, "V": V, "temperature": cfg["temperature"],
                    "top_k": cfg["top_k"], "top_p": cfg["top_p"], "lenience": cfg["lenience"],
-                   "pipeline": "philox -> spec_sample(draft rows) -> philox -> spec_verify"},
+                   "pipeline": "philox -> spec_sample(draft rows) -> philox -> " +
+                               ("spec_verify_presampled" if presampled else "spec_verify")},
         "roofline": None,
         "logits_read_per_step": elems,
         "mean_tokens_per_call": float(n.mean() + 1.0),
@@ -445,6 +450,9 @@ def main():
     ap.add_argument("--pipeline", action="store_true",
                     help="time the draft -> verify hand-off with device uniforms instead: "
                          "Philox, draft sampling, Philox, verify")
+    ap.add_argument("--no-presampled", action="store_true",
+                    help="with --pipeline: stream the draft rows again in spec_verify instead of "
+                         "taking their summaries from the sampling call")
     ap.add_argument("--mentor-kl", type=float, default=0.0,
                     help="KL bound D > 0: mentored decoding (top-k workloads)")
     ap.add_argument("--no-probs", action="store_true",

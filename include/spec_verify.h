@@ -127,6 +127,27 @@ int spec_verify_profiled(const void* target_logits, const void* draft_logits, sv
                          hipStream_t stream, hipEvent_t* events, int n_events);
 
 /*
+ * spec_verify for draft rows that spec_sample has already processed.  The draft model draws
+ * each draft token from its processed row (spec_sample); that call leaves in its workspace the
+ * row's summary (maximum, kept-set threshold and normaliser, the kept tokens), which is exactly
+ * what verification needs of the draft row.  With `sample_workspace` holding the workspace of
+ * one spec_sample call on the B*K draft rows, row b*K + k = draft_logits[b, k] (so
+ * draft_rows == K), made with the same dtype, V and sampling parameters and not used by
+ * another call since, only the B*(K+1) target rows are streamed; the draft logits are still
+ * read at single tokens.  Results are identical to spec_verify's.  Needs K >= 1, temperature
+ * > 0 and top_k in 1..256 (mentored decoding included), else SV_ERR_INVALID_ARG;
+ * sample_workspace_bytes >= spec_sample_workspace_size(B*K, V, dtype, params), else
+ * SV_ERR_WORKSPACE_TOO_SMALL.  Other arguments as spec_verify.
+ */
+int spec_verify_presampled(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                           int B, int K, int V, const int32_t* draft_tokens,
+                           const float* uniforms, const sv_sampling* params,
+                           int32_t* out_tokens, int32_t* out_num_accepted,
+                           float* out_accept_prob, float* out_q_draft, float* out_p_draft,
+                           const void* sample_workspace, size_t sample_workspace_bytes,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Draw one token per row from its processed distribution: the draft model's own sampling
  * step (Chen et al. notes, A1: the draft samples its K tokens one at a time).  Identical to
  * spec_verify with K = 0 on each row (the "bonus" draw).

@@ -32,6 +32,7 @@ EXPORTS = [
     "spec_sample_workspace_size", "spec_sample",
     "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_tree_profiled",
     "spec_build_tree", "spec_philox_uniform", "spec_acceptance_rate", "spec_verify_rates",
+    "spec_verify_presampled",
     "spec_expected_tokens",
     "spec_walltime_speedup", "spec_ops_factor", "spec_optimal_gamma",
     "spec_verify_status_string",
@@ -55,6 +56,9 @@ def load(path=LIB_PATH):
     lib.spec_verify_rates.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, psamp, vp, vp, vp,
                                       vp, vp, vp, vp, sz, vp]
     lib.spec_verify_rates.restype = i32
+    lib.spec_verify_presampled.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, psamp, vp, vp, vp,
+                                           vp, vp, vp, sz, vp, sz, vp]
+    lib.spec_verify_presampled.restype = i32
     lib.spec_sample_workspace_size.argtypes = [i32, i32, i32, psamp]
     lib.spec_sample_workspace_size.restype = sz
     lib.spec_sample.argtypes = [vp, i32, i32, i32, vp, psamp, vp, vp, sz, vp]
@@ -164,7 +168,7 @@ def _stream(device, stream):
 
 def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperature=1.0, top_k=0,
                 top_p=1.0, lenience=1.0, mentor_kl=0.0, out=None, want_probs=True,
-                want_rates=False, stream=None, events=None):
+                want_rates=False, presampled=None, stream=None, events=None):
     """Verify-and-resample for a batch (see include/spec_verify.h).
 
     target_logits [B, K+1, V], draft_logits [B, K or K+1, V] (bf16 or fp32, same dtype),
@@ -175,6 +179,9 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
     temperature > 0, top_k in 1..256).
     ``want_rates``: also return rate [B, K], the acceptance rate sum_x min(p, q/l) of each
     position (spec_verify_rates: the same results plus the rates, one pass over the logits).
+    ``presampled``: the ``summary`` buffer of a spec_sample call on draft_logits viewed as
+    [B*K, V] with the same sampling parameters (spec_verify_presampled: the draft rows are not
+    streamed again; same results).
     ``events``: optional list of >= 2 hipEvent_t handles (ints) for per-phase timing.
     """
     dev = target_logits.device
@@ -221,7 +228,16 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
             _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out.get("accept_prob")),
             _ptr(out.get("q_draft")), _ptr(out.get("p_draft")), _ptr(ws), ws.numel(),
             _stream(dev, stream)]
-    if want_rates:
+    if presampled is not None:
+        if want_rates or events is not None:
+            raise ValueError("presampled cannot be combined with want_rates or events")
+        if draft_rows != K:
+            raise ValueError("presampled needs draft_logits [B, K, V]")
+        _need(presampled, "presampled", dev, torch.uint8)
+        _check("spec_verify_presampled", _lib.spec_verify_presampled(
+            args[0], args[1], dt, B, K, V, *args[7:15], _ptr(presampled), presampled.numel(),
+            *args[15:]))
+    elif want_rates:
         _check("spec_verify_rates", _lib.spec_verify_rates(*args[:15], _ptr(out["rate"]),
                                                            *args[15:]))
     elif events is None:
@@ -232,8 +248,23 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
     return out
 
 
-def spec_sample(logits, uniforms, *, temperature=1.0, top_k=0, top_p=1.0, out=None, stream=None):
-    """One token per row of logits [R, V] from its processed distribution; uniforms [R]."""
+def sample_summary(R, V, dtype, *, temperature=1.0, top_k=0, top_p=1.0, device=None):
+    """A device buffer for spec_sample(summary=...) over R rows of V logits of torch dtype
+    ``dtype``: it keeps the rows' summaries for spec_verify(presampled=...)."""
+    dt = _dtype_code(torch.empty(0, dtype=dtype))
+    samp = sampling(temperature, top_k, top_p, 1.0)
+    need = _lib.spec_sample_workspace_size(R, V, dt, ctypes.byref(samp))
+    if need == 0:
+        raise SpecVerifyError("spec_sample_workspace_size", 1)
+    return torch.empty(need, dtype=torch.uint8,
+                       device=device if device is not None else torch.device("cuda"))
+
+
+def spec_sample(logits, uniforms, *, temperature=1.0, top_k=0, top_p=1.0, out=None,
+                summary=None, stream=None):
+    """One token per row of logits [R, V] from its processed distribution; uniforms [R].
+    ``summary``: a buffer from sample_summary; the rows' summaries are kept there (instead of
+    the stream's shared workspace) for a later spec_verify(presampled=summary)."""
     dev = logits.device
     R, V = logits.shape
     _need(logits, "logits", dev)
@@ -246,7 +277,11 @@ def spec_sample(logits, uniforms, *, temperature=1.0, top_k=0, top_p=1.0, out=No
     need = _lib.spec_sample_workspace_size(R, V, dt, ctypes.byref(samp))
     if need == 0:
         raise SpecVerifyError("spec_sample_workspace_size", 1)
-    ws = workspace(dev, need, stream)
+    if summary is not None:
+        _need(summary, "summary", dev, torch.uint8)
+        ws = summary
+    else:
+        ws = workspace(dev, need, stream)
     _check("spec_sample", _lib.spec_sample(_ptr(logits), dt, R, V, _ptr(uniforms),
                                            ctypes.byref(samp), _ptr(out), _ptr(ws), ws.numel(),
                                            _stream(dev, stream)))

@@ -162,7 +162,8 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
                 int draft_rows, const int32_t* drafts, const float* uniforms,
                 const sv_sampling* params, int32_t* out_tokens, int32_t* out_n, float* out_a,
                 float* out_q, float* out_p, float* out_beta, void* workspace,
-                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int n_events) {
+                size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int n_events,
+                const void* sample_ws = nullptr, size_t sample_ws_bytes = 0) {
   if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
   if (!valid_params(params)) return SV_ERR_INVALID_ARG;
   if (K > 0 && draft_rows != K && draft_rows != K + 1) return SV_ERR_INVALID_ARG;
@@ -175,8 +176,18 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
     return SV_ERR_INVALID_ARG;
   if (events && n_events < 2) return SV_ERR_INVALID_ARG;
   const Samp s = make_samp(params, V);
+  // draft rows summarised by an earlier spec_sample over them (rows b*K + k there)
+  if (sample_ws && (K < 1 || draft_rows != K || !s.compact)) return SV_ERR_INVALID_ARG;
   const size_t need = layout_verify(d, s, nullptr, nullptr);
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
+  Workspace ws_s{};
+  if (sample_ws) {
+    Dims ds{};
+    if (!make_dims(B * K, 0, V, 0, dtype, &ds)) return SV_ERR_INVALID_ARG;
+    if (sample_ws_bytes < layout_verify(ds, s, nullptr, nullptr))
+      return SV_ERR_WORKSPACE_TOO_SMALL;
+    layout_verify(ds, s, const_cast<void*>(sample_ws), &ws_s);
+  }
   set_alignment(&d, ((size_t)V * esize(dtype)) % 16 == 0 && aligned16(target) &&
                         (K == 0 || aligned16(draft)));
   Workspace ws{};
@@ -184,7 +195,7 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
   if (!out_n) out_n = ws.nbuf;
   const hipError_t e = launch_verify(target, draft, dtype, d, s, drafts, uniforms, out_tokens,
                                      out_n, out_a, out_q, out_p, out_beta, false, ws, stream,
-                                     events, n_events);
+                                     events, n_events, sample_ws ? &ws_s : nullptr);
   return e == hipSuccess ? SV_OK : SV_ERR_LAUNCH;
 }
 
@@ -210,6 +221,20 @@ int spec_verify(const void* target_logits, const void* draft_logits, sv_dtype dt
                      uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
                      out_q_draft, out_p_draft, nullptr, workspace, workspace_bytes, stream,
                      nullptr, 0);
+}
+
+int spec_verify_presampled(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                           int B, int K, int V, const int32_t* draft_tokens,
+                           const float* uniforms, const sv_sampling* params,
+                           int32_t* out_tokens, int32_t* out_num_accepted,
+                           float* out_accept_prob, float* out_q_draft, float* out_p_draft,
+                           const void* sample_workspace, size_t sample_workspace_bytes,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!out_num_accepted || !sample_workspace) return SV_ERR_INVALID_ARG;
+  return verify_impl(target_logits, draft_logits, dtype, B, K, V, K, draft_tokens, uniforms,
+                     params, out_tokens, out_num_accepted, out_accept_prob, out_q_draft,
+                     out_p_draft, nullptr, workspace, workspace_bytes, stream, nullptr, 0,
+                     sample_workspace, sample_workspace_bytes);
 }
 
 int spec_verify_rates(const void* target_logits, const void* draft_logits, sv_dtype dtype,

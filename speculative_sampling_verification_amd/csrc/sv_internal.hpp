@@ -145,7 +145,8 @@ hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, con
                          const Samp& s, const int32_t* drafts, const float* uniforms,
                          int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
                          float* out_p, float* out_beta, bool rates_only, const Workspace& ws,
-                         hipStream_t stream, hipEvent_t* events, int n_events);
+                         hipStream_t stream, hipEvent_t* events, int n_events,
+                         const Workspace* presampled = nullptr);
 hipError_t launch_philox_uniform(uint64_t key0, uint64_t key1, uint64_t counter, int64_t n,
                                  float* out, hipStream_t stream);
 hipError_t launch_rest_tree(const int32_t* cands, int B, int M, int L, int N, int32_t* parent,

@@ -1853,9 +1853,12 @@ __device__ void row_merge_block(const E* __restrict__ row, const Dims& dm, const
 template <class E>
 __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt,
                                                        const E* __restrict__ drf, Dims dm,
-                                                       Samp sp, Workspace ws) {
+                                                       Samp sp, Workspace ws, int targets_only) {
   constexpr int EPV = Tr<E>::kEpv;
-  const int r = xcd_contiguous((int)blockIdx.x, dm.rows);
+  // targets_only: the grid covers the B (K+1) target rows (the draft rows' summaries are given)
+  const int nr = targets_only ? dm.B * (dm.K + 1) : dm.rows;
+  const int ri = xcd_contiguous((int)blockIdx.x, nr);
+  const int r = targets_only ? target_row(dm, ri / (dm.K + 1), ri % (dm.K + 1)) : ri;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   __shared__ RowLds S;
   const E* row = row_ptr(dm, tgt, drf, r);
@@ -1932,6 +1935,22 @@ __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt
       row_merge_block<E, true>(row, dm, sp, r, ws, bins, S.red);
     else
       row_merge_block<E, false>(row, dm, sp, r, ws, bins, S.red);
+  }
+}
+
+// Row summaries of the draft rows taken from a spec_sample call on them (row b*K + k there):
+// RowStat and, for compact rows, the kept list, into the verify workspace's draft rows.
+__global__ __launch_bounds__(64) void k_take_draft_summaries(Dims dm, Workspace src,
+                                                             Workspace ws) {
+  const int pos = blockIdx.x;  // b * K + k
+  const int b = pos / dm.K, k = pos - b * dm.K;
+  const int dst = draft_row(dm, b, k);
+  const RowStat rs = src.rstat[pos];
+  if (threadIdx.x == 0) ws.rstat[dst] = rs;
+  if (rs.kind == kRowCompact) {
+    const uint2* from = src.kept + (size_t)pos * kKeptCap;
+    uint2* to = ws.kept + (size_t)dst * kKeptCap;
+    for (int e = threadIdx.x; e < rs.nkept; e += 64) to[e] = from[e];
   }
 }
 
@@ -2851,12 +2870,20 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
                            const int32_t* drafts, const float* uni, int32_t* out_tokens,
                            int32_t* out_n, float* out_a, float* out_q, float* out_p,
                            float* out_beta, bool rates_only, const Workspace& ws, hipStream_t st,
-                           hipEvent_t* ev, int nev) {
+                           hipEvent_t* ev, int nev, const Workspace* presampled) {
   if (ev && nev >= 1) (void)hipEventRecord(ev[0], st);
   const unsigned grid_chunks = (unsigned)((size_t)dm.rows * dm.nchunks);
   const Outs o{drafts, uni, out_tokens, out_n, out_a, out_q, out_p};
   if (sp.compact) {
-    hipLaunchKernelGGL((k_topk_row<E>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
+    if (presampled && dm.K > 0) {  // draft rows summarised by spec_sample: stream the targets only
+      hipLaunchKernelGGL(k_take_draft_summaries, dim3(dm.B * dm.K), dim3(64), 0, st, dm,
+                         *presampled, ws);
+      hipLaunchKernelGGL((k_topk_row<E>), dim3(dm.B * (dm.K + 1)), dim3(kThreads), 0, st, t, d,
+                         dm, sp, ws, 1);
+    } else {
+      hipLaunchKernelGGL((k_topk_row<E>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws,
+                         0);
+    }
     if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
     if (out_beta) {  // acceptance rates from the row summaries (read-only for the steps below)
       hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm,
@@ -2924,26 +2951,29 @@ hipError_t launch_verify(const void* target, const void* draft, sv_dtype dt, con
                          const Samp& s, const int32_t* drafts, const float* uniforms,
                          int32_t* out_tokens, int32_t* out_n, float* out_a, float* out_q,
                          float* out_p, float* out_beta, bool rates_only, const Workspace& ws,
-                         hipStream_t stream, hipEvent_t* events, int n_events) {
+                         hipStream_t stream, hipEvent_t* events, int n_events,
+                         const Workspace* presampled) {
   (void)hipGetLastError();  // clear a stale error so the status reflects these launches
   if (dt == SV_DTYPE_BF16) {
     auto t = static_cast<const uint16_t*>(target);
     auto dr = static_cast<const uint16_t*>(draft);
     if (d.vec)
       return launch_verify_t<uint16_t, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
-                                             out_a, out_q, out_p, out_beta, rates_only, ws, stream, events,
-                                             n_events);
+                                             out_a, out_q, out_p, out_beta, rates_only, ws,
+                                             stream, events, n_events, presampled);
     return launch_verify_t<uint16_t, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n,
-                                            out_a, out_q, out_p, out_beta, rates_only, ws, stream, events,
-                                            n_events);
+                                            out_a, out_q, out_p, out_beta, rates_only, ws, stream,
+                                            events, n_events, presampled);
   }
   auto t = static_cast<const float*>(target);
   auto dr = static_cast<const float*>(draft);
   if (d.vec)
     return launch_verify_t<float, true>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
-                                        out_q, out_p, out_beta, rates_only, ws, stream, events, n_events);
+                                        out_q, out_p, out_beta, rates_only, ws, stream, events,
+                                        n_events, presampled);
   return launch_verify_t<float, false>(t, dr, d, s, drafts, uniforms, out_tokens, out_n, out_a,
-                                       out_q, out_p, out_beta, rates_only, ws, stream, events, n_events);
+                                       out_q, out_p, out_beta, rates_only, ws, stream, events,
+                                       n_events, presampled);
 }
 
 hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int32_t* parent,

@@ -190,3 +190,22 @@ def test_python_binding_rejects_bad_tensors(svl):
         svl.spec_verify(t.double(), t, torch.zeros((2, 2), dtype=torch.int32), torch.zeros((2, 3)))
     with pytest.raises((TypeError, ValueError)):
         svl.spec_verify(t, t[:, :2], torch.zeros((2, 2), dtype=torch.int64), torch.zeros((2, 3)))
+
+
+def test_verify_presampled_bad_arguments(svl):
+    INVALID, WS = 1, 3
+    L = svl.lib()
+    dummy = ctypes.c_void_p(4096)  # never dereferenced: every call below fails validation
+
+    def call(K=3, p=None, sws=dummy, swsb=1 << 30, on=dummy):
+        p = p or svl.sampling(0.8, 50, 1.0, 1.0)
+        return L.spec_verify_presampled(dummy, dummy, 1, 2, K, 1000, dummy, dummy,
+                                        ctypes.byref(p), dummy, on, None, None, None, sws, swsb,
+                                        dummy, 0, None)
+    assert call(sws=None) == INVALID
+    assert call(on=None) == INVALID
+    assert call(K=0) == INVALID
+    assert call(p=svl.sampling(1.0, 0, 1.0, 1.0)) == INVALID  # dense rows keep no summary
+    assert call(p=svl.sampling(0.0, 50, 1.0, 1.0)) == INVALID  # greedy
+    assert call(swsb=16) == WS
+    assert call() == WS  # valid arguments but no verify workspace
