@@ -109,7 +109,7 @@ def test_topp_extremes(P, T):
 
 
 # ------------------------------------------------------------------ layouts and edge cases
-def test_unaligned_vocab_scalar_path():
+def test_unaligned_vocab():
     _announce("unaligned rows: bf16 V=50001 top-k 50, fp32 V=1001 dense")
     t, d = S.zipf_logits(3, 2, 50001, 1.1, 1.0, "bf16", seed=12)
     verify_case(t, d, dict(temperature=0.7, top_k=50), seed=12)
