@@ -236,6 +236,8 @@ __device__ __forceinline__ int load_chunk_frame(const E* __restrict__ row, int V
     regs[4 * i + 3] = x.w;
   }
   // slots outside [ph, fl): whole vectors past the end, and the row's first and last vector
+  // (only chunks holding the row's start or end have any)
+  if (c0 >= ph && c0 + ce <= fl) return ph;
 #pragma unroll
   for (int i = 0; i < kVecPerThread; ++i) {
     const int a0 = c0 + (tid + kThreads * i) * EPV;
@@ -351,17 +353,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
       p.pad[0] = etop;
     }
   } else {
+    // slots outside the row hold -inf, so they cannot equal a finite maximum; a chunk with no
+    // finite logit reports its first index (it never wins the row's merge)
     int best = INT_MAX;
+    if (mx > -INFINITY) {
 #pragma unroll
-    for (int i = 0; i < kVecPerThread; ++i) {
+      for (int i = 0; i < kVecPerThread; ++i) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < 4; ++d) {
 #pragma unroll
-        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
-          const int idx = slot_index<E>(c0, i, d, h);
-          if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx >= 0 && idx < best) best = idx;
+          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+            const int idx = slot_index<E>(c0, i, d, h);
+            if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx < best) best = idx;
+          }
         }
       }
+    } else {
+      best = max(c0, 0);
     }
     p.argmax = block_min_i(best, red);
   }
