@@ -81,7 +81,7 @@ def _traffic_from_profiles(kernel, workload):
     return float(fetch.group(1)) + float(write.group(1))
 
 
-def cpu_baseline(name, target, draft, seconds, mentor_kl=0.0):
+def cpu_baseline(name, target, draft, seconds, mentor_kl=0.0, lenience=None):
     """Time the CPU oracle on the same inputs: whole steps (every sequence) repeated until
     `seconds` have passed (at least one step).  Mentored decoding, whose oracle solves every
     position over the full vocabulary, is timed on groups of 4 sequences instead, until the
@@ -89,7 +89,9 @@ def cpu_baseline(name, target, draft, seconds, mentor_kl=0.0):
     import numpy as np
     import oracle.spec_verify_oracle as O
     from workloads import synthetic as S
-    cfg = S.WORKLOADS[name]
+    cfg = dict(S.WORKLOADS[name])
+    if lenience is not None:
+        cfg["lenience"] = lenience
     B, K, V = cfg["B"], cfg["K"], cfg["V"]
     tf = target.float().cpu().numpy()
     df = draft.float().cpu().numpy()
@@ -450,6 +452,8 @@ def main():
     ap.add_argument("--pipeline", action="store_true",
                     help="time the draft -> verify hand-off with device uniforms instead: "
                          "Philox, draft sampling, Philox, verify")
+    ap.add_argument("--lenience", type=float, default=None,
+                    help="override the workload's lenience l (accept iff u < min(1, q/(l p)))")
     ap.add_argument("--no-presampled", action="store_true",
                     help="with --pipeline: stream the draft rows again in spec_verify instead of "
                          "taking their summaries from the sampling call")
@@ -475,7 +479,9 @@ def main():
     from workloads import synthetic as S
 
     name = args.workload or S.METRIC_WORKLOAD
-    cfg = S.WORKLOADS[name]
+    cfg = dict(S.WORKLOADS[name])
+    if args.lenience is not None:
+        cfg["lenience"] = args.lenience
     if cfg["gen"] == "tree":
         bench_tree(args, name, cfg)
         return
@@ -544,10 +550,12 @@ def main():
     a = out["accept_prob"].cpu().numpy() if "accept_prob" in out else None
     mentored = args.mentor_kl > 0
     res = {
-        "metric": METRIC if name == S.METRIC_WORKLOAD and not mentored else
+        "metric": METRIC if (name == S.METRIC_WORKLOAD and not mentored and
+                             cfg["lenience"] == 1.0) else
                   f"verify throughput: logit elems/s + % HBM peak, B={B} K={K} V={V} "
                   f"{cfg['dtype']}" + (f", mentored decoding D={args.mentor_kl}"
-                                       if mentored else ""),
+                                       if mentored else "") +
+                  (f", lenience {cfg['lenience']}" if cfg["lenience"] != 1.0 else ""),
         "value": elems / (ms_per_step * 1e-3),
         "unit": "logit elems/s",
         "n_gpus": 1,
@@ -583,7 +591,7 @@ def main():
                                       (drafts, u))
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(name, target, draft, args.cpu_seconds,
-                                           args.mentor_kl)
+                                           args.mentor_kl, cfg["lenience"])
     print(json.dumps(res), flush=True)
 
 
