@@ -222,9 +222,9 @@ def bench_tree(args, name, cfg):
         "data": "synthetic",
         "config": {"workload": name, "B": B, "N": N, "V": V, "max_depth": D,
                    "planted": cfg["planted"], "input_sets": len(sets)},
-        "roofline": {"bound": "hbm", "kernel": "k_chunk", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": "k_chunk_argmax", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": _traffic_from_profiles("k_chunk", name), "kernel_ms": kern_avg,
+                     "traffic": _traffic_from_profiles("k_chunk_argmax", name), "kernel_ms": kern_avg,
                      "algorithmic_bytes_per_launch": logit_bytes},
         "gpu_event_ms_per_step": float(np.median(step_ms)),
         "ms_per_step_with_phase_events": wall_ev * 1e3 / args.steps,
@@ -544,7 +544,12 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     kern_avg = float(np.mean(kern_ms))
     achieved = logit_bytes / (kern_avg * 1e-3) / 1e9
-    dominant = "k_topk_row" if 0 < cfg["top_k"] <= 256 and cfg["temperature"] > 0 else "k_chunk"
+    if cfg["temperature"] == 0:
+        dominant = "k_chunk_argmax"
+    elif 0 < cfg["top_k"] <= 256:
+        dominant = "k_topk_row"
+    else:
+        dominant = "k_chunk"
     traffic = _traffic_from_profiles(dominant, name)
     n = out["num_accepted"].cpu().numpy()
     a = out["accept_prob"].cpu().numpy() if "accept_prob" in out else None

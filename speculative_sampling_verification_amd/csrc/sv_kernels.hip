@@ -213,14 +213,14 @@ __device__ __forceinline__ int row_phase(const E* row) {
 // row may take a few bytes of the neighbouring rows (the same 16-byte blocks, never another
 // page); those slots, and slots past the row end, get `fill`.  Returns ph: the element index of
 // slot_index(c0, ...) is then slot_index(c * CH - ph, ...).
-template <class E>
-__device__ __forceinline__ int load_chunk_frame(const E* __restrict__ row, int V, int c, int ce,
-                                                uint32_t (&regs)[kRegs], uint32_t fill) {
+// NV vectors per thread over frame indices [c0, c0 + ce) (a whole chunk, or a part of one).
+template <class E, int NV = kVecPerThread>
+__device__ __forceinline__ int load_frame_part(const E* __restrict__ row, int V, int c0, int ce,
+                                               uint32_t (&regs)[4 * NV], uint32_t fill) {
   constexpr int EPV = Tr<E>::kEpv;
   const int tid = threadIdx.x;
   const int ph = row_phase(row);
   const int fl = V + ph;  // frame length
-  const int c0 = c * ce;
   const int flen = max(0, min(ce, fl - c0));
   const int bytes = min(ce * (int)sizeof(E), (flen * (int)sizeof(E) + 15) & ~15);
   typedef unsigned int u4 __attribute__((ext_vector_type(4)));
@@ -228,7 +228,7 @@ __device__ __forceinline__ int load_chunk_frame(const E* __restrict__ row, int V
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<E*>(row - ph + c0), (short)0, bytes, 0x00020000);
 #pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, i * kThreads * 16, 2);
     regs[4 * i + 0] = x.x;
     regs[4 * i + 1] = x.y;
@@ -239,7 +239,7 @@ __device__ __forceinline__ int load_chunk_frame(const E* __restrict__ row, int V
   // (only chunks holding the row's start or end have any)
   if (c0 >= ph && c0 + ce <= fl) return ph;
 #pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int a0 = c0 + (tid + kThreads * i) * EPV;
     if (a0 >= ph && a0 + EPV <= fl) continue;
 #pragma unroll
@@ -261,6 +261,12 @@ __device__ __forceinline__ int load_chunk_frame(const E* __restrict__ row, int V
     }
   }
   return ph;
+}
+
+template <class E>
+__device__ __forceinline__ int load_chunk_frame(const E* __restrict__ row, int V, int c, int ce,
+                                                uint32_t (&regs)[kRegs], uint32_t fill) {
+  return load_frame_part<E>(row, V, c * ce, ce, regs, fill);
 }
 
 // Element index of slot (vector i, register d, half h) of this thread in chunk starting at c0.
@@ -374,6 +380,57 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
     p.argmax = block_min_i(best, red);
   }
   if (tid == 0) *part = p;
+}
+
+// Argmax of one (row, chunk): the chunk's maximum and the lowest index holding it, in one pass
+// over two half-tiles (32 registers per thread, so that more workgroups are resident than with
+// the dense path's whole-tile registers).  A thread visits its slots in increasing index
+// order, so a strict comparison keeps the lowest index of its maximum; slots outside the row
+// hold -inf.  Writes the same ChunkPart as k_chunk's argmax mode.
+template <class E>
+__global__ __launch_bounds__(kThreads) void k_chunk_argmax(const E* __restrict__ tgt,
+                                                           const E* __restrict__ drf, Dims dm,
+                                                           Samp sp, Workspace ws) {
+  constexpr int NV = kVecPerThread / 2;
+  const int r = blockIdx.x / dm.nchunks;
+  const int c = blockIdx.x - r * dm.nchunks;
+  const E* row = row_ptr(dm, tgt, drf, r);
+  const int half = dm.chunk_elems / 2;
+  __shared__ RedScratch red;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+#pragma unroll 1
+  for (int part = 0; part < 2; ++part) {
+    uint32_t regs[4 * NV];
+    const int f0 = c * dm.chunk_elems + part * half;  // frame index of the part's start
+    const int e0 = f0 - load_frame_part<E, NV>(row, dm.V, f0, half, regs, Tr<E>::kNegInfPair);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+          const float z = Tr<E>::elem(regs[4 * i + d], h);
+          if (z > bv) {
+            bv = z;
+            bi = slot_index<E>(e0, i, d, h);
+          }
+        }
+      }
+    }
+  }
+  const float mx = block_max_f(bv, red);
+  int best = block_min_i(bv == mx && mx > -INFINITY ? bi : INT_MAX, red);
+  if (!(mx > -INFINITY)) best = max(c * dm.chunk_elems - row_phase(row), 0);
+  (void)sp;
+  if (threadIdx.x == 0) {
+    ChunkPart p;
+    p.vmax = mx;
+    p.argmax = best;
+    p.sum = 0.0;
+    p.pad[0] = p.pad[1] = p.pad[2] = p.pad[3] = 0;
+    ws.parts[(size_t)r * dm.nchunks + c] = p;
+  }
 }
 
 // ------------------------------------------------------------------------------------------
@@ -2912,8 +2969,8 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     return hipGetLastError();
   }
   if (sp.greedy)
-    hipLaunchKernelGGL((k_chunk<E, kChunkArgmax>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d,
-                       dm, sp, ws);
+    hipLaunchKernelGGL((k_chunk_argmax<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm, sp,
+                       ws);
   else if (sp.topp_hist)
     hipLaunchKernelGGL((k_chunk<E, kChunkDense, true>), dim3(grid_chunks), dim3(kThreads), 0, st,
                        t, d, dm, sp, ws);
@@ -2995,11 +3052,11 @@ hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int
   const unsigned grid = (unsigned)((size_t)d.rows * d.nchunks);
   if (dt == SV_DTYPE_BF16) {
     auto t = static_cast<const uint16_t*>(target);
-    hipLaunchKernelGGL((k_chunk<uint16_t, kChunkArgmax>), dim3(grid), dim3(kThreads), 0, stream,
+    hipLaunchKernelGGL((k_chunk_argmax<uint16_t>), dim3(grid), dim3(kThreads), 0, stream,
                        t, t, d, sp, ws);
   } else {
     auto t = static_cast<const float*>(target);
-    hipLaunchKernelGGL((k_chunk<float, kChunkArgmax>), dim3(grid), dim3(kThreads), 0, stream, t,
+    hipLaunchKernelGGL((k_chunk_argmax<float>), dim3(grid), dim3(kThreads), 0, stream, t,
                        t, d, sp, ws);
   }
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], stream);
