@@ -93,6 +93,11 @@ bool make_dims(int B, int K, int V, int draft_rows, sv_dtype dt, Dims* d) {
   d->chunk_elems = ce;
   d->nchunks = (int)nch;
   d->vec = 0;
+  // the final draw runs one workgroup per (sequence, chunk); when that grid would leave most
+  // of the 256 CUs idle it splits each chunk into its vector rows
+  const int fce = (long long)B * nch < 1024 ? ce / kVecPerThread : ce;
+  d->fchunk_elems = fce;
+  d->nfchunks = (int)(((long long)V + fce - 1) / fce);
   return true;
 }
 
@@ -119,7 +124,8 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const size_t o_rstat = c.take(rows * sizeof(RowStat));
   const size_t o_kept = c.take(s.compact ? rows * kKeptCap * sizeof(uint2) : 0);
   const size_t o_seq = c.take((size_t)d.B * sizeof(SeqState));
-  const size_t o_fpart = c.take(s.greedy ? 0 : (size_t)d.B * nch * sizeof(double2));
+  const size_t o_fpart = c.take(s.greedy ? 0 : (size_t)d.B * d.nfchunks * sizeof(double2));
+  const size_t o_dstat = c.take(s.greedy ? 0 : (size_t)d.B * 2 * sizeof(RowStat));
   const size_t o_n = c.take((size_t)d.B * sizeof(int32_t));
   const bool th = s.topp_hist != 0;
   const size_t o_hist = c.take(th ? rows * nch * kHistBins * sizeof(unsigned long long) : 0);
@@ -133,6 +139,7 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
     ws->kept = s.compact ? at<uint2>(base, o_kept) : nullptr;
     ws->seq = at<SeqState>(base, o_seq);
     ws->fpart = s.greedy ? nullptr : at<double2>(base, o_fpart);
+    ws->dstat = s.greedy ? nullptr : at<RowStat>(base, o_dstat);
     ws->nbuf = at<int32_t>(base, o_n);
     ws->hist = th ? at<unsigned long long>(base, o_hist) : nullptr;
     ws->tprow = th ? at<TopPRow>(base, o_tprow) : nullptr;

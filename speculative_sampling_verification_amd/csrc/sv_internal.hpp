@@ -39,12 +39,9 @@ constexpr int64_t kPhiloxMaxN = (int64_t)1 << 40;  // uniforms per spec_philox_u
 // Row kinds written by k_row.
 enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
 
-// Mode of k_chunk.
-enum ChunkMode : int { kChunkDense = 0, kChunkArgmax = 1 };
-
 struct alignas(16) ChunkPart {
   float vmax;      // largest logit of the chunk
-  int argmax;      // lowest index holding vmax (argmax mode), else -1
+  int argmax;      // lowest index holding vmax (k_chunk_argmax), else -1
   double sum;      // sum of exp((z - vmax) / T) over the chunk (dense mode), else 0
   int pad[4];
 };
@@ -102,6 +99,8 @@ struct Dims {
   int chunk_elems;  // elements per chunk
   int nchunks;      // chunks per row
   int vec;          // 1: 16-byte loads are legal for every row
+  int fchunk_elems; // elements per chunk of the final draw (a chunk, or one vector row of it)
+  int nfchunks;     // final-draw chunks per row, counted from the row's first element
 };
 
 struct Samp {
@@ -124,7 +123,9 @@ struct Workspace {
   RowStat* rstat;    // [rows]
   uint2* kept;       // [rows][kKeptCap]  (index, float bits)      compact only
   SeqState* seq;     // [B]
-  double2* fpart;    // [B][nchunks]  (residual mass, target mass)
+  double2* fpart;    // [B][nfchunks]  (residual mass, target mass)
+  RowStat* dstat;    // [B][2] statistics of the final draw's rows (target; draft, or the
+                     // target again for the bonus draw)
   int32_t* nbuf;     // [B] accepted counts when the caller does not want them
   unsigned long long* hist;  // [rows][nchunks][kHistBins] fixed-point mass   top-p histogram only
   TopPRow* tprow;            // [rows]                                        top-p histogram only

@@ -276,9 +276,10 @@ __device__ __forceinline__ int slot_index(int c0, int i, int d, int h) {
 }
 
 // ------------------------------------------------------------------------------------------
-// k_chunk: one workgroup per (row, chunk).  Reads each logit of the chunk once.
-//   dense : vmax and sum exp((z - vmax) / T) over the chunk
-//   argmax: vmax and the lowest index holding it
+// k_chunk: one workgroup per (row, chunk).  Reads each logit of the chunk once: vmax and
+// sum exp((z - vmax) / T) over the chunk (HIST: and the chunk's top-p mass histogram).
+// ROWSTAT: a row of one chunk with nothing truncated, whose row statistics are the chunk's
+// own; they are written here and the merge over chunks is not launched.
 // ------------------------------------------------------------------------------------------
 // Grid edge of a logit for the top-p mass histogram: floor(8 z / T), clamped so that any finite
 // logit (and -inf) maps to an int.  Every kernel bins with this one function.
@@ -288,7 +289,7 @@ __device__ __forceinline__ int topp_edge(float z, float it) {
   return (int)f;
 }
 
-template <class E, int MODE, bool HIST = false>
+template <class E, bool HIST = false, bool ROWSTAT = false>
 __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
                                                     const E* __restrict__ drf, Dims dm, Samp sp,
                                                     Workspace ws) {
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
   p.argmax = -1;
   p.sum = 0.0;
   p.pad[0] = p.pad[1] = p.pad[2] = p.pad[3] = 0;
-  if constexpr (MODE == kChunkDense) {
+  {
     double s = 0.0;
     const float it = sp.inv_t;
     const int etop = topp_edge(mx, it);
@@ -358,28 +359,21 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
       for (int j = tid; j < kHistBins; j += kThreads) dst[j] = s_hist[j];
       p.pad[0] = etop;
     }
-  } else {
-    // slots outside the row hold -inf, so they cannot equal a finite maximum; a chunk with no
-    // finite logit reports its first index (it never wins the row's merge)
-    int best = INT_MAX;
-    if (mx > -INFINITY) {
-#pragma unroll
-      for (int i = 0; i < kVecPerThread; ++i) {
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-#pragma unroll
-          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
-            const int idx = slot_index<E>(c0, i, d, h);
-            if (Tr<E>::elem(regs[4 * i + d], h) == mx && idx < best) best = idx;
-          }
-        }
-      }
-    } else {
-      best = max(c0, 0);
-    }
-    p.argmax = block_min_i(best, red);
   }
-  if (tid == 0) *part = p;
+  if (tid == 0) {
+    *part = p;
+    if constexpr (ROWSTAT) {  // the row is this one chunk and nothing is truncated
+      RowStat out;
+      out.m = mx;
+      out.thr = -INFINITY;
+      out.S = p.sum;
+      out.argmax = -1;
+      out.nkept = -1;
+      out.kind = kRowDense;
+      out.pad = 0;
+      ws.rstat[r] = out;
+    }
+  }
 }
 
 // Argmax of one (row, chunk): the chunk's maximum and the lowest index holding it, in one pass
@@ -1062,6 +1056,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
   const int n = seq_accept_wave(tgt, drf, dm, sp, ws, o, b);
 
   const RowStat rt = ws.rstat[target_row(dm, b, n)];
+  // the draft row of position n (the target row again for the bonus draw), loaded beside rt
+  const RowStat rd_n = ws.rstat[n < K ? draft_row(dm, b, n) : target_row(dm, b, n)];
   SeqState st;
   st.n = n;
   st.need_dense = 0;
@@ -1122,6 +1118,10 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
   if (lane == 0) {
     if (!st.need_dense) out_tokens[(size_t)b * (K + 1) + n] = tok;
     ws.seq[b] = st;
+    if (st.need_dense) {  // read by the final draw's kernels with the state, in one step
+      ws.dstat[2 * b] = rt;
+      ws.dstat[2 * b + 1] = rd_n;
+    }
   }
 }
 
@@ -1174,11 +1174,13 @@ __device__ __forceinline__ void draw_weights(float zt, float zd, const DrawRows&
   if (g.resid) w = fmaxf(q - kept_exp(zd, g.rd, it) * g.inv_sd, 0.0f);
 }
 
-__device__ __forceinline__ DrawRows draw_rows(const Dims& dm, const Workspace& ws, int b, int n) {
+// From the final draw's row statistics that k_seq stored for sequence b (rt, rd).
+__device__ __forceinline__ DrawRows draw_rows(const Dims& dm, int n, const RowStat& rt,
+                                              const RowStat& rd) {
   DrawRows g;
   g.resid = n < dm.K;
-  g.rt = ws.rstat[target_row(dm, b, n)];
-  g.rd = g.resid ? ws.rstat[draft_row(dm, b, n)] : g.rt;
+  g.rt = rt;
+  g.rd = g.resid ? rd : rt;
   g.inv_st = (float)(1.0 / g.rt.S);
   g.inv_sd = (float)(1.0 / g.rd.S);
   return g;
@@ -1230,30 +1232,36 @@ __device__ __forceinline__ void load_vecs(const E* __restrict__ row, int end, in
 }
 
 // ------------------------------------------------------------------------------------------
-// k_final_partial: grid = B x chunks; mass of the final weights per chunk (residual, target).
+// k_final_partial: grid = B x final chunks; mass of the final weights per chunk (residual,
+// target).  A final chunk is FR vector rows of 256 threads x 16 bytes (FR = kVecPerThread: a
+// whole chunk; FR = 1 when the sequences are few and each chunk is split into its rows).
 // ------------------------------------------------------------------------------------------
-template <class E, bool VEC>
+template <class E, bool VEC, int FR>
 __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict__ tgt,
                                                             const E* __restrict__ drf, Dims dm,
                                                             Samp sp, Workspace ws) {
-  const int bid = xcd_contiguous((int)blockIdx.x, dm.B * dm.nchunks);
-  const int b = bid / dm.nchunks;
-  const int c = bid - b * dm.nchunks;
+  const int bid = xcd_contiguous((int)blockIdx.x, dm.B * dm.nfchunks);
+  const int b = bid / dm.nfchunks;
+  const int c = bid - b * dm.nfchunks;
+  // the state and the rows' statistics in one step (the statistics are stale, and unused,
+  // when the sequence needs no dense draw)
   const SeqState st = ws.seq[b];
+  const RowStat rt = ws.dstat[2 * b], rd = ws.dstat[2 * b + 1];
   if (!st.need_dense) return;
   __shared__ RedScratch red;
   const int n = st.n;
-  const DrawRows g = draw_rows(dm, ws, b, n);
+  const DrawRows g = draw_rows(dm, n, rt, rd);
   const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
   const E* drow = g.resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : trow;
-  const int c0 = c * dm.chunk_elems;
-  const int cend = min(c0 + dm.chunk_elems, dm.V);
+  const int c0 = c * dm.fchunk_elems;
+  const int cend = min(c0 + dm.fchunk_elems, dm.V);
   const float it = sp.inv_t;
   constexpr int EPV = Tr<E>::kEpv;
   // steps of NV vectors per thread of both rows; the next step's loads are issued before a
   // step is summed
-  constexpr int NV = EPV == 8 ? 2 : 4;
-  constexpr int NS = kVecPerThread / NV;
+  constexpr int NV0 = EPV == 8 ? 2 : 4;
+  constexpr int NV = NV0 < FR ? NV0 : FR;
+  constexpr int NS = FR / NV;
   constexpr int STEP = kThreads * NV * EPV;
   double W = 0.0, Q = 0.0;
   auto sum_step = [&](const uint32_t(&xt)[4 * NV], const uint32_t(&xd)[4 * NV], int s) {
@@ -1279,8 +1287,9 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
   uint32_t at[4 * NV], ad[4 * NV], bt[4 * NV], bd[4 * NV];
   load_vecs<E, VEC, NV, true>(trow, cend, c0, at);
   if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, c0, ad);
+  if constexpr (NS == 1) sum_step(at, ad, 0);
 #pragma unroll 1
-  for (int s = 0; s < NS; s += 2) {
+  for (int s = 0; NS > 1 && s < NS; s += 2) {
     load_vecs<E, VEC, NV, true>(trow, cend, c0 + (s + 1) * STEP, bt);
     if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, c0 + (s + 1) * STEP, bd);
     sum_step(at, ad, s);
@@ -1291,7 +1300,7 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
   }
   W = block_sum_d(W, red);
   Q = block_sum_d(Q, red);
-  if (threadIdx.x == 0) ws.fpart[(size_t)b * dm.nchunks + c] = make_double2(W, Q);
+  if (threadIdx.x == 0) ws.fpart[(size_t)b * dm.nfchunks + c] = make_double2(W, Q);
 }
 
 // Exclusive prefix of one double per thread over the workgroup, in thread order (fixed order:
@@ -1312,54 +1321,61 @@ __device__ double block_exclusive_d(double v, double& total, RedScratch& red) {
   return base + (x - v);
 }
 
-// Mass of chunk c: the residual's, or q's.
-__device__ __forceinline__ double chunk_mass(const double2* fp, int c, bool use_q) {
-  return use_q ? fp[c].y : fp[c].x;
-}
 
 // ------------------------------------------------------------------------------------------
-// k_final_pick: grid = B.  Chooses the chunk holding u*W from the chunk totals (scanned in
-// order), then the token inside it in three steps, all in index order: the chunk is loaded as
-// a register tile (thread t, vector i covers elements c0 + (t + 256 i) * EPV ...), so vector
-// row i (all threads' vector i) precedes row i + 1; the row sums locate the vector row, a
-// workgroup scan over the row's vectors locates the vector, and its owner finds the index.
-// With a single chunk the chunk pass is skipped and the totals come from the tile itself.
+// k_final_pick: grid = B.  Chooses the final chunk holding u*W from the chunk totals (scanned
+// in order), then the token inside it in three steps, all in index order: the chunk is loaded
+// as a register tile of NR vector rows (thread t, vector i covers elements
+// c0 + (t + 256 i) * EPV ...), so vector row i (all threads' vector i) precedes row i + 1; the
+// row sums locate the vector row, a workgroup scan over the row's vectors locates the vector,
+// and its owner finds the index.  With a single chunk the chunk pass is skipped and the totals
+// come from the tile itself.
 // ------------------------------------------------------------------------------------------
-template <class E, bool VEC>
+template <class E, bool VEC, int NR>
 __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ tgt,
                                                          const E* __restrict__ drf, Dims dm,
                                                          Samp sp, Workspace ws,
                                                          const float* __restrict__ uni,
                                                          int32_t* __restrict__ out_tokens) {
   const int b = blockIdx.x;
-  const SeqState st = ws.seq[b];
-  if (!st.need_dense) return;
   const int tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   constexpr int EPV = Tr<E>::kEpv;
-  constexpr int NR = kVecPerThread;  // vector rows of a chunk
+  const int K = dm.K;
+  const bool single = dm.nfchunks == 1;
+  // chunk totals: thread t owns chunks [t * per, (t + 1) * per)
+  const double2* fp = ws.fpart + (size_t)b * dm.nfchunks;
+  const int per = (dm.nfchunks + kThreads - 1) / kThreads;
+  const int ca = min(dm.nfchunks, tid * per), cb = min(dm.nfchunks, ca + per);
+  // the state, the rows' statistics, the uniform and the chunk totals in one step (all but
+  // the state are stale, and unused, when the sequence needs no dense draw)
+  const SeqState st = ws.seq[b];
+  const RowStat srt = ws.dstat[2 * b], srd = ws.dstat[2 * b + 1];
+  const double u = (double)uni[(size_t)b * (K + 1) + K];
+  // a thread's first chunk stays in registers (with at most 256 chunks, its only one)
+  const double2 first = !single && ca < cb ? fp[ca] : make_double2(0.0, 0.0);
+  auto mass = [&](int cc, bool q) {
+    const double2 m = cc == ca ? first : fp[cc];
+    return q ? m.y : m.x;
+  };
+  double w_loc = 0.0, q_loc = 0.0;
+  if (!single) {
+    for (int cc = ca; cc < cb; ++cc) {
+      w_loc += mass(cc, false);
+      q_loc += mass(cc, true);
+    }
+  }
+  if (!st.need_dense) return;
   __shared__ RedScratch red;
   __shared__ float s_vw[NR][kThreads], s_vq[NR][kThreads];  // per-vector sums
   __shared__ double s_rw[NR], s_rq[NR];                       // per-row sums
   __shared__ int s_chunk, s_last, s_t, s_tl;
   __shared__ double s_before;
   const int n = st.n;
-  const int K = dm.K;
-  const DrawRows g = draw_rows(dm, ws, b, n);
-  const double u = (double)uni[(size_t)b * (K + 1) + K];
-  const bool single = dm.nchunks == 1;
+  const DrawRows g = draw_rows(dm, n, srt, srd);
   bool use_q = !g.resid;
   double target = 0.0;
   int c = 0;
   if (!single) {
-    const double2* fp = ws.fpart + (size_t)b * dm.nchunks;
-    // chunk totals: thread t owns chunks [t * per, (t + 1) * per)
-    const int per = (dm.nchunks + kThreads - 1) / kThreads;
-    const int ca = min(dm.nchunks, tid * per), cb = min(dm.nchunks, ca + per);
-    double w_loc = 0.0, q_loc = 0.0;
-    for (int cc = ca; cc < cb; ++cc) {
-      w_loc += chunk_mass(fp, cc, false);
-      q_loc += chunk_mass(fp, cc, true);
-    }
     double Wt, Qt;
     double w_ex = block_exclusive_d(w_loc, Wt, red);
     const double q_ex = block_exclusive_d(q_loc, Qt, red);
@@ -1374,7 +1390,7 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
     double cum = w_ex;
     int found = INT_MAX, lastc = -1;
     for (int cc = ca; cc < cb; ++cc) {
-      const double v = chunk_mass(fp, cc, use_q);
+      const double v = mass(cc, use_q);
       if (v > 0.0) lastc = cc;
       if (found == INT_MAX && cum + v > target) found = cc;
       cum += v;
@@ -1385,21 +1401,21 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
     c = s_chunk != INT_MAX ? s_chunk : s_last;
     if (c >= ca && c < cb) {  // the owner of chunk c: the mass before it, as summed above
       double cb4 = w_ex;
-      for (int cc = ca; cc < c; ++cc) cb4 += chunk_mass(fp, cc, use_q);
+      for (int cc = ca; cc < c; ++cc) cb4 += mass(cc, use_q);
       s_before = cb4;
     }
   }
   const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
   const E* drow = g.resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : trow;
-  const int c0 = c * dm.chunk_elems;
-  const int cend = min(c0 + dm.chunk_elems, dm.V);
+  const int c0 = c * dm.fchunk_elems;
+  const int cend = min(c0 + dm.fchunk_elems, dm.V);
   const float it = sp.inv_t;
   // per-vector sums of the chunk
-  constexpr int NV = 4;
+  constexpr int NV = NR < 4 ? NR : 4;
+  uint32_t rt[4 * NV], rd[4 * NV];  // with NR = 1 the whole tile, kept for the last step
 #pragma unroll 1
   for (int s = 0; s < NR / NV; ++s) {
     const int base = c0 + s * kThreads * NV * EPV;
-    uint32_t rt[4 * NV], rd[4 * NV];
     load_vecs<E, VEC, NV, true>(trow, cend, base, rt);
     if (g.resid) load_vecs<E, VEC, NV, true>(drow, cend, base, rd);
 #pragma unroll
@@ -1498,8 +1514,19 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
     if (tt >= 0) {
       const int e = c0 + (tt + kThreads * ri) * EPV;
       float zt[EPV], zd[EPV];
-      load_vec_f<E, VEC>(trow, cend, e, zt);
-      if (g.resid) load_vec_f<E, VEC>(drow, cend, e, zd);
+      if constexpr (NR == 1) {  // this thread's vector of the tile, as summed above
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+#pragma unroll
+          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+            zt[d * Tr<E>::kPerDword + h] = e < cend ? Tr<E>::elem(rt[d], h) : -INFINITY;
+            zd[d * Tr<E>::kPerDword + h] = g.resid ? Tr<E>::elem(rd[d], h) : 0.0f;
+          }
+        }
+      } else {
+        load_vec_f<E, VEC>(trow, cend, e, zt);
+        if (g.resid) load_vec_f<E, VEC>(drow, cend, e, zd);
+      }
       double run = cum + vex;
       int lastpos = -1;
 #pragma unroll
@@ -2939,6 +2966,9 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
   if (ev && nev >= 1) (void)hipEventRecord(ev[0], st);
   const unsigned grid_chunks = (unsigned)((size_t)dm.rows * dm.nchunks);
   const Outs o{drafts, uni, out_tokens, out_n, out_a, out_q, out_p};
+  // rows of one chunk with nothing truncated: k_chunk's partials are the row statistics
+  const bool row_is_chunk = dm.nchunks == 1 && !sp.greedy && !sp.topp_hist &&
+                            !(sp.top_k > 0 && sp.top_k < dm.V) && !(sp.top_p < 1.0f);
   if (sp.compact) {
     if (presampled && dm.K > 0) {  // draft rows summarised by spec_sample: stream the targets only
       hipLaunchKernelGGL(k_take_draft_summaries, dim3(dm.B * dm.K), dim3(64), 0, st, dm,
@@ -2972,13 +3002,17 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_chunk_argmax<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm, sp,
                        ws);
   else if (sp.topp_hist)
-    hipLaunchKernelGGL((k_chunk<E, kChunkDense, true>), dim3(grid_chunks), dim3(kThreads), 0, st,
-                       t, d, dm, sp, ws);
+    hipLaunchKernelGGL((k_chunk<E, true>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm,
+                       sp, ws);
+  else if (row_is_chunk)
+    hipLaunchKernelGGL((k_chunk<E, false, true>), dim3(grid_chunks), dim3(kThreads), 0, st, t,
+                       d, dm, sp, ws);
   else
-    hipLaunchKernelGGL((k_chunk<E, kChunkDense>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d,
-                       dm, sp, ws);
+    hipLaunchKernelGGL((k_chunk<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm, sp,
+                       ws);
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
-  hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
+  if (!row_is_chunk)
+    hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
   if (sp.topp_hist) {
     hipLaunchKernelGGL((k_topp_cand<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm,
                        sp, ws);
@@ -3000,11 +3034,20 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
   }
   hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
   if (!sp.greedy) {
-    if (dm.nchunks > 1)
-      hipLaunchKernelGGL((k_final_partial<E, VEC>), dim3((unsigned)((size_t)dm.B * dm.nchunks)),
-                         dim3(kThreads), 0, st, t, d, dm, sp, ws);
-    hipLaunchKernelGGL((k_final_pick<E, VEC>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm, sp,
-                       ws, uni, out_tokens);
+    const dim3 pgrid((unsigned)((size_t)dm.B * dm.nfchunks));
+    if (dm.fchunk_elems == dm.chunk_elems) {
+      if (dm.nfchunks > 1)
+        hipLaunchKernelGGL((k_final_partial<E, VEC, kVecPerThread>), pgrid, dim3(kThreads), 0,
+                           st, t, d, dm, sp, ws);
+      hipLaunchKernelGGL((k_final_pick<E, VEC, kVecPerThread>), dim3(dm.B), dim3(kThreads), 0,
+                         st, t, d, dm, sp, ws, uni, out_tokens);
+    } else {  // one vector row per final chunk
+      if (dm.nfchunks > 1)
+        hipLaunchKernelGGL((k_final_partial<E, VEC, 1>), pgrid, dim3(kThreads), 0, st, t, d,
+                           dm, sp, ws);
+      hipLaunchKernelGGL((k_final_pick<E, VEC, 1>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm,
+                         sp, ws, uni, out_tokens);
+    }
   }
   if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);
   return hipGetLastError();

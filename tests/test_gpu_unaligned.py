@@ -167,3 +167,25 @@ def test_acceptance_rate_unaligned(svm):
                 q = O.row_distribution(tf[b, j], T, k, np.float32(1.0))
                 p = O.row_distribution(df[b, j], T, k, np.float32(1.0))
                 assert abs(beta[b, j] - O.acceptance_rate(q, p, np.float32(1.0))) <= 1e-5
+
+
+# The final draw runs one workgroup per (sequence, final chunk): a whole chunk of 256 threads x
+# 16 vectors when the sequences are many (B x chunks >= 1024), one vector row of it otherwise.
+FINAL_GRAIN_CASES = [
+    ("whole chunks, unaligned fp32 B=256 V=49153", 256, 49153, "f32", 3),
+    ("whole chunks, unaligned bf16 B=256 V=98305", 256, 98305, "bf16", 1),
+    ("vector rows, unaligned bf16 B=8 V=30001", 8, 30001, "bf16", 5),
+    ("vector rows, unaligned fp32 B=3 V=5000", 3, 5000, "f32", 2),
+]
+
+
+@pytest.mark.parametrize("name,B,V,dtype,offset", FINAL_GRAIN_CASES,
+                         ids=[c[0] for c in FINAL_GRAIN_CASES])
+def test_final_draw_grain(svm, name, B, V, dtype, offset):
+    _announce(f"dense final draw, {name}, offset {offset}")
+    t, d = S.normal_logits(B, 1, V, 3.0, 0.8, 1.5, dtype, seed=V % 107)
+    params = dict(temperature=1.0)
+    drafts, u = make_inputs(t, d, params, V % 61)
+    g = _run(svm, _offset_copy(t, offset), _offset_copy(d, offset + 1), drafts, u, params)
+    o = run_oracle(t, d, drafts, u, params)
+    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
