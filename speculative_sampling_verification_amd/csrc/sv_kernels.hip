@@ -1321,6 +1321,37 @@ __device__ double block_exclusive_d(double v, double& total, RedScratch& red) {
   return base + (x - v);
 }
 
+// The same for two doubles per thread at once (one set of shuffles and barriers): returns the
+// exclusive prefix of a and sets b_ex, and the totals.
+__device__ double block_exclusive_d2(double a, double b, double& a_tot, double& b_tot,
+                                     double& b_ex) {
+  __shared__ double s_w[2][kThreads / 64];
+  double x = a, y = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double xs = __shfl_up(x, o), ys = __shfl_up(y, o);
+    if (lane_id() >= o) {
+      x += xs;
+      y += ys;
+    }
+  }
+  __syncthreads();
+  if (lane_id() == 63) {
+    s_w[0][wave_id()] = x;
+    s_w[1][wave_id()] = y;
+  }
+  __syncthreads();
+  double ba = 0.0, bb = 0.0;
+  for (int w = 0; w < wave_id(); ++w) {
+    ba += s_w[0][w];
+    bb += s_w[1][w];
+  }
+  a_tot = ((s_w[0][0] + s_w[0][1]) + s_w[0][2]) + s_w[0][3];
+  b_tot = ((s_w[1][0] + s_w[1][1]) + s_w[1][2]) + s_w[1][3];
+  b_ex = bb + (y - b);
+  return ba + (x - a);
+}
+
 
 // ------------------------------------------------------------------------------------------
 // k_final_pick: grid = B.  Chooses the final chunk holding u*W from the chunk totals (scanned
@@ -1377,8 +1408,8 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
   int c = 0;
   if (!single) {
     double Wt, Qt;
-    double w_ex = block_exclusive_d(w_loc, Wt, red);
-    const double q_ex = block_exclusive_d(q_loc, Qt, red);
+    double q_ex;
+    double w_ex = block_exclusive_d2(w_loc, q_loc, Wt, Qt, q_ex);
     use_q = !(Wt > 0.0) || !g.resid;
     if (use_q) w_ex = q_ex;
     target = u * (use_q ? Qt : Wt);
@@ -1501,9 +1532,12 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
     s_tl = -1;
   }
   __syncthreads();
-  if (v > 0.0) {
-    atomicMax(&s_tl, tid);
-    if (!clamp && cum + vex + v > target) atomicMin(&s_t, tid);
+  // the last positive vector and the first one past the target: one LDS atomic per wave
+  const unsigned long long pos = __ballot(v > 0.0);
+  const unsigned long long hit = __ballot(v > 0.0 && !clamp && cum + vex + v > target);
+  if (lane == 0) {
+    if (pos) atomicMax(&s_tl, wv * 64 + 63 - __clzll((long long)pos));
+    if (hit) atomicMin(&s_t, wv * 64 + __ffsll((long long)hit) - 1);
   }
   __syncthreads();
   int tt = s_t;
