@@ -93,9 +93,11 @@ bool make_dims(int B, int K, int V, int draft_rows, sv_dtype dt, Dims* d) {
   d->chunk_elems = ce;
   d->nchunks = (int)nch;
   d->vec = 0;
-  // the final draw runs one workgroup per (sequence, chunk); when that grid would leave most
-  // of the 256 CUs idle it splits each chunk into its vector rows
-  const int fce = (long long)B * nch < 1024 ? ce / kVecPerThread : ce;
+  // the final draw runs one workgroup per (sequence, final chunk): one vector row of a chunk
+  // when whole chunks would leave most of the 256 CUs idle, a quarter chunk (several rounds
+  // of short workgroups) up to 64 K workgroups, else whole chunks
+  const long long bn = (long long)B * nch;
+  const int fce = bn < 1024 ? ce / kVecPerThread : bn < 16384 ? ce / 4 : ce;
   d->fchunk_elems = fce;
   d->nfchunks = (int)(((long long)V + fce - 1) / fce);
   return true;

@@ -1234,7 +1234,7 @@ __device__ __forceinline__ void load_vecs(const E* __restrict__ row, int end, in
 // ------------------------------------------------------------------------------------------
 // k_final_partial: grid = B x final chunks; mass of the final weights per chunk (residual,
 // target).  A final chunk is FR vector rows of 256 threads x 16 bytes (FR = kVecPerThread: a
-// whole chunk; FR = 1 when the sequences are few and each chunk is split into its rows).
+// whole chunk; FR = 4 or 1 when the sequences are fewer and each chunk is split).
 // ------------------------------------------------------------------------------------------
 template <class E, bool VEC, int FR>
 __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict__ tgt,
@@ -1443,7 +1443,7 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
   const float it = sp.inv_t;
   // per-vector sums of the chunk
   constexpr int NV = NR < 4 ? NR : 4;
-  uint32_t rt[4 * NV], rd[4 * NV];  // with NR = 1 the whole tile, kept for the last step
+  uint32_t rt[4 * NV], rd[4 * NV];  // with NR <= 4 the whole tile, kept for the last step
 #pragma unroll 1
   for (int s = 0; s < NR / NV; ++s) {
     const int base = c0 + s * kThreads * NV * EPV;
@@ -1548,13 +1548,29 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
     if (tt >= 0) {
       const int e = c0 + (tt + kThreads * ri) * EPV;
       float zt[EPV], zd[EPV];
-      if constexpr (NR == 1) {  // this thread's vector of the tile, as summed above
+      if constexpr (NR == NV) {  // this thread's vector ri of the tile, as summed above
+        uint32_t wt[4], wd[4];
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          wt[d] = rt[d];
+          wd[d] = rd[d];
+        }
+#pragma unroll
+        for (int i = 1; i < NV; ++i) {
+          if (ri == i) {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              wt[d] = rt[4 * i + d];
+              wd[d] = rd[4 * i + d];
+            }
+          }
+        }
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
 #pragma unroll
           for (int h = 0; h < Tr<E>::kPerDword; ++h) {
-            zt[d * Tr<E>::kPerDword + h] = e < cend ? Tr<E>::elem(rt[d], h) : -INFINITY;
-            zd[d * Tr<E>::kPerDword + h] = g.resid ? Tr<E>::elem(rd[d], h) : 0.0f;
+            zt[d * Tr<E>::kPerDword + h] = e < cend ? Tr<E>::elem(wt[d], h) : -INFINITY;
+            zd[d * Tr<E>::kPerDword + h] = g.resid ? Tr<E>::elem(wd[d], h) : 0.0f;
           }
         }
       } else {
@@ -3075,6 +3091,12 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
                            st, t, d, dm, sp, ws);
       hipLaunchKernelGGL((k_final_pick<E, VEC, kVecPerThread>), dim3(dm.B), dim3(kThreads), 0,
                          st, t, d, dm, sp, ws, uni, out_tokens);
+    } else if (dm.fchunk_elems * 4 == dm.chunk_elems) {  // four vector rows per final chunk
+      if (dm.nfchunks > 1)
+        hipLaunchKernelGGL((k_final_partial<E, VEC, 4>), pgrid, dim3(kThreads), 0, st, t, d,
+                           dm, sp, ws);
+      hipLaunchKernelGGL((k_final_pick<E, VEC, 4>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm,
+                         sp, ws, uni, out_tokens);
     } else {  // one vector row per final chunk
       if (dm.nfchunks > 1)
         hipLaunchKernelGGL((k_final_partial<E, VEC, 1>), pgrid, dim3(kThreads), 0, st, t, d,

@@ -169,11 +169,12 @@ def test_acceptance_rate_unaligned(svm):
                 assert abs(beta[b, j] - O.acceptance_rate(q, p, np.float32(1.0))) <= 1e-5
 
 
-# The final draw runs one workgroup per (sequence, final chunk): a whole chunk of 256 threads x
-# 16 vectors when the sequences are many (B x chunks >= 1024), one vector row of it otherwise.
+# The final draw runs one workgroup per (sequence, final chunk): a chunk of 256 threads x 16
+# vectors split into quarters when B x chunks is in [1024, 16384), into its vector rows below
+# that, and whole above it.
 FINAL_GRAIN_CASES = [
-    ("whole chunks, unaligned fp32 B=256 V=49153", 256, 49153, "f32", 3),
-    ("whole chunks, unaligned bf16 B=256 V=98305", 256, 98305, "bf16", 1),
+    ("quarter chunks, unaligned fp32 B=256 V=49153", 256, 49153, "f32", 3),
+    ("quarter chunks, unaligned bf16 B=256 V=98305", 256, 98305, "bf16", 1),
     ("vector rows, unaligned bf16 B=8 V=30001", 8, 30001, "bf16", 5),
     ("vector rows, unaligned fp32 B=3 V=5000", 3, 5000, "f32", 2),
 ]
@@ -189,3 +190,26 @@ def test_final_draw_grain(svm, name, B, V, dtype, offset):
     g = _run(svm, _offset_copy(t, offset), _offset_copy(d, offset + 1), drafts, u, params)
     o = run_oracle(t, d, drafts, u, params)
     compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_final_draw_whole_chunks_many_rows(svm, offset):
+    # 8192 rows of two chunks each: B x chunks = 16384, so the final draw takes whole chunks
+    _announce(f"dense spec_sample, whole final chunks: R=8192 V=16385 fp32, offset {offset}, "
+              "64 sampled rows against the oracle")
+    import oracle.spec_verify_oracle as O
+    R, V = 8192, 16385
+    t, _ = S.normal_logits(R, 0, V, 3.0, 0.8, 1.5, "f32", seed=91 + offset)
+    rows = t[:, 0].contiguous()
+    u = S.philox_uniforms(92 + offset, (R,))
+    dev = _offset_copy(rows, offset) if offset else rows.cuda()
+    g = svm.spec_sample(dev, torch.from_numpy(u).cuda(), temperature=1.0).cpu().numpy()
+    pick = np.random.default_rng(93).choice(R, 64, replace=False)
+    flips = 0
+    for r in pick:
+        o = O.sample_rows(rows[r:r + 1].numpy(), u[r:r + 1], np.float32(1.0), 0, np.float32(1.0))
+        if g[r] != o[0]:
+            q = O.row_distribution(rows[r].numpy(), np.float32(1.0), 0, np.float32(1.0))
+            assert O.inverse_cdf_margin(q, float(u[r]), int(g[r])) < 1e-6, r
+            flips += 1
+    assert flips <= 1
