@@ -459,6 +459,8 @@ def main():
                          "taking their summaries from the sampling call")
     ap.add_argument("--mentor-kl", type=float, default=0.0,
                     help="KL bound D > 0: mentored decoding (top-k workloads)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay timing (graph_ms_per_step)")
     ap.add_argument("--no-probs", action="store_true",
                     help="do not request per-position accept probabilities (mentored decoding "
                          "then solves only the positions its shortcut cannot accept)")
@@ -525,6 +527,21 @@ def main():
         svm.spec_verify(target, draft, drafts, u, out=out, events=evs[i], **kw)
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t0
+    # the same step captured once in a HIP graph and replayed K times: the launch path of a
+    # serving loop that replays its verify step (reported beside `value`, which is eager)
+    graph_ms = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            svm.spec_verify(target, draft, drafts, u, out=out, **kw)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     def elapsed(a, b):
         return _elapsed(hip, a, b)
@@ -585,6 +602,7 @@ def main():
         "gpu_event_ms_per_step": float(np.median(step_ms)),
         "gpu_region_ms_per_step": gpu_region_ms / args.steps,
         "ms_per_step_with_phase_events": wall_ev * 1e3 / args.steps,
+        "graph_ms_per_step": graph_ms,
         "mean_accept_prob": float(a.mean()) if a is not None and a.size else None,
         "mean_tokens_per_call": float(n.mean() + 1.0),
         "accepted_hist": np.bincount(n, minlength=K + 1).tolist(),
