@@ -135,6 +135,8 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const size_t o_tcand = c.take(th ? rows * kTopPCandCap * sizeof(uint2) : 0);
   const bool me = s.mentor && d.K > 0;
   const size_t o_ment = c.take(me ? (size_t)d.B * d.K * sizeof(MentorSol) : 0);
+  const bool bp = !s.compact && !s.greedy;
+  const size_t o_bpart = c.take(bp ? (size_t)d.B * d.K * d.nfchunks * sizeof(double) : 0);
   if (ws) {
     ws->parts = s.compact ? nullptr : at<ChunkPart>(base, o_parts);
     ws->rstat = at<RowStat>(base, o_rstat);
@@ -147,6 +149,7 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
     ws->tprow = th ? at<TopPRow>(base, o_tprow) : nullptr;
     ws->tcand = th ? at<uint2>(base, o_tcand) : nullptr;
     ws->ment = me ? at<MentorSol>(base, o_ment) : nullptr;
+    ws->bpart = bp ? at<double>(base, o_bpart) : nullptr;
   }
   return c.off;
 }

@@ -131,6 +131,7 @@ struct Workspace {
   TopPRow* tprow;            // [rows]                                        top-p histogram only
   uint2* tcand;              // [rows][kTopPCandCap] (index, bits)            top-p histogram only
   MentorSol* ment;           // [B][K]                                        mentored only
+  double* bpart;             // [B*K][nfchunks] acceptance-rate partials      dense rows only
 };
 
 inline int chunk_elems_for(sv_dtype dt) {

@@ -2966,8 +2966,10 @@ __global__ __launch_bounds__(kThreads) void k_beta_partial(const E* __restrict__
                                                            const E* __restrict__ drf, Dims dm,
                                                            Samp sp, Workspace ws) {
   __shared__ RedScratch red;
-  const int pos = blockIdx.x / dm.nchunks;
-  const int c = blockIdx.x - pos * dm.nchunks;
+  // one workgroup per (position, final chunk): the final draw's grain, so that few sequences
+  // still fill the CUs
+  const int pos = blockIdx.x / dm.nfchunks;
+  const int c = blockIdx.x - pos * dm.nfchunks;
   const int b = pos / dm.K, k = pos - b * dm.K;
   const RowStat rt = ws.rstat[target_row(dm, b, k)];
   const RowStat rd = ws.rstat[draft_row(dm, b, k)];
@@ -2976,8 +2978,8 @@ __global__ __launch_bounds__(kThreads) void k_beta_partial(const E* __restrict__
   constexpr int EPV = Tr<E>::kEpv;
   const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
   const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
-  const int e0 = c * dm.chunk_elems;
-  const int e1 = min(dm.V, e0 + dm.chunk_elems);
+  const int e0 = c * dm.fchunk_elems;
+  const int e1 = min(dm.V, e0 + dm.fchunk_elems);
   // fp32 per element with the normalisers folded into one factor per row, fp64 across vectors
   const float ft = (float)(inv_l / rt.S), fd = (float)(1.0 / rd.S);
   double acc = 0.0;
@@ -2992,16 +2994,18 @@ __global__ __launch_bounds__(kThreads) void k_beta_partial(const E* __restrict__
     acc += (double)part;
   }
   acc = block_sum_d(acc, red);
-  if (threadIdx.x == 0) ws.parts[(size_t)pos * dm.nchunks + c].sum = acc;
+  if (threadIdx.x == 0) ws.bpart[(size_t)pos * dm.nfchunks + c] = acc;
 }
 
+// One wave per position: lanes take the chunks in a fixed stride, then a fixed-order wave sum.
 __global__ __launch_bounds__(kThreads) void k_beta_merge(Dims dm, Workspace ws,
                                                          float* __restrict__ out_beta) {
-  const int pos = blockIdx.x * kThreads + threadIdx.x;
-  if (pos >= dm.B * dm.K) return;
+  const int pos = blockIdx.x * (kThreads / 64) + wave_id();
+  if (pos >= dm.B * dm.K) return;  // the whole wave
   double acc = 0.0;
-  for (int c = 0; c < dm.nchunks; ++c) acc += ws.parts[(size_t)pos * dm.nchunks + c].sum;
-  out_beta[pos] = (float)acc;
+  for (int c = lane_id(); c < dm.nfchunks; c += 64) acc += ws.bpart[(size_t)pos * dm.nfchunks + c];
+  acc = wave_reduce(acc, [](double x, double y) { return x + y; });
+  if (lane_id() == 0) out_beta[pos] = (float)acc;
 }
 
 // ------------------------------------------------------------------------------------------
@@ -3069,15 +3073,15 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_topp_select<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm,
                        sp, ws);
   }
-  if (out_beta) {  // acceptance rates; the chunk partials are free once k_row has run
+  if (out_beta) {  // acceptance rates
     if (sp.greedy) {
       hipLaunchKernelGGL((k_beta<E, VEC>), dim3(dm.B * dm.K), dim3(kThreads), 0, st, t, d, dm,
                          sp, ws, out_beta);
     } else {
       const int npos = dm.B * dm.K;
-      hipLaunchKernelGGL((k_beta_partial<E, VEC>), dim3((unsigned)((size_t)npos * dm.nchunks)),
+      hipLaunchKernelGGL((k_beta_partial<E, VEC>), dim3((unsigned)((size_t)npos * dm.nfchunks)),
                          dim3(kThreads), 0, st, t, d, dm, sp, ws);
-      hipLaunchKernelGGL(k_beta_merge, dim3((npos + kThreads - 1) / kThreads), dim3(kThreads), 0,
+      hipLaunchKernelGGL(k_beta_merge, dim3((npos + 3) / 4), dim3(kThreads), 0,
                          st, dm, ws, out_beta);
     }
     if (rates_only) return hipGetLastError();
