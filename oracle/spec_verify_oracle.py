@@ -77,7 +77,9 @@ def row_distribution(z, temperature, top_k=0, top_p=1.0, diagnostics=None):
     tests pass float32 values, the same numbers the GPU library receives).  ``diagnostics``,
     if a dict, receives ``topp_margin``: the distance of the running sum from P at the top-p
     boundary (min over the last excluded and the first included prefix), which says how close
-    a floating-point decision was.
+    a floating-point decision was; when top-p is applied also ``topp_cumsum`` (the running sums
+    in the order used, probability descending, index ascending) and ``topp_cut`` (the position
+    j* in that order of the last token taken before ties are added).
     """
     z = np.asarray(z, dtype=np.float64).ravel()
     V = z.size
@@ -117,6 +119,8 @@ def row_distribution(z, temperature, top_k=0, top_p=1.0, diagnostics=None):
         if diagnostics is not None:
             before = c[j_star - 1] if j_star > 0 else 0.0
             diagnostics["topp_margin"] = float(min(abs(before - P), abs(c[j_star] - P)))
+            diagnostics["topp_cumsum"] = c
+            diagnostics["topp_cut"] = j_star
         keep_p = (prob >= t_p) & (prob > 0)
         prob = np.where(keep_p, prob, 0.0)
         prob = prob / prob.sum()

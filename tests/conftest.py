@@ -26,3 +26,23 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    # boundary flips counted by every GPU-vs-oracle check of the session (tests/parity.py)
+    parity = sys.modules.get("parity")
+    log = getattr(parity, "FLIP_LOG", None)
+    if not log:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "boundary flips, GPU vs oracle (accept / draw / top-p)")
+    total = {"accept": 0, "draw": 0, "topp": 0}
+    seqs = 0
+    for label, flips, nseq in log:
+        seqs += nseq
+        for k in total:
+            total[k] += flips[k]
+        if any(flips.values()):
+            tr.write_line(f"{label}: {flips} over {nseq} sequences")
+    tr.write_line(f"{len(log)} checks, {seqs} sequences: accept {total['accept']}, "
+                  f"draw {total['draw']}, topp {total['topp']}")

@@ -1,14 +1,32 @@
-"""Helpers for GPU-vs-oracle parity tests.
+"""GPU-vs-oracle parity checks (used by the GPU tests, smoke() and the benchmark's sampled
+oracle check).
 
 Inputs come from ``workloads.synthetic`` (seeded), draft tokens from the oracle's own draft
 sampler, uniforms from numpy Philox; the same arrays go to the HIP library and to the oracle.
 
-The bar (fixed for this method): accepted counts and tokens bit-exact, except boundary flips
-where a floating-point decision sits within 1e-6 of its threshold -- an accept test with
-|u - a_k| < 1e-6, a final draw whose u*W lies within 1e-6*W of the CDF interval of the GPU's
-token, or a top-p boundary whose running sum is within 1e-6 of P.  Flips are counted and
-returned.  Probabilities (a_k, q_k(x~), p_k(x~)) agree within 1e-5 absolute + 1e-4 relative.
+The bar (fixed for this method): accepted counts and tokens bit-exact, probabilities (a_k,
+q_k(x~), p_k(x~)) within 1e-5 absolute + 1e-4 relative, except boundary flips, where a
+floating-point decision sits within 1e-6 of its threshold.  Three kinds are admitted, each
+counted:
+
+  accept  an accept test decided the other way with |u_k - a_k| < 1e-6;
+  draw    a final token whose CDF interval [C_{i-1}, C_i) lies within 1e-6 W of u W;
+  topp    a row whose top-p running sum passes P within 1e-6 of it, read with a neighbouring
+          cut: the GPU kept the oracle's set cut at another position j whose running sum c_j
+          lies within 1e-6 of P (the oracle's distribution at nucleus P' = c_j, |P' - P| < 1e-6).
+
+Every decision is checked against the oracle on exactly the rows it reads.  Accept test k reads
+target row k and draft row k, and so does the final draw when the sequence stops at k; the bonus
+draw reads target row K.  For each position the checker looks for one reading of that position's
+two rows (the oracle's own first; the top-p alternatives only for rows inside the band) under
+which every GPU output of the position equals the oracle's: the probabilities within tolerance,
+the accept decision and the drawn token, up to accept and draw flips.  A reading of a row is
+never used for a decision that does not read that row, and one reading must explain all the
+outputs that read it.  Among the explanations, the one with the fewest flips is counted.
 """
+
+import os
+from collections import Counter
 
 import numpy as np
 import torch
@@ -18,13 +36,19 @@ from workloads import synthetic as S
 
 FLIP_BAND = 1e-6
 ATOL, RTOL = 1e-5, 1e-4
+FLIP_KINDS = ("accept", "draw", "topp")
+
+# (case label, flip counts, sequences checked) of every check in this process; the test
+# session prints them (tests/conftest.py) and the benchmark puts its own into its JSON line.
+FLIP_LOG = []
 
 
+# ---------------------------------------------------------------------------------- inputs
 def make_inputs(target, draft, params, seed):
     """Draft tokens (oracle sampler on the draft rows) and uniforms for given logits."""
     B, K1, V = target.shape
     K = K1 - 1
-    df = draft.float().cpu().numpy()
+    df = draft.float().cpu().numpy() if K > 0 else None
     if K > 0:
         u_draw = S.philox_uniforms(seed + 1, (B, K))
         drafts = np.stack([O.sample_rows(df[:, k], u_draw[:, k], params["temperature"],
@@ -51,141 +75,255 @@ def run_gpu(target, draft, drafts, u, params, device="cuda"):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
+def _np(x):
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.float().cpu().numpy()
+    return np.asarray(x, dtype=np.float32)
+
+
+def _samp(params):
+    return (np.float32(params["temperature"]), int(params.get("top_k", 0)),
+            np.float32(params.get("top_p", 1.0)))
+
+
 def run_oracle(target, draft, drafts, u, params):
-    tf = target.float().cpu().numpy()
-    df = draft.float().cpu().numpy() if draft is not None else np.zeros((tf.shape[0], 0, tf.shape[2]))
-    return O.spec_verify(tf, df, drafts, u, np.float32(params["temperature"]),
-                         params.get("top_k", 0), np.float32(params.get("top_p", 1.0)),
-                         np.float32(params.get("lenience", 1.0)))
+    """The lossless oracle on the whole batch (its own reading of every row)."""
+    tf = _np(target)
+    df = _np(draft) if draft is not None else np.zeros((tf.shape[0], 0, tf.shape[2]))
+    T, k, P = _samp(params)
+    return O.spec_verify(tf, df, drafts, u, T, k, P, np.float32(params.get("lenience", 1.0)))
 
 
 def run_oracle_mentored(target, draft, drafts, u, params):
-    tf = target.float().cpu().numpy()
-    df = draft.float().cpu().numpy()
-    return O.mentored_spec_verify(tf, df, drafts, u, np.float32(params["temperature"]),
-                                  params.get("top_k", 0), np.float32(params.get("top_p", 1.0)),
+    T, k, P = _samp(params)
+    return O.mentored_spec_verify(_np(target), _np(draft), drafts, u, T, k, P,
                                   np.float32(params["mentor_kl"]))
 
 
-def oracle_mentored_weights(target, draft, o, params, b):
-    """The oracle's final-draw weights for sequence b under mentored decoding."""
-    tf = target.float().cpu().numpy()
-    n = int(o["n"][b])
-    K = tf.shape[1] - 1
-    T, k, P = np.float32(params["temperature"]), params.get("top_k", 0), np.float32(
-        params.get("top_p", 1.0))
-    q = O.row_distribution(tf[b, n], T, k, P)
-    if n == K:
-        return q
-    p = O.row_distribution(draft.float().cpu().numpy()[b, n], T, k, P)
-    w = O.mentored_solve(q, p, np.float32(params["mentor_kl"]))["w"]
-    return w if np.sum(w) > 0 else q
+# ---------------------------------------------------------------------------------- rules
+class Lossless:
+    """Accept test and final weights of the lossless rule with lenience l (the oracle's steps:
+    accept_probability, then residual_weights, i.e. (q - p)_+ or q when that has no mass)."""
+
+    def __init__(self, lenience=1.0):
+        self.lenience = np.float32(lenience)
+
+    def position(self, q, p, x):
+        V = q.size
+        inside = 0 <= x < V
+        q_x = float(q[x]) if inside else 0.0
+        p_x = float(p[x]) if inside else 0.0
+        return {"a": float(O.accept_probability(q_x, p_x, self.lenience)), "q_x": q_x,
+                "p_x": p_x, "weights": lambda: O.residual_weights(q, p)[0]}
 
 
-def verify_mentored_case(target, draft, params, seed=0, max_flip_frac=0.02, drafts=None,
-                         u=None):
-    """Parity of mentored decoding (params["mentor_kl"] > 0) against the oracle; returns
-    (flips, gpu results, oracle results)."""
+class Mentored:
+    """Mentored decoding with KL bound D: a = r at the draft token, replacement weights w (q
+    when w has no mass), as the oracle's mentored_verify_sequence takes them."""
+
+    def __init__(self, D):
+        self.D = np.float32(D)
+
+    def position(self, q, p, x):
+        V = q.size
+        sol = O.mentored_solve(q, p, self.D)
+        inside = 0 <= x < V
+        q_x = float(q[x]) if inside else 0.0
+        p_x = float(p[x]) if inside else 0.0
+        a = float(sol["r"][x]) if inside and (q_x > 0 or p_x > 0) else 0.0
+
+        def weights():
+            w = sol["w"]
+            return w if np.sum(w) > 0 else q
+        return {"a": a, "q_x": q_x, "p_x": p_x, "weights": weights}
+
+
+def rule_for(params):
+    if params.get("mentor_kl", 0.0) > 0 and params["temperature"] > 0:
+        return Mentored(params["mentor_kl"])
+    return Lossless(params.get("lenience", 1.0))
+
+
+# ---------------------------------------------------------------------------------- readings
+def row_readings(z, temperature, top_k, top_p):
+    """The admissible distributions of one row: the oracle's own first, then (only when its
+    top-p running sum passes P within FLIP_BAND) the distributions cut at each other position j
+    whose running sum lies within FLIP_BAND of P -- the oracle at nucleus P' = c_j.  A GPU whose
+    running sums are off by less than the band can only cut at one of these."""
+    d = {}
+    base = O.row_distribution(z, temperature, top_k, top_p, d)
+    out = [base]
+    if d.get("topp_margin", np.inf) < FLIP_BAND:
+        c, js = d["topp_cumsum"], d["topp_cut"]
+        P = float(top_p)
+        lo = int(np.searchsorted(c, P - FLIP_BAND, side="right"))  # first c_j > P - band
+        hi = min(int(np.searchsorted(c, P + FLIP_BAND, side="left")), c.size - 1)
+        seen = {np.packbits(base > 0).tobytes()}
+        for j in range(lo, hi + 1):
+            if j == js:
+                continue
+            alt = O.row_distribution(z, temperature, top_k, float(c[j]))
+            sig = np.packbits(alt > 0).tobytes()
+            if sig not in seen:
+                seen.add(sig)
+                out.append(alt)
+    return out
+
+
+# ---------------------------------------------------------------------------------- checks
+def _close(g, o):
+    return abs(float(g) - float(o)) <= ATOL + RTOL * abs(float(o))
+
+
+def check_sequence(gb, rows_t, rows_d, drafts_b, u_b, rule, label=""):
+    """Check one sequence's GPU outputs gb = {n, tokens[K+1], and optionally a, q, p [K]}
+    against the oracle.  rows_t[k] / rows_d[k] are the admissible readings of target / draft row
+    k (the oracle's own first).  Returns (flips Counter, oracle n, oracle tokens) where the
+    oracle's values are those of its own readings."""
+    K = len(drafts_b)
+    ng = int(gb["n"])
+    tok = np.asarray(gb["tokens"]).astype(np.int64)
+    uK = float(u_b[K])
+    if not 0 <= ng <= K:
+        raise AssertionError(f"{label}: accepted count {ng} outside [0, {K}]")
+    np.testing.assert_array_equal(tok[:ng], np.asarray(drafts_b[:ng], dtype=np.int64),
+                                  err_msg=f"{label}: accepted drafts")
+    assert (tok[ng + 1:] == -1).all(), f"{label}: padding after position {ng}: {tok}"
+    flips = Counter()
+    cache = {}
+
+    def position(k, i, j):  # the rule at position k under readings i (target) and j (draft)
+        if (k, i, j) not in cache:
+            cache[(k, i, j)] = rule.position(rows_t[k][i], rows_d[k][j], int(drafts_b[k]))
+        return cache[(k, i, j)]
+
+    # the oracle's own outcome (readings 0): its n and tokens
+    n_o, tok_o = K, None
+    for k in range(K + 1):
+        if k < K:
+            pos = position(k, 0, 0)
+            if float(u_b[k]) < pos["a"]:
+                continue
+            n_o = k
+            tok_o = O.inverse_cdf(pos["weights"](), uK)
+        else:
+            tok_o = O.inverse_cdf(rows_t[K][0], uK)
+        break
+    oracle_tokens = np.full(K + 1, -1, dtype=np.int64)
+    oracle_tokens[:n_o] = np.asarray(drafts_b[:n_o], dtype=np.int64)
+    oracle_tokens[n_o] = tok_o
+
+    for k in range(K):
+        best, failures = None, []
+        for i in range(len(rows_t[k])):
+            for j in range(len(rows_d[k])):
+                pos = position(k, i, j)
+                f = Counter(topp=int(i > 0) + int(j > 0))
+                why = None
+                if "a" in gb:
+                    for key, ov in (("a", pos["a"]), ("q", pos["q_x"]), ("p", pos["p_x"])):
+                        if why is None and not _close(gb[key][k], ov):
+                            why = f"{key}={float(gb[key][k])!r} vs oracle {ov!r}"
+                if why is None and k <= ng:
+                    acc_o = float(u_b[k]) < pos["a"]
+                    if acc_o != (k < ng):
+                        if abs(float(u_b[k]) - pos["a"]) < FLIP_BAND:
+                            f["accept"] += 1
+                        else:
+                            why = (f"GPU {'accepted' if k < ng else 'rejected'} with "
+                                   f"u={float(u_b[k])!r}, oracle a={pos['a']!r}")
+                if why is None and k == ng:
+                    w = pos["weights"]()
+                    t_o = O.inverse_cdf(w, uK)
+                    if t_o != tok[ng]:
+                        if O.inverse_cdf_margin(w, uK, int(tok[ng])) < FLIP_BAND:
+                            f["draw"] += 1
+                        else:
+                            why = f"final token {tok[ng]} vs oracle {t_o}"
+                if why is None:
+                    cost = sum(f.values())
+                    if best is None or cost < best[0]:
+                        best = (cost, f)
+                else:
+                    failures.append(f"reading ({i},{j}): {why}")
+                if best is not None and best[0] == 0:
+                    break
+            if best is not None and best[0] == 0:
+                break
+        if best is None:
+            raise AssertionError(f"{label} position {k} (GPU n={ng}, oracle n={n_o}): no "
+                                 f"admissible reading explains the GPU: {failures[:4]}")
+        flips.update(best[1])
+    if ng == K:
+        best, failures = None, []
+        for i, qt in enumerate(rows_t[K]):
+            f = Counter(topp=int(i > 0))
+            t_o = O.inverse_cdf(qt, uK)
+            if t_o != tok[K]:
+                if O.inverse_cdf_margin(qt, uK, int(tok[K])) < FLIP_BAND:
+                    f["draw"] += 1
+                else:
+                    failures.append(f"reading {i}: bonus token {tok[K]} vs oracle {t_o}")
+                    continue
+            if best is None or sum(f.values()) < best[0]:
+                best = (sum(f.values()), f)
+            if best[0] == 0:
+                break
+        if best is None:
+            raise AssertionError(f"{label} bonus draw: {failures[:4]}")
+        flips.update(best[1])
+    return flips, n_o, oracle_tokens
+
+
+def check(g, target, draft, drafts, u, params, max_flip_frac=0.02, rule=None, label=None,
+          max_flips=None):
+    """Check GPU results g (spec_verify's dict, numpy) for every sequence of target [B, K+1, V]
+    / draft [B, >=K, V] (torch or numpy, on the host) with drafts [B, K] and u [B, K+1].
+
+    Returns (flips, oracle) with flips = {accept, draw, topp} counts and oracle = {n, tokens}
+    from the oracle's own readings.  Raises AssertionError on any difference that is not a
+    counted boundary flip, or when the flips exceed max_flips (default: max(1, max_flip_frac *
+    B), or 0 when max_flip_frac is 0)."""
+    tf = _np(target)
+    df = _np(draft)
+    B, K1, V = tf.shape
+    K = K1 - 1
+    T, k_, P = _samp(params)
+    rule = rule or rule_for(params)
+    label = label or os.environ.get("PYTEST_CURRENT_TEST", "check").split(" ")[0]
+    flips = Counter({kind: 0 for kind in FLIP_KINDS})
+    o_n = np.zeros(B, dtype=np.int64)
+    o_tok = np.full((B, K + 1), -1, dtype=np.int64)
+    for b in range(B):
+        rows_t = [row_readings(tf[b, i], T, k_, P) for i in range(K + 1)]
+        rows_d = [row_readings(df[b, i], T, k_, P) for i in range(K)]
+        gb = {"n": g["num_accepted"][b], "tokens": g["tokens"][b]}
+        if "accept_prob" in g and K > 0:
+            gb.update(a=g["accept_prob"][b], q=g["q_draft"][b], p=g["p_draft"][b])
+        f, o_n[b], o_tok[b] = check_sequence(gb, rows_t, rows_d, drafts[b], u[b], rule,
+                                             f"{label} seq {b}")
+        flips.update(f)
+    flips = {kind: int(flips[kind]) for kind in FLIP_KINDS}
+    FLIP_LOG.append((label, flips, B))
+    print(f"[flips] {label}: {flips} over {B} sequences", flush=True)
+    if max_flips is None:
+        max_flips = 0 if max_flip_frac == 0 else max(1, int(max_flip_frac * B))
+    assert sum(flips.values()) <= max_flips, (flips, max_flips)
+    return flips, {"n": o_n, "tokens": o_tok}
+
+
+def verify_case(target, draft, params, seed=0, max_flip_frac=0.02, rule=None, drafts=None,
+                u=None):
+    """Full parity check of spec_verify on given logits (mentored decoding when
+    params["mentor_kl"] > 0, unless ``rule`` says otherwise); returns (flips, gpu, oracle)."""
     d0, u0 = make_inputs(target, draft, params, seed)
     drafts = d0 if drafts is None else drafts
     u = u0 if u is None else u
     g = run_gpu(target, draft, drafts, u, params)
-    o = run_oracle_mentored(target, draft, drafts, u, params)
-    flips = compare_with_draw_flips(
-        g, o, u, lambda b: oracle_mentored_weights(target, draft, o, params, b), max_flip_frac)
+    flips, o = check(g, target, draft, drafts, u, params, max_flip_frac, rule)
     return flips, g, o
 
 
-def compare(g, o, u, max_flip_frac=0.02):
-    """Compare GPU results ``g`` with oracle results ``o``; returns a dict of flip counts.
-
-    Raises AssertionError on any difference not explained by a boundary flip.
-    """
-    B, K1 = o["tokens"].shape
-    K = K1 - 1
-    flips = {"accept": 0, "draw": 0, "topp": 0}
-    for b in range(B):
-        topp_row = (np.min(o["topp_margin_t"][b], initial=np.inf) < FLIP_BAND or
-                    np.min(o["topp_margin_d"][b], initial=np.inf) < FLIP_BAND)
-        # probabilities
-        for key_g, key_o in (("accept_prob", "a"), ("q_draft", "q_x"), ("p_draft", "p_x")):
-            if key_g not in g or K == 0:
-                continue
-            gv, ov = g[key_g][b].astype(np.float64), o[key_o][b]
-            bad = np.abs(gv - ov) > ATOL + RTOL * np.abs(ov)
-            if bad.any() and not topp_row:
-                raise AssertionError(f"seq {b}: {key_g} {gv[bad]} vs oracle {ov[bad]}")
-            if bad.any():
-                flips["topp"] += 1
-        ng, no = int(g["num_accepted"][b]), int(o["n"][b])
-        if ng != no:
-            k = min(ng, no)  # first position whose decision differs
-            if topp_row:
-                flips["topp"] += 1
-                continue
-            if abs(float(u[b, k]) - o["a"][b, k]) < FLIP_BAND:
-                flips["accept"] += 1
-                continue
-            raise AssertionError(f"seq {b}: accepted {ng} vs oracle {no}; u={u[b, k]!r} "
-                                 f"a={o['a'][b, k]!r}")
-        n = no
-        np.testing.assert_array_equal(g["tokens"][b, :n], o["tokens"][b, :n],
-                                      err_msg=f"seq {b}: accepted drafts")
-        assert (g["tokens"][b, n + 1:] == -1).all(), f"seq {b}: padding"
-        tg, to = int(g["tokens"][b, n]), int(o["tokens"][b, n])
-        if tg != to:
-            if topp_row:
-                flips["topp"] += 1
-                continue
-            # the oracle's final weights for sequence b are not kept per batch; recompute
-            raise AssertionError(f"seq {b}: final token {tg} vs oracle {to} (n={n})")
-    total = sum(flips.values())
-    assert total <= max(1, int(max_flip_frac * B)), flips
-    return flips
-
-
-def compare_with_draw_flips(g, o, u, weights_fn, max_flip_frac=0.02):
-    """Like ``compare`` but classifies final-token differences with the oracle's weights.
-
-    weights_fn(b) returns the oracle's final-draw weights of sequence b.
-    """
-    B = o["tokens"].shape[0]
-    flips = {"accept": 0, "draw": 0, "topp": 0}
-    g2 = {k: v.copy() for k, v in g.items()}
-    for b in range(B):
-        n = int(o["n"][b])
-        if int(g["num_accepted"][b]) == n and int(g["tokens"][b, n]) != int(o["tokens"][b, n]):
-            w = weights_fn(b)
-            K1 = o["tokens"].shape[1]
-            margin = O.inverse_cdf_margin(w, float(u[b, K1 - 1]), int(g["tokens"][b, n]))
-            if margin < FLIP_BAND:
-                flips["draw"] += 1
-                g2["tokens"][b, n] = o["tokens"][b, n]
-    rest = compare(g2, o, u, max_flip_frac)
-    for k in flips:
-        flips[k] += rest[k]
-    return flips
-
-
-def oracle_final_weights(target, draft, o, params, b):
-    """The oracle's final-draw weights for sequence b (residual or bonus row)."""
-    tf = target.float().cpu().numpy()
-    n = int(o["n"][b])
-    K = tf.shape[1] - 1
-    T, k, P = np.float32(params["temperature"]), params.get("top_k", 0), np.float32(
-        params.get("top_p", 1.0))
-    q = O.row_distribution(tf[b, n], T, k, P)
-    if n == K:
-        return q
-    p = O.row_distribution(draft.float().cpu().numpy()[b, n], T, k, P)
-    w, _ = O.residual_weights(q, p)
-    return w
-
-
-def verify_case(target, draft, params, seed=0, max_flip_frac=0.02):
-    """Full parity check of spec_verify on given logits; returns the flip counts."""
-    drafts, u = make_inputs(target, draft, params, seed)
-    g = run_gpu(target, draft, drafts, u, params)
-    o = run_oracle(target, draft, drafts, u, params)
-    return compare_with_draw_flips(
-        g, o, u, lambda b: oracle_final_weights(target, draft, o, params, b), max_flip_frac)
+verify_mentored_case = verify_case

@@ -13,8 +13,7 @@ import torch
 
 from workloads import synthetic as S
 
-from parity import (compare, make_inputs, run_gpu, run_oracle, verify_case,
-                    verify_mentored_case)
+from parity import Lossless, check, make_inputs, run_gpu, verify_case, verify_mentored_case
 
 pytestmark = pytest.mark.gpu
 
@@ -107,8 +106,7 @@ def test_mentored_greedy_is_lossless():
     drafts, u = make_inputs(t, d, dict(temperature=1.0), 48)
     drafts[:, :3] = t.float().argmax(dim=2).numpy()[:, :3]
     g = run_gpu(t, d, drafts, u, dict(temperature=0.0, mentor_kl=0.3))
-    o = run_oracle(t, d, drafts, u, dict(temperature=0.0))
-    compare(g, o, u, max_flip_frac=0.0)
+    check(g, t, d, drafts, u, dict(temperature=0.0), max_flip_frac=0.0)
 
 
 def test_mentored_out_of_range_draft_tokens():
@@ -141,7 +139,8 @@ def test_mentored_tie_overflow_rows_use_lossless_rule():
     g = torch.Generator().manual_seed(50)
     t = torch.randint(0, 4, (3, 3, 40000), generator=g).float().to(torch.bfloat16)
     d = torch.randint(0, 4, (3, 2, 40000), generator=g).float().to(torch.bfloat16)
-    verify_case(t, d, dict(temperature=1.0, top_k=50, mentor_kl=0.2), seed=50)
+    verify_case(t, d, dict(temperature=1.0, top_k=50, mentor_kl=0.2), seed=50,
+                rule=Lossless(1.0))
 
 
 def test_mentored_invalid_combinations(_lib):
@@ -174,10 +173,5 @@ def test_mentored_full_size_sampled():
     u[pick] = u_s
     g = run_gpu(t, d, drafts, u, params)
     gs = {k: v[pick] for k, v in g.items()}
-    from parity import (compare_with_draw_flips, oracle_mentored_weights,
-                        run_oracle_mentored)
-    o = run_oracle_mentored(tt, dd, drafts_s, u_s, params)
-    compare_with_draw_flips(gs, o, u_s,
-                            lambda b: oracle_mentored_weights(tt, dd, o, params, b),
-                            max_flip_frac=0.34)
+    check(gs, tt, dd, drafts_s, u_s, params)
     assert ((g["num_accepted"] >= 0) & (g["num_accepted"] <= K)).all()

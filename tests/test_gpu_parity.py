@@ -12,7 +12,7 @@ import torch
 import oracle.spec_verify_oracle as O
 from workloads import synthetic as S
 
-from parity import FLIP_BAND, compare, make_inputs, run_gpu, run_oracle, verify_case
+from parity import check, make_inputs, run_gpu, run_oracle, verify_case
 
 pytestmark = pytest.mark.gpu
 
@@ -125,8 +125,7 @@ def test_greedy_temperature_zero():
     drafts[:, :3] = g_arg[:, :3]  # make some drafts match the target argmax
     params = dict(temperature=0.0)
     g = run_gpu(t, d, drafts, u, params)
-    o = run_oracle(t, d, drafts, u, params)
-    compare(g, o, u, max_flip_frac=0.0)
+    check(g, t, d, drafts, u, params, max_flip_frac=0.0)
 
 
 def test_p_equals_q_accepts_everything():
@@ -163,8 +162,7 @@ def test_out_of_range_drafts_rejected():
     g = run_gpu(t, d, drafts, u, dict(temperature=1.0))
     assert (g["num_accepted"] == 0).all()
     assert (g["accept_prob"][:, 0] == 0.0).all()
-    o = run_oracle(t, d, drafts, u, dict(temperature=1.0))
-    compare(g, o, u)
+    check(g, t, d, drafts, u, dict(temperature=1.0))
 
 
 def test_masked_minus_inf_logits():
@@ -242,11 +240,7 @@ def _full_size_check(name, nseq, seed):
     u[pick] = u_s
     g = run_gpu(t, d, drafts, u, params)
     gs = {k: v[pick] for k, v in g.items()}
-    o = run_oracle(tt, dd, drafts_s, u_s, params)
-    from parity import compare_with_draw_flips, oracle_final_weights
-    return compare_with_draw_flips(gs, o, u_s,
-                                   lambda b: oracle_final_weights(tt, dd, o, params, b),
-                                   max_flip_frac=0.25)
+    return check(gs, tt, dd, drafts_s, u_s, params)[0]
 
 
 def test_full_size_topk_metric_workload():

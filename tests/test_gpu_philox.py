@@ -9,7 +9,7 @@ import torch
 import oracle.spec_verify_oracle as O
 from workloads import synthetic as S
 
-from parity import compare_with_draw_flips, oracle_final_weights, run_oracle
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -77,5 +77,4 @@ def test_device_handoff_end_to_end(svm):
     drafts_o = np.stack([O.sample_rows(df[:, k], uo_draw[:, k], np.float32(0.8), 50, 1.0)
                          for k in range(K)], axis=1)
     np.testing.assert_array_equal(drafts.cpu().numpy(), drafts_o)
-    o = run_oracle(t, d, drafts_o, uo_ver, params)
-    compare_with_draw_flips(g, o, uo_ver, lambda b: oracle_final_weights(t, d, o, params, b))
+    check(g, t, d, drafts_o, uo_ver, params)

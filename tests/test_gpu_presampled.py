@@ -9,7 +9,7 @@ import torch
 
 from workloads import synthetic as S
 
-from parity import compare_with_draw_flips, oracle_final_weights, run_oracle
+from parity import check
 
 pytestmark = pytest.mark.gpu
 
@@ -59,9 +59,7 @@ def test_presampled_equals_spec_verify(svm, name, params, shape, V, dtype):
     B, K = shape
     t, d = S.zipf_logits(B, K, V, 1.1, 1.0, dtype, seed=V % 89)
     drafts, u, g = _pipeline(svm, t, d, params, V % 83)
-    if "mentor_kl" not in params:
-        o = run_oracle(t, d, drafts, u, params)
-        compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+    check(g, t, d, drafts, u, params)
 
 
 def test_presampled_tie_overflow_rows(svm):

@@ -12,8 +12,7 @@ import torch
 
 from workloads import synthetic as S
 
-from parity import (compare_with_draw_flips, make_inputs, oracle_final_weights, run_oracle,
-                    verify_case)
+from parity import check, make_inputs, verify_case
 
 pytestmark = pytest.mark.gpu
 
@@ -60,8 +59,7 @@ def test_tensor_offset_bf16(svm, offset):
     params = dict(temperature=0.9, top_k=30)
     drafts, u = make_inputs(t, d, params, 60 + offset)
     g = _run(svm, _offset_copy(t, offset), _offset_copy(d, offset + 2), drafts, u, params)
-    o = run_oracle(t, d, drafts, u, params)
-    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+    check(g, t, d, drafts, u, params)
 
 
 @pytest.mark.parametrize("V,offset", [(5, 3), (9, 1), (17, 6)])
@@ -71,8 +69,7 @@ def test_tiny_rows_all_fringe(svm, V, offset):
     params = dict(temperature=1.0, top_k=3)
     drafts, u = make_inputs(t, d, params, 70 + V)
     g = _run(svm, _offset_copy(t, offset), _offset_copy(d, offset), drafts, u, params)
-    o = run_oracle(t, d, drafts, u, params)
-    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+    check(g, t, d, drafts, u, params)
 
 
 def test_tie_overflow_unaligned(svm):
@@ -124,8 +121,7 @@ def test_dense_paths_tensor_offset(svm, name, params, V, dtype):
     t, d = S.zipf_logits(4, 3, V, 1.1, 1.0, dtype, seed=V % 103)
     drafts, u = make_inputs(t, d, params, V % 79)
     g = _run(svm, _offset_copy(t, 3), _offset_copy(d, 1), drafts, u, params)
-    o = run_oracle(t, d, drafts, u, params)
-    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+    check(g, t, d, drafts, u, params)
 
 
 def test_tree_unaligned(svm):
@@ -188,8 +184,7 @@ def test_final_draw_grain(svm, name, B, V, dtype, offset):
     params = dict(temperature=1.0)
     drafts, u = make_inputs(t, d, params, V % 61)
     g = _run(svm, _offset_copy(t, offset), _offset_copy(d, offset + 1), drafts, u, params)
-    o = run_oracle(t, d, drafts, u, params)
-    compare_with_draw_flips(g, o, u, lambda b: oracle_final_weights(t, d, o, params, b))
+    check(g, t, d, drafts, u, params)
 
 
 @pytest.mark.parametrize("offset", [0, 1])

@@ -125,6 +125,32 @@ def test_chi_square_second_position_distinct_rows():
     assert chi2 < CHI2_99_DF7, chi2
 
 
+@pytest.mark.parametrize("K,lenience,sparsity", [(1, 1.0, 0.0), (4, 1.0, 0.3), (1, 0.3, 0.0),
+                                                 (4, 0.3, 0.3)])
+def test_trial_verifier_equals_the_sequence_verifier(K, lenience, sparsity):
+    """The statistical pins run verify_sequence_trials (all trials per numpy call); the GPU is
+    compared with verify_sequence (_verify_core).  Both must give the same n and the same
+    tokens on every trial, so that the chi-square and law-of-n pins cover the function the GPU
+    is held to.  Rows include zeros (disjoint parts of the supports) and draft tokens outside
+    [0, V) are mixed in."""
+    rng = np.random.default_rng(100 + K)
+    V = 8
+    q_rows = [_rand_dist(rng, V, sparsity) for _ in range(K + 1)]
+    p_rows = [_rand_dist(rng, V, sparsity) for _ in range(K)]
+    trials = 10_000
+    g = np.random.Generator(np.random.Philox(400 + K))
+    drafts = np.stack([O.inverse_cdf(p_rows[k], g.random(trials)) for k in range(K)], axis=1)
+    u = g.random((trials, K + 1))
+    u[::97] = 0.0  # u = 0 accepts every a > 0 and draws the first positive weight
+    n_t, first_t, tok_t = O.verify_sequence_trials(q_rows, p_rows, drafts, u, lenience)
+    for i in range(trials):
+        r = O.verify_sequence(q_rows, p_rows, drafts[i], u[i], lenience)
+        assert r["n"] == n_t[i], i
+        np.testing.assert_array_equal(r["tokens"], tok_t[i], err_msg=str(i))
+    assert (first_t == tok_t[:, 0]).all()
+    assert len(set(n_t.tolist())) > 1  # both outcomes occur
+
+
 # --------------------------------------------------------------------------- tokens per call
 def test_mean_tokens_iid_rows():
     rng = np.random.default_rng(8)
