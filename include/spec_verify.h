@@ -48,8 +48,9 @@
  *   - Logits must be finite or -inf, and every row needs at least one finite logit.
  *   - `workspace` is caller-owned device memory of at least *_workspace_size() bytes.  It
  *     needs no initialisation; calls that share a workspace must be ordered on one stream.
- *   - The library keeps no global state and is deterministic: equal inputs give bitwise equal
- *     outputs (fixed-order reductions, no floating-point atomics).
+ *   - The library keeps no global state (apart from spec_verify_noalloc's scratch buffer, one
+ *     per GPU) and is deterministic: equal inputs give bitwise equal outputs (fixed-order
+ *     reductions, no floating-point atomics).
  */
 #ifndef SPEC_VERIFY_H
 #define SPEC_VERIFY_H
@@ -68,7 +69,9 @@ typedef enum {
   SV_ERR_INVALID_ARG = 1,          /* a size, pointer or sampling parameter is out of range */
   SV_ERR_UNSUPPORTED_DTYPE = 2,    /* dtype is not SV_DTYPE_F32 / SV_DTYPE_BF16 */
   SV_ERR_WORKSPACE_TOO_SMALL = 3,  /* workspace_bytes < the matching *_workspace_size() */
-  SV_ERR_LAUNCH = 4                /* a kernel launch failed (hipGetLastError) */
+  SV_ERR_LAUNCH = 4,               /* a kernel launch failed (hipGetLastError) */
+  SV_ERR_SCRATCH_TOO_SMALL = 5     /* spec_verify_noalloc: the problem's workspace exceeds the
+                                      library's built-in scratch buffer */
 } sv_status;
 
 typedef enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 } sv_dtype;
@@ -112,6 +115,31 @@ int spec_verify(const void* target_logits, const void* draft_logits, sv_dtype dt
                 const sv_sampling* params, int32_t* out_tokens, int32_t* out_num_accepted,
                 float* out_accept_prob, float* out_q_draft, float* out_p_draft, void* workspace,
                 size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * spec_verify without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation): the
+ * library's own scratch buffer stands in for the workspace.  That buffer is one static device
+ * array of SPEC_VERIFY_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, held from the library's load
+ * until the process ends; its device address is looked up once per GPU, on the first call
+ * whose stream is on that GPU.  The call allocates nothing (no hipMalloc, no library
+ * allocator).
+ *   - Arguments and results are those of spec_verify; the results are identical.
+ *   - A problem whose spec_verify_workspace_size() exceeds the buffer returns
+ *     SV_ERR_SCRATCH_TOO_SMALL before anything is enqueued (64 MiB covers, e.g., B=256 K=7
+ *     V=128256 bf16 with top-k 50, which needs about 30 MiB).
+ *   - Every call on one GPU uses that GPU's buffer and leaves its contents behind; the kernels
+ *     need no initialisation of it.  Calls that may overlap on one GPU (different streams,
+ *     host threads, or graph replays in flight) race on the buffer and must be serialised
+ *     by the caller, e.g. by issuing them all on one stream.
+ *   - SV_ERR_LAUNCH if the buffer's address cannot be obtained from the HIP runtime.
+ */
+#define SPEC_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                        int B, int K, int V, int draft_rows, const int32_t* draft_tokens,
+                        const float* uniforms, const sv_sampling* params, int32_t* out_tokens,
+                        int32_t* out_num_accepted, float* out_accept_prob, float* out_q_draft,
+                        float* out_p_draft, hipStream_t stream);
 
 /*
  * spec_verify with per-phase timing, for profiling.  `events` holds n_events >= 2 events

@@ -17,6 +17,8 @@ _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG_DIR, "libspecverify.so")
 
 SV_OK = 0
+SV_ERR_SCRATCH_TOO_SMALL = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SPEC_VERIFY_NOALLOC_SCRATCH_BYTES
 SV_DTYPE_F32 = 0
 SV_DTYPE_BF16 = 1
 
@@ -32,7 +34,7 @@ EXPORTS = [
     "spec_sample_workspace_size", "spec_sample",
     "spec_verify_tree_workspace_size", "spec_verify_tree", "spec_verify_tree_profiled",
     "spec_build_tree", "spec_philox_uniform", "spec_acceptance_rate", "spec_verify_rates",
-    "spec_verify_presampled",
+    "spec_verify_presampled", "spec_verify_noalloc",
     "spec_expected_tokens",
     "spec_walltime_speedup", "spec_ops_factor", "spec_optimal_gamma",
     "spec_verify_status_string",
@@ -59,6 +61,8 @@ def load(path=LIB_PATH):
     lib.spec_verify_presampled.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, psamp, vp, vp, vp,
                                            vp, vp, vp, sz, vp, sz, vp]
     lib.spec_verify_presampled.restype = i32
+    lib.spec_verify_noalloc.argtypes = lib.spec_verify.argtypes[:15] + [vp]
+    lib.spec_verify_noalloc.restype = i32
     lib.spec_sample_workspace_size.argtypes = [i32, i32, i32, psamp]
     lib.spec_sample_workspace_size.restype = sz
     lib.spec_sample.argtypes = [vp, i32, i32, i32, vp, psamp, vp, vp, sz, vp]
@@ -245,6 +249,42 @@ def spec_verify(target_logits, draft_logits, draft_tokens, uniforms, *, temperat
     else:
         arr = (ctypes.c_void_p * len(events))(*events)
         _check("spec_verify_profiled", _lib.spec_verify_profiled(*args, arr, len(events)))
+    return out
+
+
+def spec_verify_noalloc(target_logits, draft_logits, draft_tokens, uniforms, out, *,
+                        temperature=1.0, top_k=0, top_p=1.0, lenience=1.0, mentor_kl=0.0,
+                        stream=None):
+    """spec_verify through the entry point that takes no workspace (the library's own scratch
+    buffer, one per GPU; see include/spec_verify.h), for callers that cannot allocate.  ``out``
+    must hold the output tensors (tokens, num_accepted and optionally accept_prob, q_draft,
+    p_draft), so that this call allocates nothing.  Raises SpecVerifyError with status 5 when
+    the problem needs more scratch than the buffer holds."""
+    dev = target_logits.device
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    _need(target_logits, "target_logits", dev)
+    dt = _dtype_code(target_logits)
+    if K > 0:
+        _need(draft_logits, "draft_logits", dev, target_logits.dtype)
+        if draft_logits.dim() != 3 or draft_logits.shape[0] != B or draft_logits.shape[2] != V:
+            raise ValueError("draft_logits must be [B, K or K+1, V]")
+        draft_rows = draft_logits.shape[1]
+        _need(draft_tokens, "draft_tokens", dev, torch.int32, (B, K))
+    else:
+        draft_rows = 0
+    _need(uniforms, "uniforms", dev, torch.float32, (B, K + 1))
+    _need(out["tokens"], "out tokens", dev, torch.int32, (B, K + 1))
+    _need(out["num_accepted"], "out num_accepted", dev, torch.int32, (B,))
+    for k in ("accept_prob", "q_draft", "p_draft"):
+        if k in out:
+            _need(out[k], f"out {k}", dev, torch.float32, (B, K))
+    samp = sampling(temperature, top_k, top_p, lenience, mentor_kl)
+    _check("spec_verify_noalloc", _lib.spec_verify_noalloc(
+        _ptr(target_logits), _ptr(draft_logits) if K > 0 else None, dt, B, K, V, draft_rows,
+        _ptr(draft_tokens) if K > 0 else None, _ptr(uniforms), ctypes.byref(samp),
+        _ptr(out["tokens"]), _ptr(out["num_accepted"]), _ptr(out.get("accept_prob")),
+        _ptr(out.get("q_draft")), _ptr(out.get("p_draft")), _stream(dev, stream)))
     return out
 
 

@@ -2,11 +2,19 @@
 // kernel dispatch.  No allocation, no synchronisation; everything is enqueued on the caller's
 // stream.  See include/spec_verify.h for the contract of each function.
 
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "sv_internal.hpp"
+
+// Scratch memory of spec_verify_noalloc, for callers that cannot allocate: one copy of this
+// array per GPU, held from the library's load until the process ends.  Host code never uses
+// its name as an address (on the host it is only a stand-in for the device symbol): the device
+// address comes from hipGetSymbolAddress, once per device, in noalloc_scratch() below.
+static __device__ __align__(256) unsigned char scratch[sv::kNoAllocScratchBytes];
 
 namespace sv {
 namespace {
@@ -170,12 +178,44 @@ using namespace sv;
 
 namespace {
 
+// Device address of the scratch array on the GPU that `stream` belongs to (the current device
+// for the null stream), looked up with that device current on the first call for the device
+// and kept per device.  SV_ERR_LAUNCH if a HIP query fails.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+int noalloc_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  const hipError_t ed = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (ed != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_LAUNCH;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      int cur = -1;
+      if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_LAUNCH;
+      if (cur != dev && hipSetDevice(dev) != hipSuccess) return SV_ERR_LAUNCH;
+      void* q = nullptr;
+      const hipError_t eg = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (cur != dev) (void)hipSetDevice(cur);
+      if (eg != hipSuccess || q == nullptr) return SV_ERR_LAUNCH;
+      g_scratch_ptr[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return SV_OK;
+}
+
 int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, int K, int V,
                 int draft_rows, const int32_t* drafts, const float* uniforms,
                 const sv_sampling* params, int32_t* out_tokens, int32_t* out_n, float* out_a,
                 float* out_q, float* out_p, float* out_beta, void* workspace,
                 size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int n_events,
-                const void* sample_ws = nullptr, size_t sample_ws_bytes = 0) {
+                const void* sample_ws = nullptr, size_t sample_ws_bytes = 0,
+                bool use_scratch = false) {
   if (!valid_dtype(dtype)) return SV_ERR_UNSUPPORTED_DTYPE;
   if (!valid_params(params)) return SV_ERR_INVALID_ARG;
   if (K > 0 && draft_rows != K && draft_rows != K + 1) return SV_ERR_INVALID_ARG;
@@ -191,6 +231,12 @@ int verify_impl(const void* target, const void* draft, sv_dtype dtype, int B, in
   // draft rows summarised by an earlier spec_sample over them (rows b*K + k there)
   if (sample_ws && (K < 1 || draft_rows != K || !s.compact)) return SV_ERR_INVALID_ARG;
   const size_t need = layout_verify(d, s, nullptr, nullptr);
+  if (use_scratch) {  // spec_verify_noalloc: the library's scratch array is the workspace
+    if (need > kNoAllocScratchBytes) return SV_ERR_SCRATCH_TOO_SMALL;
+    const int st = noalloc_scratch(stream, &workspace);
+    if (st != SV_OK) return st;
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (!workspace || workspace_bytes < need) return SV_ERR_WORKSPACE_TOO_SMALL;
   Workspace ws_s{};
   if (sample_ws) {
@@ -233,6 +279,18 @@ int spec_verify(const void* target_logits, const void* draft_logits, sv_dtype dt
                      uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
                      out_q_draft, out_p_draft, nullptr, workspace, workspace_bytes, stream,
                      nullptr, 0);
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, sv_dtype dtype,
+                        int B, int K, int V, int draft_rows, const int32_t* draft_tokens,
+                        const float* uniforms, const sv_sampling* params, int32_t* out_tokens,
+                        int32_t* out_num_accepted, float* out_accept_prob, float* out_q_draft,
+                        float* out_p_draft, hipStream_t stream) {
+  if (!out_num_accepted) return SV_ERR_INVALID_ARG;
+  return verify_impl(target_logits, draft_logits, dtype, B, K, V, draft_rows, draft_tokens,
+                     uniforms, params, out_tokens, out_num_accepted, out_accept_prob,
+                     out_q_draft, out_p_draft, nullptr, nullptr, 0, stream, nullptr, 0, nullptr,
+                     0, true);
 }
 
 int spec_verify_presampled(const void* target_logits, const void* draft_logits, sv_dtype dtype,
@@ -427,6 +485,8 @@ const char* spec_verify_status_string(int status) {
     case SV_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
     case SV_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case SV_ERR_LAUNCH: return "kernel launch failed";
+    case SV_ERR_SCRATCH_TOO_SMALL:
+      return "problem needs more than spec_verify_noalloc's built-in scratch buffer";
     default: return "unknown status";
   }
 }

@@ -35,6 +35,7 @@ constexpr int kRestMaxM = 128;  // candidates per sequence (REST tree builder)
 constexpr int kRestMaxL = 32;   // tokens per candidate
 constexpr int kRestMaxN = 256;  // tree nodes, root included
 constexpr int64_t kPhiloxMaxN = (int64_t)1 << 40;  // uniforms per spec_philox_uniform call
+constexpr size_t kNoAllocScratchBytes = SPEC_VERIFY_NOALLOC_SCRATCH_BYTES;  // spec_verify_noalloc
 
 // Row kinds written by k_row.
 enum RowKind : int { kRowDense = 0, kRowCompact = 1, kRowGreedy = 2 };
