@@ -1624,10 +1624,12 @@ struct alignas(16) RowLds {
   // kWaveListCap + 63 are per-lane sinks for the stores of lanes without a candidate
   uint32_t key[4][kWaveListCap + 64];
   uint32_t idx[4][kWaveListCap + 64];
-  float e[4][kWaveListCap];       // exp((z - m) / T) of each candidate (row merge)
   RedScratch red;
   uint32_t tmax[kThreads];        // per-thread maxima of tile 0
   uint32_t tau;
+  uint32_t wtau[4];               // each wave's latest filter threshold, read by the others
+  uint32_t ckey[kKeptCap];        // the row's top-k set, compacted by the merge (keys) ...
+  uint32_t cidx[kKeptCap];        // ... and vocabulary indices
   int cnt[4];
   int ovf[4];
   int fallback;
@@ -1700,6 +1702,19 @@ __device__ __forceinline__ void wl_raise(RowLds& S, WaveList& L, int k) {
   }
   L.count = base;
   const uint32_t t = filter_tau<E>(x);
+  if (t > L.tau) L.tau = t;
+  // publish it: every wave's threshold is at most the row's k-th largest, so each wave may
+  // filter with the largest one published (a stale read is a lower, still valid, bound)
+  if (lane == 0) __hip_atomic_store(&S.wtau[L.w], L.tau, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// The largest threshold any wave of the row has published, if above the wave's own.
+__device__ __forceinline__ void wl_shared_tau(RowLds& S, WaveList& L) {
+  uint32_t t = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    t = max(t, __hip_atomic_load(&S.wtau[w], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+  t = (uint32_t)__builtin_amdgcn_readfirstlane((int)t);
   if (t > L.tau) L.tau = t;
 }
 
@@ -1842,117 +1857,171 @@ __device__ __forceinline__ void filter_tile(const uint32_t (&regs)[kRegs], int c
   }
 }
 
+// Top-p on the renormalised top-k set (compacted in S.ckey, nk <= 64 QL entries, all >= x):
+// the largest key v such that the entries at or above v carry at least P of the kept mass
+// (every entry tied with the boundary is kept), bit by bit from the most significant, each
+// lane holding entries lane + 64 i.  Masses are fp64 sums in a fixed order (slots, then the
+// wave butterfly), so the result does not change from run to run.  Sets tkey and Ssum (the
+// kept set's normaliser).
+template <class E, int QL>
+__device__ void topp_compact(const Samp& sp, RowLds& S, int nk, float m, double& Ssum,
+                             uint32_t& tkey) {
+  constexpr int KB = Tr<E>::kKeyBits;
+  const int lane = lane_id();
+  const float it = sp.inv_t;
+  uint32_t kc[QL];
+  float ec[QL];
+#pragma unroll
+  for (int i = 0; i < QL; ++i) {
+    const int j = lane + 64 * i;
+    kc[i] = j < nk ? S.ckey[j] : 0u;
+    ec[i] = j < nk ? fast_exp((Tr<E>::key_to_float(kc[i]) - m) * it) : 0.0f;
+  }
+  auto mass_ge = [&](uint32_t v) {
+    // opaque weights: the conversions are redone per call rather than kept live
+#pragma unroll
+    for (int i = 0; i < QL; ++i) asm volatile("" : "+v"(ec[i]));
+    double t = 0.0;
+#pragma unroll
+    for (int i = 0; i < QL; ++i)
+      if (kc[i] >= v) t += (double)ec[i];
+    return wave_reduce(t, [](double a, double b) { return a + b; });
+  };
+  const uint32_t x = tkey;
+  const double need = (double)sp.top_p * Ssum;
+  // the result lies in [x, the largest key]: only the bits below their common prefix vary
+  uint32_t mk = 0;
+#pragma unroll
+  for (int i = 0; i < QL; ++i) mk = kc[i] > mk ? kc[i] : mk;
+  mk = wave_reduce(mk, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  const int hb = 31 - __builtin_clz((x ^ mk) | 1u);
+  uint32_t v = hb == 31 ? 0u : x & ~((2u << hb) - 1u);
+  for (int bit = hb; bit >= 0; --bit) {
+    const uint32_t cand = v | (1u << bit);
+    // every entry is >= x, so mass_ge(cand) = Ssum >= need for cand <= x
+    if (cand <= x || mass_ge(cand) >= need) v = cand;
+  }
+  tkey = v;
+  Ssum = mass_ge(tkey);
+}
+
 // One wave merges the row from the four wave lists: the row maximum (the largest candidate:
 // the maximum is >= every threshold used), the k-th largest key, top-p on the kept set if
 // requested; writes RowStat and the kept list (candidate order).  Returns 1, writing nothing,
-// when the kept set would not fit kKeptCap.
-template <class E>
-__device__ int row_merge_lists(const Samp& sp, int r, const Workspace& ws, RowLds& S) {
+// when the kept set would not fit kKeptCap.  Each lane first takes its entries of the four
+// lists into registers (entry lane + 64 i of list w in slot [w][i], PL slots per list, key 0 in
+// slots past a list's end), so that the bit-by-bit selections below are register compares and
+// ballots, with no LDS traffic per bit; row_merge_lists picks the smallest PL that holds the
+// longest list.
+template <class E, int PL>
+__device__ int row_merge_slots(const Samp& sp, int r, const Workspace& ws, RowLds& S) {
+  constexpr int KB = Tr<E>::kKeyBits;
   const int lane = lane_id();
   int cnt[4];
 #pragma unroll
   for (int w = 0; w < 4; ++w) cnt[w] = S.cnt[w];
-  uint32_t first[4];  // the first 64 entries of each list stay in registers
-  uint32_t mk = 0;
+  uint32_t kr[4][PL];  // canonical keys of this lane's entries; 0 = no entry (valid keys are >= 1)
+  uint32_t mk = 0, lo = 0xFFFFFFFFu;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    first[w] = lane < cnt[w] ? S.key[w][lane] : 0u;
-    mk = first[w] > mk ? first[w] : mk;
-    for (int j = lane + 64; j < cnt[w]; j += 64) mk = S.key[w][j] > mk ? S.key[w][j] : mk;
-  }
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const int j = lane + 64 * i;
+      kr[w][i] = j < cnt[w] ? S.key[w][j] : 0u;
+      mk = kr[w][i] > mk ? kr[w][i] : mk;
+      if (j < cnt[w]) lo = kr[w][i] < lo ? kr[w][i] : lo;
+    }
   mk = wave_reduce(mk, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  lo = wave_reduce(lo, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
   const float m = Tr<E>::key_to_float(mk);
-  uint32_t x = 0;
-  for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
-    const uint32_t cand = x | (1u << bit);
+  auto count_ge = [&](uint32_t v) {
     int c = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      c += __popcll(__ballot(first[w] >= cand));
-      for (int j0 = 64; j0 < cnt[w]; j0 += 64) {
-        const int j = j0 + lane;
-        c += __popcll(__ballot(j < cnt[w] && S.key[w][j] >= cand));
-      }
-    }
-    if (c >= sp.top_k) x = cand;
-  }
-  const float it = sp.inv_t;
-  double part = 0.0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    for (int j = lane; j < cnt[w]; j += 64) {
-      const uint32_t kj = S.key[w][j];
-      const float ev = kj >= x ? fast_exp((Tr<E>::key_to_float(kj) - m) * it) : 0.0f;
-      S.e[w][j] = ev;
-      part += (double)ev;
-    }
-  }
-  double Ssum = wave_reduce(part, [](double a, double b) { return a + b; });
-  uint32_t tkey = x;
-  if (sp.top_p < 1.0f) {
-    // For each kept entry, the mass of the kept entries ordered before it by (logit
-    // descending, index ascending); the boundary is the entry whose running sum first
-    // reaches P.
-    wave_lds_sync();
-    const double P = (double)sp.top_p;
-    uint32_t hit = 0;
-    for (int w = 0; w < 4; ++w) {
-      for (int j = lane; j < cnt[w]; j += 64) {
-        const uint32_t ke = S.key[w][j], ie = S.idx[w][j];
-        if (ke < x) continue;
-        double ex = 0.0;
-        for (int w2 = 0; w2 < 4; ++w2) {
-          for (int q = 0; q < cnt[w2]; ++q) {
-            const uint32_t kq = S.key[w2][q];
-            if (kq >= x && (kq > ke || (kq == ke && S.idx[w2][q] < ie))) ex += (double)S.e[w2][q];
-          }
-        }
-        const double lo = ex / Ssum, hi = (ex + (double)S.e[w][j]) / Ssum;
-        if (hi >= P && lo < P) hit = ke;
-      }
-    }
-    hit = wave_reduce(hit, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
-    if (hit != 0) tkey = hit;  // otherwise rounding left the total below P: keep everything
-    part = 0.0;
     for (int w = 0; w < 4; ++w)
-      for (int j = lane; j < cnt[w]; j += 64)
-        if (S.key[w][j] >= tkey) part += (double)S.e[w][j];
-    Ssum = wave_reduce(part, [](double a, double b) { return a + b; });
+#pragma unroll
+      for (int i = 0; i < PL; ++i) c += __popcll(__ballot(kr[w][i] >= v));
+    return c;
+  };
+  // the k-th largest key, ties counted: the largest x with at least k entries >= x.  It lies
+  // in [lo, mk] (at least k entries exist), so it shares their common high bits; the search
+  // runs over the bits below.
+  int hb = lo <= mk ? 31 - __builtin_clz((lo ^ mk) | 1u) : KB - 1;
+  uint32_t x = lo <= mk ? lo & ~((2u << hb) - 1u) : 0u;
+  if (hb == 31) x = 0u;
+  for (int bit = hb; bit >= 0; --bit) {
+    const uint32_t cand = x | (1u << bit);
+    if (count_ge(cand) >= sp.top_k) x = cand;
   }
+  if (x < 1u) x = 1u;  // key 0 marks no entry
+  const float it = sp.inv_t;
+  double part = 0.0;  // the top-k set's sum of exp((z - m) / T)
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      if (kr[w][i] >= x) part += (double)fast_exp((Tr<E>::key_to_float(kr[w][i]) - m) * it);
+  double Ssum = wave_reduce(part, [](double a, double b) { return a + b; });
+  // the top-k set (every entry >= x) compacted into LDS in slot order
+  const unsigned long long below = lanes_below();
   int nk = 0;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
-    for (int j0 = 0; j0 < cnt[w]; j0 += 64) {
-      const int j = j0 + lane;
-      nk += __popcll(__ballot(j < cnt[w] && S.key[w][j] >= tkey));
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const bool keep = kr[w][i] >= x;
+      const unsigned long long mkp = __ballot(keep);
+      const int pos = nk + __popcll(mkp & below);
+      if (keep && pos < kKeptCap) {
+        S.ckey[pos] = kr[w][i];
+        S.cidx[pos] = S.idx[w][lane + 64 * i];
+      }
+      nk += __popcll(mkp);
     }
   if (nk > kKeptCap) return 1;
+  wave_lds_sync();
+  uint32_t tkey = x;
+  if (sp.top_p < 1.0f) {
+    if (nk <= 128)
+      topp_compact<E, 2>(sp, S, nk, m, Ssum, tkey);
+    else if (nk <= 320)
+      topp_compact<E, 5>(sp, S, nk, m, Ssum, tkey);
+    else
+      topp_compact<E, kKeptCap / 64>(sp, S, nk, m, Ssum, tkey);
+  }
   uint2* dst = ws.kept + (size_t)r * kKeptCap;
-  const unsigned long long below = lanes_below();
   int base = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w)
-    for (int j0 = 0; j0 < cnt[w]; j0 += 64) {
-      const int j = j0 + lane;
-      const bool keep = j < cnt[w] && S.key[w][j] >= tkey;
-      const unsigned long long mkp = __ballot(keep);
-      if (keep)
-        dst[base + __popcll(mkp & below)] =
-            make_uint2(S.idx[w][j], __float_as_uint(Tr<E>::key_to_float(S.key[w][j])));
-      base += __popcll(mkp);
-    }
+  for (int j0 = 0; j0 < nk; j0 += 64) {
+    const int j = j0 + lane;
+    const uint32_t kj = j < nk ? S.ckey[j] : 0u;
+    const bool keep = kj >= tkey;
+    const unsigned long long mkp = __ballot(keep);
+    if (keep)
+      dst[base + __popcll(mkp & below)] =
+          make_uint2(S.cidx[j], __float_as_uint(Tr<E>::key_to_float(kj)));
+    base += __popcll(mkp);
+  }
   if (lane == 0) {
     RowStat rs;
     rs.m = m;
     rs.thr = Tr<E>::key_to_float(tkey);
     rs.S = Ssum;
     rs.argmax = -1;
-    rs.nkept = nk;
+    rs.nkept = base;
     rs.kind = kRowCompact;
     rs.pad = 0;
     ws.rstat[r] = rs;
   }
   return 0;
+}
+
+template <class E>
+__device__ int row_merge_lists(const Samp& sp, int r, const Workspace& ws, RowLds& S) {
+  const int longest = max(max(S.cnt[0], S.cnt[1]), max(S.cnt[2], S.cnt[3]));
+  if (longest <= 128) return row_merge_slots<E, 2>(sp, r, ws, S);
+  if (longest <= 256) return row_merge_slots<E, 4>(sp, r, ws, S);
+  if constexpr (Tr<E>::kKeyBits == 16)  // (with 32-bit keys this instantiation spills)
+    if (longest <= 384) return row_merge_slots<E, 6>(sp, r, ws, S);
+  return row_merge_slots<E, kWaveListCap / 64>(sp, r, ws, S);
 }
 
 // Whole-row fallback (all threads) when the candidates do not fit: the row maximum and exact
@@ -1992,8 +2061,8 @@ __device__ void row_merge_block(const E* __restrict__ row, const Dims& dm, const
 // and a wave raises tau to its own list's k-th largest whenever the list grows long.  No
 // barrier after tile 0.  At the end one wave selects the row's k-th largest among the
 // candidates (the row's top-k set, ties included, is among them).
-template <class E>
-__global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt,
+template <class E, bool GROUPS4>
+__global__ __launch_bounds__(kThreads, 5) void k_topk_row(const E* __restrict__ tgt,
                                                        const E* __restrict__ drf, Dims dm,
                                                        Samp sp, Workspace ws, int targets_only) {
   constexpr int EPV = Tr<E>::kEpv;
@@ -2023,31 +2092,66 @@ __global__ __launch_bounds__(kThreads) void k_topk_row(const E* __restrict__ tgt
     unsigned long long valid[kVecPerThread];
     tile_valid<E>(clen, valid);
     if (c == 0) {
-      uint32_t tm = 0;
+      // Maxima of disjoint groups of the tile: the k-th largest of them is at most the tile's
+      // k-th largest.  One group per thread (256 maxima), or with GROUPS4 (top-k above 64) four
+      // per thread (registers [16 g, 16 g + 16), 1024 maxima in the still empty lists), whose
+      // k-th largest lies much closer to the tile's and so admits far fewer candidates; that
+      // variant is a kernel of its own, as its selection needs more registers.
+      constexpr bool groups4 = GROUPS4;
+      uint32_t* gm = &S.key[0][0];
+      if constexpr (groups4) {
 #pragma unroll
-      for (int j = 0; j < kRegs; ++j) tm = Tr<E>::dword_max(tm, tile_key<E>(regs, j, valid));
-      S.tmax[tid] = Tr<E>::dword_hmax(tm);
+        for (int g = 0; g < 4; ++g) {
+          uint32_t tm = 0;
+#pragma unroll
+          for (int j = 16 * g; j < 16 * g + 16; ++j)
+            tm = Tr<E>::dword_max(tm, tile_key<E>(regs, j, valid));
+          gm[g * kThreads + tid] = Tr<E>::dword_hmax(tm);
+        }
+      } else {
+        uint32_t tm = 0;
+#pragma unroll
+        for (int j = 0; j < kRegs; ++j) tm = Tr<E>::dword_max(tm, tile_key<E>(regs, j, valid));
+        S.tmax[tid] = Tr<E>::dword_hmax(tm);
+      }
       // Opaque to the compiler, so that it recomputes the keys in filter_tile rather than
       // keeping all 64 of them live across the selection below.
 #pragma unroll
       for (int j = 0; j < kRegs; ++j) asm volatile("" : "+v"(regs[j]));
       __syncthreads();
       if (wv == 0) {
-        const uint32_t a0 = S.tmax[lane], a1 = S.tmax[lane + 64];
-        const uint32_t a2 = S.tmax[lane + 128], a3 = S.tmax[lane + 192];
         uint32_t x = 0;
-        for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
-          const uint32_t cand = x | (1u << bit);
-          const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand)) +
-                          __popcll(__ballot(a2 >= cand)) + __popcll(__ballot(a3 >= cand));
-          if (cnt >= k) x = cand;
+        if constexpr (groups4) {
+          uint32_t a[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) a[i] = gm[lane + 64 * i];
+          for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+            const uint32_t cand = x | (1u << bit);
+            int cnt = 0;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) cnt += __popcll(__ballot(a[i] >= cand));
+            if (cnt >= k) x = cand;
+          }
+        } else {
+          const uint32_t a0 = S.tmax[lane], a1 = S.tmax[lane + 64];
+          const uint32_t a2 = S.tmax[lane + 128], a3 = S.tmax[lane + 192];
+          for (int bit = Tr<E>::kKeyBits - 1; bit >= 0; --bit) {
+            const uint32_t cand = x | (1u << bit);
+            const int cnt = __popcll(__ballot(a0 >= cand)) + __popcll(__ballot(a1 >= cand)) +
+                            __popcll(__ballot(a2 >= cand)) + __popcll(__ballot(a3 >= cand));
+            if (cnt >= k) x = cand;
+          }
         }
-        if (lane == 0) S.tau = filter_tau<E>(x);
+        if (lane == 0) {
+          S.tau = filter_tau<E>(x);
+#pragma unroll
+          for (int w = 0; w < 4; ++w) S.wtau[w] = S.tau;
+        }
       }
       __syncthreads();
       L.tau = S.tau;
       filter_tile<E, true>(regs, h + c0, valid, S, L, k, raise_at);
-    } else if (L.tau > Tr<E>::kKeyPos0) {
+    } else if ((wl_shared_tau(S, L), L.tau > Tr<E>::kKeyPos0)) {
       filter_tile<E, false>(regs, h + c0, valid, S, L, k, raise_at);
     } else {
       filter_tile<E, true>(regs, h + c0, valid, S, L, k, raise_at);
@@ -2837,33 +2941,50 @@ __global__ __launch_bounds__(kThreads) void k_seq_compact(const E* __restrict__ 
 }
 
 // ------------------------------------------------------------------------------------------
-// Tree walk: one wave per sequence.  Node argmaxes from the chunk parts (first chunk wins
-// ties, so the lowest index), then acceptance in index order (parents precede children).
+// Tree walk: one workgroup per sequence (REST article, section on retrieval-based speculative
+// decoding: a node is accepted exactly when its parent is and its token is the argmax of the
+// parent's target row).  Node argmaxes come from the chunk parts (first chunk wins ties, so the
+// lowest index).  Acceptance is a conjunction along the path to the root, found for every node
+// at once by pointer jumping: each node holds (ancestor a, distance d to it, ok = every edge
+// from the node up to a matches); a round replaces it by (a of a, d + d of a, ok and ok of a),
+// so after ceil(log2 N) rounds every ancestor is a terminal: the root (a self-loop with d = 0,
+// ok = 1) or a node with an invalid parent (a self-loop with ok = 0).  A node is then accepted
+// iff ok and d <= max_depth, d being its depth; the deepest accepted node, lowest index on
+// ties, comes from one max-reduction, and its path is read back through the parents.
 // ------------------------------------------------------------------------------------------
 constexpr int kTreeMaxNodes = 2048;
+constexpr int kTreeThreads = 256;
+// (ancestor: bits 0-10, distance: bits 11-21, ok: bit 22) of a node
+constexpr uint32_t kJumpA = 2047u, kJumpOk = 1u << 22;
 
-__global__ __launch_bounds__(kSeqThreads) void k_tree_walk(Dims dm, Workspace ws,
-                                                           const int32_t* __restrict__ parent,
-                                                           const int32_t* __restrict__ tokens,
-                                                           int max_depth,
-                                                           int32_t* __restrict__ out_tokens,
-                                                           int32_t* __restrict__ out_n,
-                                                           int32_t* __restrict__ out_last) {
+__global__ __launch_bounds__(kTreeThreads) void k_tree_walk(Dims dm, Workspace ws,
+                                                            const int32_t* __restrict__ parent,
+                                                            const int32_t* __restrict__ tokens,
+                                                            int max_depth,
+                                                            int32_t* __restrict__ out_tokens,
+                                                            int32_t* __restrict__ out_n,
+                                                            int32_t* __restrict__ out_last) {
   const int b = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   const int N = dm.K;  // nodes per tree (stored in K for the tree launch)
+  constexpr int PER = kTreeMaxNodes / kTreeThreads;
   __shared__ int s_g[kTreeMaxNodes];
   __shared__ int s_par[kTreeMaxNodes];
   __shared__ int s_tok[kTreeMaxNodes];
-  __shared__ int s_depth[kTreeMaxNodes];
-  __shared__ unsigned char s_acc[kTreeMaxNodes];
-  for (int i = lane; i < N; i += kSeqThreads) {
+  __shared__ uint32_t s_jump[2][kTreeMaxNodes];
+  __shared__ int s_best[kTreeThreads / 64];
+  // argmax of every node's row; parents and tokens
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + kTreeThreads * j;
+    if (i >= N) break;
     const ChunkPart* p = ws.parts + ((size_t)b * N + i) * dm.nchunks;
     float best = p[0].vmax;
     int am = p[0].argmax;
     for (int c = 1; c < dm.nchunks; ++c) {
-      if (p[c].vmax > best) {
-        best = p[c].vmax;
+      const float v = p[c].vmax;
+      if (v > best) {
+        best = v;
         am = p[c].argmax;
       }
     }
@@ -2872,29 +2993,65 @@ __global__ __launch_bounds__(kSeqThreads) void k_tree_walk(Dims dm, Workspace ws
     s_tok[i] = tokens[(size_t)b * N + i];
   }
   __syncthreads();
-  if (lane == 0) {
-    s_acc[0] = 1;
-    s_depth[0] = 0;
-    int best = 0;
-    for (int i = 1; i < N; ++i) {
+  // initial words: the root is a terminal; a node with a valid parent points at it with
+  // distance 1 and ok = (its token is the parent's argmax); an invalid parent makes the node a
+  // terminal that is not ok, and so every node below it
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + kTreeThreads * j;
+    if (i >= N) break;
+    uint32_t w;
+    if (i == 0) {
+      w = kJumpOk;
+    } else {
       const int par = s_par[i];
-      s_acc[i] = 0;
-      s_depth[i] = 0;
-      if (par < 0 || par >= i) continue;
-      const int dep = s_depth[par] + 1;
-      s_depth[i] = dep;
-      s_acc[i] = s_acc[par] && dep <= max_depth && s_tok[i] == s_g[par];
-      if (s_acc[i] && dep > s_depth[best]) best = i;
+      if (par >= 0 && par < i)
+        w = (uint32_t)par | (1u << 11) | (s_tok[i] == s_g[par] ? kJumpOk : 0u);
+      else
+        w = (uint32_t)i;
     }
-    const int depth = s_depth[best];
-    int32_t* o = out_tokens + (size_t)b * (max_depth + 1);
+    s_jump[0][i] = w;
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int span = 1; span < N; span <<= 1) {  // ceil(log2 N) rounds
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int i = tid + kTreeThreads * j;
+      if (i >= N) break;
+      const uint32_t w = s_jump[cur][i];
+      const uint32_t wa = s_jump[cur][w & kJumpA];
+      const uint32_t d = ((w >> 11) & kJumpA) + ((wa >> 11) & kJumpA);
+      s_jump[cur ^ 1][i] = (wa & kJumpA) | (d << 11) | (w & wa & kJumpOk);
+    }
+    __syncthreads();
+    cur ^= 1;
+  }
+  // deepest accepted node, lowest index on ties: max of (depth, 2047 - index)
+  int key = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + kTreeThreads * j;
+    if (i >= N) break;
+    const uint32_t w = s_jump[cur][i];
+    const int d = (int)((w >> 11) & kJumpA);
+    if ((w & kJumpOk) && d <= max_depth) key = max(key, (d << 11) | (2047 - i));
+  }
+  key = wave_reduce(key, [](int x, int y) { return x > y ? x : y; });
+  if (lane_id() == 0) s_best[wave_id()] = key;
+  __syncthreads();
+  key = max(max(s_best[0], s_best[1]), max(s_best[2], s_best[3]));
+  const int best = 2047 - (key & 2047);
+  const int depth = key >> 11;
+  int32_t* o = out_tokens + (size_t)b * (max_depth + 1);
+  for (int j = depth + 1 + tid; j <= max_depth; j += kTreeThreads) o[j] = -1;
+  if (tid == 0) {
     int i = best;
     for (int j = depth - 1; j >= 0; --j) {
       o[j] = s_tok[i];
       i = s_par[i];
     }
     o[depth] = s_g[best];
-    for (int j = depth + 1; j <= max_depth; ++j) o[j] = -1;
     out_n[b] = depth;
     if (out_last) out_last[b] = best;
   }
@@ -3024,14 +3181,15 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
   const bool row_is_chunk = dm.nchunks == 1 && !sp.greedy && !sp.topp_hist &&
                             !(sp.top_k > 0 && sp.top_k < dm.V) && !(sp.top_p < 1.0f);
   if (sp.compact) {
+    // large k: the tile-0 threshold from 1024 group maxima (a kernel of its own)
+    auto topk_row = sp.top_k > 64 ? k_topk_row<E, true> : k_topk_row<E, false>;
     if (presampled && dm.K > 0) {  // draft rows summarised by spec_sample: stream the targets only
       hipLaunchKernelGGL(k_take_draft_summaries, dim3(dm.B * dm.K), dim3(64), 0, st, dm,
                          *presampled, ws);
-      hipLaunchKernelGGL((k_topk_row<E>), dim3(dm.B * (dm.K + 1)), dim3(kThreads), 0, st, t, d,
-                         dm, sp, ws, 1);
+      hipLaunchKernelGGL(topk_row, dim3(dm.B * (dm.K + 1)), dim3(kThreads), 0, st, t, d, dm, sp,
+                         ws, 1);
     } else {
-      hipLaunchKernelGGL((k_topk_row<E>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws,
-                         0);
+      hipLaunchKernelGGL(topk_row, dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws, 0);
     }
     if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
     if (out_beta) {  // acceptance rates from the row summaries (read-only for the steps below)
@@ -3163,7 +3321,7 @@ hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int
                        t, d, sp, ws);
   }
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], stream);
-  hipLaunchKernelGGL(k_tree_walk, dim3(d.B), dim3(kSeqThreads), 0, stream, d, ws, parent, tokens,
+  hipLaunchKernelGGL(k_tree_walk, dim3(d.B), dim3(kTreeThreads), 0, stream, d, ws, parent, tokens,
                      max_depth, out_tokens, out_n, out_last);
   if (ev && nev >= 3) (void)hipEventRecord(ev[2], stream);
   return hipGetLastError();

@@ -29,10 +29,8 @@ import os
 from collections import Counter
 
 import numpy as np
-import torch
 
 import oracle.spec_verify_oracle as O
-from workloads import synthetic as S
 
 FLIP_BAND = 1e-6
 ATOL, RTOL = 1e-5, 1e-4
@@ -46,6 +44,7 @@ FLIP_LOG = []
 # ---------------------------------------------------------------------------------- inputs
 def make_inputs(target, draft, params, seed):
     """Draft tokens (oracle sampler on the draft rows) and uniforms for given logits."""
+    from workloads import synthetic as S
     B, K1, V = target.shape
     K = K1 - 1
     df = draft.float().cpu().numpy() if K > 0 else None
@@ -61,6 +60,7 @@ def make_inputs(target, draft, params, seed):
 
 
 def run_gpu(target, draft, drafts, u, params, device="cuda"):
+    import torch
     import speculative_sampling_verification_amd as svm
     t = target.to(device)
     d = draft.to(device) if draft is not None else None
@@ -76,9 +76,10 @@ def run_gpu(target, draft, drafts, u, params, device="cuda"):
 
 
 def _np(x):
+    """Host float32 array of a torch tensor (on any device) or an array."""
     if x is None:
         return None
-    if isinstance(x, torch.Tensor):
+    if hasattr(x, "cpu") and hasattr(x, "float"):
         return x.float().cpu().numpy()
     return np.asarray(x, dtype=np.float32)
 

@@ -256,3 +256,15 @@ def test_full_size_topp_workload():
 def test_full_size_dense_workload():
     _announce("full size B=64 K=4 V=32000 bf16 T=1, 16 sampled sequences")
     _full_size_check("normal_B64_K4_V32000_bf16", 16, 33)
+
+
+def test_full_size_topk_topp_workload():
+    _announce("full size B=256 K=7 V=128256 bf16 top-k 256 + top-p 0.9 T=0.7, 8 sampled sequences")
+    _full_size_check("zipf_B256_K7_V128256_bf16_topk256_topp90", 8, 34)
+
+
+def test_topk256_topp_bf16_ties():
+    _announce("top-k 256 + top-p 0.9 on bf16 rows with many tied logits, B=6 K=3 V=50000")
+    t, d = S.zipf_logits(6, 3, 50000, 1.1, 1.0, "bf16", seed=35)
+    t, d = (t * 4).round() / 4, (d * 4).round() / 4  # coarse values: ties at both boundaries
+    verify_case(t, d, dict(temperature=0.7, top_k=256, top_p=0.9), seed=35)

@@ -9,7 +9,8 @@ Recipes (all noise is i.i.d. per element and fresh for every row):
 
 * ``normal``  (small fp32 case and the B=64 bf16 case): draft d ~ N(0, sd^2),
   target t = scale * d + N(0, noise^2).  Target row K has a fresh, unstored draft row behind it.
-* ``zipf``    (B=256 K=7 V=128256 bf16 top-k case and B=128 K=3 V=256000 fp32 top-p case):
+* ``zipf``    (B=256 K=7 V=128256 bf16 top-k case, the same shape with top-k 256 + top-p 0.9, and
+  B=128 K=3 V=256000 fp32 top-p case):
   per (sequence, position) a random permutation gives each token a rank r in 1..V;
   base = -s*ln(r) + sigma*N(0,1); target = base + sigma*N(0,1) and draft = base + sigma*N(0,1),
   the target and draft rows of one position sharing ``base``.
@@ -47,6 +48,9 @@ WORKLOADS = {
     "zipf_B256_K7_V128256_bf16_topk50": dict(
         B=256, K=7, V=128256, dtype="bf16", gen="zipf", s=1.1, sigma=1.0,
         temperature=0.7, top_k=50, top_p=1.0, lenience=1.0),
+    "zipf_B256_K7_V128256_bf16_topk256_topp90": dict(
+        B=256, K=7, V=128256, dtype="bf16", gen="zipf", s=1.1, sigma=1.0,
+        temperature=0.7, top_k=256, top_p=0.9, lenience=1.0),
     "zipf_B128_K3_V256000_f32_topp95": dict(
         B=128, K=3, V=256000, dtype="f32", gen="zipf", s=1.1, sigma=2.0,
         temperature=1.0, top_k=0, top_p=0.95, lenience=1.0),
