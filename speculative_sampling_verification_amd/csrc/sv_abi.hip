@@ -141,6 +141,10 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const size_t o_hist = c.take(th ? rows * nch * kHistBins * sizeof(unsigned long long) : 0);
   const size_t o_tprow = c.take(th ? rows * sizeof(TopPRow) : 0);
   const size_t o_tcand = c.take(th ? rows * kTopPCandCap * sizeof(uint2) : 0);
+  const size_t tsegs = th ? (size_t)d.B * (d.K + 1) * nch : 0;  // target-row chunk segments
+  const size_t o_tkept = c.take(tsegs * kTopPSegCap * sizeof(uint2));
+  const size_t o_tkcnt = c.take(tsegs * sizeof(int));
+  const size_t o_lpart = c.take(th ? (size_t)d.B * nch * sizeof(ulonglong2) : 0);
   const bool me = s.mentor && d.K > 0;
   const size_t o_ment = c.take(me ? (size_t)d.B * d.K * sizeof(MentorSol) : 0);
   const bool bp = !s.compact && !s.greedy;
@@ -156,6 +160,9 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
     ws->hist = th ? at<unsigned long long>(base, o_hist) : nullptr;
     ws->tprow = th ? at<TopPRow>(base, o_tprow) : nullptr;
     ws->tcand = th ? at<uint2>(base, o_tcand) : nullptr;
+    ws->tkept = th ? at<uint2>(base, o_tkept) : nullptr;
+    ws->tkcnt = th ? at<int>(base, o_tkcnt) : nullptr;
+    ws->lpart = th ? at<ulonglong2>(base, o_lpart) : nullptr;
     ws->ment = me ? at<MentorSol>(base, o_ment) : nullptr;
     ws->bpart = bp ? at<double>(base, o_bpart) : nullptr;
   }

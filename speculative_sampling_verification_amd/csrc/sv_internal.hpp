@@ -7,7 +7,8 @@
 //                                     parameters (max m, threshold thr, normaliser S)
 //   k_seq     grid = B             : accept tests, first-rejection scan, and the final draw when
 //                                     the final row is greedy
-//   k_final_partial / k_final_pick : the final draw over a full row pair
+//   k_final_partial / k_final_pick : the final draw over a full row pair (top-p: or over the
+//                                     kept segments k_topp_cand wrote for the target row)
 // With compact top-k rows (top-k <= kCompactMaxK) two launches do everything: k_topk_row (one
 // workgroup per row: streaming, candidate selection and the row merge) and k_seq_compact (one
 // workgroup per sequence: accept tests and the final draw).
@@ -30,6 +31,7 @@ constexpr int kSeqThreads = 64;      // one wave per sequence
 constexpr int kHistBins = 512;       // top-p mass histogram bins per chunk ...
 constexpr int kHistPerUnit = 8;      // ... on a grid of 1/8 of a unit of z / T
 constexpr int kTopPCandCap = 4096;   // boundary candidates a top-p row may hold
+constexpr int kTopPSegCap = 1024;    // kept-list entries of one chunk of a top-p target row
 constexpr int kMentorBisectionSteps = 50;  // bisection steps on alpha (mentored decoding)
 constexpr int kRestMaxM = 128;  // candidates per sequence (REST tree builder)
 constexpr int kRestMaxL = 32;   // tokens per candidate
@@ -89,7 +91,7 @@ struct alignas(16) SeqState {
   int n;           // accepted drafts
   int need_dense;  // 1 if the final draw runs in k_final_partial / k_final_pick
   int fallback;    // 1 if the residual had zero mass and q was used
-  int pad;
+  int need_list;   // 1 if the final draw runs over the target row's kept segments (top-p)
 };
 
 struct Dims {
@@ -131,6 +133,13 @@ struct Workspace {
   unsigned long long* hist;  // [rows][nchunks][kHistBins] fixed-point mass   top-p histogram only
   TopPRow* tprow;            // [rows]                                        top-p histogram only
   uint2* tcand;              // [rows][kTopPCandCap] (index, bits)            top-p histogram only
+  uint2* tkept;              // [B*(K+1)][nchunks][kTopPSegCap] (index, bits) of every element
+                             // of a target row's chunk at or above the boundary bracket, in no
+                             // particular order                             top-p histogram only
+  int* tkcnt;                // [B*(K+1)][nchunks] entries of each segment (> kTopPSegCap:
+                             // overflowed)                                   top-p histogram only
+  ulonglong2* lpart;         // [B][nchunks] the final draw's fixed-point masses (residual, q) of
+                             // each segment                                  top-p histogram only
   MentorSol* ment;           // [B][K]                                        mentored only
   double* bpart;             // [B*K][nfchunks] acceptance-rate partials      dense rows only
 };

@@ -117,6 +117,10 @@ constexpr int kRegs = kVecPerThread * 4;  // 32-bit registers per thread holding
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// Lanes of the wave below this one, as a ballot mask.
+__device__ __forceinline__ unsigned long long lanes_below() {
+  return (1ull << lane_id()) - 1ull;
+}
 
 template <class T, class Op>
 __device__ __forceinline__ T wave_reduce(T v, Op op) {
@@ -667,8 +671,17 @@ __device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPar
 
 // Candidates of the boundary bins, appended to the row's list (in no particular order:
 // k_topp_select's result does not depend on it).  A chunk gathers its candidates in LDS and
-// reserves room in the row's list with one atomic add.
+// reserves room in the row's list with one atomic add.  A chunk of a target row also writes its
+// kept segment: every element at or above the candidate range's lower edge (everything top-p may
+// keep), up to kTopPSegCap, and its count; the final draw reads the segments instead of the row.
 constexpr int kToppChunkCap = 2048;  // candidates one chunk may gather
+
+// Index of row r's kept list (its target row index b * (K + 1) + k), or -1 for a draft row.
+__device__ __forceinline__ int kept_list_of(const Dims& dm, int r) {
+  if (dm.rows_per_seq == 1) return r;
+  const int b = r / dm.rows_per_seq, j = r - b * dm.rows_per_seq;
+  return j <= dm.K ? b * (dm.K + 1) + j : -1;
+}
 
 template <class E>
 __global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tgt,
@@ -680,10 +693,15 @@ __global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tg
   const int tid = threadIdx.x;
   const E* row = row_ptr(dm, tgt, drf, r);
   const int e_lo = ws.tprow[r].e_lo, e_hi = ws.tprow[r].e_hi;
+  const int kl = kept_list_of(dm, r);
   const float it = sp.inv_t;
   __shared__ uint2 s_c[kToppChunkCap];
-  __shared__ int s_n, s_base;
-  if (tid == 0) s_n = 0;
+  __shared__ uint2 s_k[kTopPSegCap];
+  __shared__ int s_n, s_nk, s_base;
+  if (tid == 0) {
+    s_n = 0;
+    s_nk = 0;
+  }
   uint32_t regs[kRegs];
   const int c0 = c * dm.chunk_elems -
                  load_chunk_frame<E>(row, dm.V, c, dm.chunk_elems, regs, Tr<E>::kNegInfPair);
@@ -696,24 +714,37 @@ __global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tg
       for (int h = 0; h < Tr<E>::kPerDword; ++h) {
         const float z = Tr<E>::elem(regs[4 * i + d], h);
         const int e = topp_edge(z, it);
-        if (z > -INFINITY && e >= e_lo && e <= e_hi) {
-          const int pos = atomicAdd(&s_n, 1);
-          if (pos < kToppChunkCap)
-            s_c[pos] = make_uint2(slot_index<E>(c0, i, d, h), __float_as_uint(z));
+        if (z > -INFINITY && e >= e_lo) {
+          const uint2 entry = make_uint2(slot_index<E>(c0, i, d, h), __float_as_uint(z));
+          if (e <= e_hi) {
+            const int pos = atomicAdd(&s_n, 1);
+            if (pos < kToppChunkCap) s_c[pos] = entry;
+          }
+          if (kl >= 0) {
+            const int pos = atomicAdd(&s_nk, 1);
+            if (pos < kTopPSegCap) s_k[pos] = entry;
+          }
         }
       }
     }
   }
   __syncthreads();
-  const int n = s_n;
+  const int n = s_n, nk = s_nk;
+  if (kl >= 0) {  // the segment (a count above kTopPSegCap marks it overflowed)
+    const size_t seg = (size_t)kl * dm.nchunks + c;
+    if (tid == 0) ws.tkcnt[seg] = nk;
+    if (nk <= kTopPSegCap)
+      for (int j = tid; j < nk; j += kThreads) ws.tkept[seg * kTopPSegCap + j] = s_k[j];
+  }
   if (n == 0) return;
   if (tid == 0)  // a chunk that overflowed its buffer pushes the row past the list capacity
     s_base = atomicAdd(&ws.tprow[r].count, n <= kToppChunkCap ? n : kTopPCandCap + 1);
   __syncthreads();
-  const int base = s_base;
-  uint2* list = ws.tcand + (size_t)r * kTopPCandCap;
-  if (n <= kToppChunkCap)
+  if (n <= kToppChunkCap) {
+    const int base = s_base;
+    uint2* list = ws.tcand + (size_t)r * kTopPCandCap;
     for (int j = tid; j < n && base + j < kTopPCandCap; j += kThreads) list[base + j] = s_c[j];
+  }
 }
 
 // Order-preserving key of a float (see Tr), with -0 merged into +0.
@@ -1037,6 +1068,20 @@ __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ 
   return n;
 }
 
+// A top-p target row's kept segments hold every element at or above the candidate range's lower
+// edge; they hold the whole kept set {z >= thr} iff none overflowed and the threshold's edge is
+// inside that range (a row whose boundary selection re-read the row may have a threshold below
+// it).  Called by a whole wave; the same answer in every lane.
+__device__ __forceinline__ bool kept_list_complete(const Dims& dm, const Samp& sp,
+                                                   const Workspace& ws, int b, int n,
+                                                   const RowStat& rt) {
+  const TopPRow tr = ws.tprow[target_row(dm, b, n)];
+  bool ok = tr.e_lo == INT_MIN || topp_edge(rt.thr, sp.inv_t) >= tr.e_lo;
+  const int* cnt = ws.tkcnt + (size_t)(b * (dm.K + 1) + n) * dm.nchunks;
+  for (int c = lane_id(); c < dm.nchunks; c += 64) ok = ok && cnt[c] <= kTopPSegCap;
+  return __ballot(!ok) == 0ull;
+}
+
 // ------------------------------------------------------------------------------------------
 // k_seq: one wave per sequence.  Accept tests, first rejection, and the final draw when the
 // final row is greedy or compact.
@@ -1062,7 +1107,7 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
   st.n = n;
   st.need_dense = 0;
   st.fallback = 0;
-  st.pad = 0;
+  st.need_list = 0;
   int tok = -1;
   if (rt.kind == kRowGreedy) {
     // one-hot q and p: the residual is one-hot at the target argmax or empty (then q is used)
@@ -1112,13 +1157,15 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
       if (pick < 0) pick = 0;
       tok = (int)kept[pick].x;
     }
+  } else if (sp.topp_hist && kept_list_complete(dm, sp, ws, b, n, rt)) {
+    st.need_list = 1;  // top-p: the draw reads the target row's kept list
   } else {
     st.need_dense = 1;
   }
   if (lane == 0) {
-    if (!st.need_dense) out_tokens[(size_t)b * (K + 1) + n] = tok;
+    if (!st.need_dense && !st.need_list) out_tokens[(size_t)b * (K + 1) + n] = tok;
     ws.seq[b] = st;
-    if (st.need_dense) {  // read by the final draw's kernels with the state, in one step
+    if (st.need_dense || st.need_list) {  // read by the final draw's kernels with the state
       ws.dstat[2 * b] = rt;
       ws.dstat[2 * b + 1] = rd_n;
     }
@@ -1232,22 +1279,260 @@ __device__ __forceinline__ void load_vecs(const E* __restrict__ row, int end, in
 }
 
 // ------------------------------------------------------------------------------------------
+// The final draw of a top-p sequence from the kept segments of its target row n (every element
+// top-p may keep, per chunk, in no particular order): q = exp((z - m) / T) / S on the kept set
+// {z >= thr}, p at the same index from the draft row (the residual (q - p)_+ is zero wherever q
+// is), or q alone for the bonus draw.  Weights are taken in 2^-62 fixed point, so that every
+// sum is exact whatever the order of its terms; the token is the smallest index whose
+// cumulative weight in index order exceeds u * W.
+//   final_lpart  (in k_final_partial, one workgroup per segment): each segment's masses
+//   final_lpick  (in k_final_pick, one workgroup per sequence): the segment holding u * W from
+//                the masses in chunk order, then the index inside it by two digits (bins of 256
+//                indices, then single indices)
+// ------------------------------------------------------------------------------------------
+template <class E>
+__device__ __forceinline__ void list_weights(uint2 en, const RowStat& rt, const RowStat& rd,
+                                             bool resid, const E* __restrict__ drow, float it,
+                                             unsigned long long& wq, unsigned long long& ww) {
+  const float z = __uint_as_float(en.y);
+  const double q = z >= rt.thr ? (double)fast_exp((z - rt.m) * it) / rt.S : 0.0;
+  double w = q;
+  if (resid && q > 0.0) {
+    const double p = (double)kept_exp(load_logit(drow, (int)en.x), rd, it) / rd.S;
+    w = q - p > 0.0 ? q - p : 0.0;
+  }
+  wq = (unsigned long long)(q * 0x1p62);
+  ww = (unsigned long long)(w * 0x1p62);
+}
+
+template <class E>
+__device__ void final_lpart(const E* __restrict__ tgt, const E* __restrict__ drf, const Dims& dm,
+                            const Samp& sp, const Workspace& ws, int b, int c, const SeqState& st,
+                            const RowStat& rt, const RowStat& rd) {
+  const int K = dm.K, n = st.n;
+  const bool resid = n < K;
+  const size_t seg = (size_t)(b * (K + 1) + n) * dm.nchunks + c;
+  const int cnt = ws.tkcnt[seg];
+  const uint2* list = ws.tkept + seg * kTopPSegCap;
+  const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
+  unsigned long long W = 0, Q = 0;
+  for (int e = threadIdx.x; e < cnt; e += kThreads) {
+    unsigned long long wq, ww;
+    list_weights<E>(list[e], rt, rd, resid, drow, sp.inv_t, wq, ww);
+    W += ww;
+    Q += wq;
+  }
+  auto add = [](unsigned long long x, unsigned long long y) { return x + y; };
+  W = wave_reduce(W, add);
+  Q = wave_reduce(Q, add);
+  __shared__ unsigned long long s_wq[2][kThreads / 64];
+  if (lane_id() == 0) {
+    s_wq[0][wave_id()] = W;
+    s_wq[1][wave_id()] = Q;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    ws.lpart[(size_t)b * dm.nchunks + c] =
+        make_ulonglong2(s_wq[0][0] + s_wq[0][1] + s_wq[0][2] + s_wq[0][3],
+                        s_wq[1][0] + s_wq[1][1] + s_wq[1][2] + s_wq[1][3]);
+}
+
+// One wave: the first of PER * 64 bins, in order, at which the running mass exceeds rem (bins
+// without mass never qualify); if rounding leaves none, the last bin with mass.  Returns the bin
+// and sets before to the mass of the bins ahead of it.
+template <int PER>
+__device__ int wave_pick_bin(const unsigned long long* bins, double rem,
+                             unsigned long long& before) {
+  const int lane = lane_id();
+  unsigned long long bv[PER], loc = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    bv[i] = bins[PER * lane + i];
+    loc += bv[i];
+  }
+  unsigned long long inc = loc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  unsigned long long cum = inc - loc, bf = 0, bl = 0;
+  int hit = -1, last = -1;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (hit < 0 && bv[i] > 0 && (double)(cum + bv[i]) > rem) {
+      hit = i;
+      bf = cum;
+    }
+    if (bv[i] > 0) {
+      last = i;
+      bl = cum;
+    }
+    cum += bv[i];
+  }
+  const unsigned long long hl = __ballot(hit >= 0), pl = __ballot(last >= 0);
+  if (hl) {
+    const int f = __ffsll((long long)hl) - 1;
+    before = __shfl(bf, f);
+    return __shfl(PER * lane + hit, f);
+  }
+  const int f = pl ? 63 - __clzll((long long)pl) : 0;
+  before = pl ? __shfl(bl, f) : 0ull;
+  return pl ? __shfl(PER * lane + last, f) : 0;
+}
+
+template <class E>
+__device__ void final_lpick(const E* __restrict__ tgt, const E* __restrict__ drf, const Dims& dm,
+                            const Samp& sp, const Workspace& ws, const float* __restrict__ uni,
+                            int32_t* __restrict__ out_tokens, int b, const SeqState& st,
+                            const RowStat& rt, const RowStat& rd) {
+  const int tid = threadIdx.x, lane = lane_id();
+  const int K = dm.K, n = st.n;
+  const bool resid = n < K;
+  constexpr int PE = kTopPSegCap / kThreads;  // entries per thread
+  __shared__ unsigned long long s_bins[256];
+  __shared__ int s_c, s_d1;
+  __shared__ double s_rem;
+  __shared__ int s_useq;
+  // the segment holding u * W: wave 0 scans the segments' masses in chunk order
+  if (tid < 64) {
+    const ulonglong2* lp = ws.lpart + (size_t)b * dm.nchunks;
+    unsigned long long W = 0, Q = 0;
+    for (int c = lane; c < dm.nchunks; c += 64) {
+      W += lp[c].x;
+      Q += lp[c].y;
+    }
+    auto add = [](unsigned long long x, unsigned long long y) { return x + y; };
+    W = wave_reduce(W, add);
+    Q = wave_reduce(Q, add);
+    const bool use_q = !resid || W == 0ull;
+    double rem = (double)uni[(size_t)b * (K + 1) + K] * (double)(use_q ? Q : W);
+    unsigned long long carry = 0;
+    int pick = -1, last = -1;
+    unsigned long long before_last = 0;
+    double rem_pick = 0.0;
+    for (int c0 = 0; c0 < dm.nchunks && pick < 0; c0 += 64) {
+      const int c = c0 + lane;
+      const unsigned long long m = c < dm.nchunks ? (use_q ? lp[c].y : lp[c].x) : 0ull;
+      unsigned long long inc = m;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      const unsigned long long cb = carry + inc - m;  // mass of the chunks ahead of c
+      const unsigned long long hl = __ballot(m > 0 && (double)(cb + m) > rem);
+      const unsigned long long pl = __ballot(m > 0);
+      if (hl) {
+        const int f = __ffsll((long long)hl) - 1;
+        pick = c0 + f;
+        rem_pick = rem - (double)__shfl(cb, f);
+      } else if (pl) {
+        const int f = 63 - __clzll((long long)pl);
+        last = c0 + f;
+        before_last = __shfl(cb, f);
+      }
+      carry += __shfl(inc, 63);
+    }
+    if (pick < 0) {  // rounding left u W at or past the total: the last chunk with mass
+      pick = last < 0 ? 0 : last;
+      rem_pick = rem - (double)before_last;
+    }
+    if (lane == 0) {
+      s_c = pick;
+      s_rem = rem_pick;
+      s_useq = use_q ? 1 : 0;
+    }
+  }
+  s_bins[tid] = 0ull;
+  __syncthreads();
+  const int c = s_c;
+  const bool use_q = s_useq != 0;
+  double rem = s_rem;
+  // the segment's entries, in registers: index relative to the chunk's first slot, weight
+  const size_t seg = (size_t)(b * (K + 1) + n) * dm.nchunks + c;
+  const int cnt = min(ws.tkcnt[seg], kTopPSegCap);
+  const uint2* list = ws.tkept + seg * kTopPSegCap;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
+  const int base = c * dm.chunk_elems - row_phase(trow);  // element index of the chunk's first slot
+  const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
+  int ri[PE];
+  unsigned long long xw[PE];
+#pragma unroll
+  for (int i = 0; i < PE; ++i) {
+    const int e = tid + kThreads * i;
+    ri[i] = -1;
+    xw[i] = 0ull;
+    if (e < cnt) {
+      const uint2 en = list[e];
+      unsigned long long wq, ww;
+      list_weights<E>(en, rt, rd, resid, drow, sp.inv_t, wq, ww);
+      ri[i] = (int)en.x - base;
+      xw[i] = use_q ? wq : ww;
+    }
+  }
+  // first digit: bins of 256 indices (a chunk spans at most 32768 indices: 128 bins)
+#pragma unroll
+  for (int i = 0; i < PE; ++i)
+    if (xw[i]) atomicAdd(&s_bins[ri[i] >> 8], xw[i]);
+  __syncthreads();
+  if (tid < 64) {
+    unsigned long long before;
+    const int d1 = wave_pick_bin<4>(s_bins, rem, before);
+    if (lane == 0) {
+      s_d1 = d1;
+      s_rem = rem - (double)before;
+    }
+  }
+  __syncthreads();
+  const int d1 = s_d1;
+  rem = s_rem;
+  s_bins[tid] = 0ull;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PE; ++i)
+    if (xw[i] && (ri[i] >> 8) == d1) atomicAdd(&s_bins[ri[i] & 255], xw[i]);
+  __syncthreads();
+  if (tid < 64) {
+    unsigned long long before;
+    const int d2 = wave_pick_bin<4>(s_bins, rem, before);
+    if (lane == 0) {
+      out_tokens[(size_t)b * (K + 1) + n] = base + (d1 << 8) + d2;
+      if (resid && use_q) {  // the residual had zero mass: q is used (reported)
+        SeqState s2 = st;
+        s2.fallback = 1;
+        ws.seq[b] = s2;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // k_final_partial: grid = B x final chunks; mass of the final weights per chunk (residual,
 // target).  A final chunk is FR vector rows of 256 threads x 16 bytes (FR = kVecPerThread: a
 // whole chunk; FR = 4 or 1 when the sequences are fewer and each chunk is split).
 // ------------------------------------------------------------------------------------------
-template <class E, bool VEC, int FR>
+template <class E, bool VEC, int FR, bool LIST>
 __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict__ tgt,
                                                             const E* __restrict__ drf, Dims dm,
                                                             Samp sp, Workspace ws) {
-  const int bid = xcd_contiguous((int)blockIdx.x, dm.B * dm.nfchunks);
-  const int b = bid / dm.nfchunks;
-  const int c = bid - b * dm.nfchunks;
+  // LIST (top-p): max(final chunks, chunks) workgroups per sequence; a sequence drawn from its
+  // kept segments takes the first `chunks` of them, one per segment
+  const int G = LIST ? max(dm.nfchunks, dm.nchunks) : dm.nfchunks;
+  const int bid = xcd_contiguous((int)blockIdx.x, dm.B * G);
+  const int b = bid / G;
+  const int c = bid - b * G;
   // the state and the rows' statistics in one step (the statistics are stale, and unused,
-  // when the sequence needs no dense draw)
+  // when the sequence needs no draw here)
   const SeqState st = ws.seq[b];
   const RowStat rt = ws.dstat[2 * b], rd = ws.dstat[2 * b + 1];
-  if (!st.need_dense) return;
+  if constexpr (LIST) {
+    if (st.need_list) {
+      if (c < dm.nchunks) final_lpart<E>(tgt, drf, dm, sp, ws, b, c, st, rt, rd);
+      return;
+    }
+  }
+  if (!st.need_dense || c >= dm.nfchunks) return;
   __shared__ RedScratch red;
   const int n = st.n;
   const DrawRows g = draw_rows(dm, n, rt, rd);
@@ -1362,7 +1647,7 @@ __device__ double block_exclusive_d2(double a, double b, double& a_tot, double& 
 // and its owner finds the index.  With a single chunk the chunk pass is skipped and the totals
 // come from the tile itself.
 // ------------------------------------------------------------------------------------------
-template <class E, bool VEC, int NR>
+template <class E, bool VEC, int NR, bool LIST>
 __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ tgt,
                                                          const E* __restrict__ drf, Dims dm,
                                                          Samp sp, Workspace ws,
@@ -1393,6 +1678,12 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
     for (int cc = ca; cc < cb; ++cc) {
       w_loc += mass(cc, false);
       q_loc += mass(cc, true);
+    }
+  }
+  if constexpr (LIST) {
+    if (st.need_list) {  // top-p: the draw from the kept segments
+      final_lpick<E>(tgt, drf, dm, sp, ws, uni, out_tokens, b, st, srt, srd);
+      return;
     }
   }
   if (!st.need_dense) return;
@@ -1615,9 +1906,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-__device__ __forceinline__ unsigned long long lanes_below() {
-  return (1ull << lane_id()) - 1ull;
-}
 
 struct alignas(16) RowLds {
   // per-wave candidate lists: canonical keys and vocabulary indices; entries kWaveListCap ..
@@ -3168,6 +3456,35 @@ __global__ __launch_bounds__(kThreads) void k_beta_merge(Dims dm, Workspace ws,
 // ------------------------------------------------------------------------------------------
 // Launch helpers
 // ------------------------------------------------------------------------------------------
+// The final draw's two kernels at the grain Dims chose (see make_dims); LIST also draws the
+// top-p sequences whose kept segments are complete.
+template <class E, bool VEC, bool LIST>
+void launch_final(const E* t, const E* d, const Dims& dm, const Samp& sp, const Workspace& ws,
+                  const float* uni, int32_t* out_tokens, hipStream_t st) {
+  const int G = LIST ? max(dm.nfchunks, dm.nchunks) : dm.nfchunks;
+  const dim3 pgrid((unsigned)((size_t)dm.B * G));
+  const bool partial = LIST || dm.nfchunks > 1;
+  if (dm.fchunk_elems == dm.chunk_elems) {
+    if (partial)
+      hipLaunchKernelGGL((k_final_partial<E, VEC, kVecPerThread, LIST>), pgrid, dim3(kThreads), 0,
+                         st, t, d, dm, sp, ws);
+    hipLaunchKernelGGL((k_final_pick<E, VEC, kVecPerThread, LIST>), dim3(dm.B), dim3(kThreads), 0,
+                       st, t, d, dm, sp, ws, uni, out_tokens);
+  } else if (dm.fchunk_elems * 4 == dm.chunk_elems) {  // four vector rows per final chunk
+    if (partial)
+      hipLaunchKernelGGL((k_final_partial<E, VEC, 4, LIST>), pgrid, dim3(kThreads), 0, st, t, d,
+                         dm, sp, ws);
+    hipLaunchKernelGGL((k_final_pick<E, VEC, 4, LIST>), dim3(dm.B), dim3(kThreads), 0, st, t, d,
+                       dm, sp, ws, uni, out_tokens);
+  } else {  // one vector row per final chunk
+    if (partial)
+      hipLaunchKernelGGL((k_final_partial<E, VEC, 1, LIST>), pgrid, dim3(kThreads), 0, st, t, d,
+                         dm, sp, ws);
+    hipLaunchKernelGGL((k_final_pick<E, VEC, 1, LIST>), dim3(dm.B), dim3(kThreads), 0, st, t, d,
+                       dm, sp, ws, uni, out_tokens);
+  }
+}
+
 template <class E, bool VEC>
 hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& sp,
                            const int32_t* drafts, const float* uni, int32_t* out_tokens,
@@ -3246,26 +3563,10 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
   }
   hipLaunchKernelGGL((k_seq<E>), dim3(dm.B), dim3(kSeqThreads), 0, st, t, d, dm, sp, ws, o);
   if (!sp.greedy) {
-    const dim3 pgrid((unsigned)((size_t)dm.B * dm.nfchunks));
-    if (dm.fchunk_elems == dm.chunk_elems) {
-      if (dm.nfchunks > 1)
-        hipLaunchKernelGGL((k_final_partial<E, VEC, kVecPerThread>), pgrid, dim3(kThreads), 0,
-                           st, t, d, dm, sp, ws);
-      hipLaunchKernelGGL((k_final_pick<E, VEC, kVecPerThread>), dim3(dm.B), dim3(kThreads), 0,
-                         st, t, d, dm, sp, ws, uni, out_tokens);
-    } else if (dm.fchunk_elems * 4 == dm.chunk_elems) {  // four vector rows per final chunk
-      if (dm.nfchunks > 1)
-        hipLaunchKernelGGL((k_final_partial<E, VEC, 4>), pgrid, dim3(kThreads), 0, st, t, d,
-                           dm, sp, ws);
-      hipLaunchKernelGGL((k_final_pick<E, VEC, 4>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm,
-                         sp, ws, uni, out_tokens);
-    } else {  // one vector row per final chunk
-      if (dm.nfchunks > 1)
-        hipLaunchKernelGGL((k_final_partial<E, VEC, 1>), pgrid, dim3(kThreads), 0, st, t, d,
-                           dm, sp, ws);
-      hipLaunchKernelGGL((k_final_pick<E, VEC, 1>), dim3(dm.B), dim3(kThreads), 0, st, t, d, dm,
-                         sp, ws, uni, out_tokens);
-    }
+    if (sp.topp_hist)  // each sequence drawn from its kept segments or, if incomplete, its rows
+      launch_final<E, VEC, true>(t, d, dm, sp, ws, uni, out_tokens, st);
+    else
+      launch_final<E, VEC, false>(t, d, dm, sp, ws, uni, out_tokens, st);
   }
   if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);
   return hipGetLastError();
