@@ -771,10 +771,12 @@ __global__ __launch_bounds__(kThreads) void k_topp_select(const E* __restrict__ 
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   __shared__ unsigned long long s_buf[kTopPCandCap / 2];  // candidate keys; radix bins on fallback
+  __shared__ unsigned long long s_wt[kTopPCandCap];       // candidate weights
   __shared__ unsigned long long s_bins[256];
   __shared__ RedScratch red;
   __shared__ uint32_t s_prefix;
   __shared__ unsigned long long s_need;
+  __shared__ uint32_t s_kmin[4], s_kmax[4];
   uint32_t* s_key = reinterpret_cast<uint32_t*>(s_buf);
   RowStat rs = ws.rstat[r];
   const TopPRow tr = ws.tprow[r];
@@ -788,16 +790,33 @@ __global__ __launch_bounds__(kThreads) void k_topp_select(const E* __restrict__ 
   if (!fallback) {
     const uint2* list = ws.tcand + (size_t)r * kTopPCandCap;
     unsigned long long tot = 0;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     for (int i = tid; i < n; i += kThreads) {
       const uint32_t key = float_key(__uint_as_float(list[i].y));
+      const unsigned long long w = topp_weight(key, m, it);
       s_key[i] = key;
-      tot += topp_weight(key, m, it);
+      s_wt[i] = w;
+      tot += w;
+      kmin = min(kmin, key);
+      kmax = max(kmax, key);
     }
     tot = wave_reduce(tot, [](unsigned long long x, unsigned long long y) { return x + y; });
-    if (lane_id() == 0) red.u[wave_id()] = tot;
-    if (tid == 0) s_prefix = 0u;
+    kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+    kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    if (lane_id() == 0) {
+      red.u[wave_id()] = tot;
+      s_kmin[wave_id()] = kmin;
+      s_kmax[wave_id()] = kmax;
+    }
     __syncthreads();
     tot = red.u[0] + red.u[1] + red.u[2] + red.u[3];
+    kmin = min(min(s_kmin[0], s_kmin[1]), min(s_kmin[2], s_kmin[3]));
+    kmax = max(max(s_kmax[0], s_kmax[1]), max(s_kmax[2], s_kmax[3]));
+    // the candidates share every key bit above the highest one where kmin and kmax differ, so
+    // the digits start at the 8-bit digit holding that bit
+    const int hb = kmin == kmax ? 0 : 31 - __clz(kmin ^ kmax);
+    const int s0 = (hb / 8) * 8;
+    if (tid == 0) s_prefix = s0 + 8 >= 32 ? 0u : (kmin & ~((1u << (s0 + 8)) - 1u));
     const double rem = (double)sp.top_p * S - tr.mass_above;
     unsigned long long need = 1ull;
     if (rem > 0.0) {
@@ -814,14 +833,14 @@ __global__ __launch_bounds__(kThreads) void k_topp_select(const E* __restrict__ 
       }
     } else {
       if (tid == 0) s_need = need;
-      for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int shift = s0; shift >= 0; shift -= 8) {
         for (int j = tid; j < 256; j += kThreads) s_bins[j] = 0ull;
         __syncthreads();
         const uint32_t prefix = s_prefix;
         for (int i = tid; i < n; i += kThreads) {
           const uint32_t key = s_key[i];
-          if (shift == 24 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
-            atomicAdd(&s_bins[(key >> shift) & 255u], topp_weight(key, m, it));
+          if (shift + 8 >= 32 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
+            atomicAdd(&s_bins[(key >> shift) & 255u], s_wt[i]);
         }
         __syncthreads();
         if (tid < 64) {  // digits from 255 down: lane L holds 255 - 4L - i, i = 0..3
@@ -861,7 +880,7 @@ __global__ __launch_bounds__(kThreads) void k_topp_select(const E* __restrict__ 
       thr = Tr<float>::key_to_float(v);
       unsigned long long own = 0;
       for (int i = tid; i < n; i += kThreads)
-        if (s_key[i] >= v) own += topp_weight(s_key[i], m, it);
+        if (s_key[i] >= v) own += s_wt[i];
       own = wave_reduce(own, [](unsigned long long x, unsigned long long y) { return x + y; });
       __syncthreads();
       if (lane_id() == 0) red.u[wave_id()] = own;
