@@ -74,7 +74,10 @@ typedef enum {
                                       library's built-in scratch buffer */
 } sv_status;
 
-typedef enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 } sv_dtype;
+/* Element type of the logit tensors.  An int32_t rather than an enum, so that whatever value a
+   caller passes is a valid argument for the library to check (SV_ERR_UNSUPPORTED_DTYPE). */
+typedef int32_t sv_dtype;
+enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 };
 
 /* Sampling parameters, applied identically to q and p (Chen et al. notes, A2). */
 typedef struct {

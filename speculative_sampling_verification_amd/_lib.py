@@ -165,6 +165,34 @@ def workspace(device, nbytes, stream=None):
     return buf
 
 
+def release_workspaces(device=None):
+    """Frees the cached workspaces (of one device, or of all) and the outgrown ones kept for
+    captured graphs, after the device has finished the work queued on them.  A HIP graph
+    captured over calls of this binding must not be replayed afterwards; the next call
+    allocates afresh.  Returns the number of bytes released."""
+    freed = 0
+    devs = {d for (_, d, _) in _workspaces} | {b.device.index for b in _outgrown}
+    for d in devs:
+        if device is None or torch.device(device).index in (None, d):
+            torch.cuda.synchronize(d)
+    keep = {}
+    for key, buf in _workspaces.items():
+        if device is None or torch.device(device).index in (None, key[1]):
+            freed += buf.numel()
+        else:
+            keep[key] = buf
+    _workspaces.clear()
+    _workspaces.update(keep)
+    rest = []
+    for buf in _outgrown:
+        if device is None or torch.device(device).index in (None, buf.device.index):
+            freed += buf.numel()
+        else:
+            rest.append(buf)
+    _outgrown[:] = rest
+    return freed
+
+
 def _stream(device, stream):
     s = stream if stream is not None else torch.cuda.current_stream(device)
     return ctypes.c_void_p(s.cuda_stream)

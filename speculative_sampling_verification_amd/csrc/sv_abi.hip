@@ -438,7 +438,7 @@ int spec_acceptance_rate(const void* target_logits, const void* draft_logits, sv
 double spec_expected_tokens(double alpha, int gamma) {
   if (!(alpha >= 0.0 && alpha <= 1.0) || gamma < 0) return NAN;
   if (alpha == 1.0) return (double)gamma + 1.0;
-  return (1.0 - std::pow(alpha, gamma + 1)) / (1.0 - alpha);
+  return (1.0 - std::pow(alpha, (double)gamma + 1.0)) / (1.0 - alpha);
 }
 
 double spec_walltime_speedup(double alpha, int gamma, double c) {

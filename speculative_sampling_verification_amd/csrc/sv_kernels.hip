@@ -3575,7 +3575,8 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
       const int npos = dm.B * dm.K;
       hipLaunchKernelGGL((k_beta_partial<E, VEC>), dim3((unsigned)((size_t)npos * dm.nfchunks)),
                          dim3(kThreads), 0, st, t, d, dm, sp, ws);
-      hipLaunchKernelGGL(k_beta_merge, dim3((npos + 3) / 4), dim3(kThreads), 0,
+      constexpr int kWaves = kThreads / 64;  // one wave per position
+      hipLaunchKernelGGL(k_beta_merge, dim3((npos + kWaves - 1) / kWaves), dim3(kThreads), 0,
                          st, dm, ws, out_beta);
     }
     if (rates_only) return hipGetLastError();

@@ -85,6 +85,44 @@ def test_alpha_matches_accept_decisions(svm):
     assert abs(svm.expected_tokens(alpha, 4) - O.expected_tokens_per_call(alpha, 4)) < 1e-12
 
 
+# The dense acceptance rates are summed at the final draw's grain, which make_dims picks from
+# B x chunks: one vector row per workgroup below 1024, a quarter chunk below 16384, else a whole
+# chunk.  Each grain on rows aligned to 16 bytes and on rows off that phase (V not a multiple of
+# the 4 fp32 elements of a vector), checked against the oracle on sampled positions.
+@pytest.mark.parametrize("B,V,grain", [
+    (256, 49153, "quarter chunks, rows off the 16-byte phase"),
+    (352, 49152, "quarter chunks, aligned rows"),
+    (8192, 16385, "whole chunks, rows off the 16-byte phase"),
+    (16384, 16384, "whole chunks, aligned rows"),
+])
+@pytest.mark.parametrize("params", [dict(temperature=1.0), dict(temperature=0.8, top_p=0.9)],
+                         ids=["dense", "top-p 0.9"])
+def test_acceptance_rate_grains(svm, B, V, grain, params):
+    _announce(f"acceptance rate at the {grain}: fp32 B={B} K=1 V={V} {params}")
+    t, d = S.zipf_logits(B, 1, V, 1.1, 1.0, "f32", device="cuda", seed=77)
+    g = svm.spec_acceptance_rate(t, d, **params).cpu().numpy()
+    torch.cuda.synchronize()
+    T = np.float32(params["temperature"])
+    P = np.float32(params.get("top_p", 1.0))
+    rng = np.random.default_rng(78)
+    pick = np.concatenate([[0, B - 1], rng.choice(np.arange(1, B - 1), 6, replace=False)])
+    checked = 0
+    for b in pick:
+        tf = t[b, 0].float().cpu().numpy()
+        df = d[b, 0].float().cpu().numpy()
+        dt, dd = {}, {}
+        q = O.row_distribution(tf, T, 0, P, diagnostics=dt)
+        p = O.row_distribution(df, T, 0, P, diagnostics=dd)
+        if min(dt["topp_margin"], dd["topp_margin"]) < 1e-6:
+            continue  # a top-p boundary within rounding: either kept set is correct
+        o = O.acceptance_rate(q, p, 1.0)
+        assert abs(g[b, 0] - o) <= 1e-5, (b, g[b, 0], o)
+        checked += 1
+    assert checked >= 6
+    del t, d
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("name,params,shape,V,dtype", [
     ("compact top-k 50 bf16", dict(temperature=0.7, top_k=50), (16, 7), 50000, "bf16"),
     ("dense fp32", dict(temperature=1.0), (6, 3), 40000, "f32"),

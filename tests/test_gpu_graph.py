@@ -199,3 +199,25 @@ def test_two_streams_at_once(svm):
         for k in ref_a:
             np.testing.assert_array_equal(oa[k].cpu().numpy(), ref_a[k].numpy(), err_msg=k)
             np.testing.assert_array_equal(ob[k].cpu().numpy(), ref_b[k].numpy(), err_msg=k)
+
+
+def test_release_workspaces_frees_the_cache(svm):
+    _announce("release_workspaces frees the cached and outgrown workspaces; calls still work")
+    from speculative_sampling_verification_amd import _lib
+    params = dict(temperature=0.7, top_k=50)
+    small = [h.cuda() for h in _fresh(900, (4, 3), 32000, "bf16", "zipf")]
+    big = [h.cuda() for h in _fresh(901, (16, 5), 128256, "bf16", "zipf")]
+    svm.release_workspaces()  # a clean cache, whatever ran before in this process
+    assert not _lib._workspaces and not _lib._outgrown
+    ref = {k: v.cpu() for k, v in svm.spec_verify(*small, **params).items()}
+    svm.spec_verify(*big, **params)  # grows the stream's workspace: the small one is outgrown
+    torch.cuda.synchronize()
+    assert _lib._workspaces and _lib._outgrown
+    held = sum(b.numel() for b in _lib._workspaces.values()) + sum(
+        b.numel() for b in _lib._outgrown)
+    assert svm.release_workspaces() == held
+    assert not _lib._workspaces and not _lib._outgrown
+    again = svm.spec_verify(*small, **params)  # allocates afresh
+    torch.cuda.synchronize()
+    for k in ref:
+        np.testing.assert_array_equal(again[k].cpu().numpy(), ref[k].numpy(), err_msg=k)
