@@ -2511,8 +2511,8 @@ __global__ __launch_bounds__(64) void k_take_draft_summaries(Dims dm, Workspace 
 // the smallest index whose cumulative weight in index order exceeds u * W; the largest index of
 // positive weight if rounding leaves none.
 // The same pick over at most 64 entries held one per lane (lane e: index ie, weight we; lanes
-// >= nk hold none): each lane reads the others' entries in order, adding in the order of the
-// general loop of pick_staged_wave, so both give the same token.
+// >= nk hold none): each lane reads the others' entries in order and sums the weights of those
+// at or below its own index; the smallest index whose sum exceeds u W is the token.
 __device__ int pick_lanes(int nk, uint32_t ie, double we, double W, double u) {
   const int lane = lane_id();
   const double target = u * W;
@@ -2547,19 +2547,30 @@ __device__ int pick_staged_wave(int nk, double W, double u, const uint32_t* s_id
     wave_lds_sync();
     return tok;
   }
-  for (int e = lane_id(); e < nk; e += 64) {
-    const uint32_t ie = s_idx[e];
-    const double we = s_w[e];
-    double pre = 0.0;
-    for (int j = 0; j < nk; ++j)
-      if (s_idx[j] <= ie) pre += s_w[j];
-    if (we > 0.0) {
-      if (pre > target && ie < pick) pick = ie;
-      if ((int)ie > lastpos) lastpos = (int)ie;
-    }
-  }
-  pick = wave_reduce(pick, [](uint32_t a, uint32_t c) { return a < c ? a : c; });
+  // More entries than lanes: the smallest index i with C(i) > u W, C(i) = the weight of the
+  // entries with index <= i, by bisection on i.  C is summed per lane in a fixed order and then
+  // over the lanes in a fixed tree, both additions of non-negative terms, so it does not
+  // decrease as i grows and the bisection finds the index a scan in index order would.
+  for (int e = lane_id(); e < nk; e += 64)
+    if (s_w[e] > 0.0 && (int)s_idx[e] > lastpos) lastpos = (int)s_idx[e];
   lastpos = wave_reduce(lastpos, [](int a, int c) { return a > c ? a : c; });
+  auto C = [&](uint32_t i) {
+    double t = 0.0;
+    for (int e = lane_id(); e < nk; e += 64)
+      if (s_idx[e] <= i) t += s_w[e];
+    return wave_reduce(t, [](double a, double c) { return a + c; });
+  };
+  if (lastpos >= 0 && C((uint32_t)lastpos) > target) {  // else rounding: the last index
+    uint32_t a = 0, c = (uint32_t)lastpos;
+    while (a < c) {
+      const uint32_t mid = a + (c - a) / 2;
+      if (C(mid) > target)
+        c = mid;
+      else
+        a = mid + 1;
+    }
+    pick = a;
+  }
   wave_lds_sync();
   return pick != 0xFFFFFFFFu ? (int)pick : lastpos;
 }
@@ -2613,19 +2624,38 @@ __device__ int final_draw_compact_wave(const E* __restrict__ tgt, const E* __res
     }
     return draw_small_wave(nk, ie, zt, zd, rt, rd, resid, it, u);
   }
+  // entries lane + 64 i, four per lane at a time: the four kept entries, then the four draft
+  // logits at their indices, are loaded together (two round trips per 256 entries, not two per
+  // entry); the weights are added in entry order
   double Wp = 0.0;
-  for (int e = lane; e < nk; e += 64) {
-    const uint2 v = kept[e];
-    const double q = (double)fast_exp((__uint_as_float(v.y) - rt.m) * it) / rt.S;
-    double w = q;
-    if (resid) {
-      const float zd = Tr<E>::to_float(Tr<E>::bits_of(drow[v.x]));
-      const double p = (double)kept_exp(zd, rd, it) / rd.S;
-      w = q - p > 0.0 ? q - p : 0.0;
+  for (int e0 = 0; e0 < nk; e0 += 256) {
+    uint2 v[4];
+    float zd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + lane + 64 * i;
+      v[i] = e < nk ? kept[e] : make_uint2(0u, 0u);
     }
-    s_idx[e] = v.x;
-    s_w[e] = w;
-    Wp += w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + lane + 64 * i;
+      zd[i] = (resid && e < nk) ? Tr<E>::to_float(Tr<E>::bits_of(drow[v[i].x])) : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = e0 + lane + 64 * i;
+      if (e < nk) {
+        const double q = (double)fast_exp((__uint_as_float(v[i].y) - rt.m) * it) / rt.S;
+        double w = q;
+        if (resid) {
+          const double p = (double)kept_exp(zd[i], rd, it) / rd.S;
+          w = q - p > 0.0 ? q - p : 0.0;
+        }
+        s_idx[e] = v[i].x;
+        s_w[e] = w;
+        Wp += w;
+      }
+    }
   }
   double W = wave_reduce(Wp, [](double a, double c) { return a + c; });
   if (!(W > 0.0)) {  // empty residual: draw from q
