@@ -3294,6 +3294,70 @@ constexpr int kTreeThreads = 256;
 // (ancestor: bits 0-10, distance: bits 11-21, ok: bit 22) of a node
 constexpr uint32_t kJumpA = 2047u, kJumpOk = 1u << 22;
 
+// The same walk for trees of at most 64 nodes: one wave per sequence, node i in lane i; the
+// pointer jumping runs on shuffles (no LDS, no barriers) and the path is read back by readlane.
+__global__ __launch_bounds__(64) void k_tree_walk64(Dims dm, Workspace ws,
+                                                    const int32_t* __restrict__ parent,
+                                                    const int32_t* __restrict__ tokens,
+                                                    int max_depth,
+                                                    int32_t* __restrict__ out_tokens,
+                                                    int32_t* __restrict__ out_n,
+                                                    int32_t* __restrict__ out_last) {
+  const int b = blockIdx.x;
+  const int i = lane_id();
+  const int N = dm.K;  // nodes per tree (stored in K for the tree launch), at most 64
+  int g = 0, par = -1, tok = 0;
+  if (i < N) {
+    const ChunkPart* p = ws.parts + ((size_t)b * N + i) * dm.nchunks;
+    float best = p[0].vmax;
+    int am = p[0].argmax;
+    for (int c = 1; c < dm.nchunks; ++c) {
+      const float v = p[c].vmax;
+      if (v > best) {
+        best = v;
+        am = p[c].argmax;
+      }
+    }
+    g = am;
+    par = parent[(size_t)b * N + i];
+    tok = tokens[(size_t)b * N + i];
+  }
+  const bool valid = i > 0 && i < N && par >= 0 && par < i;
+  const int gp = __shfl(g, valid ? par : 0);  // the parent's argmax
+  // the root and the lanes past N are terminals (those lanes never accepted); an invalid parent
+  // makes a terminal that is not ok
+  uint32_t w = i == 0 ? kJumpOk
+                      : valid ? (uint32_t)par | (1u << 11) | (tok == gp ? kJumpOk : 0u)
+                              : (uint32_t)i;
+  for (int span = 1; span < N; span <<= 1) {  // ceil(log2 N) rounds
+    const uint32_t wa = (uint32_t)__shfl((int)w, (int)(w & kJumpA));
+    const uint32_t d = ((w >> 11) & kJumpA) + ((wa >> 11) & kJumpA);
+    w = (wa & kJumpA) | (d << 11) | (w & wa & kJumpOk);
+  }
+  // deepest accepted node, lowest index on ties (the root is always accepted)
+  int key = 0;
+  if (i < N) {
+    const int d = (int)((w >> 11) & kJumpA);
+    if ((w & kJumpOk) && d <= max_depth) key = (d << 11) | (2047 - i);
+  }
+  key = wave_reduce(key, [](int x, int y) { return x > y ? x : y; });
+  const int best = 2047 - (key & 2047);
+  const int depth = key >> 11;
+  int32_t* o = out_tokens + (size_t)b * (max_depth + 1);
+  for (int j = depth + 1 + i; j <= max_depth; j += 64) o[j] = -1;
+  int cur = best;
+  for (int j = depth - 1; j >= 0; --j) {  // the path, from best up to the root's child
+    const int t = __builtin_amdgcn_readlane(tok, cur);
+    if (i == 0) o[j] = t;
+    cur = __builtin_amdgcn_readlane(par, cur);
+  }
+  if (i == 0) {
+    o[depth] = __builtin_amdgcn_readlane(g, best);
+    out_n[b] = depth;
+    if (out_last) out_last[b] = best;
+  }
+}
+
 __global__ __launch_bounds__(kTreeThreads) void k_tree_walk(Dims dm, Workspace ws,
                                                             const int32_t* __restrict__ parent,
                                                             const int32_t* __restrict__ tokens,
@@ -3672,8 +3736,12 @@ hipError_t launch_tree(const void* target, sv_dtype dt, const Dims& d, const int
                        t, d, sp, ws);
   }
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], stream);
-  hipLaunchKernelGGL(k_tree_walk, dim3(d.B), dim3(kTreeThreads), 0, stream, d, ws, parent, tokens,
-                     max_depth, out_tokens, out_n, out_last);
+  if (d.K <= 64)  // one wave per tree
+    hipLaunchKernelGGL(k_tree_walk64, dim3(d.B), dim3(64), 0, stream, d, ws, parent, tokens,
+                       max_depth, out_tokens, out_n, out_last);
+  else
+    hipLaunchKernelGGL(k_tree_walk, dim3(d.B), dim3(kTreeThreads), 0, stream, d, ws, parent,
+                       tokens, max_depth, out_tokens, out_n, out_last);
   if (ev && nev >= 3) (void)hipEventRecord(ev[2], stream);
   return hipGetLastError();
 }

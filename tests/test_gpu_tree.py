@@ -85,3 +85,13 @@ def test_chain_tree_equals_greedy_spec_verify():
     torch.cuda.synchronize()
     np.testing.assert_array_equal(tr["num_accepted"], sv["num_accepted"].cpu().numpy())
     np.testing.assert_array_equal(tr["tokens"], sv["tokens"].cpu().numpy())
+
+
+@pytest.mark.parametrize("N", [1, 2, 63, 64, 65, 200])
+def test_tree_sizes_around_one_wave(N):
+    """Trees of up to 64 nodes are walked by one wave (a node per lane), larger ones by a
+    workgroup: both sides of the switch, and its edges, against the oracle."""
+    _announce(f"tree B=6 N={N} V=32000 bf16, max_depth 6 and 64")
+    logits, parent, tokens = S.tree_inputs(6, N, 32000, planted=True, seed=46 + N)
+    _check(logits, parent, tokens, 6)
+    _check(logits, parent, tokens, 64)
