@@ -587,6 +587,10 @@ __device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPar
   // order, one bin per thread and chunk (the shift is one-to-one below the last bin), so every
   // bin's sum has a fixed order; the last bin's share is summed per thread and reduced.
   constexpr int PT = kHistBins / kThreads;
+  // each chunk's scale exp((vmax - m) / T) (in 2^-40 units; 0: no mass) and shift em - edge of
+  // its maximum, computed once per chunk, in blocks of kThreads chunks
+  __shared__ double s_sc[kThreads];
+  __shared__ long long s_dc[kThreads];
 #pragma unroll
   for (int i = 0; i < PT; ++i) s_mass[tid + i * kThreads] = 0.0;
   double rest = 0.0;
@@ -598,15 +602,25 @@ __device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPar
   };
   load_h(0);
   for (int c = 0; c < dm.nchunks; ++c) {
+    const int cq = c % kThreads;
+    if (cq == 0) {  // the scales of the next block of chunks
+      __syncthreads();
+      const int cc = c + tid;
+      if (cc < dm.nchunks) {
+        const ChunkPart p = parts[cc];
+        const bool live = p.vmax > -INFINITY;
+        s_sc[tid] = live ? exp((double)(p.vmax - m) / (double)sp.temperature) * 0x1p-40 : 0.0;
+        s_dc[tid] = live ? (long long)em - p.pad[0] : 0;
+      }
+    }
     unsigned long long h[PT];
 #pragma unroll
     for (int i = 0; i < PT; ++i) h[i] = hn[i];
     load_h(c + 1);
-    const ChunkPart p = parts[c];
     __syncthreads();
-    if (p.vmax > -INFINITY) {
-      const double sc = exp((double)(p.vmax - m) / (double)sp.temperature) * 0x1p-40;
-      const long long dc = (long long)em - p.pad[0];
+    const double sc = s_sc[cq];
+    if (sc > 0.0) {  // (a chunk with no mass, or whose scale underflows, adds nothing)
+      const long long dc = s_dc[cq];
 #pragma unroll
       for (int i = 0; i < PT; ++i) {
         const int j = tid + i * kThreads;
