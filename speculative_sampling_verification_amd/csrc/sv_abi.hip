@@ -101,6 +101,7 @@ bool make_dims(int B, int K, int V, int draft_rows, sv_dtype dt, Dims* d) {
   d->chunk_elems = ce;
   d->nchunks = (int)nch;
   d->vec = 0;
+  d->esize = (int)esize(dt);
   // the final draw runs one workgroup per (sequence, final chunk): one vector row of a chunk
   // when whole chunks would leave most of the 256 CUs idle, a quarter chunk (several rounds
   // of short workgroups) up to 64 K workgroups, else whole chunks
@@ -140,11 +141,13 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const bool th = s.topp_hist != 0;
   const size_t o_hist = c.take(th ? rows * nch * kHistBins * sizeof(unsigned long long) : 0);
   const size_t o_tprow = c.take(th ? rows * sizeof(TopPRow) : 0);
-  const size_t o_tcand = c.take(th ? rows * kTopPCandCap * sizeof(uint2) : 0);
-  const size_t tsegs = th ? (size_t)d.B * (d.K + 1) * nch : 0;  // target-row chunk segments
-  const size_t o_tkept = c.take(tsegs * kTopPSegCap * sizeof(uint2));
+  const bool cd = topp_codes(d, s);  // fp32: candidates kept in LDS, edge codes instead
+  const size_t o_tcand = c.take(th && !cd ? rows * kTopPCandCap * sizeof(uint2) : 0);
+  const size_t tsegs = th && !cd ? (size_t)d.B * (d.K + 1) * nch : 0;  // bf16 kept segments
+  const size_t o_tkept = c.take(tsegs * kTopPSegCap * sizeof(uint32_t));
   const size_t o_tkcnt = c.take(tsegs * sizeof(int));
   const size_t o_lpart = c.take(th ? (size_t)d.B * nch * sizeof(ulonglong2) : 0);
+  const size_t o_codes = c.take(cd ? rows * nch * (size_t)d.chunk_elems : 0);
   const bool me = s.mentor && d.K > 0;
   const size_t o_ment = c.take(me ? (size_t)d.B * d.K * sizeof(MentorSol) : 0);
   const bool bp = !s.compact && !s.greedy;
@@ -159,10 +162,11 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
     ws->nbuf = at<int32_t>(base, o_n);
     ws->hist = th ? at<unsigned long long>(base, o_hist) : nullptr;
     ws->tprow = th ? at<TopPRow>(base, o_tprow) : nullptr;
-    ws->tcand = th ? at<uint2>(base, o_tcand) : nullptr;
-    ws->tkept = th ? at<uint2>(base, o_tkept) : nullptr;
-    ws->tkcnt = th ? at<int>(base, o_tkcnt) : nullptr;
+    ws->tcand = th && !cd ? at<uint2>(base, o_tcand) : nullptr;
+    ws->tkept = tsegs ? at<uint32_t>(base, o_tkept) : nullptr;
+    ws->tkcnt = tsegs ? at<int>(base, o_tkcnt) : nullptr;
     ws->lpart = th ? at<ulonglong2>(base, o_lpart) : nullptr;
+    ws->codes = cd ? at<uint8_t>(base, o_codes) : nullptr;
     ws->ment = me ? at<MentorSol>(base, o_ment) : nullptr;
     ws->bpart = bp ? at<double>(base, o_bpart) : nullptr;
   }

@@ -65,8 +65,16 @@ struct alignas(16) TopPRow {
   double mass_above;  // sum of exp((z - m) / T) over the elements above e_hi
   int e_lo, e_hi;     // candidate edge range (e_lo = INT_MIN: open below)
   int count;          // candidates appended (may exceed kTopPCandCap: the row falls back)
-  int pad;
+  int coded;          // 1: the row's edge codes resolve [e_lo, e_hi] (the candidate pass reads
+                      // the codes instead of the logits)
+  int em;             // the grid edge of the row maximum
+  int pad[3];
 };
+
+// Edge codes (fp32 top-p rows): one byte per element of a chunk frame, the element's grid edge
+// below its chunk's top edge, etop - floor(8 z / T), or kCodeFar when that is kCodeFar or more
+// (or the element is -inf, or outside the row).
+constexpr int kCodeFar = 255;
 
 // How a draft position is decided under mentored decoding.
 enum MentorMode : int {
@@ -104,6 +112,7 @@ struct Dims {
   int vec;          // 1: 16-byte loads are legal for every row
   int fchunk_elems; // elements per chunk of the final draw (a chunk, or one vector row of it)
   int nfchunks;     // final-draw chunks per row, counted from the row's first element
+  int esize;        // bytes per logit (2: bf16, 4: fp32)
 };
 
 struct Samp {
@@ -132,14 +141,15 @@ struct Workspace {
   int32_t* nbuf;     // [B] accepted counts when the caller does not want them
   unsigned long long* hist;  // [rows][nchunks][kHistBins] fixed-point mass   top-p histogram only
   TopPRow* tprow;            // [rows]                                        top-p histogram only
-  uint2* tcand;              // [rows][kTopPCandCap] (index, bits)            top-p histogram only
-  uint2* tkept;              // [B*(K+1)][nchunks][kTopPSegCap] (index, bits) of every element
-                             // of a target row's chunk at or above the boundary bracket, in no
+  uint2* tcand;              // [rows][kTopPCandCap] (index, bits)            top-p bf16 only
+  uint32_t* tkept;           // [B*(K+1)][nchunks][kTopPSegCap] index of every element of a
+                             // target row's chunk at or above the boundary bracket, in no
                              // particular order                             top-p histogram only
   int* tkcnt;                // [B*(K+1)][nchunks] entries of each segment (> kTopPSegCap:
                              // overflowed)                                   top-p histogram only
   ulonglong2* lpart;         // [B][nchunks] the final draw's fixed-point masses (residual, q) of
                              // each segment                                  top-p histogram only
+  uint8_t* codes;            // [rows][nchunks * chunk_elems] edge codes     top-p fp32 only
   MentorSol* ment;           // [B][K]                                        mentored only
   double* bpart;             // [B*K][nfchunks] acceptance-rate partials      dense rows only
 };
@@ -147,6 +157,9 @@ struct Workspace {
 inline int chunk_elems_for(sv_dtype dt) {
   return kThreads * kVecPerThread * (dt == SV_DTYPE_BF16 ? 8 : 4);
 }
+
+// Top-p rows carry edge codes when a code (one byte) is smaller than the logit: fp32.
+inline bool topp_codes(const Dims& d, const Samp& s) { return s.topp_hist && d.esize == 4; }
 
 // Workspace layout; returns the byte size and, when base != nullptr, fills ws.
 size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws);

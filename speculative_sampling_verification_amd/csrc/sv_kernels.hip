@@ -111,6 +111,12 @@ __device__ __forceinline__ float fast_exp(float x) {
 
 constexpr int kRegs = kVecPerThread * 4;  // 32-bit registers per thread holding one chunk
 
+// One logit of a row, as a float.
+template <class E>
+__device__ __forceinline__ float load_logit(const E* row, int idx) {
+  return Tr<E>::to_float(Tr<E>::bits_of(row[idx]));
+}
+
 // ------------------------------------------------------------------------------------------
 // Block reductions (256 threads = 4 waves of 64).  Fixed butterfly inside a wave, then the
 // four wave results in order: deterministic.
@@ -122,10 +128,42 @@ __device__ __forceinline__ unsigned long long lanes_below() {
   return (1ull << lane_id()) - 1ull;
 }
 
+// The value of lane (this lane ^ O), with no lane-address register: below 32 a ds_swizzle in
+// bit-mask mode (and 0x1F, xor O: an immediate pattern); across the halves v_permlane32_swap,
+// which exchanges the upper half of its first operand with the lower half of its second (both
+// v here), so the lower lanes find their partner in the second result, the upper lanes in the
+// first.
+template <int O>
+__device__ __forceinline__ int xor_lane_i(int v) {
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return lane_id() < 32 ? (int)r[1] : (int)r[0];
+  } else {
+    return __builtin_amdgcn_ds_swizzle(v, 0x1F | (O << 10));
+  }
+}
+template <int O, class T>
+__device__ __forceinline__ T xor_lane(T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, xor_lane_i<O>(__builtin_bit_cast(int, v)));
+  } else {
+    typedef int i2 __attribute__((ext_vector_type(2)));
+    i2 x = __builtin_bit_cast(i2, v);
+    x.x = xor_lane_i<O>(x.x);
+    x.y = xor_lane_i<O>(x.y);
+    return __builtin_bit_cast(T, x);
+  }
+}
+
 template <class T, class Op>
 __device__ __forceinline__ T wave_reduce(T v, Op op) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o));
+  v = op(v, xor_lane<32>(v));
+  v = op(v, xor_lane<16>(v));
+  v = op(v, xor_lane<8>(v));
+  v = op(v, xor_lane<4>(v));
+  v = op(v, xor_lane<2>(v));
+  v = op(v, xor_lane<1>(v));
   return v;
 }
 
@@ -333,10 +371,17 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
     double s = 0.0;
     const float it = sp.inv_t;
     const int etop = topp_edge(mx, it);
+    // fp32 top-p rows: each element's edge code, one byte per slot of the chunk frame (byte a of
+    // the chunk's codes is frame slot c * CH + a), four per vector, stored as one dword
+    constexpr bool CODES = HIST && sizeof(E) == 4;
+    uint32_t* codes = nullptr;
+    if constexpr (CODES) codes = reinterpret_cast<uint32_t*>(
+        ws.codes + ((size_t)r * dm.nchunks + c) * dm.chunk_elems);
     if (mx > -INFINITY) {
 #pragma unroll
       for (int i = 0; i < kVecPerThread; ++i) {
         float sv = 0.f;  // one vector's EPV terms in fp32, then into the fp64 total
+        uint32_t cw = 0u;
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
 #pragma unroll
@@ -347,15 +392,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
             if constexpr (HIST) {
               // mass in 2^-40 fixed point relative to the chunk maximum, so that the bin sums
               // are exact integer additions whatever their order
+              uint32_t code = kCodeFar;
               if (e > 0.0f) {
-                const int j = min(etop - topp_edge(z, it), kHistBins - 1);
+                const int g = etop - topp_edge(z, it);
+                const int j = min(g, kHistBins - 1);
                 atomicAdd(&s_hist[j], __float2ull_rz(e * 1099511627776.0f));
+                code = (uint32_t)min(g, kCodeFar);
               }
+              cw |= code << (8 * d);
             }
           }
         }
+        if constexpr (CODES) codes[threadIdx.x + kThreads * i] = cw;
         s += (double)sv;
       }
+    } else if constexpr (CODES) {
+#pragma unroll
+      for (int i = 0; i < kVecPerThread; ++i) codes[threadIdx.x + kThreads * i] = 0xFFFFFFFFu;
     }
     p.sum = block_sum_d(s, red);  // its barriers also order the histogram updates
     if constexpr (HIST) {
@@ -573,20 +626,50 @@ __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_
 // any number of tokens that fits an int stays below 1 - P for every float P < 1, so the
 // boundary is never among them unless the candidate range is already open below.
 // ------------------------------------------------------------------------------------------
-__device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPart* parts,
-                           float m, double S, double* s_mass, const Workspace& ws) {
+// Histogram loads of a batch of chunks [c0, c0 + kHistBatch) of row r (zeros past the row), so
+// that callers can issue the first batch before they need it.
+constexpr int kHistPT = kHistBins / kThreads;  // bins per thread
+template <int NB>  // chunks per batch
+using HistBatch = unsigned long long[NB][kHistPT];
+
+template <int NB>
+__device__ __forceinline__ void hist_batch_load(const Dims& dm, const Workspace& ws, int r, int c0,
+                                                int ce, HistBatch<NB>& h) {
+  // a buffer over chunks [c0, ce) of the row: loads past it read 0, with no branch
+  typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      ws.hist + ((size_t)r * dm.nchunks + c0) * kHistBins, (short)0,
+      max(0, ce - c0) * kHistBins * (int)sizeof(unsigned long long), 0x00020000);
+#pragma unroll
+  for (int q = 0; q < NB; ++q)
+#pragma unroll
+    for (int i = 0; i < kHistPT; ++i) {
+      const u2 x = __builtin_amdgcn_raw_buffer_load_b64(
+          rs, (int)((threadIdx.x + i * kThreads) * sizeof(unsigned long long)),
+          q * kHistBins * (int)sizeof(unsigned long long), 0);
+      h[q][i] = (unsigned long long)x.x | ((unsigned long long)x.y << 32);
+    }
+}
+
+// parts: the row's chunk partials (global memory or an LDS copy); h0: the histograms of the
+// first batch of NB chunks, loaded by hist_batch_load(dm, ws, r, 0, min(kThreads, nchunks), h0).
+template <int NB>
+__device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r,
+                                           const ChunkPart* parts, float m, double S,
+                                           double* s_mass, const Workspace& ws, HistBatch<NB>& h0,
+                                           TopPRow* s_out = nullptr) {
   const int tid = threadIdx.x;
   __shared__ RedScratch red;
   int emt = INT_MIN;
   for (int c = tid; c < dm.nchunks; c += kThreads)
     if (parts[c].vmax > -INFINITY) emt = max(emt, parts[c].pad[0]);
   const int em = block_max_i(emt, red);
-  const unsigned long long* hist = ws.hist + (size_t)r * dm.nchunks * kHistBins;
   // row bin B holds the elements with edge em - B (B = kHistBins - 1: that edge and below);
   // chunk c's bin j lands in row bin j + (em - edge of chunk c's maximum).  Chunks are added in
-  // order, one bin per thread and chunk (the shift is one-to-one below the last bin), so every
-  // bin's sum has a fixed order; the last bin's share is summed per thread and reduced.
-  constexpr int PT = kHistBins / kThreads;
+  // order, one bin per thread and chunk (the shift is one-to-one below the last bin; a barrier
+  // between chunks), so every bin's sum has a fixed order; the last bin's share is summed per
+  // thread and reduced.  The histograms are loaded NB chunks at a time.
+  constexpr int PT = kHistPT;
   // each chunk's scale exp((vmax - m) / T) (in 2^-40 units; 0: no mass) and shift em - edge of
   // its maximum, computed once per chunk, in blocks of kThreads chunks
   __shared__ double s_sc[kThreads];
@@ -594,42 +677,45 @@ __device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPar
 #pragma unroll
   for (int i = 0; i < PT; ++i) s_mass[tid + i * kThreads] = 0.0;
   double rest = 0.0;
-  unsigned long long hn[PT];
-  auto load_h = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < PT; ++i)
-      hn[i] = c < dm.nchunks ? hist[(size_t)c * kHistBins + tid + i * kThreads] : 0ull;
-  };
-  load_h(0);
-  for (int c = 0; c < dm.nchunks; ++c) {
-    const int cq = c % kThreads;
-    if (cq == 0) {  // the scales of the next block of chunks
-      __syncthreads();
-      const int cc = c + tid;
-      if (cc < dm.nchunks) {
-        const ChunkPart p = parts[cc];
-        const bool live = p.vmax > -INFINITY;
-        s_sc[tid] = live ? exp((double)(p.vmax - m) / (double)sp.temperature) * 0x1p-40 : 0.0;
-        s_dc[tid] = live ? (long long)em - p.pad[0] : 0;
-      }
-    }
-    unsigned long long h[PT];
-#pragma unroll
-    for (int i = 0; i < PT; ++i) h[i] = hn[i];
-    load_h(c + 1);
+  for (int cb = 0; cb < dm.nchunks; cb += kThreads) {
     __syncthreads();
-    const double sc = s_sc[cq];
-    if (sc > 0.0) {  // (a chunk with no mass, or whose scale underflows, adds nothing)
-      const long long dc = s_dc[cq];
+    const int cc = cb + tid;
+    if (cc < dm.nchunks) {  // the scales of this block of chunks
+      const ChunkPart p = parts[cc];
+      const bool live = p.vmax > -INFINITY;
+      s_sc[tid] = live ? exp((double)(p.vmax - m) / (double)sp.temperature) * 0x1p-40 : 0.0;
+      s_dc[tid] = live ? (long long)em - p.pad[0] : 0;
+    }
+    const int ce = min(cb + kThreads, dm.nchunks);
+    auto add_batch = [&](const HistBatch<NB>& h, int c0) {
 #pragma unroll
-      for (int i = 0; i < PT; ++i) {
-        const int j = tid + i * kThreads;
-        const double v = (double)h[i] * sc;
-        if (j == kHistBins - 1 || j + dc >= kHistBins - 1)
-          rest += v;
-        else
-          s_mass[j + dc] += v;
+      for (int q = 0; q < NB; ++q) {
+        if (c0 + q >= ce) break;
+        __syncthreads();
+        const double sc = s_sc[c0 + q - cb];
+        if (sc > 0.0) {  // (a chunk with no mass, or whose scale underflows, adds nothing)
+          const long long dc = s_dc[c0 + q - cb];
+#pragma unroll
+          for (int i = 0; i < PT; ++i) {
+            const int j = tid + i * kThreads;
+            const double v = (double)h[q][i] * sc;
+            if (j == kHistBins - 1 || j + dc >= kHistBins - 1)
+              rest += v;
+            else
+              s_mass[j + dc] += v;
+          }
+        }
       }
+    };
+    int c0 = cb;
+    if (cb == 0) {
+      add_batch(h0, 0);
+      c0 = NB;
+    }
+    for (; c0 < ce; c0 += NB) {
+      HistBatch<NB> hl;
+      hist_batch_load<NB>(dm, ws, r, c0, ce, hl);
+      add_batch(hl, c0);
     }
   }
   rest = block_sum_d(rest, red);
@@ -677,8 +763,13 @@ __device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPar
       t.e_hi = em - lo;
       t.e_lo = hi == kHistBins - 1 ? INT_MIN : em - hi;
       t.count = 0;
-      t.pad = 0;
+      // every chunk's top edge is at most em, so a code below kCodeFar resolves any edge down
+      // to em - (kCodeFar - 1): the codes decide the range when it ends above that
+      t.coded = ws.codes != nullptr && hi <= kCodeFar - 1 ? 1 : 0;
+      t.em = em;
+      t.pad[0] = t.pad[1] = t.pad[2] = 0;
       ws.tprow[r] = t;
+      if (s_out) *s_out = t;
     }
   }
 }
@@ -686,8 +777,10 @@ __device__ void topp_range(const Dims& dm, const Samp& sp, int r, const ChunkPar
 // Candidates of the boundary bins, appended to the row's list (in no particular order:
 // k_topp_select's result does not depend on it).  A chunk gathers its candidates in LDS and
 // reserves room in the row's list with one atomic add.  A chunk of a target row also writes its
-// kept segment: every element at or above the candidate range's lower edge (everything top-p may
-// keep), up to kTopPSegCap, and its count; the final draw reads the segments instead of the row.
+// kept segment: the index of every element at or above the candidate range's lower edge
+// (everything top-p may keep), up to kTopPSegCap, and its count; the final draw reads the
+// segments instead of the row.  bf16 rows (fp32 rows take k_topp_row, from edge codes); the
+// chunk's logits are read in two halves.
 constexpr int kToppChunkCap = 2048;  // candidates one chunk may gather
 
 // Index of row r's kept list (its target row index b * (K + 1) + k), or -1 for a draft row.
@@ -706,37 +799,47 @@ __global__ __launch_bounds__(kThreads) void k_topp_cand(const E* __restrict__ tg
   const int c = bid - r * dm.nchunks;
   const int tid = threadIdx.x;
   const E* row = row_ptr(dm, tgt, drf, r);
-  const int e_lo = ws.tprow[r].e_lo, e_hi = ws.tprow[r].e_hi;
+  const TopPRow tr = ws.tprow[r];
+  const int e_lo = tr.e_lo, e_hi = tr.e_hi;
   const int kl = kept_list_of(dm, r);
   const float it = sp.inv_t;
+  // candidates: (index, logit bits as fp32)
   __shared__ uint2 s_c[kToppChunkCap];
-  __shared__ uint2 s_k[kTopPSegCap];
+  __shared__ uint32_t s_k[kTopPSegCap];
   __shared__ int s_n, s_nk, s_base;
   if (tid == 0) {
     s_n = 0;
     s_nk = 0;
   }
-  uint32_t regs[kRegs];
-  const int c0 = c * dm.chunk_elems -
-                 load_chunk_frame<E>(row, dm.V, c, dm.chunk_elems, regs, Tr<E>::kNegInfPair);
-  __syncthreads();
+  auto push = [&](int idx, uint32_t bits, bool cand) {
+    if (cand) {
+      const int pos = atomicAdd(&s_n, 1);
+      if (pos < kToppChunkCap) s_c[pos] = make_uint2((uint32_t)idx, bits);
+    }
+    if (kl >= 0) {
+      const int pos = atomicAdd(&s_nk, 1);
+      if (pos < kTopPSegCap) s_k[pos] = (uint32_t)idx;
+    }
+  };
+  {  // the chunk's logits, in two halves
+    constexpr int NV = kVecPerThread / 2;
+    const int half = dm.chunk_elems / 2;
+    __syncthreads();
+#pragma unroll 1
+    for (int part = 0; part < 2; ++part) {
+      uint32_t regs[4 * NV];
+      const int f0 = c * dm.chunk_elems + part * half;  // frame index of the half's start
+      const int e0 = f0 - load_frame_part<E, NV>(row, dm.V, f0, half, regs, Tr<E>::kNegInfPair);
 #pragma unroll
-  for (int i = 0; i < kVecPerThread; ++i) {
+      for (int i = 0; i < NV; ++i) {
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
+        for (int d = 0; d < 4; ++d) {
 #pragma unroll
-      for (int h = 0; h < Tr<E>::kPerDword; ++h) {
-        const float z = Tr<E>::elem(regs[4 * i + d], h);
-        const int e = topp_edge(z, it);
-        if (z > -INFINITY && e >= e_lo) {
-          const uint2 entry = make_uint2(slot_index<E>(c0, i, d, h), __float_as_uint(z));
-          if (e <= e_hi) {
-            const int pos = atomicAdd(&s_n, 1);
-            if (pos < kToppChunkCap) s_c[pos] = entry;
-          }
-          if (kl >= 0) {
-            const int pos = atomicAdd(&s_nk, 1);
-            if (pos < kTopPSegCap) s_k[pos] = entry;
+          for (int h = 0; h < Tr<E>::kPerDword; ++h) {
+            const float z = Tr<E>::elem(regs[4 * i + d], h);
+            const int e = topp_edge(z, it);
+            if (z > -INFINITY && e >= e_lo)
+              push(slot_index<E>(e0, i, d, h), __float_as_uint(z), e <= e_hi);
           }
         }
       }
@@ -919,6 +1022,285 @@ __global__ __launch_bounds__(kThreads) void k_topp_select(const E* __restrict__ 
 }
 
 // ------------------------------------------------------------------------------------------
+// k_topp_row (fp32 top-p rows): one workgroup per row does what k_row, k_topp_cand and
+// k_topp_select do for bf16 rows, from the chunk partials, the histograms and the edge codes
+// that k_chunk wrote: the row's maximum and normaliser, the boundary bracket, a scan of the
+// row's codes (two chunks in flight) that collects the candidates' indices in LDS and writes a
+// target row's kept segments, the candidates' logits, and the exact threshold by the
+// mass-weighted digit selection of k_topp_select (weights recomputed per digit, not stored).
+// Rows whose bracket the codes do not reach, or whose candidates overflow, take the exact
+// whole-row selection.
+// ------------------------------------------------------------------------------------------
+template <bool VEC>
+__global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restrict__ tgt,
+                                                       const float* __restrict__ drf, Dims dm,
+                                                       Samp sp, Workspace ws) {
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* row = row_ptr(dm, tgt, drf, r);
+  const ChunkPart* parts = ws.parts + (size_t)r * dm.nchunks;
+  // candidate indices, then their keys; the boundary mass histogram before; radix bins of the
+  // whole-row selection
+  __shared__ unsigned long long s_buf[kTopPCandCap / 2];
+  __shared__ unsigned long long s_bins[256];
+  __shared__ RedScratch red;
+  __shared__ TopPRow s_tr;
+  __shared__ int s_wn[kThreads / 64];
+  constexpr int kPartsCache = 64;  // rows of up to this many chunks keep their partials in LDS
+  constexpr int kRowHistBatch = 8;  // chunks per batch of histogram loads
+  __shared__ ChunkPart s_parts[kPartsCache];
+  __shared__ uint32_t s_prefix;
+  __shared__ unsigned long long s_need;
+  __shared__ uint32_t s_kmin[4], s_kmax[4];
+  uint32_t* s_key = reinterpret_cast<uint32_t*>(s_buf);
+  const float it = sp.inv_t;
+
+  // the first histograms are loaded before anything else (the bracket needs them first), then
+  // the chunk partials once, into LDS when the row has few chunks
+  HistBatch<kRowHistBatch> h0;
+  hist_batch_load<kRowHistBatch>(dm, ws, r, 0, min(kThreads, dm.nchunks), h0);
+  const bool pcached = dm.nchunks <= kPartsCache;
+  if (pcached && tid < dm.nchunks) s_parts[tid] = parts[tid];
+  __syncthreads();
+  const ChunkPart* pp = pcached ? s_parts : parts;
+  // the row's maximum and normaliser from the chunk partials (fixed order, as k_row)
+  float mt = -INFINITY;
+  for (int c = tid; c < dm.nchunks; c += kThreads) mt = fmaxf(mt, pp[c].vmax);
+  const float m = block_max_f(mt, red);
+  double st = 0.0;
+  for (int c = tid; c < dm.nchunks; c += kThreads) {
+    const ChunkPart p = pp[c];
+    if (p.sum > 0.0) st += p.sum * exp((double)(p.vmax - m) / (double)sp.temperature);
+  }
+  const double S = block_sum_d(st, red);
+  topp_range<kRowHistBatch>(dm, sp, r, pp, m, S, reinterpret_cast<double*>(s_buf), ws, h0,
+                            &s_tr);
+  __syncthreads();
+  const TopPRow tr = s_tr;
+  bool fallback = !tr.coded;
+  // candidates: one list per wave (a quarter of s_key), filled by ballot compaction
+  constexpr int kWaveCand = kTopPCandCap / (kThreads / 64);
+  uint32_t* wlist = s_key + wave_id() * kWaveCand;
+  int wcount = 0;  // uniform in the wave
+  if (!fallback) {
+    // byte a of chunk c's codes is frame slot c * CH + a, element c * CH - ph + a; thread t
+    // holds bytes 16 (t + 256 i) .. + 15 of a chunk
+    constexpr int NC = 4;  // 16-byte code vectors per thread and chunk (CH = 16384)
+    typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+    const uint8_t* rcodes = ws.codes + (size_t)r * dm.nchunks * dm.chunk_elems;
+    const int c_ph = row_phase(row);
+    auto load_codes = [&](int c, uint32_t(&w)[4 * NC]) {
+      const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(rcodes + (size_t)c * dm.chunk_elems), (short)0,
+          c < dm.nchunks ? dm.chunk_elems : 0, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {  // out of range (c past the row): zeros, never scanned
+        const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, i * kThreads * 16, 0);
+        w[4 * i + 0] = x.x;
+        w[4 * i + 1] = x.y;
+        w[4 * i + 2] = x.z;
+        w[4 * i + 3] = x.w;
+      }
+    };
+    const unsigned long long below = lanes_below();
+    // edge = etop - code: a candidate iff e_lo <= edge <= e_hi, i.e. etop - e_hi <= code <=
+    // etop - e_lo (below kCodeFar for a coded row, so far codes never pass)
+    auto scan = [&](int c, const uint32_t(&w)[4 * NC]) {
+      const ChunkPart p = pp[c];
+      if (!(p.vmax > -INFINITY)) return;  // no finite logit in the chunk
+      const int etop = p.pad[0];
+      const uint32_t glo = (uint32_t)max(etop - tr.e_hi, 0);
+      const int ghi = etop - tr.e_lo;
+      if (ghi < (int)glo) return;
+      const uint32_t span = (uint32_t)ghi - glo;  // code - glo <= span, unsigned
+      const int c0 = c * dm.chunk_elems - c_ph;
+#pragma unroll
+      for (int j = 0; j < 4 * NC; ++j) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const uint32_t g = (w[j] >> (8 * b)) & 0xFFu;
+          const bool hit = g - glo <= span;
+          const unsigned long long m = __ballot(hit);
+          if (m) {
+            if (hit) {
+              const int pos = wcount + __popcll(m & below);
+              if (pos < kWaveCand)
+                wlist[pos] = (uint32_t)(c0 + 16 * (tid + kThreads * (j >> 2)) + 4 * (j & 3) + b);
+            }
+            wcount += __popcll(m);
+          }
+        }
+      }
+    };
+    // four chunks in flight: each buffer is refilled with the chunk four ahead once scanned
+    uint32_t wa[4 * NC], wb[4 * NC], wc[4 * NC], wd[4 * NC];
+    load_codes(0, wa);
+    load_codes(1, wb);
+    load_codes(2, wc);
+    load_codes(3, wd);
+    for (int c = 0; c < dm.nchunks; c += 4) {
+      scan(c, wa);
+      load_codes(c + 4, wa);
+      if (c + 1 >= dm.nchunks) break;
+      scan(c + 1, wb);
+      load_codes(c + 5, wb);
+      if (c + 2 >= dm.nchunks) break;
+      scan(c + 2, wc);
+      load_codes(c + 6, wc);
+      if (c + 3 >= dm.nchunks) break;
+      scan(c + 3, wd);
+      load_codes(c + 7, wd);
+    }
+    if (lane_id() == 0) s_wn[wave_id()] = wcount;
+    __syncthreads();
+    for (int w = 0; w < kThreads / 64; ++w)
+      if (s_wn[w] > kWaveCand) fallback = true;
+  }
+  double Skept = 0.0;
+  float thr = -INFINITY;
+  if (!fallback) {
+    // the wave lists in place, one after another: entry i of list w at w * kWaveCand + i
+    int nw[kThreads / 64];
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) nw[w] = s_wn[w];
+    auto for_cands = [&](auto&& f) {
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w)
+        for (int i = tid; i < nw[w]; i += kThreads) f(w * kWaveCand + i);
+    };
+    // the candidates' logits: every load issued before the first is used (at most
+    // kWaveCand / kThreads per thread and list)
+    constexpr int PL = kWaveCand / kThreads;
+    float zc[kThreads / 64][PL];
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w)
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const int i = tid + k * kThreads;
+        zc[w][k] = i < nw[w] ? row[s_key[w * kWaveCand + i]] : 0.0f;
+      }
+    unsigned long long tot = 0;
+    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w)
+#pragma unroll
+      for (int k = 0; k < PL; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < nw[w]) {  // as keys
+          const uint32_t key = float_key(zc[w][k]);
+          s_key[w * kWaveCand + i] = key;
+          tot += topp_weight(key, m, it);
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+        }
+      }
+    tot = wave_reduce(tot, [](unsigned long long x, unsigned long long y) { return x + y; });
+    kmin = wave_reduce(kmin, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+    kmax = wave_reduce(kmax, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+    if (lane_id() == 0) {
+      red.u[wave_id()] = tot;
+      s_kmin[wave_id()] = kmin;
+      s_kmax[wave_id()] = kmax;
+    }
+    __syncthreads();
+    tot = red.u[0] + red.u[1] + red.u[2] + red.u[3];
+    kmin = min(min(s_kmin[0], s_kmin[1]), min(s_kmin[2], s_kmin[3]));
+    kmax = max(max(s_kmax[0], s_kmax[1]), max(s_kmax[2], s_kmax[3]));
+    // the candidates share every key bit above the highest one where kmin and kmax differ, so
+    // the digits start at the 8-bit digit holding that bit
+    const int hb = kmin == kmax ? 0 : 31 - __clz(kmin ^ kmax);
+    const int s0 = (hb / 8) * 8;
+    const double rem = (double)sp.top_p * S - tr.mass_above;
+    unsigned long long need = 1ull;
+    if (rem > 0.0) {
+      const double q = ceil(rem * 1099511627776.0);
+      need = q < 1.8e19 ? (unsigned long long)q : ~0ull;
+      if (need == 0ull) need = 1ull;
+    }
+    __syncthreads();  // every thread has read red and the key bounds
+    if (need > tot) {  // the candidates' mass does not reach the target (rounding)
+      fallback = true;
+    } else {
+      if (tid == 0) {
+        s_need = need;
+        s_prefix = s0 + 8 >= 32 ? 0u : (kmin & ~((1u << (s0 + 8)) - 1u));
+      }
+      for (int shift = s0; shift >= 0; shift -= 8) {
+        s_bins[tid] = 0ull;
+        __syncthreads();
+        const uint32_t prefix = s_prefix;
+        for_cands([&](int i) {
+          const uint32_t key = s_key[i];
+          if (shift + 8 >= 32 || (key >> (shift + 8)) == (prefix >> (shift + 8)))
+            atomicAdd(&s_bins[(key >> shift) & 255u], topp_weight(key, m, it));
+        });
+        __syncthreads();
+        if (tid < 64) {  // digits from 255 down: lane L holds 255 - 4L - i, i = 0..3
+          const int L = tid;
+          unsigned long long bv[4], loc = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            bv[i] = s_bins[255 - 4 * L - i];
+            loc += bv[i];
+          }
+          unsigned long long inc = loc;
+#pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long y = __shfl_up(inc, o);
+            if (L >= o) inc += y;
+          }
+          const unsigned long long want = s_need;
+          unsigned long long cum = inc - loc, before = 0;
+          int hit = -1;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (hit < 0 && cum + bv[i] >= want) {
+              hit = i;
+              before = cum;
+            }
+            cum += bv[i];
+          }
+          const unsigned long long lanes = __ballot(hit >= 0);
+          if (lanes && L == __ffsll((long long)lanes) - 1) {
+            s_prefix = prefix | ((uint32_t)(255 - 4 * L - hit) << shift);
+            s_need = want - before;
+          }
+        }
+        __syncthreads();
+      }
+      const uint32_t v = s_prefix;
+      thr = Tr<float>::key_to_float(v);
+      unsigned long long own = 0;
+      for_cands([&](int i) {
+        if (s_key[i] >= v) own += topp_weight(s_key[i], m, it);
+      });
+      own = wave_reduce(own, [](unsigned long long x, unsigned long long y) { return x + y; });
+      if (lane_id() == 0) red.u[wave_id()] = own;
+      __syncthreads();
+      Skept = tr.mass_above + (double)(red.u[0] + red.u[1] + red.u[2] + red.u[3]) * 0x1p-40;
+    }
+  }
+  if (fallback) {
+    __syncthreads();
+    const uint32_t key =
+        radix_select<float, VEC, true>(row, dm.V, m, it, 0u, (double)sp.top_p, s_buf);
+    thr = Tr<float>::key_to_float(key);
+    Skept = dense_sum<float, VEC>(row, dm.V, m, it, thr, red);
+  }
+  if (tid == 0) {
+    RowStat out;
+    out.m = m;
+    out.thr = thr;
+    out.S = Skept;
+    out.argmax = -1;
+    out.nkept = -1;
+    out.kind = kRowDense;
+    out.pad = 0;
+    ws.rstat[r] = out;
+  }
+}
+
+// ------------------------------------------------------------------------------------------
 // k_row: one workgroup per row.  Produces RowStat (m, thr, S) from the chunk partials; top-k
 // above the compact limit and top-p select their thresholds by re-reading the row.
 // ------------------------------------------------------------------------------------------
@@ -986,7 +1368,9 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
   if (sp.topp_hist) {
     // top-p without top-k: locate the boundary bin of the merged mass histogram; the exact
     // threshold is taken among the boundary candidates by k_topp_select
-    topp_range(dm, sp, r, parts, m, s_S, reinterpret_cast<double*>(s_bins), ws);
+    HistBatch<2> h0;
+    hist_batch_load<2>(dm, ws, r, 0, min(kThreads, dm.nchunks), h0);
+    topp_range<2>(dm, sp, r, parts, m, s_S, reinterpret_cast<double*>(s_bins), ws, h0);
     if (tid == 0) {
       out.thr = -INFINITY;
       out.S = s_S;
@@ -1018,11 +1402,6 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
 // Unnormalised weight of a logit in a row's kept set: exp((z - m) / T) in fp32.
 __device__ __forceinline__ float kept_exp(float z, const RowStat& rs, float it) {
   return z >= rs.thr ? fast_exp((z - rs.m) * it) : 0.0f;
-}
-
-template <class E>
-__device__ __forceinline__ float load_logit(const E* row, int idx) {
-  return Tr<E>::to_float(Tr<E>::bits_of(row[idx]));
 }
 
 struct Outs {
@@ -1101,14 +1480,20 @@ __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ 
   return n;
 }
 
-// A top-p target row's kept segments hold every element at or above the candidate range's lower
-// edge; they hold the whole kept set {z >= thr} iff none overflowed and the threshold's edge is
-// inside that range (a row whose boundary selection re-read the row may have a threshold below
-// it).  Called by a whole wave; the same answer in every lane.
+// A top-p target row's kept segments (bf16) hold every element at or above the candidate range's
+// lower edge; they hold the whole kept set {z >= thr} iff none overflowed and the threshold's
+// edge is inside that range (a row whose boundary selection re-read the row may have a threshold
+// below it).  fp32 rows: see below.  Called by a whole wave; the same answer in every lane.
 __device__ __forceinline__ bool kept_list_complete(const Dims& dm, const Samp& sp,
                                                    const Workspace& ws, int b, int n,
                                                    const RowStat& rt) {
   const TopPRow tr = ws.tprow[target_row(dm, b, n)];
+  if (ws.codes) {
+    // fp32 rows carry edge codes instead of segments: the draw scans them, which finds every
+    // kept element when each has a code below kCodeFar, i.e. when the threshold's edge is at
+    // most kCodeFar - 1 steps below the row maximum's (and every chunk maximum is at most that)
+    return rt.thr > -INFINITY && topp_edge(rt.thr, sp.inv_t) >= tr.em - (kCodeFar - 1);
+  }
   bool ok = tr.e_lo == INT_MIN || topp_edge(rt.thr, sp.inv_t) >= tr.e_lo;
   const int* cnt = ws.tkcnt + (size_t)(b * (dm.K + 1) + n) * dm.nchunks;
   for (int c = lane_id(); c < dm.nchunks; c += 64) ok = ok && cnt[c] <= kTopPSegCap;
@@ -1324,14 +1709,15 @@ __device__ __forceinline__ void load_vecs(const E* __restrict__ row, int end, in
 //                indices, then single indices)
 // ------------------------------------------------------------------------------------------
 template <class E>
-__device__ __forceinline__ void list_weights(uint2 en, const RowStat& rt, const RowStat& rd,
-                                             bool resid, const E* __restrict__ drow, float it,
+__device__ __forceinline__ void list_weights(int idx, const RowStat& rt, const RowStat& rd,
+                                             bool resid, const E* __restrict__ trow,
+                                             const E* __restrict__ drow, float it,
                                              unsigned long long& wq, unsigned long long& ww) {
-  const float z = __uint_as_float(en.y);
+  const float z = load_logit(trow, idx);
   const double q = z >= rt.thr ? (double)fast_exp((z - rt.m) * it) / rt.S : 0.0;
   double w = q;
   if (resid && q > 0.0) {
-    const double p = (double)kept_exp(load_logit(drow, (int)en.x), rd, it) / rd.S;
+    const double p = (double)kept_exp(load_logit(drow, idx), rd, it) / rd.S;
     w = q - p > 0.0 ? q - p : 0.0;
   }
   wq = (unsigned long long)(q * 0x1p62);
@@ -1346,12 +1732,13 @@ __device__ void final_lpart(const E* __restrict__ tgt, const E* __restrict__ drf
   const bool resid = n < K;
   const size_t seg = (size_t)(b * (K + 1) + n) * dm.nchunks + c;
   const int cnt = ws.tkcnt[seg];
-  const uint2* list = ws.tkept + seg * kTopPSegCap;
+  const uint32_t* list = ws.tkept + seg * kTopPSegCap;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
   const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
   unsigned long long W = 0, Q = 0;
   for (int e = threadIdx.x; e < cnt; e += kThreads) {
     unsigned long long wq, ww;
-    list_weights<E>(list[e], rt, rd, resid, drow, sp.inv_t, wq, ww);
+    list_weights<E>((int)list[e], rt, rd, resid, trow, drow, sp.inv_t, wq, ww);
     W += ww;
     Q += wq;
   }
@@ -1414,20 +1801,16 @@ __device__ int wave_pick_bin(const unsigned long long* bins, double rem,
   return pl ? __shfl(PER * lane + last, f) : 0;
 }
 
-template <class E>
-__device__ void final_lpick(const E* __restrict__ tgt, const E* __restrict__ drf, const Dims& dm,
-                            const Samp& sp, const Workspace& ws, const float* __restrict__ uni,
-                            int32_t* __restrict__ out_tokens, int b, const SeqState& st,
-                            const RowStat& rt, const RowStat& rd) {
+// The segment (chunk) holding u * W of a list draw: wave 0 scans the segments' masses in chunk
+// order.  Called by the whole workgroup; returns the chunk, the mass left to cover inside it, and
+// whether q replaces the residual (no residual, or a residual without mass).
+__device__ int pick_list_chunk(const Dims& dm, const Workspace& ws, const float* __restrict__ uni,
+                               int b, bool resid, double& rem_out, bool& use_q_out) {
   const int tid = threadIdx.x, lane = lane_id();
-  const int K = dm.K, n = st.n;
-  const bool resid = n < K;
-  constexpr int PE = kTopPSegCap / kThreads;  // entries per thread
-  __shared__ unsigned long long s_bins[256];
-  __shared__ int s_c, s_d1;
+  const int K = dm.K;
+  __shared__ int s_c;
   __shared__ double s_rem;
   __shared__ int s_useq;
-  // the segment holding u * W: wave 0 scans the segments' masses in chunk order
   if (tid < 64) {
     const ulonglong2* lp = ws.lpart + (size_t)b * dm.nchunks;
     unsigned long long W = 0, Q = 0;
@@ -1477,37 +1860,27 @@ __device__ void final_lpick(const E* __restrict__ tgt, const E* __restrict__ drf
       s_useq = use_q ? 1 : 0;
     }
   }
+  __syncthreads();
+  rem_out = s_rem;
+  use_q_out = s_useq != 0;
+  return s_c;
+}
+
+// The index of the pick inside a chunk from its entries' positions a (relative to the chunk's
+// first slot, below 32768) and weights: the first of 128 bins of 256 positions whose running
+// mass passes rem, then the position inside it; add(a, w) is called by the caller for every
+// entry in each of the two rounds (round 0: bins of 256, round 1: positions of bin d1).
+template <class F>
+__device__ int pick_in_chunk(double rem, F&& entries) {
+  const int tid = threadIdx.x, lane = lane_id();
+  __shared__ unsigned long long s_bins[256];
+  __shared__ int s_d1;
+  __shared__ double s_rem;
   s_bins[tid] = 0ull;
   __syncthreads();
-  const int c = s_c;
-  const bool use_q = s_useq != 0;
-  double rem = s_rem;
-  // the segment's entries, in registers: index relative to the chunk's first slot, weight
-  const size_t seg = (size_t)(b * (K + 1) + n) * dm.nchunks + c;
-  const int cnt = min(ws.tkcnt[seg], kTopPSegCap);
-  const uint2* list = ws.tkept + seg * kTopPSegCap;
-  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
-  const int base = c * dm.chunk_elems - row_phase(trow);  // element index of the chunk's first slot
-  const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
-  int ri[PE];
-  unsigned long long xw[PE];
-#pragma unroll
-  for (int i = 0; i < PE; ++i) {
-    const int e = tid + kThreads * i;
-    ri[i] = -1;
-    xw[i] = 0ull;
-    if (e < cnt) {
-      const uint2 en = list[e];
-      unsigned long long wq, ww;
-      list_weights<E>(en, rt, rd, resid, drow, sp.inv_t, wq, ww);
-      ri[i] = (int)en.x - base;
-      xw[i] = use_q ? wq : ww;
-    }
-  }
-  // first digit: bins of 256 indices (a chunk spans at most 32768 indices: 128 bins)
-#pragma unroll
-  for (int i = 0; i < PE; ++i)
-    if (xw[i]) atomicAdd(&s_bins[ri[i] >> 8], xw[i]);
+  entries(-1, [&](int a, unsigned long long w) {
+    if (w) atomicAdd(&s_bins[a >> 8], w);
+  });
   __syncthreads();
   if (tid < 64) {
     unsigned long long before;
@@ -1522,20 +1895,200 @@ __device__ void final_lpick(const E* __restrict__ tgt, const E* __restrict__ drf
   rem = s_rem;
   s_bins[tid] = 0ull;
   __syncthreads();
-#pragma unroll
-  for (int i = 0; i < PE; ++i)
-    if (xw[i] && (ri[i] >> 8) == d1) atomicAdd(&s_bins[ri[i] & 255], xw[i]);
+  entries(d1, [&](int a, unsigned long long w) {
+    if (w && (a >> 8) == d1) atomicAdd(&s_bins[a & 255], w);
+  });
   __syncthreads();
+  int pick = 0;
   if (tid < 64) {
     unsigned long long before;
-    const int d2 = wave_pick_bin<4>(s_bins, rem, before);
-    if (lane == 0) {
-      out_tokens[(size_t)b * (K + 1) + n] = base + (d1 << 8) + d2;
-      if (resid && use_q) {  // the residual had zero mass: q is used (reported)
-        SeqState s2 = st;
-        s2.fallback = 1;
-        ws.seq[b] = s2;
+    pick = (d1 << 8) + wave_pick_bin<4>(s_bins, rem, before);
+  }
+  return pick;  // valid in wave 0
+}
+
+template <class E>
+__device__ void final_lpick(const E* __restrict__ tgt, const E* __restrict__ drf, const Dims& dm,
+                            const Samp& sp, const Workspace& ws, const float* __restrict__ uni,
+                            int32_t* __restrict__ out_tokens, int b, const SeqState& st,
+                            const RowStat& rt, const RowStat& rd) {
+  const int tid = threadIdx.x;
+  const int K = dm.K, n = st.n;
+  const bool resid = n < K;
+  constexpr int PE = kTopPSegCap / kThreads;  // entries per thread
+  double rem;
+  bool use_q;
+  const int c = pick_list_chunk(dm, ws, uni, b, resid, rem, use_q);
+  // the segment's entries, in registers: index relative to the chunk's first slot, weight
+  const size_t seg = (size_t)(b * (K + 1) + n) * dm.nchunks + c;
+  const int cnt = min(ws.tkcnt[seg], kTopPSegCap);
+  const uint32_t* list = ws.tkept + seg * kTopPSegCap;
+  const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, n));
+  const int base = c * dm.chunk_elems - row_phase(trow);  // element index of the chunk's first slot
+  const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
+  int ri[PE];
+  unsigned long long xw[PE];
+#pragma unroll
+  for (int i = 0; i < PE; ++i) {
+    const int e = tid + kThreads * i;
+    ri[i] = -1;
+    xw[i] = 0ull;
+    if (e < cnt) {
+      const int idx = (int)list[e];
+      unsigned long long wq, ww;
+      list_weights<E>(idx, rt, rd, resid, trow, drow, sp.inv_t, wq, ww);
+      ri[i] = idx - base;
+      xw[i] = use_q ? wq : ww;
+    }
+  }
+  const int a = pick_in_chunk(rem, [&](int, auto&& add) {
+#pragma unroll
+    for (int i = 0; i < PE; ++i)
+      if (xw[i]) add(ri[i], xw[i]);
+  });
+  if (tid == 0) {
+    out_tokens[(size_t)b * (K + 1) + n] = base + a;
+    if (resid && use_q) {  // the residual had zero mass: q is used (reported)
+      SeqState s2 = st;
+      s2.fallback = 1;
+      ws.seq[b] = s2;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Final draw over the edge codes of an fp32 top-p target row (the kept set found from its codes,
+// q and p gathered at its indices only).  A thread holds 64 codes of the chunk, bytes
+// 16 (t + 256 i) .. + 15 for i < 4; bit 16 i + j of its hit mask is byte j of vector i, which is
+// slot 16 t + 4096 i + j of the chunk.
+// ------------------------------------------------------------------------------------------
+__device__ __forceinline__ int coded_slot(int k) {
+  return 16 * (int)threadIdx.x + 4096 * (k >> 4) + (k & 15);
+}
+
+// Hit mask of this thread in chunk c of row r: the slots whose code is at most gk.
+__device__ __forceinline__ unsigned long long coded_hits(const Dims& dm, const Workspace& ws, int r,
+                                                         int c, int gk) {
+  typedef unsigned int u4 __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      ws.codes + ((size_t)r * dm.nchunks + c) * dm.chunk_elems, (short)0, dm.chunk_elems,
+      0x00020000);
+  unsigned long long mask = 0ull;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, i * kThreads * 16,
+                                                       0);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb)
+        if ((int)((w[d] >> (8 * bb)) & 0xFFu) <= gk) mask |= 1ull << (16 * i + 4 * d + bb);
+  }
+  return mask;
+}
+
+// Calls f(slot, wq, ww) for every hit of the mask, with the weights of list_weights; the
+// logits of up to four hits are loaded together.
+template <class F>
+__device__ __forceinline__ void coded_weights(unsigned long long mask, int base, const RowStat& rt,
+                                              const RowStat& rd, bool resid,
+                                              const float* __restrict__ trow,
+                                              const float* __restrict__ drow, float it, F&& f) {
+  while (mask) {
+    int a[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      a[k] = -1;
+      if (mask) {
+        a[k] = coded_slot(__ffsll((long long)mask) - 1);
+        mask &= mask - 1ull;
       }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (a[k] >= 0) {
+        unsigned long long wq, ww;
+        list_weights<float>(base + a[k], rt, rd, resid, trow, drow, it, wq, ww);
+        f(a[k], wq, ww);
+      }
+    }
+  }
+}
+
+// The chunk's masses of the final weights, as final_lpart, from the codes.
+__device__ void final_cpart(const float* __restrict__ tgt, const float* __restrict__ drf,
+                            const Dims& dm, const Samp& sp, const Workspace& ws, int b, int c,
+                            const SeqState& st, const RowStat& rt, const RowStat& rd) {
+  const int n = st.n;
+  const bool resid = n < dm.K;
+  const int r = target_row(dm, b, n);
+  const float* trow = row_ptr(dm, tgt, drf, r);
+  const float* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
+  const ChunkPart part = ws.parts[(size_t)r * dm.nchunks + c];
+  // kept elements have an edge at or above the threshold's: code <= etop - edge(thr)
+  const int gk = part.vmax > -INFINITY ? part.pad[0] - topp_edge(rt.thr, sp.inv_t) : -1;
+  const unsigned long long mask = coded_hits(dm, ws, r, c, gk);
+  const int base = c * dm.chunk_elems - row_phase(trow);
+  unsigned long long W = 0, Q = 0;
+  coded_weights(mask, base, rt, rd, resid, trow, drow, sp.inv_t,
+                [&](int, unsigned long long wq, unsigned long long ww) {
+                  W += ww;
+                  Q += wq;
+                });
+  auto add = [](unsigned long long x, unsigned long long y) { return x + y; };
+  W = wave_reduce(W, add);
+  Q = wave_reduce(Q, add);
+  __shared__ unsigned long long s_wq[2][kThreads / 64];
+  if (lane_id() == 0) {
+    s_wq[0][wave_id()] = W;
+    s_wq[1][wave_id()] = Q;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)
+    ws.lpart[(size_t)b * dm.nchunks + c] =
+        make_ulonglong2(s_wq[0][0] + s_wq[0][1] + s_wq[0][2] + s_wq[0][3],
+                        s_wq[1][0] + s_wq[1][1] + s_wq[1][2] + s_wq[1][3]);
+}
+
+// The draw, as final_lpick, from the codes: the chunk from the masses of final_cpart, the
+// position inside it from the chunk's hits (round 1 only rescans the 16 threads whose slots lie
+// in bin d1).
+__device__ void final_cpick(const float* __restrict__ tgt, const float* __restrict__ drf,
+                            const Dims& dm, const Samp& sp, const Workspace& ws,
+                            const float* __restrict__ uni, int32_t* __restrict__ out_tokens, int b,
+                            const SeqState& st, const RowStat& rt, const RowStat& rd) {
+  const int K = dm.K, n = st.n;
+  const bool resid = n < K;
+  double rem;
+  bool use_q;
+  const int c = pick_list_chunk(dm, ws, uni, b, resid, rem, use_q);
+  const int r = target_row(dm, b, n);
+  const float* trow = row_ptr(dm, tgt, drf, r);
+  const float* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
+  const ChunkPart part = ws.parts[(size_t)r * dm.nchunks + c];
+  const int gk = part.vmax > -INFINITY ? part.pad[0] - topp_edge(rt.thr, sp.inv_t) : -1;
+  const unsigned long long mask = coded_hits(dm, ws, r, c, gk);
+  const int base = c * dm.chunk_elems - row_phase(trow);
+  const float it = sp.inv_t;
+  const int a = pick_in_chunk(rem, [&](int d1, auto&& add) {
+    unsigned long long m = mask;
+    if (d1 >= 0) {  // bin d1 holds slots 256 d1 .. + 255: vector d1 / 16 of threads 16 (d1 % 16) ..
+      const bool mine = ((int)threadIdx.x >> 4) == (d1 & 15);
+      m = mine ? (mask >> (16 * (d1 >> 4))) & 0xFFFFull : 0ull;
+      m <<= 16 * (d1 >> 4);
+    }
+    coded_weights(m, base, rt, rd, resid, trow, drow, it,
+                  [&](int s, unsigned long long wq, unsigned long long ww) {
+                    add(s, use_q ? wq : ww);
+                  });
+  });
+  if (threadIdx.x == 0) {
+    out_tokens[(size_t)b * (K + 1) + n] = base + a;
+    if (resid && use_q) {  // the residual had zero mass: q is used (reported)
+      SeqState s2 = st;
+      s2.fallback = 1;
+      ws.seq[b] = s2;
     }
   }
 }
@@ -1561,7 +2114,12 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
   const RowStat rt = ws.dstat[2 * b], rd = ws.dstat[2 * b + 1];
   if constexpr (LIST) {
     if (st.need_list) {
-      if (c < dm.nchunks) final_lpart<E>(tgt, drf, dm, sp, ws, b, c, st, rt, rd);
+      if (c < dm.nchunks) {
+        if constexpr (sizeof(E) == 4)
+          final_cpart(tgt, drf, dm, sp, ws, b, c, st, rt, rd);
+        else
+          final_lpart<E>(tgt, drf, dm, sp, ws, b, c, st, rt, rd);
+      }
       return;
     }
   }
@@ -1714,8 +2272,11 @@ __global__ __launch_bounds__(kThreads) void k_final_pick(const E* __restrict__ t
     }
   }
   if constexpr (LIST) {
-    if (st.need_list) {  // top-p: the draw from the kept segments
-      final_lpick<E>(tgt, drf, dm, sp, ws, uni, out_tokens, b, st, srt, srd);
+    if (st.need_list) {  // top-p: the draw from the kept segments (bf16) or the codes (fp32)
+      if constexpr (sizeof(E) == 4)
+        final_cpick(tgt, drf, dm, sp, ws, uni, out_tokens, b, st, srt, srd);
+      else
+        final_lpick<E>(tgt, drf, dm, sp, ws, uni, out_tokens, b, st, srt, srd);
       return;
     }
   }
@@ -3667,13 +4228,23 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     hipLaunchKernelGGL((k_chunk<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm, sp,
                        ws);
   if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
-  if (!row_is_chunk)
-    hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp, ws);
-  if (sp.topp_hist) {
-    hipLaunchKernelGGL((k_topp_cand<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm,
-                       sp, ws);
-    hipLaunchKernelGGL((k_topp_select<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm,
-                       sp, ws);
+  if constexpr (sizeof(E) == 4) {
+    if (sp.topp_hist)  // fp32 top-p: the bracket, the codes' candidates and the selection
+      hipLaunchKernelGGL((k_topp_row<VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
+                         ws);
+    else if (!row_is_chunk)
+      hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
+                         ws);
+  } else {
+    if (!row_is_chunk)
+      hipLaunchKernelGGL((k_row<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d, dm, sp,
+                         ws);
+    if (sp.topp_hist) {
+      hipLaunchKernelGGL((k_topp_cand<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm,
+                         sp, ws);
+      hipLaunchKernelGGL((k_topp_select<E, VEC>), dim3(dm.rows), dim3(kThreads), 0, st, t, d,
+                         dm, sp, ws);
+    }
   }
   if (out_beta) {  // acceptance rates
     if (sp.greedy) {

@@ -108,6 +108,20 @@ def test_topp_extremes(P, T):
     verify_case(t, d, dict(temperature=T, top_p=P), seed=24)
 
 
+def test_topp_fp32_boundary_candidate_overflow():
+    _announce("fp32 logits on 4 levels, top-p 0.9: boundary bin overflows -> row-pass selection")
+    g = torch.Generator().manual_seed(42)
+    t = torch.randint(0, 4, (3, 3, 40000), generator=g).float()
+    d = torch.randint(0, 4, (3, 2, 40000), generator=g).float()
+    verify_case(t, d, dict(temperature=1.0, top_p=0.9), seed=42)
+
+
+def test_topp_fp32_kept_segments_overflow():
+    _announce("normal fp32 sd 0.5 top-p 0.95 V=40000: kept segments overflow -> dense final draw")
+    t, d = S.normal_logits(6, 3, 40000, 0.5, 1.0, 0.2, "f32", seed=43)
+    verify_case(t, d, dict(temperature=1.0, top_p=0.95), seed=43)
+
+
 # ------------------------------------------------------------------ layouts and edge cases
 def test_unaligned_vocab():
     _announce("unaligned rows: bf16 V=50001 top-k 50, fp32 V=1001 dense")
