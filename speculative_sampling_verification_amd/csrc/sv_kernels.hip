@@ -1966,25 +1966,32 @@ __device__ __forceinline__ int coded_slot(int k) {
   return 16 * (int)threadIdx.x + 4096 * (k >> 4) + (k & 15);
 }
 
-// Hit mask of this thread in chunk c of row r: the slots whose code is at most gk.
-__device__ __forceinline__ unsigned long long coded_hits(const Dims& dm, const Workspace& ws, int r,
-                                                         int c, int gk) {
+// This thread's 64 codes of chunk c of row r.
+__device__ __forceinline__ void coded_load(const Dims& dm, const Workspace& ws, int r, int c,
+                                           uint32_t (&w)[16]) {
   typedef unsigned int u4 __attribute__((ext_vector_type(4)));
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       ws.codes + ((size_t)r * dm.nchunks + c) * dm.chunk_elems, (short)0, dm.chunk_elems,
       0x00020000);
-  unsigned long long mask = 0ull;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)threadIdx.x * 16, i * kThreads * 16,
                                                        0);
-    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-#pragma unroll
-      for (int bb = 0; bb < 4; ++bb)
-        if ((int)((w[d] >> (8 * bb)) & 0xFFu) <= gk) mask |= 1ull << (16 * i + 4 * d + bb);
+    w[4 * i + 0] = x.x;
+    w[4 * i + 1] = x.y;
+    w[4 * i + 2] = x.z;
+    w[4 * i + 3] = x.w;
   }
+}
+
+// Hit mask of this thread's codes: the slots whose code is at most gk.
+__device__ __forceinline__ unsigned long long coded_hits(const uint32_t (&w)[16], int gk) {
+  unsigned long long mask = 0ull;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+#pragma unroll
+    for (int bb = 0; bb < 4; ++bb)
+      if ((int)((w[j] >> (8 * bb)) & 0xFFu) <= gk) mask |= 1ull << (4 * j + bb);
   return mask;
 }
 
@@ -2025,10 +2032,12 @@ __device__ void final_cpart(const float* __restrict__ tgt, const float* __restri
   const int r = target_row(dm, b, n);
   const float* trow = row_ptr(dm, tgt, drf, r);
   const float* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
+  uint32_t w[16];
+  coded_load(dm, ws, r, c, w);  // issued with the chunk's partial: both depend on n only
   const ChunkPart part = ws.parts[(size_t)r * dm.nchunks + c];
   // kept elements have an edge at or above the threshold's: code <= etop - edge(thr)
   const int gk = part.vmax > -INFINITY ? part.pad[0] - topp_edge(rt.thr, sp.inv_t) : -1;
-  const unsigned long long mask = coded_hits(dm, ws, r, c, gk);
+  const unsigned long long mask = coded_hits(w, gk);
   const int base = c * dm.chunk_elems - row_phase(trow);
   unsigned long long W = 0, Q = 0;
   coded_weights(mask, base, rt, rd, resid, trow, drow, sp.inv_t,
@@ -2066,9 +2075,11 @@ __device__ void final_cpick(const float* __restrict__ tgt, const float* __restri
   const int r = target_row(dm, b, n);
   const float* trow = row_ptr(dm, tgt, drf, r);
   const float* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
+  uint32_t w[16];
+  coded_load(dm, ws, r, c, w);
   const ChunkPart part = ws.parts[(size_t)r * dm.nchunks + c];
   const int gk = part.vmax > -INFINITY ? part.pad[0] - topp_edge(rt.thr, sp.inv_t) : -1;
-  const unsigned long long mask = coded_hits(dm, ws, r, c, gk);
+  const unsigned long long mask = coded_hits(w, gk);
   const int base = c * dm.chunk_elems - row_phase(trow);
   const float it = sp.inv_t;
   const int a = pick_in_chunk(rem, [&](int d1, auto&& add) {
