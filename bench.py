@@ -111,6 +111,14 @@ def _pct(xs_ms):
             "iterations": int(a.size)}
 
 
+def _small_path(K, V, cfg):
+    """Whether the library takes its single-launch path for small problems: dense rows (T > 0,
+    nothing truncated) and all 2K+1 rows of a sequence in one workgroup's registers (V <= 256 L
+    and 2K+1 <= 64 / L for L = 4, 8 or 16)."""
+    dense = cfg["temperature"] > 0 and not (0 < cfg["top_k"] < V) and cfg["top_p"] >= 1.0
+    return dense and any(V <= 256 * L and 2 * K + 1 <= 64 // L for L in (4, 8, 16))
+
+
 def _n_sets(set_bytes):
     """Input sets to rotate: one if a set is larger than twice the last-level cache, else
     enough sets (at least 8, at most 64) to pass that."""
@@ -748,6 +756,8 @@ def bench_verify(args, name, cfg):
         dominant = "k_chunk_argmax"
     elif 0 < cfg["top_k"] <= 256:
         dominant = "k_topk_row"
+    elif _small_path(K, V, cfg):
+        dominant = "k_small"
     else:
         dominant = "k_chunk"
     traffic = _traffic_from_profiles(dominant, name)

@@ -167,6 +167,25 @@ __device__ __forceinline__ T wave_reduce(T v, Op op) {
   return v;
 }
 
+// wave_reduce of N independent values at once: each butterfly step is issued for all N before
+// the next, so that the lane exchanges of different values overlap.
+template <int N, class T, class Op>
+__device__ __forceinline__ void wave_reduce_n(T (&v)[N], Op op) {
+#define SV_STEP(O)                                              \
+  {                                                             \
+    T x[N];                                                     \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) x[i] = xor_lane<O>(v[i]); \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = op(v[i], x[i]);    \
+  }
+  SV_STEP(32)
+  SV_STEP(16)
+  SV_STEP(8)
+  SV_STEP(4)
+  SV_STEP(2)
+  SV_STEP(1)
+#undef SV_STEP
+}
+
 struct RedScratch {
   double d[4];
   float f[4];
@@ -1418,10 +1437,13 @@ struct Outs {
 // accept x~_k with probability min(1, q/p); lenience scales the comparison, App. F of the
 // Leviathan blog).  Writes a/q/p, the accepted drafts, the -1 padding after position n and n;
 // position n itself is written by the final draw.  Returns n in every lane.
-template <class E>
+// rstat(r): the statistics of row r (from memory, or from a caller's copy in LDS);
+// zx(k, x, zt, zd): the logits of target row k and draft row k at token x (0 <= x < V); x_pre:
+// this lane's draft token when the caller loaded it already (lane k, k < 64), else -2
+template <class E, class RS, class ZX>
 __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
                                const Dims& dm, const Samp& sp, const Workspace& ws,
-                               const Outs& o, int b) {
+                               const Outs& o, int b, RS&& rstat, ZX&& zx, int x_pre) {
   const int lane = lane_id();
   const int K = dm.K, V = dm.V;
   const double T = (double)sp.temperature;
@@ -1431,9 +1453,9 @@ __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ 
     const int k = k0 + lane;
     bool rej = false;
     if (k < K) {
-      const int x = o.drafts[(size_t)b * K + k];
-      const RowStat rt = ws.rstat[target_row(dm, b, k)];
-      const RowStat rd = ws.rstat[draft_row(dm, b, k)];
+      const int x = (k0 == 0 && x_pre != -2) ? x_pre : o.drafts[(size_t)b * K + k];
+      const RowStat rt = rstat(target_row(dm, b, k));
+      const RowStat rd = rstat(draft_row(dm, b, k));
       double q = 0.0, p = 0.0, a;
       const MentorSol* ms = sp.mentor ? ws.ment + (size_t)b * K + k : nullptr;
       if (ms && ms->mode != kMentorLossless) {  // mentored decoding: r at the draft token
@@ -1446,10 +1468,8 @@ __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ 
             q = (x == rt.argmax) ? 1.0 : 0.0;
             p = (x == rd.argmax) ? 1.0 : 0.0;
           } else {
-            const E* trow = row_ptr(dm, tgt, drf, target_row(dm, b, k));
-            const E* drow = row_ptr(dm, tgt, drf, draft_row(dm, b, k));
-            const float zt = Tr<E>::to_float(Tr<E>::bits_of(trow[x]));
-            const float zd = Tr<E>::to_float(Tr<E>::bits_of(drow[x]));
+            float zt, zd;
+            zx(k, x, zt, zd);
             if (zt >= rt.thr) q = exp(((double)zt - (double)rt.m) / T) / rt.S;
             if (zd >= rd.thr) p = exp(((double)zd - (double)rd.m) / T) / rd.S;
           }
@@ -1478,6 +1498,20 @@ __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ 
   }
   if (lane == 0) o.n[b] = n;
   return n;
+}
+
+// The same with the statistics from the workspace.
+template <class E>
+__device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
+                               const Dims& dm, const Samp& sp, const Workspace& ws,
+                               const Outs& o, int b) {
+  return seq_accept_wave(
+      tgt, drf, dm, sp, ws, o, b, [&](int r) { return ws.rstat[r]; },
+      [&](int k, int x, float& zt, float& zd) {
+        zt = load_logit(row_ptr(dm, tgt, drf, target_row(dm, b, k)), x);
+        zd = load_logit(row_ptr(dm, tgt, drf, draft_row(dm, b, k)), x);
+      },
+      -2);
 }
 
 // A top-p target row's kept segments (bf16) hold every element at or above the candidate range's
@@ -1650,6 +1684,7 @@ __device__ __forceinline__ DrawRows draw_rows(const Dims& dm, int n, const RowSt
   g.inv_sd = (float)(1.0 / g.rd.S);
   return g;
 }
+
 
 // NV 16-byte vectors per thread from a row.  STRIDED: vector i of thread t at element
 // base + (t + 256 i) * EPV; otherwise a contiguous run, vector i at base + i * EPV.  With VEC the
@@ -2237,6 +2272,163 @@ __device__ double block_exclusive_d2(double a, double b, double& a_tot, double& 
   b_tot = ((s_w[1][0] + s_w[1][1]) + s_w[1][2]) + s_w[1][3];
   b_ex = bb + (y - b);
   return ba + (x - a);
+}
+
+// ------------------------------------------------------------------------------------------
+// k_small: problems whose every sequence fits one workgroup's registers (2K+1 rows of V logits,
+// at most kSmallRegs per thread), dense rows only (T > 0, nothing truncated): one workgroup per
+// sequence reads its rows once and does the row statistics, the accept scan and the final
+// draw in a single launch (the multi-kernel path needs four launches, which dominate at such
+// sizes).  Thread t holds elements [t L, t L + L) of every row (-inf past V); the final draw
+// takes the first thread whose range of the running weight passes u W (weights as in the
+// chunked draw: fp32 per element with reciprocal normalisers, fp64 across), then the element
+// inside it; past the end (rounding), the last element with weight.
+// ------------------------------------------------------------------------------------------
+constexpr int kSmallRegs = 64;
+
+template <class E, int L>
+__global__ __launch_bounds__(kThreads) void k_small(const E* __restrict__ tgt,
+                                                    const E* __restrict__ drf, Dims dm, Samp sp,
+                                                    Workspace ws, Outs o) {
+  constexpr int RMAX = kSmallRegs / L;
+  const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wv = wave_id();
+  const int K = dm.K, R = dm.rows_per_seq;  // rows: target 0..K, then draft 0..K-1
+  const float it = sp.inv_t;
+  __shared__ float s_m[RMAX][kThreads / 64];
+  __shared__ double s_s[RMAX][kThreads / 64];
+  __shared__ RowStat s_rs[RMAX];
+  __shared__ int s_n;
+  __shared__ RedScratch red;
+  const int e0 = tid * L;
+  __shared__ int s_x[RMAX];           // draft tokens
+  __shared__ float s_zx[RMAX][2];     // target and draft logits at them
+  if (tid < K) s_x[tid] = o.drafts[(size_t)b * K + tid];
+  float z[RMAX][L];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const E* row = row_ptr(dm, tgt, drf, b * R + (r < R ? r : 0));
+#pragma unroll
+    for (int e = 0; e < L; ++e)
+      z[r][e] = (r < R && e0 + e < dm.V) ? load_logit(row, e0 + e) : -INFINITY;
+  }
+  // row maxima, then normalisers: fp32 over a thread's elements, fp64 across (fixed orders;
+  // rows past R hold -inf: they are reduced too, and never read)
+  {
+    float mx[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      mx[r] = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < L; ++e) mx[r] = fmaxf(mx[r], z[r][e]);
+    }
+    wave_reduce_n(mx, [](float x, float y) { return fmaxf(x, y); });
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) s_m[r][wv] = mx[r];
+  }
+  __syncthreads();
+  // the logits at the draft tokens, from the thread holding them: row r is target row r
+  // (r <= K) or draft row r - K - 1, either read at draft token k of its position
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    const bool is_t = r <= K;
+    const int k = is_t ? r : r - K - 1;
+    const int x = r < R && k < K ? s_x[k] : -1;
+    if (x >= 0 && x < dm.V && x / L == tid) {
+      float v = 0.0f;
+#pragma unroll
+      for (int j = 0; j < L; ++j)
+        if (e0 + j == x) v = z[r][j];
+      s_zx[k][is_t ? 0 : 1] = v;
+    }
+  }
+  {
+    double sd[RMAX];
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const float m = fmaxf(fmaxf(s_m[r][0], s_m[r][1]), fmaxf(s_m[r][2], s_m[r][3]));
+      float sv = 0.0f;
+      if (r < R) {
+#pragma unroll
+        for (int e = 0; e < L; ++e) sv += fast_exp((z[r][e] - m) * it);
+      }
+      sd[r] = (double)sv;
+    }
+    wave_reduce_n(sd, [](double x, double y) { return x + y; });
+    if (lane == 0)
+#pragma unroll
+      for (int r = 0; r < RMAX; ++r) s_s[r][wv] = sd[r];
+  }
+  __syncthreads();
+  if (tid < R) {
+    RowStat rs;
+    rs.m = fmaxf(fmaxf(s_m[tid][0], s_m[tid][1]), fmaxf(s_m[tid][2], s_m[tid][3]));
+    rs.thr = -INFINITY;
+    rs.S = ((s_s[tid][0] + s_s[tid][1]) + s_s[tid][2]) + s_s[tid][3];
+    rs.argmax = -1;
+    rs.nkept = -1;
+    rs.kind = kRowDense;
+    rs.pad = 0;
+    s_rs[tid] = rs;
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int base = b * R;
+    const int n = seq_accept_wave(
+        tgt, drf, dm, sp, ws, o, b, [&](int r) { return s_rs[r - base]; },
+        [&](int k, int, float& zt, float& zd) {
+          zt = s_zx[k][0];
+          zd = s_zx[k][1];
+        },
+        lane < K ? s_x[lane] : -2);
+    if (lane == 0) s_n = n;
+  }
+  __syncthreads();
+  const int n = s_n;
+  const bool resid = n < K;
+  const DrawRows g = draw_rows(dm, n, s_rs[n], s_rs[resid ? K + 1 + n : n]);
+  // the final pair's weights, its rows taken from the registers by predicated moves
+  float wq[L], ww[L];
+#pragma unroll
+  for (int e = 0; e < L; ++e) {
+    float zt = -INFINITY, zd = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      if (r == n) zt = z[r][e];
+      if (resid && r == K + 1 + n) zd = z[r][e];
+    }
+    draw_weights(zt, zd, g, it, ww[e], wq[e]);
+  }
+  double wl = 0.0, ql = 0.0;  // this thread's masses, in index order
+#pragma unroll
+  for (int e = 0; e < L; ++e) {
+    wl += (double)ww[e];
+    ql += (double)wq[e];
+  }
+  double Wt, Qt, qex;
+  const double wex = block_exclusive_d2(wl, ql, Wt, Qt, qex);
+  const bool use_q = !resid || !(Wt > 0.0);
+  const double ex = use_q ? qex : wex, loc = use_q ? ql : wl;
+  const double target = (double)o.uni[(size_t)b * (K + 1) + K] * (use_q ? Qt : Wt);
+  // the first thread whose range passes the target, else the last thread with mass
+  const int th = block_min_i(loc > 0.0 && ex + loc > target ? tid : INT_MAX, red);
+  const int tl = block_max_i(loc > 0.0 ? tid : -1, red);
+  const int owner = th != INT_MAX ? th : tl;
+  if (tid == owner) {
+    const double rem = target - ex;
+    double cum = 0.0;
+    int pick = -1, last = 0;
+#pragma unroll
+    for (int e = 0; e < L; ++e) {
+      const double v = (double)(use_q ? wq[e] : ww[e]);
+      if (v > 0.0) {
+        last = e;
+        cum += v;
+        if (pick < 0 && th != INT_MAX && cum > rem) pick = e;
+      }
+    }
+    o.tokens[(size_t)b * (K + 1) + n] = e0 + (pick >= 0 ? pick : last);
+  }
 }
 
 
@@ -4225,6 +4417,21 @@ hipError_t launch_verify_t(const E* t, const E* d, const Dims& dm, const Samp& s
     }
     if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);
     return hipGetLastError();
+  }
+  // small problems: one launch, one workgroup per sequence holding all of its rows
+  const bool dense_rows = !sp.greedy && !sp.topp_hist && !sp.generic_trunc && sp.top_k == 0 &&
+                          !(sp.top_p < 1.0f) && !out_beta;
+  const int R = dm.rows_per_seq;
+  if (dense_rows && dm.draft_rows >= dm.K) {
+    auto small = [&](auto kern, int L) {
+      if (dm.V > kThreads * L || R > kSmallRegs / L) return false;
+      hipLaunchKernelGGL(kern, dim3(dm.B), dim3(kThreads), 0, st, t, d, dm, sp, ws, o);
+      if (ev && nev >= 2) (void)hipEventRecord(ev[1], st);
+      if (ev && nev >= 3) (void)hipEventRecord(ev[2], st);
+      return true;
+    };
+    if (small(k_small<E, 4>, 4) || small(k_small<E, 8>, 8) || small(k_small<E, 16>, 16))
+      return hipGetLastError();
   }
   if (sp.greedy)
     hipLaunchKernelGGL((k_chunk_argmax<E>), dim3(grid_chunks), dim3(kThreads), 0, st, t, d, dm, sp,
