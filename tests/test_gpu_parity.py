@@ -108,6 +108,32 @@ def test_topp_extremes(P, T):
     verify_case(t, d, dict(temperature=T, top_p=P), seed=24)
 
 
+@pytest.mark.parametrize("V", [9000, 16384, 16385, 49153])
+def test_topp_fp32_chunk_edges(V):
+    """fp32 top-p rows of one chunk, exactly one chunk, one element past it, and three chunks and
+    a ragged tail (16 384 logits per chunk): the histogram pass writes the edge codes of every
+    slot of each chunk frame, and slots outside the row must never become candidates."""
+    _announce(f"zipf fp32 top-p 0.9 T=0.8 B=5 K=2 V={V}: chunk edges of the edge codes")
+    t, d = S.zipf_logits(5, 2, V, 1.1, 2.0, "f32", seed=V + 7)
+    verify_case(t, d, dict(temperature=0.8, top_p=0.9), seed=V + 7)
+
+
+def test_topp_fp32_sample_and_bonus(_lib):
+    """spec_sample and the K = 0 bonus draw with fp32 top-p: the draw from a row's kept set found
+    from its edge codes, against the oracle's sampler."""
+    _announce("spec_sample fp32 top-p 0.95, R=24 V=70000, and K=0 verification")
+    t, _ = S.zipf_logits(24, 0, 70000, 1.1, 2.0, "f32", seed=68)
+    rows = t[:, 0].contiguous()
+    u = S.philox_uniforms(69, (24,))
+    got = _lib.spec_sample(rows.cuda(), torch.from_numpy(u.copy()).cuda(), temperature=1.0,
+                           top_p=0.95).cpu().numpy()
+    want = O.sample_rows(rows.numpy(), u, np.float32(1.0), 0, np.float32(0.95))
+    np.testing.assert_array_equal(got, want)
+    drafts, uu = make_inputs(t, t[:, :0], dict(temperature=1.0, top_p=0.95), 70)
+    g = run_gpu(t, None, drafts, uu, dict(temperature=1.0, top_p=0.95))
+    check(g, t, None, drafts, uu, dict(temperature=1.0, top_p=0.95))
+
+
 def test_topp_fp32_boundary_candidate_overflow():
     _announce("fp32 logits on 4 levels, top-p 0.9: boundary bin overflows -> row-pass selection")
     g = torch.Generator().manual_seed(42)
