@@ -118,6 +118,14 @@ def test_topp_fp32_chunk_edges(V):
     verify_case(t, d, dict(temperature=0.8, top_p=0.9), seed=V + 7)
 
 
+def test_topp_fp32_long_rows():
+    """fp32 top-p rows of 68 chunks (V = 1.1 M): more chunks than the per-row kernel keeps in
+    LDS, so their partials are read from memory."""
+    _announce("zipf fp32 top-p 0.9 B=1 K=1 V=1100000: 68 chunks per row")
+    t, d = S.zipf_logits(1, 1, 1100000, 1.1, 2.0, "f32", seed=71)
+    verify_case(t, d, dict(temperature=1.0, top_p=0.9), seed=71)
+
+
 def test_topp_fp32_sample_and_bonus(_lib):
     """spec_sample and the K = 0 bonus draw with fp32 top-p: the draw from a row's kept set found
     from its edge codes, against the oracle's sampler."""
