@@ -128,6 +128,12 @@ __device__ __forceinline__ unsigned long long lanes_below() {
   return (1ull << lane_id()) - 1ull;
 }
 
+// base + the number of set bits of mask in the lanes below this one (two mbcnt instructions).
+__device__ __forceinline__ int lane_rank(unsigned long long mask, int base) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                        __builtin_amdgcn_mbcnt_lo((uint32_t)mask, (uint32_t)base));
+}
+
 // The value of lane (this lane ^ O), with no lane-address register: below 32 a ds_swizzle in
 // bit-mask mode (and 0x1F, xor O: an immediate pattern); across the halves v_permlane32_swap,
 // which exchanges the upper half of its first operand with the lower half of its second (both
@@ -1071,6 +1077,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
   __shared__ uint32_t s_prefix;
   __shared__ unsigned long long s_need;
   __shared__ uint32_t s_kmin[4], s_kmax[4];
+  constexpr int kBandCache = 1024;  // chunks whose code band is kept in LDS
+  __shared__ uint32_t s_band[kBandCache];
   uint32_t* s_key = reinterpret_cast<uint32_t*>(s_buf);
   const float it = sp.inv_t;
 
@@ -1096,7 +1104,26 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
                             &s_tr);
   __syncthreads();
   const TopPRow tr = s_tr;
-  bool fallback = !tr.coded;
+  // A chunk's candidates are its codes in [glo, glo + span]: edge = etop - code lies in
+  // [e_lo, e_hi] iff etop - e_hi <= code <= etop - e_lo (below kCodeFar for a coded row, so far
+  // codes never pass).  Packed glo | span << 16, or kNoBand for a chunk with no finite logit or
+  // an empty band.  The bands are kept in LDS, so that the scan reads them without a memory
+  // load that would wait on the code loads in flight; rows of more than kBandCache chunks (over
+  // 16.7 million logits) take the whole-row selection.
+  bool fallback = !tr.coded || dm.nchunks > kBandCache;
+  constexpr uint32_t kNoBand = 0xFFFFFFFFu;
+  if (!fallback) {
+    for (int c = tid; c < dm.nchunks; c += kThreads) {
+      const ChunkPart p = parts[c];
+      const int etop = p.pad[0];
+      const int glo = max(etop - tr.e_hi, 0);
+      const int ghi = etop - tr.e_lo;
+      s_band[c] = !(p.vmax > -INFINITY) || ghi < glo
+                      ? kNoBand
+                      : (uint32_t)glo | ((uint32_t)(ghi - glo) << 16);
+    }
+    __syncthreads();
+  }
   // candidates: one list per wave (a quarter of s_key), filled by ballot compaction
   constexpr int kWaveCand = kTopPCandCap / (kThreads / 64);
   uint32_t* wlist = s_key + wave_id() * kWaveCand;
@@ -1121,17 +1148,11 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
         w[4 * i + 3] = x.w;
       }
     };
-    const unsigned long long below = lanes_below();
-    // edge = etop - code: a candidate iff e_lo <= edge <= e_hi, i.e. etop - e_hi <= code <=
-    // etop - e_lo (below kCodeFar for a coded row, so far codes never pass)
     auto scan = [&](int c, const uint32_t(&w)[4 * NC]) {
-      const ChunkPart p = pp[c];
-      if (!(p.vmax > -INFINITY)) return;  // no finite logit in the chunk
-      const int etop = p.pad[0];
-      const uint32_t glo = (uint32_t)max(etop - tr.e_hi, 0);
-      const int ghi = etop - tr.e_lo;
-      if (ghi < (int)glo) return;
-      const uint32_t span = (uint32_t)ghi - glo;  // code - glo <= span, unsigned
+      const uint32_t band = s_band[c];
+      if (band == kNoBand) return;
+      const uint32_t glo = band & 0xFFFFu;
+      const uint32_t span = band >> 16;  // a candidate iff code - glo <= span, unsigned
       const int c0 = c * dm.chunk_elems - c_ph;
 #pragma unroll
       for (int j = 0; j < 4 * NC; ++j) {
@@ -1142,7 +1163,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
           const unsigned long long m = __ballot(hit);
           if (m) {
             if (hit) {
-              const int pos = wcount + __popcll(m & below);
+              const int pos = lane_rank(m, wcount);
               if (pos < kWaveCand)
                 wlist[pos] = (uint32_t)(c0 + 16 * (tid + kThreads * (j >> 2)) + 4 * (j & 3) + b);
             }
@@ -1153,21 +1174,26 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
     };
     // four chunks in flight: each buffer is refilled with the chunk four ahead once scanned
     uint32_t wa[4 * NC], wb[4 * NC], wc[4 * NC], wd[4 * NC];
+    // issued in chunk order (no reordering by the scheduler), so that the loop's first scan
+    // waits for the oldest loads only
     load_codes(0, wa);
+    __builtin_amdgcn_sched_barrier(0);
     load_codes(1, wb);
+    __builtin_amdgcn_sched_barrier(0);
     load_codes(2, wc);
+    __builtin_amdgcn_sched_barrier(0);
     load_codes(3, wd);
+    __builtin_amdgcn_sched_barrier(0);
+    // (no early exit: one back edge, so the loop's waits stay those of the steady state; loads
+    // past the row's end read nothing)
     for (int c = 0; c < dm.nchunks; c += 4) {
       scan(c, wa);
       load_codes(c + 4, wa);
-      if (c + 1 >= dm.nchunks) break;
-      scan(c + 1, wb);
+      if (c + 1 < dm.nchunks) scan(c + 1, wb);
       load_codes(c + 5, wb);
-      if (c + 2 >= dm.nchunks) break;
-      scan(c + 2, wc);
+      if (c + 2 < dm.nchunks) scan(c + 2, wc);
       load_codes(c + 6, wc);
-      if (c + 3 >= dm.nchunks) break;
-      scan(c + 3, wd);
+      if (c + 3 < dm.nchunks) scan(c + 3, wd);
       load_codes(c + 7, wd);
     }
     if (lane_id() == 0) s_wn[wave_id()] = wcount;
@@ -1743,20 +1769,29 @@ __device__ __forceinline__ void load_vecs(const E* __restrict__ row, int end, in
 //                the masses in chunk order, then the index inside it by two digits (bins of 256
 //                indices, then single indices)
 // ------------------------------------------------------------------------------------------
+// The weights from the two logits at an index (zd unused for the bonus draw).
+__device__ __forceinline__ void list_weights_z(float z, float zd, const RowStat& rt,
+                                               const RowStat& rd, bool resid, float it,
+                                               unsigned long long& wq, unsigned long long& ww) {
+  const double q = z >= rt.thr ? (double)fast_exp((z - rt.m) * it) / rt.S : 0.0;
+  double w = q;
+  if (resid && q > 0.0) {
+    const double p = (double)kept_exp(zd, rd, it) / rd.S;
+    w = q - p > 0.0 ? q - p : 0.0;
+  }
+  wq = (unsigned long long)(q * 0x1p62);
+  ww = (unsigned long long)(w * 0x1p62);
+}
+
+// Both logits are loaded before either is used (one memory round trip, not two).
 template <class E>
 __device__ __forceinline__ void list_weights(int idx, const RowStat& rt, const RowStat& rd,
                                              bool resid, const E* __restrict__ trow,
                                              const E* __restrict__ drow, float it,
                                              unsigned long long& wq, unsigned long long& ww) {
   const float z = load_logit(trow, idx);
-  const double q = z >= rt.thr ? (double)fast_exp((z - rt.m) * it) / rt.S : 0.0;
-  double w = q;
-  if (resid && q > 0.0) {
-    const double p = (double)kept_exp(load_logit(drow, idx), rd, it) / rd.S;
-    w = q - p > 0.0 ? q - p : 0.0;
-  }
-  wq = (unsigned long long)(q * 0x1p62);
-  ww = (unsigned long long)(w * 0x1p62);
+  const float zd = resid ? load_logit(drow, idx) : 0.0f;
+  list_weights_z(z, zd, rt, rd, resid, it, wq, ww);
 }
 
 template <class E>
@@ -2031,16 +2066,18 @@ __device__ __forceinline__ unsigned long long coded_hits(const uint32_t (&w)[16]
 }
 
 // Calls f(slot, wq, ww) for every hit of the mask, with the weights of list_weights; the
-// logits of up to four hits are loaded together.
+// logits of up to eight hits (both rows) are loaded together, before any of them is used.
 template <class F>
 __device__ __forceinline__ void coded_weights(unsigned long long mask, int base, const RowStat& rt,
                                               const RowStat& rd, bool resid,
                                               const float* __restrict__ trow,
                                               const float* __restrict__ drow, float it, F&& f) {
+  constexpr int NB = 8;
   while (mask) {
-    int a[4];
+    int a[NB];
+    float zt[NB], zd[NB];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NB; ++k) {
       a[k] = -1;
       if (mask) {
         a[k] = coded_slot(__ffsll((long long)mask) - 1);
@@ -2048,10 +2085,15 @@ __device__ __forceinline__ void coded_weights(unsigned long long mask, int base,
       }
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < NB; ++k) {
+      zt[k] = a[k] >= 0 ? trow[base + a[k]] : 0.0f;
+      zd[k] = a[k] >= 0 && resid ? drow[base + a[k]] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
       if (a[k] >= 0) {
         unsigned long long wq, ww;
-        list_weights<float>(base + a[k], rt, rd, resid, trow, drow, it, wq, ww);
+        list_weights_z(zt[k], zd[k], rt, rd, resid, it, wq, ww);
         f(a[k], wq, ww);
       }
     }
@@ -2150,10 +2192,12 @@ __global__ __launch_bounds__(kThreads) void k_final_partial(const E* __restrict_
                                                             Samp sp, Workspace ws) {
   // LIST (top-p): max(final chunks, chunks) workgroups per sequence; a sequence drawn from its
   // kept segments takes the first `chunks` of them, one per segment
+  // (LIST: chunk-major, blockIdx = c B + b, so that the workgroups of the kept-list draws,
+  // c < chunks, are dispatched first and spread over the XCDs)
   const int G = LIST ? max(dm.nfchunks, dm.nchunks) : dm.nfchunks;
-  const int bid = xcd_contiguous((int)blockIdx.x, dm.B * G);
-  const int b = bid / G;
-  const int c = bid - b * G;
+  const int bid = LIST ? (int)blockIdx.x : xcd_contiguous((int)blockIdx.x, dm.B * G);
+  const int b = LIST ? bid % dm.B : bid / G;
+  const int c = LIST ? bid / dm.B : bid - (bid / G) * G;
   // the state and the rows' statistics in one step (the statistics are stale, and unused,
   // when the sequence needs no draw here)
   const SeqState st = ws.seq[b];
