@@ -139,7 +139,8 @@ size_t layout_verify(const Dims& d, const Samp& s, void* base, Workspace* ws) {
   const size_t o_dstat = c.take(s.greedy ? 0 : (size_t)d.B * 2 * sizeof(RowStat));
   const size_t o_n = c.take((size_t)d.B * sizeof(int32_t));
   const bool th = s.topp_hist != 0;
-  const size_t o_hist = c.take(th ? rows * nch * kHistBins * sizeof(unsigned long long) : 0);
+  const size_t o_hist =
+      c.take(th ? rows * nch * hist_bins(d.esize) * sizeof(unsigned long long) : 0);
   const size_t o_tprow = c.take(th ? rows * sizeof(TopPRow) : 0);
   const bool cd = topp_codes(d, s);  // fp32: candidates kept in LDS, edge codes instead
   const size_t o_tcand = c.take(th && !cd ? rows * kTopPCandCap * sizeof(uint2) : 0);

@@ -28,8 +28,12 @@ constexpr int kVecPerThread = 16;    // 16-byte vectors each thread holds per ch
 constexpr int kCompactMaxK = 256;    // top-k <= this uses the compact candidate path
 constexpr int kKeptCap = 1024;       // kept tokens a compact row may hold
 constexpr int kSeqThreads = 64;      // one wave per sequence
-constexpr int kHistBins = 512;       // top-p mass histogram bins per chunk ...
+constexpr int kHistBins = 512;       // top-p mass histogram bins per chunk (bf16) ...
 constexpr int kHistPerUnit = 8;      // ... on a grid of 1/8 of a unit of z / T
+constexpr int kHistBinsF32 = 256;    // fp32 rows: as many as the edge codes resolve (the last
+                                     // bin, like code kCodeFar, holds everything lower)
+// Histogram bins per chunk for logits of esize bytes.
+inline int hist_bins(int esize) { return esize == 4 ? kHistBinsF32 : kHistBins; }
 constexpr int kTopPCandCap = 4096;   // boundary candidates a top-p row may hold
 constexpr int kTopPSegCap = 1024;    // kept-list entries of one chunk of a top-p target row
 constexpr int kMentorBisectionSteps = 50;  // bisection steps on alpha (mentored decoding)
@@ -139,7 +143,7 @@ struct Workspace {
   RowStat* dstat;    // [B][2] statistics of the final draw's rows (target; draft, or the
                      // target again for the bonus draw)
   int32_t* nbuf;     // [B] accepted counts when the caller does not want them
-  unsigned long long* hist;  // [rows][nchunks][kHistBins] fixed-point mass   top-p histogram only
+  unsigned long long* hist;  // [rows][nchunks][hist_bins] fixed-point mass   top-p histogram only
   TopPRow* tprow;            // [rows]                                        top-p histogram only
   uint2* tcand;              // [rows][kTopPCandCap] (index, bits)            top-p bf16 only
   uint32_t* tkept;           // [B*(K+1)][nchunks][kTopPSegCap] index of every element of a

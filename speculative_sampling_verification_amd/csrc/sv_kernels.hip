@@ -370,9 +370,10 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
   uint32_t regs[kRegs];
   ChunkPart* part = ws.parts + (size_t)r * dm.nchunks + c;
 
-  __shared__ unsigned long long s_hist[HIST ? kHistBins : 1];
+  constexpr int NBINS = sizeof(E) == 4 ? kHistBinsF32 : kHistBins;
+  __shared__ unsigned long long s_hist[HIST ? NBINS : 1];
   if constexpr (HIST)
-    for (int j = tid; j < kHistBins; j += kThreads) s_hist[j] = 0ull;
+    for (int j = tid; j < NBINS; j += kThreads) s_hist[j] = 0ull;
   // element index of the chunk's first slot (negative for a row's first chunk when unaligned)
   const int c0 = c * dm.chunk_elems -
                  load_chunk_frame<E>(row, dm.V, c, dm.chunk_elems, regs, Tr<E>::kNegInfPair);
@@ -420,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
               uint32_t code = kCodeFar;
               if (e > 0.0f) {
                 const int g = etop - topp_edge(z, it);
-                const int j = min(g, kHistBins - 1);
+                const int j = min(g, NBINS - 1);
                 atomicAdd(&s_hist[j], __float2ull_rz(e * 1099511627776.0f));
                 code = (uint32_t)min(g, kCodeFar);
               }
@@ -437,8 +438,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk(const E* __restrict__ tgt,
     }
     p.sum = block_sum_d(s, red);  // its barriers also order the histogram updates
     if constexpr (HIST) {
-      unsigned long long* dst = ws.hist + ((size_t)r * dm.nchunks + c) * kHistBins;
-      for (int j = tid; j < kHistBins; j += kThreads) dst[j] = s_hist[j];
+      unsigned long long* dst = ws.hist + ((size_t)r * dm.nchunks + c) * NBINS;
+      for (int j = tid; j < NBINS; j += kThreads) dst[j] = s_hist[j];
       p.pad[0] = etop;
     }
   }
@@ -653,48 +654,48 @@ __device__ uint32_t radix_select(const E* row, int V, float m, float it, uint32_
 // ------------------------------------------------------------------------------------------
 // Histogram loads of a batch of chunks [c0, c0 + kHistBatch) of row r (zeros past the row), so
 // that callers can issue the first batch before they need it.
-constexpr int kHistPT = kHistBins / kThreads;  // bins per thread
-template <int NB>  // chunks per batch
-using HistBatch = unsigned long long[NB][kHistPT];
+// NBINS bins per chunk (kHistBins for bf16 rows, kHistBinsF32 for fp32 rows).
+template <int NB, int NBINS>  // chunks per batch
+using HistBatch = unsigned long long[NB][NBINS / kThreads];
 
-template <int NB>
+template <int NB, int NBINS>
 __device__ __forceinline__ void hist_batch_load(const Dims& dm, const Workspace& ws, int r, int c0,
-                                                int ce, HistBatch<NB>& h) {
+                                                int ce, HistBatch<NB, NBINS>& h) {
   // a buffer over chunks [c0, ce) of the row: loads past it read 0, with no branch
   typedef unsigned int u2 __attribute__((ext_vector_type(2)));
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      ws.hist + ((size_t)r * dm.nchunks + c0) * kHistBins, (short)0,
-      max(0, ce - c0) * kHistBins * (int)sizeof(unsigned long long), 0x00020000);
+      ws.hist + ((size_t)r * dm.nchunks + c0) * NBINS, (short)0,
+      max(0, ce - c0) * NBINS * (int)sizeof(unsigned long long), 0x00020000);
 #pragma unroll
   for (int q = 0; q < NB; ++q)
 #pragma unroll
-    for (int i = 0; i < kHistPT; ++i) {
+    for (int i = 0; i < NBINS / kThreads; ++i) {
       const u2 x = __builtin_amdgcn_raw_buffer_load_b64(
           rs, (int)((threadIdx.x + i * kThreads) * sizeof(unsigned long long)),
-          q * kHistBins * (int)sizeof(unsigned long long), 0);
+          q * NBINS * (int)sizeof(unsigned long long), 0);
       h[q][i] = (unsigned long long)x.x | ((unsigned long long)x.y << 32);
     }
 }
 
 // parts: the row's chunk partials (global memory or an LDS copy); h0: the histograms of the
 // first batch of NB chunks, loaded by hist_batch_load(dm, ws, r, 0, min(kThreads, nchunks), h0).
-template <int NB>
+template <int NB, int NBINS>
 __device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r,
                                            const ChunkPart* parts, float m, double S,
-                                           double* s_mass, const Workspace& ws, HistBatch<NB>& h0,
-                                           TopPRow* s_out = nullptr) {
+                                           double* s_mass, const Workspace& ws,
+                                           HistBatch<NB, NBINS>& h0, TopPRow* s_out = nullptr) {
   const int tid = threadIdx.x;
   __shared__ RedScratch red;
   int emt = INT_MIN;
   for (int c = tid; c < dm.nchunks; c += kThreads)
     if (parts[c].vmax > -INFINITY) emt = max(emt, parts[c].pad[0]);
   const int em = block_max_i(emt, red);
-  // row bin B holds the elements with edge em - B (B = kHistBins - 1: that edge and below);
+  // row bin B holds the elements with edge em - B (B = NBINS - 1: that edge and below);
   // chunk c's bin j lands in row bin j + (em - edge of chunk c's maximum).  Chunks are added in
   // order, one bin per thread and chunk (the shift is one-to-one below the last bin; a barrier
   // between chunks), so every bin's sum has a fixed order; the last bin's share is summed per
   // thread and reduced.  The histograms are loaded NB chunks at a time.
-  constexpr int PT = kHistPT;
+  constexpr int PT = NBINS / kThreads;
   // each chunk's scale exp((vmax - m) / T) (in 2^-40 units; 0: no mass) and shift em - edge of
   // its maximum, computed once per chunk, in blocks of kThreads chunks
   __shared__ double s_sc[kThreads];
@@ -712,7 +713,7 @@ __device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r
       s_dc[tid] = live ? (long long)em - p.pad[0] : 0;
     }
     const int ce = min(cb + kThreads, dm.nchunks);
-    auto add_batch = [&](const HistBatch<NB>& h, int c0) {
+    auto add_batch = [&](const HistBatch<NB, NBINS>& h, int c0) {
 #pragma unroll
       for (int q = 0; q < NB; ++q) {
         if (c0 + q >= ce) break;
@@ -724,7 +725,7 @@ __device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r
           for (int i = 0; i < PT; ++i) {
             const int j = tid + i * kThreads;
             const double v = (double)h[q][i] * sc;
-            if (j == kHistBins - 1 || j + dc >= kHistBins - 1)
+            if (j == NBINS - 1 || j + dc >= NBINS - 1)
               rest += v;
             else
               s_mass[j + dc] += v;
@@ -738,16 +739,16 @@ __device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r
       c0 = NB;
     }
     for (; c0 < ce; c0 += NB) {
-      HistBatch<NB> hl;
-      hist_batch_load<NB>(dm, ws, r, c0, ce, hl);
+      HistBatch<NB, NBINS> hl;
+      hist_batch_load<NB, NBINS>(dm, ws, r, c0, ce, hl);
       add_batch(hl, c0);
     }
   }
   rest = block_sum_d(rest, red);
-  if (tid == 0) s_mass[kHistBins - 1] = rest;
+  if (tid == 0) s_mass[NBINS - 1] = rest;
   __syncthreads();
   if (tid < 64) {
-    constexpr int PER = kHistBins / 64;
+    constexpr int PER = NBINS / 64;
     const int lane = tid;
     double v[PER];
     double tot = 0.0;
@@ -776,7 +777,7 @@ __device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r
     last = wave_reduce(last, [](int a, int b) { return a > b ? a : b; });
     if (bstar == INT_MAX) bstar = last < 0 ? 0 : last;  // rounding kept the total below P S
     const int lo = bstar > 0 ? bstar - 1 : 0;
-    const int hi = bstar + 1 < kHistBins - 1 ? bstar + 1 : kHistBins - 1;
+    const int hi = bstar + 1 < NBINS - 1 ? bstar + 1 : NBINS - 1;
     double above = 0.0;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
@@ -786,7 +787,7 @@ __device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r
       TopPRow t;
       t.mass_above = above;
       t.e_hi = em - lo;
-      t.e_lo = hi == kHistBins - 1 ? INT_MIN : em - hi;
+      t.e_lo = hi == NBINS - 1 ? INT_MIN : em - hi;
       t.count = 0;
       // every chunk's top edge is at most em, so a code below kCodeFar resolves any edge down
       // to em - (kCodeFar - 1): the codes decide the range when it ends above that
@@ -1072,7 +1073,7 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
   __shared__ TopPRow s_tr;
   __shared__ int s_wn[kThreads / 64];
   constexpr int kPartsCache = 64;  // rows of up to this many chunks keep their partials in LDS
-  constexpr int kRowHistBatch = 8;  // chunks per batch of histogram loads
+  constexpr int kRowHistBatch = 16;  // chunks per batch of histogram loads
   __shared__ ChunkPart s_parts[kPartsCache];
   __shared__ uint32_t s_prefix;
   __shared__ unsigned long long s_need;
@@ -1084,8 +1085,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
 
   // the first histograms are loaded before anything else (the bracket needs them first), then
   // the chunk partials once, into LDS when the row has few chunks
-  HistBatch<kRowHistBatch> h0;
-  hist_batch_load<kRowHistBatch>(dm, ws, r, 0, min(kThreads, dm.nchunks), h0);
+  HistBatch<kRowHistBatch, kHistBinsF32> h0;
+  hist_batch_load<kRowHistBatch, kHistBinsF32>(dm, ws, r, 0, min(kThreads, dm.nchunks), h0);
   const bool pcached = dm.nchunks <= kPartsCache;
   if (pcached && tid < dm.nchunks) s_parts[tid] = parts[tid];
   __syncthreads();
@@ -1100,7 +1101,8 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
     if (p.sum > 0.0) st += p.sum * exp((double)(p.vmax - m) / (double)sp.temperature);
   }
   const double S = block_sum_d(st, red);
-  topp_range<kRowHistBatch>(dm, sp, r, pp, m, S, reinterpret_cast<double*>(s_buf), ws, h0,
+  topp_range<kRowHistBatch, kHistBinsF32>(dm, sp, r, pp, m, S, reinterpret_cast<double*>(s_buf),
+                                          ws, h0,
                             &s_tr);
   __syncthreads();
   const TopPRow tr = s_tr;
@@ -1413,9 +1415,10 @@ __global__ __launch_bounds__(kThreads) void k_row(const E* __restrict__ tgt,
   if (sp.topp_hist) {
     // top-p without top-k: locate the boundary bin of the merged mass histogram; the exact
     // threshold is taken among the boundary candidates by k_topp_select
-    HistBatch<2> h0;
-    hist_batch_load<2>(dm, ws, r, 0, min(kThreads, dm.nchunks), h0);
-    topp_range<2>(dm, sp, r, parts, m, s_S, reinterpret_cast<double*>(s_bins), ws, h0);
+    constexpr int NBINS = sizeof(E) == 4 ? kHistBinsF32 : kHistBins;
+    HistBatch<2, NBINS> h0;
+    hist_batch_load<2, NBINS>(dm, ws, r, 0, min(kThreads, dm.nchunks), h0);
+    topp_range<2, NBINS>(dm, sp, r, parts, m, s_S, reinterpret_cast<double*>(s_bins), ws, h0);
     if (tid == 0) {
       out.thr = -INFINITY;
       out.S = s_S;
