@@ -134,6 +134,17 @@ __device__ __forceinline__ int lane_rank(unsigned long long mask, int base) {
                                         __builtin_amdgcn_mbcnt_lo((uint32_t)mask, (uint32_t)base));
 }
 
+// 2 mk + (x < n), unsigned: the borrow of x - n (left in VCC by v_sub_co_u32) is the carry-in
+// of mk + mk (v_addc_co_u32), with the two wait states a VALU read of a VALU-written VCC needs.
+__device__ __forceinline__ uint32_t shift_in_lt(uint32_t mk, uint32_t x, uint32_t n) {
+  uint32_t out, diff;
+  asm("v_sub_co_u32 %1, vcc, %2, %3\n\ts_nop 1\n\tv_addc_co_u32 %0, vcc, %4, %4, vcc"
+      : "=v"(out), "=&v"(diff)
+      : "v"(x), "v"(n), "v"(mk)
+      : "vcc");
+  return out;
+}
+
 // The value of lane (this lane ^ O), with no lane-address register: below 32 a ds_swizzle in
 // bit-mask mode (and 0x1F, xor O: an immediate pattern); across the halves v_permlane32_swap,
 // which exchanges the upper half of its first operand with the lower half of its second (both
@@ -1150,28 +1161,34 @@ __global__ __launch_bounds__(kThreads, 4) void k_topp_row(const float* __restric
         w[4 * i + 3] = x.w;
       }
     };
+    // Per chunk, each lane first shifts its 64 tests into two hit masks (no branch per code:
+    // code k = 4 j + b ends at bit 31 - (k mod 32) of mask k / 32), then the wave appends the
+    // hits in rounds, each lane its highest remaining bit per round (a round per hit of the
+    // busiest lane).
     auto scan = [&](int c, const uint32_t(&w)[4 * NC]) {
       const uint32_t band = s_band[c];
       if (band == kNoBand) return;
       const uint32_t glo = band & 0xFFFFu;
-      const uint32_t span = band >> 16;  // a candidate iff code - glo <= span, unsigned
-      const int c0 = c * dm.chunk_elems - c_ph;
+      const uint32_t n = (band >> 16) + 1u;  // a candidate iff code - glo < n, unsigned
+      uint32_t mk[2] = {0u, 0u};
 #pragma unroll
-      for (int j = 0; j < 4 * NC; ++j) {
+      for (int j = 0; j < 4 * NC; ++j)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const uint32_t g = (w[j] >> (8 * b)) & 0xFFu;
-          const bool hit = g - glo <= span;
-          const unsigned long long m = __ballot(hit);
-          if (m) {
-            if (hit) {
-              const int pos = lane_rank(m, wcount);
-              if (pos < kWaveCand)
-                wlist[pos] = (uint32_t)(c0 + 16 * (tid + kThreads * (j >> 2)) + 4 * (j & 3) + b);
-            }
-            wcount += __popcll(m);
-          }
-        }
+        for (int b = 0; b < 4; ++b)
+          mk[j >> 3] = shift_in_lt(mk[j >> 3], ((w[j] >> (8 * b)) & 0xFFu) - glo, n);
+      const int c0 = c * dm.chunk_elems - c_ph + 16 * tid;
+      while (true) {
+        const bool has = (mk[0] | mk[1]) != 0u;
+        const unsigned long long m = __ballot(has);
+        if (!m) break;
+        const int k = mk[0] ? __builtin_clz(mk[0]) : 32 + __builtin_clz(mk[1] | 1u);
+        if (mk[0])
+          mk[0] &= ~(0x80000000u >> k);
+        else
+          mk[1] &= ~(0x80000000u >> (k - 32));
+        const int pos = lane_rank(m, wcount);
+        if (has && pos < kWaveCand) wlist[pos] = (uint32_t)(c0 + kThreads * 16 * (k >> 4) + (k & 15));
+        wcount += __popcll(m);
       }
     };
     // four chunks in flight: each buffer is refilled with the chunk four ahead once scanned
