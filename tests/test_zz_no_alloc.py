@@ -69,7 +69,7 @@ def test_noalloc_equals_spec_verify_on_two_calls_in_a_row(svm):
 
 
 def test_noalloc_refuses_a_problem_beyond_the_scratch(svm):
-    # B=128 K=3 V=256000 fp32 top-p 0.95 needs about 281 MiB of workspace
+    # B=128 K=3 V=256000 fp32 top-p 0.95 needs about 253 MiB of workspace
     B, K, V = 128, 3, 256000
     from speculative_sampling_verification_amd import _lib
     import ctypes
