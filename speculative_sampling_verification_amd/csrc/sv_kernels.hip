@@ -786,9 +786,26 @@ __device__ __forceinline__ void topp_range(const Dims& dm, const Samp& sp, int r
     }
     bstar = wave_reduce(bstar, [](int a, int b) { return a < b ? a : b; });
     last = wave_reduce(last, [](int a, int b) { return a > b ? a : b; });
-    if (bstar == INT_MAX) bstar = last < 0 ? 0 : last;  // rounding kept the total below P S
-    const int lo = bstar > 0 ? bstar - 1 : 0;
-    const int hi = bstar + 1 < NBINS - 1 ? bstar + 1 : NBINS - 1;
+    const bool crossed = bstar != INT_MAX;
+    if (!crossed) bstar = last < 0 ? 0 : last;  // rounding kept the total below P S
+    // The bin masses differ from the selection's own weights (exp relative to the row maximum,
+    // 2^-40 fixed point) by the fp32 exponentials' rounding (< 1e-6 of the mass) and the
+    // truncation to 2^-40 (< 2^-40 per element, in both).  When the crossing of P S lies
+    // farther than that from both edges of bin bstar, the boundary is in bstar and bstar alone
+    // is the candidate range; otherwise its two neighbours are taken too.
+    double before = 0.0, through = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (lane * PER + i < bstar) before += v[i];
+      if (lane * PER + i <= bstar) through += v[i];
+    }
+    before = wave_reduce(before, [](double a, double b) { return a + b; });
+    through = wave_reduce(through, [](double a, double b) { return a + b; });
+    const double eps = 2e-5 * S + (double)dm.V * 0x1p-38;
+    const bool single =
+        crossed && bstar < NBINS - 1 && before < target - eps && through >= target + eps;
+    const int lo = single ? bstar : (bstar > 0 ? bstar - 1 : 0);
+    const int hi = single ? bstar : (bstar + 1 < NBINS - 1 ? bstar + 1 : NBINS - 1);
     double above = 0.0;
 #pragma unroll
     for (int i = 0; i < PER; ++i)
