@@ -156,6 +156,27 @@ def test_topp_fp32_kept_segments_overflow():
     verify_case(t, d, dict(temperature=1.0, top_p=0.95), seed=43)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_topp_crossing_near_bin_edge(dtype):
+    """Top-p with P * S a hair (2e-6 relative) above the mass of every token at or above one edge
+    of the 1/8-unit grid: the crossing lies in the next occupied bin but within the bin masses'
+    rounding margin of its upper edge, so the candidate range takes that bin's neighbours too
+    (a crossing clear of both edges takes the one bin); the tokens still equal the oracle's.
+    P is tuned on target row (0, 0); the other rows take their own brackets."""
+    _announce(f"zipf {dtype} top-p tuned to a bin edge, B=4 K=2 V=5000")
+    t, d = S.zipf_logits(4, 2, 5000, 1.1, 2.0, dtype, seed=81)
+    z = t[0, 0].float().numpy().astype(np.float64)
+    w = np.exp(z - z.max())
+    S_ = w.sum()
+    edges = np.floor(8.0 * z)
+    levels = np.unique(edges)[::-1]  # occupied edges, from the top
+    mass = np.array([w[edges >= e].sum() for e in levels])
+    j = int(np.argmax(mass / S_ >= 0.7))  # the first edge whose mass from the top reaches 0.7
+    P = float(np.float32(mass[j] / S_ * (1.0 + 2e-6)))
+    assert mass[j] < P * S_ < mass[j + 1]
+    verify_case(t, d, dict(temperature=1.0, top_p=P), seed=81)
+
+
 # ------------------------------------------------------------------ layouts and edge cases
 def test_unaligned_vocab():
     _announce("unaligned rows: bf16 V=50001 top-k 50, fp32 V=1001 dense")
