@@ -849,7 +849,7 @@ def main():
                          "calibrating rocprofv3 byte counters); 0 disables")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: this benchmark measures one GPU; --gpus {args.gpus} is not supported "
               "(the verify step is data-parallel over sequences and needs no exchange, so "
               "N GPUs would each run this benchmark on their own share)", file=sys.stderr)
         sys.exit(2)

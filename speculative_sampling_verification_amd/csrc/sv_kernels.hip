@@ -1976,7 +1976,7 @@ __device__ int pick_list_chunk(const Dims& dm, const Workspace& ws, const float*
 // The index of the pick inside a chunk from its entries' positions a (relative to the chunk's
 // first slot, below 32768) and weights: the first of 128 bins of 256 positions whose running
 // mass passes rem, then the position inside it; add(a, w) is called by the caller for every
-// entry in each of the two rounds (round 0: bins of 256, round 1: positions of bin d1).
+// entry in each of the two passes (pass 0: bins of 256, pass 1: positions of bin d1).
 template <class F>
 __device__ int pick_in_chunk(double rem, F&& entries) {
   const int tid = threadIdx.x, lane = lane_id();
@@ -2175,7 +2175,7 @@ __device__ void final_cpart(const float* __restrict__ tgt, const float* __restri
 }
 
 // The draw, as final_lpick, from the codes: the chunk from the masses of final_cpart, the
-// position inside it from the chunk's hits (round 1 only rescans the 16 threads whose slots lie
+// position inside it from the chunk's hits (pass 1 only rescans the 16 threads whose slots lie
 // in bin d1).
 __device__ void final_cpick(const float* __restrict__ tgt, const float* __restrict__ drf,
                             const Dims& dm, const Samp& sp, const Workspace& ws,

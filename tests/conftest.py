@@ -14,7 +14,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # Tests marked gpu are skipped when no GPU is visible, so that "-m 'not gpu'" and a plain
-    # run on a CPU-only machine behave the same; on a GPU machine they run.
+    # run on a CPU-only machine behave the same; where a GPU is visible they run.
     try:
         import torch
         has_gpu = torch.cuda.is_available()
