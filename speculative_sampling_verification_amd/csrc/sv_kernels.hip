@@ -2196,11 +2196,45 @@ __device__ void final_cpick(const float* __restrict__ tgt, const float* __restri
   const unsigned long long mask = coded_hits(w, gk);
   const int base = c * dm.chunk_elems - row_phase(trow);
   const float it = sp.inv_t;
+  // this thread's first eight hits and their weights, computed once for both passes (both
+  // logits of each loaded together); a thread with more hits (rare) recomputes the rest per pass
+  constexpr int NH = 8;
+  int hs[NH];
+  unsigned long long hw[NH];
+  unsigned long long rest = mask;
+  {
+    float zt[NH], zd[NH];
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      hs[k] = -1;
+      if (rest) {
+        hs[k] = coded_slot(__ffsll((long long)rest) - 1);
+        rest &= rest - 1ull;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      zt[k] = hs[k] >= 0 ? trow[base + hs[k]] : 0.0f;
+      zd[k] = hs[k] >= 0 && resid ? drow[base + hs[k]] : 0.0f;
+    }
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      hw[k] = 0ull;
+      if (hs[k] >= 0) {
+        unsigned long long wq, ww;
+        list_weights_z(zt[k], zd[k], rt, rd, resid, it, wq, ww);
+        hw[k] = use_q ? wq : ww;
+      }
+    }
+  }
   const int a = pick_in_chunk(rem, [&](int d1, auto&& add) {
-    unsigned long long m = mask;
-    if (d1 >= 0) {  // bin d1 holds slots 256 d1 .. + 255: vector d1 / 16 of threads 16 (d1 % 16) ..
+#pragma unroll
+    for (int k = 0; k < NH; ++k)
+      if (hs[k] >= 0) add(hs[k], hw[k]);  // (the second pass keeps bin d1's)
+    unsigned long long m = rest;
+    if (m && d1 >= 0) {  // bin d1: slots 256 d1 .. + 255, vector d1 / 16 of threads 16 (d1 % 16) ..
       const bool mine = ((int)threadIdx.x >> 4) == (d1 & 15);
-      m = mine ? (mask >> (16 * (d1 >> 4))) & 0xFFFFull : 0ull;
+      m = mine ? (m >> (16 * (d1 >> 4))) & 0xFFFFull : 0ull;
       m <<= 16 * (d1 >> 4);
     }
     coded_weights(m, base, rt, rd, resid, trow, drow, it,
