@@ -2103,28 +2103,34 @@ __device__ __forceinline__ unsigned long long coded_hits(const uint32_t (&w)[16]
 }
 
 // Calls f(slot, wq, ww) for every hit of the mask, with the weights of list_weights; the
-// logits of up to eight hits (both rows) are loaded together, before any of them is used.
+// logits of up to eight hits (both rows) are loaded together, before any of them is used.  dmask
+// (same bit layout): the slots where the draft row may keep its token; elsewhere p = 0 and the
+// draft logit is not loaded.
 template <class F>
-__device__ __forceinline__ void coded_weights(unsigned long long mask, int base, const RowStat& rt,
-                                              const RowStat& rd, bool resid,
-                                              const float* __restrict__ trow,
+__device__ __forceinline__ void coded_weights(unsigned long long mask, unsigned long long dmask,
+                                              int base, const RowStat& rt, const RowStat& rd,
+                                              bool resid, const float* __restrict__ trow,
                                               const float* __restrict__ drow, float it, F&& f) {
   constexpr int NB = 8;
   while (mask) {
     int a[NB];
+    bool dk[NB];
     float zt[NB], zd[NB];
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       a[k] = -1;
+      dk[k] = false;
       if (mask) {
-        a[k] = coded_slot(__ffsll((long long)mask) - 1);
+        const int kb = __ffsll((long long)mask) - 1;
+        a[k] = coded_slot(kb);
+        dk[k] = resid && ((dmask >> kb) & 1ull);
         mask &= mask - 1ull;
       }
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
       zt[k] = a[k] >= 0 ? trow[base + a[k]] : 0.0f;
-      zd[k] = a[k] >= 0 && resid ? drow[base + a[k]] : 0.0f;
+      zd[k] = dk[k] ? drow[base + a[k]] : -INFINITY;
     }
 #pragma unroll
     for (int k = 0; k < NB; ++k) {
@@ -2135,6 +2141,24 @@ __device__ __forceinline__ void coded_weights(unsigned long long mask, int base,
       }
     }
   }
+}
+
+// The slots of chunk c of draft row n of sequence b where the draft may keep its token (code at
+// most the draft threshold's; every slot when the draft row's frame is not the target row's,
+// or when the row is not a residual draw).
+__device__ __forceinline__ unsigned long long draft_kept_mask(const Dims& dm, const Samp& sp,
+                                                              const Workspace& ws, int b, int n,
+                                                              int c, const RowStat& rd,
+                                                              const float* trow,
+                                                              const float* drow) {
+  if (drow == nullptr || row_phase(trow) != row_phase(drow)) return ~0ull;
+  const int r = draft_row(dm, b, n);
+  uint32_t w[16];
+  coded_load(dm, ws, r, c, w);
+  const ChunkPart part = ws.parts[(size_t)r * dm.nchunks + c];
+  const int gk = part.vmax > -INFINITY ? part.pad[0] - topp_edge(rd.thr, sp.inv_t) : -1;
+  // (a threshold beyond the codes' reach, gk >= kCodeFar, keeps every slot, far codes too)
+  return coded_hits(w, gk);
 }
 
 // The chunk's masses of the final weights, as final_lpart, from the codes.
@@ -2149,12 +2173,13 @@ __device__ void final_cpart(const float* __restrict__ tgt, const float* __restri
   uint32_t w[16];
   coded_load(dm, ws, r, c, w);  // issued with the chunk's partial: both depend on n only
   const ChunkPart part = ws.parts[(size_t)r * dm.nchunks + c];
+  const unsigned long long dmask = draft_kept_mask(dm, sp, ws, b, n, c, rd, trow, drow);
   // kept elements have an edge at or above the threshold's: code <= etop - edge(thr)
   const int gk = part.vmax > -INFINITY ? part.pad[0] - topp_edge(rt.thr, sp.inv_t) : -1;
   const unsigned long long mask = coded_hits(w, gk);
   const int base = c * dm.chunk_elems - row_phase(trow);
   unsigned long long W = 0, Q = 0;
-  coded_weights(mask, base, rt, rd, resid, trow, drow, sp.inv_t,
+  coded_weights(mask, dmask, base, rt, rd, resid, trow, drow, sp.inv_t,
                 [&](int, unsigned long long wq, unsigned long long ww) {
                   W += ww;
                   Q += wq;
@@ -2192,6 +2217,7 @@ __device__ void final_cpick(const float* __restrict__ tgt, const float* __restri
   uint32_t w[16];
   coded_load(dm, ws, r, c, w);
   const ChunkPart part = ws.parts[(size_t)r * dm.nchunks + c];
+  const unsigned long long dmask = draft_kept_mask(dm, sp, ws, b, n, c, rd, trow, drow);
   const int gk = part.vmax > -INFINITY ? part.pad[0] - topp_edge(rt.thr, sp.inv_t) : -1;
   const unsigned long long mask = coded_hits(w, gk);
   const int base = c * dm.chunk_elems - row_phase(trow);
@@ -2203,19 +2229,23 @@ __device__ void final_cpick(const float* __restrict__ tgt, const float* __restri
   unsigned long long hw[NH];
   unsigned long long rest = mask;
   {
+    bool dk[NH];
     float zt[NH], zd[NH];
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       hs[k] = -1;
+      dk[k] = false;
       if (rest) {
-        hs[k] = coded_slot(__ffsll((long long)rest) - 1);
+        const int kb = __ffsll((long long)rest) - 1;
+        hs[k] = coded_slot(kb);
+        dk[k] = resid && ((dmask >> kb) & 1ull);
         rest &= rest - 1ull;
       }
     }
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       zt[k] = hs[k] >= 0 ? trow[base + hs[k]] : 0.0f;
-      zd[k] = hs[k] >= 0 && resid ? drow[base + hs[k]] : 0.0f;
+      zd[k] = dk[k] ? drow[base + hs[k]] : -INFINITY;
     }
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
@@ -2237,7 +2267,7 @@ __device__ void final_cpick(const float* __restrict__ tgt, const float* __restri
       m = mine ? (m >> (16 * (d1 >> 4))) & 0xFFFFull : 0ull;
       m <<= 16 * (d1 >> 4);
     }
-    coded_weights(m, base, rt, rd, resid, trow, drow, it,
+    coded_weights(m, dmask, base, rt, rd, resid, trow, drow, it,
                   [&](int s, unsigned long long wq, unsigned long long ww) {
                     add(s, use_q ? wq : ww);
                   });
