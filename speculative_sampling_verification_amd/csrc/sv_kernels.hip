@@ -184,23 +184,44 @@ __device__ __forceinline__ T wave_reduce(T v, Op op) {
   return v;
 }
 
-// wave_reduce of N independent values at once: each butterfly step is issued for all N before
-// the next, so that the lane exchanges of different values overlap.
-template <int N, class T, class Op>
-__device__ __forceinline__ void wave_reduce_n(T (&v)[N], Op op) {
-#define SV_STEP(O)                                              \
-  {                                                             \
-    T x[N];                                                     \
-    _Pragma("unroll") for (int i = 0; i < N; ++i) x[i] = xor_lane<O>(v[i]); \
-    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = op(v[i], x[i]);    \
+// N values per lane (N a power of two, at most 64) reduced across the wave by recursive
+// halving: at the exchange with lane ^ O a lane keeps the upper half of its live values if bit
+// O of its lane id is set, else the lower half, and combines them with the partner's copies of
+// the same values, so each step halves the live values: N - 1 combines, then 6 - log2 N
+// butterfly steps on the one value left, against 6 N combines for N separate butterflies.
+// Returns the total of value (lane >> (6 - log2 N)); the lanes that share those bits all
+// hold it.
+template <int O, int C, int N, class T, class Op>
+__device__ __forceinline__ void halving_step(T (&v)[N], Op op) {  // C of the N values live
+  const bool up = (lane_id() & O) != 0;
+#pragma unroll
+  for (int j = 0; j < C / 2; ++j) {
+    const T keep = up ? v[j + C / 2] : v[j];
+    const T send = up ? v[j] : v[j + C / 2];
+    v[j] = op(keep, xor_lane<O>(send));
   }
-  SV_STEP(32)
-  SV_STEP(16)
-  SV_STEP(8)
-  SV_STEP(4)
-  SV_STEP(2)
-  SV_STEP(1)
-#undef SV_STEP
+}
+constexpr int log2_pow2(int n) { return n <= 1 ? 0 : 1 + log2_pow2(n / 2); }
+
+template <int N, class T, class Op>
+__device__ __forceinline__ T wave_reduce_halving(T (&v)[N], Op op) {
+  static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "a power of two up to 64");
+  if constexpr (N >= 2) halving_step<32, N>(v, op);
+  if constexpr (N >= 4) halving_step<16, N / 2>(v, op);
+  if constexpr (N >= 8) halving_step<8, N / 4>(v, op);
+  if constexpr (N >= 16) halving_step<4, N / 8>(v, op);
+  if constexpr (N >= 32) halving_step<2, N / 16>(v, op);
+  if constexpr (N >= 64) halving_step<1, N / 32>(v, op);
+  // the value left in v[0] is this lane's share of value lane >> (6 - log2 N); the lanes that
+  // share those bits add their shares
+  T t = v[0];
+  if constexpr (N < 64) t = op(t, xor_lane<1>(t));
+  if constexpr (N < 32) t = op(t, xor_lane<2>(t));
+  if constexpr (N < 16) t = op(t, xor_lane<4>(t));
+  if constexpr (N < 8) t = op(t, xor_lane<8>(t));
+  if constexpr (N < 4) t = op(t, xor_lane<16>(t));
+  if constexpr (N < 2) t = op(t, xor_lane<32>(t));
+  return t;
 }
 
 struct RedScratch {
@@ -2436,6 +2457,7 @@ __global__ __launch_bounds__(kThreads) void k_small(const E* __restrict__ tgt,
                                                     const E* __restrict__ drf, Dims dm, Samp sp,
                                                     Workspace ws, Outs o) {
   constexpr int RMAX = kSmallRegs / L;
+  constexpr int SH = 6 - log2_pow2(RMAX);  // row r's wave total is in lanes r << SH, ...
   const int b = blockIdx.x, tid = threadIdx.x, lane = lane_id(), wv = wave_id();
   const int K = dm.K, R = dm.rows_per_seq;  // rows: target 0..K, then draft 0..K-1
   const float it = sp.inv_t;
@@ -2456,8 +2478,9 @@ __global__ __launch_bounds__(kThreads) void k_small(const E* __restrict__ tgt,
     for (int e = 0; e < L; ++e)
       z[r][e] = (r < R && e0 + e < dm.V) ? load_logit(row, e0 + e) : -INFINITY;
   }
-  // row maxima, then normalisers: fp32 over a thread's elements, fp64 across (fixed orders;
-  // rows past R hold -inf: they are reduced too, and never read)
+  // row maxima, then normalisers: fp32 over a thread's elements, fp64 across (fixed orders; the
+  // rows of a wave reduced together by recursive halving; rows past R hold -inf: they are
+  // reduced too, and never read)
   {
     float mx[RMAX];
 #pragma unroll
@@ -2466,10 +2489,8 @@ __global__ __launch_bounds__(kThreads) void k_small(const E* __restrict__ tgt,
 #pragma unroll
       for (int e = 0; e < L; ++e) mx[r] = fmaxf(mx[r], z[r][e]);
     }
-    wave_reduce_n(mx, [](float x, float y) { return fmaxf(x, y); });
-    if (lane == 0)
-#pragma unroll
-      for (int r = 0; r < RMAX; ++r) s_m[r][wv] = mx[r];
+    const float t = wave_reduce_halving(mx, [](float x, float y) { return fmaxf(x, y); });
+    if ((lane & ((1 << SH) - 1)) == 0) s_m[lane >> SH][wv] = t;
   }
   __syncthreads();
   // the logits at the draft tokens, from the thread holding them: row r is target row r
@@ -2499,10 +2520,8 @@ __global__ __launch_bounds__(kThreads) void k_small(const E* __restrict__ tgt,
       }
       sd[r] = (double)sv;
     }
-    wave_reduce_n(sd, [](double x, double y) { return x + y; });
-    if (lane == 0)
-#pragma unroll
-      for (int r = 0; r < RMAX; ++r) s_s[r][wv] = sd[r];
+    const double t = wave_reduce_halving(sd, [](double x, double y) { return x + y; });
+    if ((lane & ((1 << SH) - 1)) == 0) s_s[lane >> SH][wv] = t;
   }
   __syncthreads();
   if (tid < R) {
