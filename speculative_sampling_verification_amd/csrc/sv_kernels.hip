@@ -1584,18 +1584,52 @@ __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ 
   return n;
 }
 
-// The same with the statistics from the workspace.
+// The same with the statistics from the workspace, each lane's position's loaded once into
+// `ls` (lane k: target row k for k <= K, draft row k for k < K; positions past the first 64 are
+// loaded where the scan reaches them), so that the statistics of the final row pair come from
+// lane n (final_row_stats) instead of a further load after the scan.
+struct LaneStats {
+  RowStat t, d;
+};
+
 template <class E>
 __device__ int seq_accept_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
                                const Dims& dm, const Samp& sp, const Workspace& ws,
-                               const Outs& o, int b) {
+                               const Outs& o, int b, LaneStats& ls) {
+  const int l = lane_id(), K = dm.K;
+  if (l <= K) ls.t = ws.rstat[target_row(dm, b, l)];
+  if (l < K) ls.d = ws.rstat[draft_row(dm, b, l)];
   return seq_accept_wave(
-      tgt, drf, dm, sp, ws, o, b, [&](int r) { return ws.rstat[r]; },
+      tgt, drf, dm, sp, ws, o, b,
+      [&](int r) {
+        if (l <= K && r == target_row(dm, b, l)) return ls.t;
+        if (l < K && r == draft_row(dm, b, l)) return ls.d;
+        return ws.rstat[r];
+      },
       [&](int k, int x, float& zt, float& zd) {
         zt = load_logit(row_ptr(dm, tgt, drf, target_row(dm, b, k)), x);
         zd = load_logit(row_ptr(dm, tgt, drf, draft_row(dm, b, k)), x);
       },
       -2);
+}
+
+// Lane l's copy of a RowStat (l the same in every lane).
+__device__ __forceinline__ RowStat lane_rowstat(const RowStat& s, int l) {
+  typedef int i8 __attribute__((ext_vector_type(8)));
+  static_assert(sizeof(RowStat) == sizeof(i8), "RowStat is eight dwords");
+  const i8 v = __builtin_bit_cast(i8, s);
+  i8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = __builtin_amdgcn_readlane(v[j], l);
+  return __builtin_bit_cast(RowStat, r);
+}
+
+// The statistics of target row n and of the final draw's other row (draft row n, or target row
+// n again for the bonus draw), from the lanes of seq_accept_wave when n < 64.
+__device__ __forceinline__ void final_row_stats(const Dims& dm, const Workspace& ws, int b, int n,
+                                                const LaneStats& ls, RowStat& rt, RowStat& rd) {
+  rt = n < 64 ? lane_rowstat(ls.t, n) : ws.rstat[target_row(dm, b, n)];
+  rd = n >= dm.K ? rt : n < 64 ? lane_rowstat(ls.d, n) : ws.rstat[draft_row(dm, b, n)];
 }
 
 // A top-p target row's kept segments (bf16) hold every element at or above the candidate range's
@@ -1634,11 +1668,11 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
   __shared__ double s_w[kKeptCap];
   __shared__ double s_q[kKeptCap];
 
-  const int n = seq_accept_wave(tgt, drf, dm, sp, ws, o, b);
-
-  const RowStat rt = ws.rstat[target_row(dm, b, n)];
-  // the draft row of position n (the target row again for the bonus draw), loaded beside rt
-  const RowStat rd_n = ws.rstat[n < K ? draft_row(dm, b, n) : target_row(dm, b, n)];
+  LaneStats ls;
+  const int n = seq_accept_wave(tgt, drf, dm, sp, ws, o, b, ls);
+  // target row n, and the draft row of position n (the target row again for the bonus draw)
+  RowStat rt, rd_n;
+  final_row_stats(dm, ws, b, n, ls, rt, rd_n);
   SeqState st;
   st.n = n;
   st.need_dense = 0;
@@ -1653,12 +1687,8 @@ __global__ __launch_bounds__(kSeqThreads) void k_seq(const E* __restrict__ tgt,
     const int nk = rt.nkept;
     const uint2* kept = ws.kept + (size_t)target_row(dm, b, n) * kKeptCap;
     const bool resid = n < K;
-    RowStat rd;
-    const E* drow = nullptr;
-    if (resid) {
-      rd = ws.rstat[draft_row(dm, b, n)];
-      drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
-    }
+    const RowStat rd = rd_n;
+    const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
     for (int j = lane; j < nk; j += kSeqThreads) {
       const uint2 e = kept[j];
       const double q = (double)fast_exp((__uint_as_float(e.y) - rt.m) * it) / rt.S;
@@ -3542,18 +3572,13 @@ __device__ int draw_small_wave(int nk, uint32_t ie, float zt, float zd, const Ro
 template <class E>
 __device__ int final_draw_compact_wave(const E* __restrict__ tgt, const E* __restrict__ drf,
                                        const Dims& dm, const Samp& sp, const Workspace& ws, int b,
-                                       int n, double u, uint32_t* s_idx, double* s_w) {
+                                       int n, const RowStat& rt, const RowStat& rd, double u,
+                                       uint32_t* s_idx, double* s_w) {
   const int lane = lane_id();
-  const RowStat rt = ws.rstat[target_row(dm, b, n)];
   const int nk = rt.nkept;
   const uint2* kept = ws.kept + (size_t)target_row(dm, b, n) * kKeptCap;
   const bool resid = n < dm.K;
-  RowStat rd = rt;
-  const E* drow = nullptr;
-  if (resid) {
-    rd = ws.rstat[draft_row(dm, b, n)];
-    drow = row_ptr(dm, tgt, drf, draft_row(dm, b, n));
-  }
+  const E* drow = resid ? row_ptr(dm, tgt, drf, draft_row(dm, b, n)) : nullptr;
   const float it = sp.inv_t;
   if (nk <= 64) {
     uint32_t ie = 0xFFFFFFFFu;
@@ -4189,8 +4214,10 @@ __global__ __launch_bounds__(kThreads) void k_seq_compact(const E* __restrict__ 
     }
   }
   if (wave_id() == 0) {
-    const int n = seq_accept_wave<E>(tgt, drf, dm, sp, ws, o, b);
-    const RowStat rt = ws.rstat[target_row(dm, b, n)];
+    LaneStats ls;
+    const int n = seq_accept_wave<E>(tgt, drf, dm, sp, ws, o, b, ls);
+    RowStat rt, rd;
+    final_row_stats(dm, ws, b, n, ls, rt, rd);
     if (lane_id() == 0) {
       s_n = n;
       s_kind = rt.kind;
@@ -4201,7 +4228,8 @@ __global__ __launch_bounds__(kThreads) void k_seq_compact(const E* __restrict__ 
       const int tok = mentor_draw_wave<E>(tgt, drf, dm, sp, ws, b, n, sol, u, s_idx, s_w);
       if (lane_id() == 0) o.tokens[(size_t)b * (K + 1) + n] = tok;
     } else if (rt.kind == kRowCompact) {
-      const int tok = final_draw_compact_wave<E>(tgt, drf, dm, sp, ws, b, n, u, s_idx, s_w);
+      const int tok =
+          final_draw_compact_wave<E>(tgt, drf, dm, sp, ws, b, n, rt, rd, u, s_idx, s_w);
       if (lane_id() == 0) o.tokens[(size_t)b * (K + 1) + n] = tok;
     }
   }
